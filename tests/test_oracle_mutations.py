@@ -1,0 +1,111 @@
+"""Planted mistakes in the oracle must trip at least one pin (CPU only).
+
+Each case monkeypatches one plausible mistake into ``oracle`` (a dropped term,
+a wrong sign, a transposed operand, a wrong index) and re-runs the pin tests
+that should catch it.  A mutation that no pin catches fails this file.
+"""
+import numpy as np
+import pytest
+
+from oracle import sol_attn as sa
+from oracle import sol_attn2 as s2
+import test_oracle_sol_attn as p1
+import test_oracle_sol_attn2 as p2
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, ValueError):
+        return True
+    return False
+
+
+def _wrap_attend(**override):
+    orig = sa.attend_query_block
+
+    def attend(q, k, v, i, sel_row, kbar, vsum, counts, scale, block=64, approx=True):
+        kw = dict(q=q, k=k, v=v, i=i, sel_row=sel_row, kbar=kbar, vsum=vsum, counts=counts,
+                  scale=scale, block=block, approx=approx)
+        kw.update({key: f(kw) for key, f in override.items()})
+        return orig(**kw)
+    return attend
+
+
+MUTATIONS_SOL1 = {
+    # numerator uses the V mean instead of the V sum
+    "vmean_not_vsum": lambda mp: mp.setattr(sa, "block_sums", sa.block_means),
+    # denominator drops the block count n_j
+    "no_count_in_denominator": lambda mp: mp.setattr(
+        sa, "attend_query_block", _wrap_attend(counts=lambda kw: np.ones_like(kw["counts"]))),
+    # output logits without the 1/sqrt(d) scale
+    "unscaled_logits": lambda mp: mp.setattr(sa, "attend_query_block", _wrap_attend(scale=lambda kw: 1.0)),
+    # threshold sign flipped: mu - beta sigma
+    "threshold_sign": lambda mp: mp.setattr(
+        sa, "diag_threshold",
+        (lambda f: (lambda qb, kb, beta, sc: f(qb, kb, -beta, sc)))(sa.diag_threshold)),
+    # proxy scores transposed (key block x query block)
+    "transposed_proxy": lambda mp: mp.setattr(
+        sa, "proxy_scores", (lambda f: (lambda qb, kb, sc: f(qb, kb, sc).T))(sa.proxy_scores)),
+    # diagonal estimator forgets to subtract mu_K^2
+    "variance_no_centering": lambda mp: mp.setattr(
+        sa, "diag_threshold",
+        lambda qb, kb, beta, sc: (lambda mu, var: (mu + beta * np.sqrt(var), mu, np.sqrt(var)))(
+            (qb @ kb.mean(0)) * sc, ((qb * qb) @ (kb * kb).mean(0)) * sc * sc)),
+    # sink block range off by one at the end
+    "sink_off_by_one": lambda mp: mp.setattr(
+        sa, "sink_block_mask",
+        (lambda f: (lambda n, s, t, block=64: np.roll(f(n, s, t, block), 1)))(sa.sink_block_mask)),
+}
+
+PINS_SOL1 = [
+    (p1.test_whole_sequence_sink_is_dense, (333, 32)),
+    (p1.test_mean_key_replacement_identity, (1.0, None)),
+    (p1.test_mean_key_replacement_identity, (1.5, (0, 70))),
+    (p1.test_one_hot_routing_selects_the_matching_block, ()),
+    (p1.test_sink_block_ranges, ()),
+    (p1.test_matches_scalar_loop_brute_force, (200, 16, 0.3, "diag", (70, 20))),
+    (p1.test_matches_scalar_loop_brute_force, (200, 8, 1.0, "diag", (None, 0))),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_SOL1))
+def test_sol_attn_mutation_is_caught(name, monkeypatch):
+    MUTATIONS_SOL1[name](monkeypatch)
+    assert any(_fails(fn, *args) for fn, args in PINS_SOL1), f"mutation {name} not caught"
+
+
+def _tail_mutation(kind):
+    orig = s2.tail_stats
+
+    def tail(qbar_a, groups, scale):
+        if kind == "no_group_count":
+            groups = [(m, 1.0, kb, vb) for (m, n, kb, vb) in groups]
+        ln_z, mu, nu = orig(qbar_a, groups, scale)
+        if kind == "mu_sign":
+            mu = -mu
+        if kind == "swap_mu_nu":
+            mu, nu = nu, mu
+        return ln_z, mu, nu
+    return tail
+
+
+MUTATIONS_SOL2 = {
+    "no_group_count": lambda mp: mp.setattr(s2, "tail_stats", _tail_mutation("no_group_count")),
+    "delta_sign": lambda mp: mp.setattr(s2, "tail_stats", _tail_mutation("mu_sign")),
+    "swap_mu_nu": lambda mp: mp.setattr(s2, "tail_stats", _tail_mutation("swap_mu_nu")),
+}
+
+PINS_SOL2 = [
+    (p2.test_singleton_groups_and_constant_anchor_queries_are_dense, ()),
+    (p2.test_anchor_one_whole_block_groups_reduce_to_sol_attn, (1.0, (None, 0))),
+    (p2.test_extra_biased_key_form, (False,)),
+    (p2.test_log_partition_gradient_is_mu_over_sqrt_d, ()),
+    (p2.test_matches_scalar_loop_brute_force, (200, 8, 1.0, "split2", (None, 0))),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_SOL2))
+def test_sol_attn2_mutation_is_caught(name, monkeypatch):
+    MUTATIONS_SOL2[name](monkeypatch)
+    assert any(_fails(fn, *args) for fn, args in PINS_SOL2), f"mutation {name} not caught"
