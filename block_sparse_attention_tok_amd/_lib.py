@@ -1,0 +1,260 @@
+"""ctypes binding of libsolattn (argument marshalling only).
+
+Every step of the Sol-Attn path runs in the library's HIP kernels; this module
+only turns torch tensors into device pointers, allocates the caller-owned
+workspace with torch, and raises on a non-OK status.  It never falls back to
+another implementation: if the shared library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsolattn.so")
+
+SOL_OK = 0
+SOL_VARIANT_SOL1 = 1
+SOL_VARIANT_SOL2 = 2
+THRESH = {"diag": 0, "exact": 1}
+
+EXPORTED = [
+    "sol_status_string", "sol_attn_validate", "sol_attn_workspace_bytes", "sol_attn_workspace_layout",
+    "sol_attn", "sol_attn_prepare", "sol_attn_fused", "sol_attn_debug_routing",
+    "sol_attn2", "sol_attn2_prepare", "sol_attn2_fused", "sol_attn2_debug_routing",
+]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov",
+        "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi")]
+
+
+class SolAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib().sol_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsolattn.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not found: build it with `python -m block_sparse_attention_tok_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, f32, i32, vp, sz = ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.sol_status_string.argtypes = [i32]
+    L.sol_status_string.restype = ctypes.c_char_p
+    L.sol_attn_validate.argtypes = [i64, i64, i64, i64, f32, i64, i64, i32]
+    L.sol_attn_validate.restype = i32
+    L.sol_attn_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
+    L.sol_attn_workspace_bytes.restype = sz
+    L.sol_attn_workspace_layout.argtypes = [i32, i64, i64, i64, i64, ctypes.POINTER(WsLayout)]
+    L.sol_attn_workspace_layout.restype = i32
+    full = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp]
+    for name in ("sol_attn", "sol_attn2"):
+        getattr(L, name).argtypes = full
+        getattr(L, name).restype = i32
+    prep = [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp, sz, vp]
+    for name in ("sol_attn_prepare", "sol_attn2_prepare"):
+        getattr(L, name).argtypes = prep
+        getattr(L, name).restype = i32
+    fused = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
+    for name in ("sol_attn_fused", "sol_attn2_fused"):
+        getattr(L, name).argtypes = fused
+        getattr(L, name).restype = i32
+    dbg = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp, vp]
+    for name in ("sol_attn_debug_routing", "sol_attn2_debug_routing"):
+        getattr(L, name).argtypes = dbg
+        getattr(L, name).restype = i32
+    _LIB = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != SOL_OK:
+        raise SolAttnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _sink_start(s: Optional[int]) -> int:
+    return -1 if s is None else int(s)
+
+
+def _check_tensors(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [batch, tokens, heads, 128]")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [batch, tokens, heads, 128]")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor")
+    if k.shape != q.shape or v.shape != q.shape or k.device != q.device or v.device != q.device:
+        raise ValueError("k and v must have the same shape and device as q")
+
+
+def workspace_bytes(variant: int, batch: int, tokens: int, heads: int, head_dim: int = 128) -> int:
+    n = lib().sol_attn_workspace_bytes(variant, batch, tokens, heads, head_dim)
+    if n == 0:
+        st = lib().sol_attn_validate(batch, tokens, heads, head_dim, 1.0, -1, 0, 0)
+        _check(st if st != SOL_OK else 2, "sol_attn_workspace_bytes")
+    return int(n)
+
+
+def workspace_layout(variant: int, batch: int, tokens: int, heads: int, head_dim: int = 128) -> WsLayout:
+    L = WsLayout()
+    _check(lib().sol_attn_workspace_layout(variant, batch, tokens, heads, head_dim, ctypes.byref(L)),
+           "sol_attn_workspace_layout")
+    return L
+
+
+def alloc_workspace(variant: int, q: torch.Tensor) -> torch.Tensor:
+    B, N, H, D = q.shape
+    return torch.empty(workspace_bytes(variant, B, N, H, D), dtype=torch.uint8, device=q.device)
+
+
+def validate(batch: int, tokens: int, heads: int, head_dim: int, tau: float, sink_start: Optional[int],
+             sink_tokens: int, thresh: str = "diag") -> int:
+    """Host-only contract check; returns the status code (0 = ok)."""
+    if thresh not in THRESH:
+        return 8
+    return lib().sol_attn_validate(batch, tokens, heads, head_dim, float(tau), _sink_start(sink_start),
+                                   int(sink_tokens), THRESH[thresh])
+
+
+def _full_call(fn_name: str, variant: int, q, k, v, tau, sink_start, sink_tokens, thresh, out, workspace):
+    _check_tensors(q, k, v)
+    if thresh not in THRESH:
+        raise ValueError("thresh must be 'diag' or 'exact'")
+    if not math.isfinite(float(tau)):
+        raise ValueError("tau must be finite")
+    B, N, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(variant, q)
+    st = getattr(lib(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, float(tau),
+                                 _sink_start(sink_start), int(sink_tokens), THRESH[thresh], _ptr(workspace),
+                                 workspace.numel(), _stream(q.device))
+    _check(st, fn_name)
+    return out
+
+
+def sol_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
+             sink_start: Optional[int] = None, sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sol-Attn forward on contiguous bf16 [batch, tokens, heads, 128] GPU tensors.
+
+    tau: threshold coefficient (higher selects fewer KV blocks; 0 is not dense).
+    sink_start None with sink_tokens > 0 keeps the last sink_tokens tokens exact.
+    """
+    return _full_call("sol_attn", SOL_VARIANT_SOL1, q, k, v, tau, sink_start, sink_tokens, thresh, out, workspace)
+
+
+def sol_attn2(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
+              sink_start: Optional[int] = None, sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sol-Attn2 forward (FP8 Q/K, complementary tail) on the same tensor contract."""
+    return _full_call("sol_attn2", SOL_VARIANT_SOL2, q, k, v, tau, sink_start, sink_tokens, thresh, out, workspace)
+
+
+def prepare(variant: int, q, k, v, tau: float, workspace: torch.Tensor, thresh: str = "diag"):
+    """Stage 1 (summaries + threshold [+ Sol-Attn2 quantization and groups]) into `workspace`."""
+    _check_tensors(q, k, v)
+    B, N, H, D = q.shape
+    name = "sol_attn_prepare" if variant == SOL_VARIANT_SOL1 else "sol_attn2_prepare"
+    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), B, N, H, D, float(tau), THRESH[thresh],
+                                _ptr(workspace), workspace.numel(), _stream(q.device)), name)
+
+
+def fused(variant: int, q, k, v, out, workspace: torch.Tensor, sink_start: Optional[int] = None,
+          sink_tokens: int = 0):
+    """Stage 2 (the fused kernel) reading a workspace prepared for the same inputs."""
+    B, N, H, D = q.shape
+    name = "sol_attn_fused" if variant == SOL_VARIANT_SOL1 else "sol_attn2_fused"
+    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
+                                int(sink_tokens), _ptr(workspace), workspace.numel(), _stream(q.device)), name)
+
+
+def debug_routing(variant: int, q, k, v, tau: float = 1.0, thresh: str = "diag", sink_start: Optional[int] = None,
+                  sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Run the full call and return (out, masks [B, H, nb, nb] bool on the CPU, workspace).
+
+    The masks are the decisions the fused kernel itself made (test export)."""
+    _check_tensors(q, k, v)
+    B, N, H, D = q.shape
+    nb = (N + 63) // 64
+    nbw = (nb + 63) // 64
+    if workspace is None:
+        workspace = alloc_workspace(variant, q)
+    words = torch.zeros(B * H * nb * nbw, dtype=torch.int64, device=q.device)
+    name = "sol_attn_debug_routing" if variant == SOL_VARIANT_SOL1 else "sol_attn2_debug_routing"
+    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, float(tau),
+                                _sink_start(sink_start), int(sink_tokens), THRESH[thresh], _ptr(workspace),
+                                workspace.numel(), _ptr(words), _stream(q.device)), name)
+    w = words.view(B, H, nb, nbw).cpu()
+    bits = torch.arange(64, dtype=torch.int64)
+    m = ((w.unsqueeze(-1) >> bits) & 1).bool().reshape(B, H, nb, nbw * 64)[..., :nb]
+    return out, m, workspace
+
+
+def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: int, heads: int) -> dict:
+    """Typed views of the workspace arrays (for tests)."""
+    L = workspace_layout(variant, batch, tokens, heads)
+    nbp = L.nbp
+    bh = batch * heads
+
+    def view(off, dtype, shape):
+        if off < 0:
+            return None
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return workspace[off:off + nbytes].view(dtype).view(*shape)
+
+    d = dict(
+        nb=L.nb, nbp=nbp,
+        qbar=view(L.qbar, torch.float32, (batch, heads, nbp, 128)),
+        kbar_t=view(L.kbar_t, torch.float32, (batch, heads, 32, nbp, 4)),
+        kbar_h=view(L.kbar_h, torch.bfloat16, (batch, heads, nbp, 128)),
+        vbar_h=view(L.vbar_h, torch.bfloat16, (batch, heads, nbp, 128)),
+        tau_i=view(L.tau_i, torch.float32, (batch, heads, nbp)),
+        kstat=view(L.kstat, torch.float32, (batch, heads, 2, 128)),
+        kcov=view(L.kcov, torch.float32, (batch, heads, 128, 128)),
+    )
+    if variant == SOL_VARIANT_SOL2:
+        tp = nbp * 64
+        d.update(
+            q8=view(L.q8, torch.uint8, (batch, heads, tp, 128)),
+            k8=view(L.k8, torch.uint8, (batch, heads, tp, 128)),
+            qscale=view(L.qscale, torch.float32, (batch, heads, nbp)),
+            kscale=view(L.kscale, torch.float32, (batch, heads, nbp)),
+            qhat=view(L.qhat, torch.float32, (batch, heads, 128)),
+            gk=view(L.gk, torch.bfloat16, (batch, heads, nbp, 2, 128)),
+            gv=view(L.gv, torch.bfloat16, (batch, heads, nbp, 2, 128)),
+            glogn=view(L.glogn, torch.float32, (batch, heads, nbp, 2)),
+            ghi=view(L.ghi, torch.int64, (batch, heads, nbp)),
+        )
+    del bh
+    return d

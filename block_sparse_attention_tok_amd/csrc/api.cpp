@@ -1,0 +1,285 @@
+// C-ABI entry points of libsolattn: host-side validation, workspace layout and
+// launch sequencing.  Declarations and argument documentation: include/solattn.h.
+#include "../../include/solattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kBlock = 64;
+constexpr int64_t kDim = 128;
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+int check_shape(int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim) {
+  if (batch < 1 || tokens < 1 || heads < 1) return SOL_ERR_SHAPE;
+  if (head_dim != kDim) return SOL_ERR_HEAD_DIM;
+  // element offsets and grid sizes stay inside 32-bit block counts / 64-bit offsets
+  const int64_t nb = (tokens + kBlock - 1) / kBlock;
+  if (tokens >= kMaxIndex || heads >= 65536 || batch >= 65536) return SOL_ERR_SHAPE;
+  if (batch * heads * nb >= kMaxIndex) return SOL_ERR_SHAPE;
+  return SOL_OK;
+}
+
+int sink_range(int64_t tokens, int64_t sink_start, int64_t sink_tokens, int* b0, int* b1) {
+  *b0 = 1;
+  *b1 = 0;                                    // empty range
+  if (sink_tokens < 0) return SOL_ERR_SINK;
+  if (sink_tokens == 0) return SOL_OK;
+  const int64_t s = sink_start < 0 ? tokens - sink_tokens : sink_start;
+  if (s < 0 || s + sink_tokens > tokens) return SOL_ERR_SINK;
+  *b0 = (int)(s / kBlock);
+  *b1 = (int)((s + sink_tokens - 1) / kBlock);
+  return SOL_OK;
+}
+
+int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim, sol_ws_layout* L) {
+  int st = check_shape(batch, tokens, heads, head_dim);
+  if (st != SOL_OK) return st;
+  if (variant != SOL_VARIANT_SOL1 && variant != SOL_VARIANT_SOL2) return SOL_ERR_ARG;
+  std::memset(L, 0xff, sizeof(*L));          // every offset -1
+  const int64_t nb = (tokens + kBlock - 1) / kBlock;
+  const int64_t nbp = (nb + 63) / 64 * 64;
+  const int64_t bh = batch * heads;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align256(off + bytes); return o; };
+  L->nb = nb;
+  L->nbp = nbp;
+  L->qbar = take(bh * nbp * kDim * 4);
+  L->kbar_t = take(bh * nbp * kDim * 4);
+  L->kbar_h = take(bh * nbp * kDim * 2);
+  L->vbar_h = take(bh * nbp * kDim * 2);
+  L->tau_i = take(bh * nbp * 4);
+  L->kstat = take(bh * 2 * kDim * 4);
+  L->kcov = take(bh * kDim * kDim * 4);
+  if (variant == SOL_VARIANT_SOL2) {
+    const int64_t tp = nbp * kBlock;
+    L->q8 = take(bh * tp * kDim);
+    L->k8 = take(bh * tp * kDim);
+    L->qscale = take(bh * nbp * 4);
+    L->kscale = take(bh * nbp * 4);
+    L->qhat = take(bh * kDim * 4);
+    L->gk = take(bh * nbp * 2 * kDim * 2);
+    L->gv = take(bh * nbp * 2 * kDim * 2);
+    L->glogn = take(bh * nbp * 2 * 4);
+    L->ghi = take(bh * nbp * 8);
+  }
+  L->total_bytes = off;
+  return SOL_OK;
+}
+
+solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
+  char* base = (char*)ws;
+  auto at = [&](int64_t o) -> char* { return o < 0 ? nullptr : base + o; };
+  solattn::Workspace w;
+  w.nb = (int)L.nb;
+  w.nbp = (int)L.nbp;
+  w.qbar = (float*)at(L.qbar);
+  w.kbar_t = (float*)at(L.kbar_t);
+  w.kbar_h = (uint16_t*)at(L.kbar_h);
+  w.vbar_h = (uint16_t*)at(L.vbar_h);
+  w.tau_i = (float*)at(L.tau_i);
+  w.kstat = (float*)at(L.kstat);
+  w.kcov = (float*)at(L.kcov);
+  w.q8 = (uint8_t*)at(L.q8);
+  w.k8 = (uint8_t*)at(L.k8);
+  w.qscale = (float*)at(L.qscale);
+  w.kscale = (float*)at(L.kscale);
+  w.qhat = (float*)at(L.qhat);
+  w.gk = (uint16_t*)at(L.gk);
+  w.gv = (uint16_t*)at(L.gv);
+  w.glogn = (float*)at(L.glogn);
+  w.ghi = (uint64_t*)at(L.ghi);
+  return w;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Common argument checks; fills the layout on success.
+int prologue(int variant, const void* q, const void* k, const void* v, int64_t batch, int64_t tokens,
+             int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes, sol_ws_layout* L) {
+  if (!q || !k || !v || !workspace) return SOL_ERR_NULL;
+  int st = layout(variant, batch, tokens, heads, head_dim, L);
+  if (st != SOL_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || ((uintptr_t)workspace & 255)) return SOL_ERR_ARG;
+  if ((int64_t)workspace_bytes < L->total_bytes) return SOL_ERR_WORKSPACE;
+  return SOL_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SOL_OK : SOL_ERR_HIP; }
+
+solattn::Shape shape_of(int64_t batch, int64_t tokens, int64_t heads) {
+  return solattn::Shape{(int)batch, (int)tokens, (int)heads};
+}
+
+int check_thresh(int thresh) { return (thresh == SOL_THRESH_DIAG || thresh == SOL_THRESH_EXACT) ? SOL_OK : SOL_ERR_ARG; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sol_status_string(int status) {
+  switch (status) {
+    case SOL_OK: return "ok";
+    case SOL_ERR_NULL: return "null pointer argument";
+    case SOL_ERR_SHAPE: return "invalid shape (batch, tokens and heads must be >= 1 and fit the index range)";
+    case SOL_ERR_HEAD_DIM: return "head_dim must be 128";
+    case SOL_ERR_TAU: return "tau must be finite";
+    case SOL_ERR_SINK: return "sink range must lie inside [0, tokens) and sink_tokens must be >= 0";
+    case SOL_ERR_WORKSPACE: return "workspace smaller than sol_attn_workspace_bytes()";
+    case SOL_ERR_HIP: return "HIP runtime or kernel launch error";
+    case SOL_ERR_ARG: return "invalid argument (threshold type, variant or pointer alignment)";
+    default: return "unknown status";
+  }
+}
+
+int sol_attn_validate(int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim, float tau,
+                      int64_t sink_start, int64_t sink_tokens, int thresh) {
+  int st = check_shape(batch, tokens, heads, head_dim);
+  if (st != SOL_OK) return st;
+  if (!std::isfinite(tau)) return SOL_ERR_TAU;
+  int b0, b1;
+  st = sink_range(tokens, sink_start, sink_tokens, &b0, &b1);
+  if (st != SOL_OK) return st;
+  return check_thresh(thresh);
+}
+
+size_t sol_attn_workspace_bytes(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim) {
+  sol_ws_layout L;
+  if (layout(variant, batch, tokens, heads, head_dim, &L) != SOL_OK) return 0;
+  return (size_t)L.total_bytes;
+}
+
+int sol_attn_workspace_layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                              sol_ws_layout* out) {
+  if (!out) return SOL_ERR_NULL;
+  return layout(variant, batch, tokens, heads, head_dim, out);
+}
+
+int sol_attn_prepare(const void* q, const void* k, const void* v, int64_t batch, int64_t tokens, int64_t heads,
+                     int64_t head_dim, float tau, int thresh, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  sol_ws_layout L;
+  int st = prologue(SOL_VARIANT_SOL1, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  if (st != SOL_OK) return st;
+  if (!std::isfinite(tau)) return SOL_ERR_TAU;
+  if ((st = check_thresh(thresh)) != SOL_OK) return st;
+  solattn::Workspace w = resolve(L, workspace);
+  solattn::Shape s = shape_of(batch, tokens, heads);
+  hipStream_t hs = (hipStream_t)stream;
+  st = hip_status(solattn::launch_summary((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s, w, hs));
+  if (st != SOL_OK) return st;
+  return hip_status(solattn::launch_threshold(s, w, tau, thresh == SOL_THRESH_EXACT, hs));
+}
+
+static int fused_common(int variant, const void* q, const void* k, const void* v, void* out, int64_t batch,
+                        int64_t tokens, int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens,
+                        void* workspace, size_t workspace_bytes, uint64_t* mask_bits, void* stream,
+                        bool out_required) {
+  sol_ws_layout L;
+  int st = prologue(variant, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  if (st != SOL_OK) return st;
+  if (out_required && !out) return SOL_ERR_NULL;
+  if (out && !aligned16(out)) return SOL_ERR_ARG;
+  int b0, b1;
+  if ((st = sink_range(tokens, sink_start, sink_tokens, &b0, &b1)) != SOL_OK) return st;
+  solattn::Workspace w = resolve(L, workspace);
+  solattn::Shape s = shape_of(batch, tokens, heads);
+  if (variant == SOL_VARIANT_SOL1)
+    return hip_status(solattn::launch_fused((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                            (uint16_t*)out, s, w, b0, b1, mask_bits, (hipStream_t)stream));
+  return hip_status(solattn::launch_fused2((const uint16_t*)v, (uint16_t*)out, s, w, b0, b1, mask_bits,
+                                           (hipStream_t)stream));
+}
+
+int sol_attn_fused(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                   int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return fused_common(SOL_VARIANT_SOL1, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
+                      workspace, workspace_bytes, nullptr, stream, true);
+}
+
+int sol_attn(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens, int64_t heads,
+             int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens, int thresh, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  if (!out) return SOL_ERR_NULL;
+  int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
+  if (st != SOL_OK) return st;
+  st = sol_attn_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);
+  if (st != SOL_OK) return st;
+  return sol_attn_fused(q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens, workspace,
+                        workspace_bytes, stream);
+}
+
+int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                           int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens,
+                           int thresh, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
+                           void* stream) {
+  if (!mask_bits) return SOL_ERR_NULL;
+  int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
+  if (st != SOL_OK) return st;
+  st = sol_attn_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);
+  if (st != SOL_OK) return st;
+  return fused_common(SOL_VARIANT_SOL1, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
+                      workspace, workspace_bytes, mask_bits, stream, false);
+}
+
+int sol_attn2_prepare(const void* q, const void* k, const void* v, int64_t batch, int64_t tokens, int64_t heads,
+                      int64_t head_dim, float tau, int thresh, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  sol_ws_layout L;
+  int st = prologue(SOL_VARIANT_SOL2, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  if (st != SOL_OK) return st;
+  if (!std::isfinite(tau)) return SOL_ERR_TAU;
+  if ((st = check_thresh(thresh)) != SOL_OK) return st;
+  solattn::Workspace w = resolve(L, workspace);
+  solattn::Shape s = shape_of(batch, tokens, heads);
+  hipStream_t hs = (hipStream_t)stream;
+  st = hip_status(solattn::launch_quant_summary((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s, w, hs));
+  if (st != SOL_OK) return st;
+  st = hip_status(solattn::launch_threshold(s, w, tau, thresh == SOL_THRESH_EXACT, hs));
+  if (st != SOL_OK) return st;
+  st = hip_status(solattn::launch_qhat(s, w, hs));
+  if (st != SOL_OK) return st;
+  return hip_status(solattn::launch_groups((const uint16_t*)v, s, w, hs));
+}
+
+int sol_attn2_fused(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                    int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return fused_common(SOL_VARIANT_SOL2, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
+                      workspace, workspace_bytes, nullptr, stream, true);
+}
+
+int sol_attn2(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens, int64_t heads,
+              int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens, int thresh, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (!out) return SOL_ERR_NULL;
+  int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
+  if (st != SOL_OK) return st;
+  st = sol_attn2_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);
+  if (st != SOL_OK) return st;
+  return sol_attn2_fused(q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens, workspace,
+                         workspace_bytes, stream);
+}
+
+int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                            int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens,
+                            int thresh, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
+                            void* stream) {
+  if (!mask_bits) return SOL_ERR_NULL;
+  int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
+  if (st != SOL_OK) return st;
+  st = sol_attn2_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);
+  if (st != SOL_OK) return st;
+  return fused_common(SOL_VARIANT_SOL2, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
+                      workspace, workspace_bytes, mask_bits, stream, false);
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal launcher declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+// Workspace pointers resolved from the byte layout (see include/solattn.h).
+struct Workspace {
+  int nb, nbp;
+  float* qbar;      // [B][H][nbp][128]
+  float* kbar_t;    // [B][H][32][nbp][4]
+  uint16_t* kbar_h; // [B][H][nbp][128] bf16
+  uint16_t* vbar_h; // [B][H][nbp][128] bf16
+  float* tau_i;     // [B][H][nbp]
+  float* kstat;     // [B][H][2][128]
+  float* kcov;      // [B][H][128][128]
+  uint8_t* q8;      // [B][H][tp][128]
+  uint8_t* k8;
+  float* qscale;    // [B][H][nbp]
+  float* kscale;
+  float* qhat;      // [B][H][128]
+  uint16_t* gk;     // [B][H][nbp][2][128] bf16
+  uint16_t* gv;
+  float* glogn;     // [B][H][nbp][2]
+  uint64_t* ghi;    // [B][H][nbp]
+};
+
+struct Shape {
+  int B, N, H;
+};
+
+// Sol-Attn stage 1: block means / sums.
+hipError_t launch_summary(const uint16_t* q, const uint16_t* k, const uint16_t* v, Shape s,
+                          const Workspace& ws, hipStream_t stream);
+// Key statistics and per-query-block thresholds (diag or exact).
+hipError_t launch_threshold(Shape s, const Workspace& ws, float tau, int exact, hipStream_t stream);
+// Sol-Attn stage 2: fused routing + proxy reuse + exact attention.
+hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                        Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* mask_out,
+                        hipStream_t stream);
+
+// Sol-Attn2 stage 1: FP8 quantization of Q/K with block means of the dequantized values
+// and V block means; then the mean-query direction and key groups.
+hipError_t launch_quant_summary(const uint16_t* q, const uint16_t* k, const uint16_t* v, Shape s,
+                                const Workspace& ws, hipStream_t stream);
+hipError_t launch_qhat(Shape s, const Workspace& ws, hipStream_t stream);
+hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream);
+// Sol-Attn2 stage 2.
+hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws,
+                         int sink_b0, int sink_b1, uint64_t* mask_out, hipStream_t stream);
+
+}  // namespace solattn

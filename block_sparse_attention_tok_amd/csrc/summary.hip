@@ -1,0 +1,196 @@
+// Block summaries and the per-query-block threshold (Sol-Attn stage 1).
+//
+// Sol-Attn paper (arXiv 2607.24027) §3.2 "Hardware-Aligned Implementation":
+// the fused kernel streams pooled keys KC[j] = K-bar_j (block means) and
+// summed values VC[j] = V-hat_j; §2 Eq. (3) pools queries the same way.  §3.1
+// Eqs. (4)-(5) and the appendix "Diagonal threshold estimator" give
+// tau_i = mu_i + beta sigma_i from statistics of the pooled keys; §4.5 keeps
+// only this threshold computation outside the attention kernel.
+#include "common.h"
+#include "kernels.h"
+
+namespace solattn {
+
+// One workgroup per (64-token block j < nbp, batch b).  In BTHD the block's
+// rows for every head form one contiguous span of 64 * H * 256 bytes, so the
+// reads are fully coalesced 16-byte loads; each thread owns 8 dims of one head
+// (a 16-byte column chunk) and sums a subset of the block's tokens in fp32.
+__global__ __launch_bounds__(256) void summary_kernel(
+    const uint4v* __restrict__ q, const uint4v* __restrict__ k, const uint4v* __restrict__ v,
+    int N, int H, int nb, int nbp, float* __restrict__ qbar, float* __restrict__ kbar_t,
+    uint4v* __restrict__ kbar_h, uint4v* __restrict__ vbar_h) {
+  extern __shared__ float red[];
+  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int C = 16 * H;                                 // 16-byte chunks per token row
+  const int R = C >= 256 ? 1 : 256 / C;                 // token groups per chunk
+  const int t0 = j * kBlock;
+  const int n = j < nb ? min(kBlock, N - t0) : 0;
+  const float inv_n = n > 0 ? 1.0f / (float)n : 0.0f;
+  const size_t rowc = (size_t)C;                        // chunks per token row
+  const size_t base = ((size_t)b * N + t0) * rowc;
+
+  for (int cbase = 0; cbase < C; cbase += (R == 1 ? 256 : C)) {
+    const int r = R == 1 ? 0 : tid / C;
+    const int c = R == 1 ? cbase + tid : tid % C;
+    const bool active = (R == 1 ? c < C : r < R);
+    float qs[8], ks[8], vs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qs[e] = ks[e] = vs[e] = 0.f;
+    if (active) {
+#pragma unroll 4
+      for (int t = r; t < n; t += R) {
+        const size_t off = base + (size_t)t * rowc + c;
+        uint4v a = q[off], bb = k[off], cc = v[off];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          qs[2 * m] += bf16_lo(a[m]);  qs[2 * m + 1] += bf16_hi(a[m]);
+          ks[2 * m] += bf16_lo(bb[m]); ks[2 * m + 1] += bf16_hi(bb[m]);
+          vs[2 * m] += bf16_lo(cc[m]); vs[2 * m + 1] += bf16_hi(cc[m]);
+        }
+      }
+    }
+    if (R > 1) {
+      if (active) {
+        float* p = red + ((size_t)r * C + c) * 24;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { p[e] = qs[e]; p[8 + e] = ks[e]; p[16 + e] = vs[e]; }
+      }
+      __syncthreads();
+      if (r == 0 && active) {
+        for (int rr = 1; rr < R; ++rr) {
+          const float* p = red + ((size_t)rr * C + c) * 24;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { qs[e] += p[e]; ks[e] += p[8 + e]; vs[e] += p[16 + e]; }
+        }
+      }
+    }
+    if (active && r == 0) {
+      const int h = c / 16, d8 = c % 16;
+      const size_t bh = (size_t)b * H + h;
+      float4* qo = (float4*)(qbar + (bh * nbp + j) * kDim + 8 * d8);
+      qo[0] = make_float4(qs[0] * inv_n, qs[1] * inv_n, qs[2] * inv_n, qs[3] * inv_n);
+      qo[1] = make_float4(qs[4] * inv_n, qs[5] * inv_n, qs[6] * inv_n, qs[7] * inv_n);
+      float kb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kb[e] = ks[e] * inv_n;
+      float4* kt = (float4*)kbar_t;
+      kt[(bh * 32 + 2 * d8) * nbp + j] = make_float4(kb[0], kb[1], kb[2], kb[3]);
+      kt[(bh * 32 + 2 * d8 + 1) * nbp + j] = make_float4(kb[4], kb[5], kb[6], kb[7]);
+      uint4v kh, vh;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        kh[m] = pack_bf16x2(kb[2 * m], kb[2 * m + 1]);
+        vh[m] = pack_bf16x2(vs[2 * m] * inv_n, vs[2 * m + 1] * inv_n);
+      }
+      kbar_h[(bh * nbp + j) * 16 + d8] = kh;
+      vbar_h[(bh * nbp + j) * 16 + d8] = vh;
+    }
+  }
+}
+
+hipError_t launch_summary(const uint16_t* q, const uint16_t* k, const uint16_t* v, Shape s,
+                          const Workspace& ws, hipStream_t stream) {
+  const int C = 16 * s.H;
+  const int R = C >= 256 ? 1 : 256 / C;
+  const size_t lds = R > 1 ? (size_t)R * C * 24 * sizeof(float) : 0;
+  dim3 grid(ws.nbp, s.B);
+  hipLaunchKernelGGL(summary_kernel, grid, dim3(256), lds, stream, (const uint4v*)q, (const uint4v*)k,
+                     (const uint4v*)v, s.N, s.H, ws.nb, ws.nbp, ws.qbar, ws.kbar_t, (uint4v*)ws.kbar_h,
+                     (uint4v*)ws.vbar_h);
+  return hipGetLastError();
+}
+
+// One workgroup per (batch, head).  mu_K and v_K are averages over the nb key
+// blocks with weight 1/nb; v_K is accumulated in the centred two-pass form
+// mean_j (K-bar_j - mu_K)^2, which equals the printed mean of squares minus the
+// squared mean.  tau_i = mu_i + tau sigma_i in scaled-logit units (1/sqrt d).
+// exact != 0 uses the full covariance (Eq. (5)): sigma_i^2 = Q-bar_i Cov Q-bar_i^T.
+__global__ __launch_bounds__(256) void threshold_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar_t, int nb, int nbp, float tau,
+    int exact, float* __restrict__ kstat, float* __restrict__ kcov, float* __restrict__ tau_i) {
+  __shared__ float s_mu[kDim], s_var[kDim], s_part[256];
+  __shared__ float s_chunk[32][kDim];                   // 32 centred key means, for the covariance
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int d = tid & 127, half = tid >> 7;
+  const float* kt = kbar_t + (size_t)bh * 32 * nbp * 4;
+  auto kval = [&](int jj, int dd) { return kt[((size_t)(dd >> 2) * nbp + jj) * 4 + (dd & 3)]; };
+
+  float acc = 0.f;
+  for (int jj = half; jj < nb; jj += 2) acc += kval(jj, d);
+  s_part[tid] = acc;
+  __syncthreads();
+  if (tid < kDim) s_mu[tid] = (s_part[tid] + s_part[tid + 128]) / (float)nb;
+  __syncthreads();
+  const float mu = s_mu[d];
+  acc = 0.f;
+  for (int jj = half; jj < nb; jj += 2) { float x = kval(jj, d) - mu; acc += x * x; }
+  s_part[tid] = acc;
+  __syncthreads();
+  if (tid < kDim) {
+    s_var[tid] = (s_part[tid] + s_part[tid + 128]) / (float)nb;
+    kstat[(size_t)bh * 256 + tid] = s_mu[tid];
+    kstat[(size_t)bh * 256 + 128 + tid] = s_var[tid];
+  }
+  __syncthreads();
+
+  float* cov = kcov + (size_t)bh * kDim * kDim;
+  if (exact) {
+    // thread owns row r = tid / 2 and 64 columns starting at 64 * (tid % 2)
+    const int r = tid >> 1, c0 = (tid & 1) * 64;
+    float cacc[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) cacc[e] = 0.f;
+    for (int j0 = 0; j0 < nb; j0 += 32) {
+      __syncthreads();
+      for (int idx = tid; idx < 32 * kDim; idx += 256) {
+        int jj = j0 + idx / kDim, dd = idx % kDim;
+        s_chunk[idx / kDim][dd] = jj < nb ? kval(jj, dd) - s_mu[dd] : 0.f;
+      }
+      __syncthreads();
+      for (int jj = 0; jj < 32; ++jj) {
+        const float xr = s_chunk[jj][r];
+#pragma unroll
+        for (int e = 0; e < 64; ++e) cacc[e] += xr * s_chunk[jj][c0 + e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 64; ++e) cov[(size_t)r * kDim + c0 + e] = cacc[e] / (float)nb;
+    __threadfence_block();
+    __syncthreads();
+  }
+
+  const float scale = 0.08838834764831845f;             // 1/sqrt(128)
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int i = wave; i < nb; i += 4) {
+    const float* qi = qbar + ((size_t)bh * nbp + i) * kDim;
+    const float q0 = qi[lane], q1 = qi[lane + 64];
+    float m = q0 * s_mu[lane] + q1 * s_mu[lane + 64];
+    float var;
+    if (exact) {
+      // (Cov q)[lane] and [lane + 64], then q . (Cov q)
+      float c0 = 0.f, c1 = 0.f;
+      for (int e = 0; e < kDim; ++e) {
+        const float qe = qi[e];
+        c0 += cov[(size_t)lane * kDim + e] * qe;
+        c1 += cov[(size_t)(lane + 64) * kDim + e] * qe;
+      }
+      var = q0 * c0 + q1 * c1;
+    } else {
+      var = q0 * q0 * s_var[lane] + q1 * q1 * s_var[lane + 64];
+    }
+    m = wave_sum(m);
+    var = wave_sum(var);
+    if (lane == 0) {
+      const float sigma = sqrtf(fmaxf(var, 0.f)) * scale;
+      tau_i[(size_t)bh * nbp + i] = m * scale + tau * sigma;
+    }
+  }
+}
+
+hipError_t launch_threshold(Shape s, const Workspace& ws, float tau, int exact, hipStream_t stream) {
+  hipLaunchKernelGGL(threshold_kernel, dim3(s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t, ws.nb,
+                     ws.nbp, tau, exact, ws.kstat, ws.kcov, ws.tau_i);
+  return hipGetLastError();
+}
+
+}  // namespace solattn

@@ -1,0 +1,179 @@
+/*
+ * libsolattn -- Sol-Attn and Sol-Attn2 forward passes for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a plain address; the header says for each
+ * whether it is host or device memory.  No call allocates device memory: the
+ * caller passes a device workspace of at least sol_attn_workspace_bytes().
+ * Launches are asynchronous on the caller's HIP stream (`stream` is a
+ * hipStream_t passed as void*, NULL = the legacy default stream); the library
+ * keeps no pointer after a call returns and holds no global state apart from
+ * the loaded code object.  Calls that share a workspace must not overlap.
+ *
+ * Tensor contract (Sol-Attn README, "Usage" and "Core API"): q, k, v and out
+ * are contiguous bfloat16 tensors of shape [batch, tokens, heads, head_dim]
+ * (BTHD), head_dim == 128, all of the same shape; out is written in the same
+ * layout.  The attention is non-causal and unmasked (stable-diffusion.cpp
+ * "Sol-Attn" docs, "Use").
+ *
+ * Errors (stable-diffusion.cpp "Sol-Attn" docs: a non-finite threshold is
+ * rejected, execution errors are never turned into dense attention): every
+ * argument error is detected on the host before any launch and returned as a
+ * sol_status; nothing is launched then and outputs are untouched.  A HIP
+ * launch error is returned as SOL_ERR_HIP.  There is no fallback path.
+ */
+#ifndef SOLATTN_H
+#define SOLATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SOL_OK = 0,
+    SOL_ERR_NULL = 1,        /* a required pointer is NULL */
+    SOL_ERR_SHAPE = 2,       /* batch/tokens/heads < 1, or sizes overflow the index range */
+    SOL_ERR_HEAD_DIM = 3,    /* head_dim != 128 */
+    SOL_ERR_TAU = 4,         /* tau is NaN or infinite */
+    SOL_ERR_SINK = 5,        /* sink_tokens < 0, or the sink range leaves [0, tokens) */
+    SOL_ERR_WORKSPACE = 6,   /* workspace smaller than sol_attn_workspace_bytes() */
+    SOL_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
+    SOL_ERR_ARG = 8          /* unknown threshold type or variant, bad alignment */
+} sol_status;
+
+/* Threshold estimator (Sol-Attn paper §3.1 Eq. (5) and its appendix
+ * "Diagonal threshold estimator").  DIAG is the default hot path. */
+typedef enum { SOL_THRESH_DIAG = 0, SOL_THRESH_EXACT = 1 } sol_thresh;
+
+/* Variants for sol_attn_workspace_bytes / sol_attn_workspace_layout. */
+typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
+
+/* Byte offsets into the workspace of the intermediate arrays (for tests and
+ * tooling; the kernels own these arrays during a call).  nbp = number of
+ * 64-token blocks rounded up to a multiple of 64; tp = nbp * 64.  An offset
+ * of -1 means the array does not exist for the variant.  All arrays are
+ * indexed [batch][head][...].
+ *   qbar     float [B][H][nbp][128]   Q block means (Sol-Attn2: of dequantized Q)
+ *   kbar_t   float [B][H][32][nbp][4] K block means, 4-dim-interleaved
+ *   kbar_h   bf16  [B][H][nbp][128]   K block means (MFMA operand)
+ *   vbar_h   bf16  [B][H][nbp][128]   V block means V-hat_j / n_j (MFMA operand)
+ *   tau_i    float [B][H][nbp]        per-query-block threshold tau_i
+ *   kstat    float [B][H][2][128]     mu_K and v_K
+ *   kcov     float [B][H][128][128]   covariance of the K block means (EXACT only)
+ *   q8, k8   uint8 [B][H][tp][128]    E4M3FN codes (Sol-Attn2)
+ *   qscale, kscale float [B][H][nbp]  E4M3 block scales (Sol-Attn2)
+ *   qhat     float [B][H][128]        mean-query direction (Sol-Attn2)
+ *   gk, gv   bf16  [B][H][nbp][2][128] group mean keys / values (Sol-Attn2)
+ *   glogn    float [B][H][nbp][2]     ln n_g, -inf for an empty group (Sol-Attn2)
+ *   ghi      uint64 [B][H][nbp]       bit u set iff token u of the block is in G_hi (Sol-Attn2)
+ */
+typedef struct {
+    int64_t total_bytes;
+    int64_t nb, nbp;
+    int64_t qbar, kbar_t, kbar_h, vbar_h, tau_i, kstat, kcov;
+    int64_t q8, k8, qscale, kscale, qhat, gk, gv, glogn, ghi;
+} sol_ws_layout;
+
+/* Static description of a status code (never NULL). */
+const char* sol_status_string(int status);
+
+/* Host-only argument check of the Sol-Attn contract; launches nothing and
+ * needs no device.  sink_start < 0 means "suffix": the sink covers the last
+ * sink_tokens tokens (Sol-Attn README, "Exact KV sink"); sink_tokens == 0
+ * means no sink. */
+int sol_attn_validate(int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                      float tau, int64_t sink_start, int64_t sink_tokens, int thresh);
+
+/* Workspace size in bytes for `variant` (sol_variant) at this shape; 0 on a
+ * shape error.  Host-only. */
+size_t sol_attn_workspace_bytes(int variant, int64_t batch, int64_t tokens, int64_t heads,
+                                int64_t head_dim);
+
+/* Fill *layout (host pointer) with the workspace offsets; host-only. */
+int sol_attn_workspace_layout(int variant, int64_t batch, int64_t tokens, int64_t heads,
+                              int64_t head_dim, sol_ws_layout* layout);
+
+/*
+ * Sol-Attn forward (Sol-Attn paper §3, Figure 4; Sol-Attn README "Core API",
+ * "Exact KV sink").  q, k, v: device, bf16 BTHD, read-only.  out: device,
+ * bf16 BTHD, written.  tau: the threshold coefficient beta of Eq. (4);
+ * higher selects fewer blocks; 0 is not dense.  sink_start/sink_tokens: the
+ * exact KV sink (every 64-token KV block overlapping the range is exact for
+ * every query).  thresh: sol_thresh.  workspace: device, >=
+ * sol_attn_workspace_bytes(SOL_VARIANT_SOL1, ...), 256-byte aligned.
+ * Runs sol_attn_prepare then sol_attn_fused.
+ */
+int sol_attn(const void* q, const void* k, const void* v, void* out,
+             int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+             float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 1 of sol_attn: block summaries (Q/K means, V sums as means) and the
+ * per-query-block threshold tau_i (paper §3.1 Eqs. (4)-(5); the paper keeps
+ * only this threshold computation outside the attention kernel, §4.5).
+ * Writes the workspace arrays qbar..kcov.  Same arguments as sol_attn minus
+ * out and the sink. */
+int sol_attn_prepare(const void* q, const void* k, const void* v,
+                     int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                     float tau, int thresh, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2 of sol_attn: the fused routing + proxy-reuse + exact online-softmax
+ * kernel (paper §3.2 "Hardware-Aligned Implementation").  Reads the workspace
+ * written by sol_attn_prepare for the same q, k, v and shape. */
+int sol_attn_fused(const void* q, const void* k, const void* v, void* out,
+                   int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                   int64_t sink_start, int64_t sink_tokens,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test and tooling export, not part of the hot path: like sol_attn, and the
+ * fused kernel also writes the routing decision it made, as bit masks
+ * mask_bits[b][h][i][w] (device, uint64, nbw = ceil(nb/64) words per query
+ * block; bit (j % 64) of word j / 64 set iff KV block j was exact for query
+ * block i).  `out` may be NULL to skip the output store. */
+int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* out,
+                           int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                           float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+                           void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
+                           void* stream);
+
+/*
+ * Sol-Attn2 forward with the complementary tail (Sol-Attn2 draft, Method,
+ * Eqs. (1)-(3); "FP8 quantization and ExpCast"): Q and K are quantized to
+ * OCP E4M3FN with one fp32 scale per (batch, head, 64-token block); V stays
+ * bf16; routing on the dequantized block means with the same threshold rule;
+ * each unselected key block contributes two key groups to a per-32-token-
+ * anchor tail with first-order mass correction; exact and tail terms share
+ * one denominator.  Arguments as sol_attn; workspace >=
+ * sol_attn_workspace_bytes(SOL_VARIANT_SOL2, ...).
+ */
+int sol_attn2(const void* q, const void* k, const void* v, void* out,
+              int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+              float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 1 of sol_attn2: quantization, block summaries, threshold, mean-query
+ * direction and key-group summaries (workspace arrays listed above). */
+int sol_attn2_prepare(const void* q, const void* k, const void* v,
+                      int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                      float tau, int thresh, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2 of sol_attn2: the fused FP8 exact + complementary-tail kernel. */
+int sol_attn2_fused(const void* q, const void* k, const void* v, void* out,
+                    int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                    int64_t sink_start, int64_t sink_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sol-Attn2 routing export, as sol_attn_debug_routing. */
+int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* out,
+                            int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                            float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+                            void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOLATTN_H */

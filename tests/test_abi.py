@@ -1,0 +1,117 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every symbol the
+header declares, and the host-side validator / workspace sizing behave as documented."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "solattn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_sparse_attention_tok_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libsolattn.so not built")
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(sol_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("sol_attn", "sol_attn2", "sol_attn_validate", "sol_attn_workspace_bytes", "sol_status_string",
+              "sol_attn_prepare", "sol_attn_fused", "sol_attn_debug_routing"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    from block_sparse_attention_tok_amd import _lib
+    assert sorted(_lib.EXPORTED) == declared_functions()
+
+
+def test_status_strings(L):
+    for s in range(0, 9):
+        assert L.sol_status_string(s)
+    assert L.sol_status_string(123) == b"unknown status"
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1024, 2, 128, 1.0, -1, 0, 0), 0),
+    ((1, 1024, 2, 128, 0.0, 0, 1024, 1), 0),
+    ((1, 1024, 2, 64, 1.0, -1, 0, 0), 3),
+    ((0, 1024, 2, 128, 1.0, -1, 0, 0), 2),
+    ((1, 0, 2, 128, 1.0, -1, 0, 0), 2),
+    ((1, 1024, 0, 128, 1.0, -1, 0, 0), 2),
+    ((1, 1024, 2, 128, math.nan, -1, 0, 0), 4),
+    ((1, 1024, 2, 128, math.inf, -1, 0, 0), 4),
+    ((1, 1024, 2, 128, -math.inf, -1, 0, 0), 4),
+    ((1, 1024, 2, 128, 1.0, 1000, 100, 0), 5),
+    ((1, 1024, 2, 128, 1.0, 0, -1, 0), 5),
+    ((1, 1024, 2, 128, 1.0, -1, 1025, 0), 5),
+    ((1, 1024, 2, 128, 1.0, -1, 1024, 0), 0),
+    ((1, 1024, 2, 128, 1.0, -1, 0, 7), 8),
+])
+def test_validate(L, args, status):
+    assert L.sol_attn_validate(*args) == status
+
+
+def test_workspace_sizes_and_layout(L):
+    from block_sparse_attention_tok_amd import _lib
+    for variant in (1, 2):
+        for (B, N, H) in ((1, 1024, 2), (1, 14040, 12), (2, 333, 3), (1, 32768, 32)):
+            n = L.sol_attn_workspace_bytes(variant, B, N, H, 128)
+            lay = _lib.workspace_layout(variant, B, N, H)
+            assert n == lay.total_bytes > 0
+            nb = (N + 63) // 64
+            assert lay.nb == nb and lay.nbp % 64 == 0 and lay.nbp >= nb
+            offs = sorted(o for name, _ in _lib.WsLayout._fields_ if name not in ("total_bytes", "nb", "nbp")
+                          for o in [getattr(lay, name)] if o >= 0)
+            assert all(o % 256 == 0 for o in offs)
+            assert offs[-1] < n
+            if variant == 1:
+                assert lay.q8 == -1 and lay.gk == -1
+    assert L.sol_attn_workspace_bytes(1, 1, 1024, 2, 64) == 0
+    assert L.sol_attn_workspace_bytes(3, 1, 1024, 2, 128) == 0
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch(L):
+    """Argument errors return a status without touching the device (NULL and fake pointers)."""
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)
+    # null inputs
+    assert L.sol_attn(None, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, 1 << 30, None) == 1
+    # non-finite tau
+    assert L.sol_attn(fake, fake, fake, fake, 1, 1024, 2, 128, float("nan"), -1, 0, 0, fake, 1 << 30, None) == 4
+    # head dim
+    assert L.sol_attn(fake, fake, fake, fake, 1, 1024, 2, 64, 1.0, -1, 0, 0, fake, 1 << 30, None) == 3
+    # sink out of range
+    assert L.sol_attn2(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, 1000, 100, 0, fake, 1 << 30, None) == 5
+    # workspace too small
+    assert L.sol_attn(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, 16, None) == 6
+    # misaligned workspace
+    assert L.sol_attn(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 0, vp(0x1010), 1 << 30, None) == 8
+    # unknown threshold type
+    assert L.sol_attn(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 9, fake, 1 << 30, None) == 8
+    # missing mask buffer for the debug export
+    assert L.sol_attn_debug_routing(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, 1 << 30,
+                                    None, None) == 1
+
+
+def test_python_validate_wrapper():
+    from block_sparse_attention_tok_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libsolattn.so not built")
+    assert _lib.validate(1, 1024, 2, 128, 1.0, None, 0) == 0
+    assert _lib.validate(1, 1024, 2, 128, 1.0, None, 2000) == 5
+    assert _lib.validate(1, 1024, 2, 128, 1.0, None, 0, "bogus") == 8

@@ -1,0 +1,178 @@
+"""GPU parity of the Sol-Attn HIP path against the CPU oracle (through the C ABI).
+
+Masks: bit-exact wherever |s_hat - tau_i| > 1e-3 (scaled-logit units).
+Outputs: relative L2 <= 1e-2 and max-abs <= 3e-2 against the float64 oracle, the
+oracle evaluated with the selection the kernel made (in-margin flips are both
+correct readings).  Small shapes compare every output row; the full-size
+workload shapes compare the full routing and a seeded sample of query blocks.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_tok_amd as bsa
+from oracle import sol_attn as sa
+from parity import compare_out, mask_check, oracle_rows, say, to_gpu
+from workloads import block_offset_tensor, long_sink, operator_bench, wan_dit
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(B, N, H, seed, offset=1.0):
+    return [block_offset_tensor(B, N, H, 128, seed + i, offset) for i in range(3)]
+
+
+def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, thresh="diag", sample=None, seed=0):
+    B, N, H, _ = q.shape
+    say(f"[sol_attn] B={B} N={N} H={H} tau={tau} sink=({sink_start},{sink_tokens}) thresh={thresh}")
+    qg, kg, vg = to_gpu(q, k, v)
+    out = torch.empty_like(qg)
+    _, masks, ws = bsa.debug_routing(1, qg, kg, vg, tau, thresh, sink_start, sink_tokens, out=out)
+    out2 = bsa.sol_attn(qg, kg, vg, tau, thresh, sink_start, sink_tokens)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "export build and product build disagree"
+    ref = sa.routing_only(q, k, tau, sink_start, sink_tokens, thresh)
+    nb = (N + 63) // 64
+    forced = np.zeros((B, H, nb, nb), dtype=bool)
+    forced[..., sa.sink_block_mask(N, sink_start, sink_tokens)] = True
+    gsel = masks.numpy()
+    flips = mask_check(gsel, ref["sel"], ref["s_hat"], ref["tau_i"], forced)
+    out_c = out.float().cpu().numpy()
+    rng = np.random.default_rng(seed)
+    got, want = [], []
+    for b in range(B):
+        for h in range(H):
+            blocks = range(nb) if sample is None else sorted(set(rng.choice(nb, size=min(sample, nb), replace=False)) | {nb - 1})
+            for i in blocks:
+                s, e = i * 64, min(i * 64 + 64, N)
+                want.append(oracle_rows(q, k, v, b, h, i, gsel[b, h, i]))
+                got.append(out_c[b, s:e, h, :])
+    err, mx = compare_out(np.concatenate(got), np.concatenate(want), what=f"N={N} tau={tau}")
+    say(f"   ok: rel L2 {err:.2e} max abs {mx:.2e}, in-margin mask flips {flips}, "
+        f"density {gsel.mean():.3f}")
+    return out, masks, ws
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.0, -0.5, 2.5])
+def test_tiny_workload_full(tau):
+    """B=1, H=2, N=1024 block-offset data: every output row and every mask bit."""
+    q, k, v = _qkv(1, 1024, 2, 1000)
+    run_case(q, k, v, tau)
+
+
+@pytest.mark.parametrize("N", [40, 64, 65, 200, 1000, 4493, 8192 + 13])
+def test_ragged_lengths(N):
+    """Partial last blocks, a sequence shorter than one block, more than one 64-block chunk."""
+    q, k, v = _qkv(1, N, 2, 1100 + N)
+    run_case(q, k, v, 0.8)
+
+
+@pytest.mark.parametrize("sink", [(0, 130), (None, 70), (200, 300), (None, 1), (0, 1)])
+def test_exact_sink(sink):
+    q, k, v = _qkv(1, 1000, 2, 1200)
+    run_case(q, k, v, 1.5, sink_start=sink[0], sink_tokens=sink[1])
+
+
+def test_whole_sequence_sink_is_dense_attention():
+    """A sink over [0, N) makes every block exact: textbook attention (fp32 CPU SDPA)."""
+    q, k, v = _qkv(1, 777, 3, 1300)
+    out, masks, _ = run_case(q, k, v, 1.0, sink_start=0, sink_tokens=777)
+    assert masks.all()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.float().transpose(1, 2), k.float().transpose(1, 2), v.float().transpose(1, 2)).transpose(1, 2)
+    compare_out(out.float().cpu().numpy(), ref.numpy(), what="dense")
+
+
+def test_batch_and_odd_heads():
+    q, k, v = _qkv(2, 700, 3, 1400)
+    run_case(q, k, v, 0.5)
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.0])
+def test_exact_covariance_threshold(tau):
+    q, k, v = _qkv(1, 2000, 2, 1500)
+    run_case(q, k, v, tau, thresh="exact")
+
+
+def test_identical_keys_are_exact():
+    """Keys constant within each block: the proxy branch is exact, so any tau gives dense attention."""
+    q, k, v = _qkv(1, 1024, 2, 1600)
+    kb = k.float().view(1, 16, 64, 2, 128).mean(dim=2, keepdim=True).expand(1, 16, 64, 2, 128)
+    k = kb.reshape(1, 1024, 2, 128).to(torch.bfloat16).contiguous()
+    out, _, _ = run_case(q, k, v, 1.0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.float().transpose(1, 2), k.float().transpose(1, 2), v.float().transpose(1, 2)).transpose(1, 2)
+    compare_out(out.float().cpu().numpy(), ref.numpy(), what="identical keys")
+
+
+def test_summaries_and_threshold_match_oracle():
+    """Workspace block means, V means and tau_i against the oracle's definitions."""
+    N, H = 1000, 3
+    q, k, v = _qkv(1, N, H, 1700)
+    qg, kg, vg = to_gpu(q, k, v)
+    ws = bsa.alloc_workspace(1, qg)
+    for thresh in ("diag", "exact"):
+        bsa.prepare(1, qg, kg, vg, 0.7, ws, thresh)
+        torch.cuda.synchronize()
+        views = bsa.workspace_views(1, ws, 1, N, H)
+        nb = views["nb"]
+        for h in range(H):
+            qh, kh, vh = (t[0, :, h, :].double().numpy() for t in (q, k, v))
+            qbar, kbar = sa.block_means(qh), sa.block_means(kh)
+            vbar = sa.block_sums(vh) / sa.block_counts(N)[:, None]
+            np.testing.assert_allclose(views["qbar"][0, h, :nb].cpu().double().numpy(), qbar, rtol=1e-5, atol=1e-6)
+            kt = views["kbar_t"][0, h, :, :nb, :].cpu().double().permute(1, 0, 2).reshape(nb, 128).numpy()
+            np.testing.assert_allclose(kt, kbar, rtol=1e-5, atol=1e-6)
+            np.testing.assert_allclose(views["kbar_h"][0, h, :nb].cpu().double().numpy(), kbar, rtol=8e-3, atol=1e-6)
+            np.testing.assert_allclose(views["vbar_h"][0, h, :nb].cpu().double().numpy(), vbar, rtol=8e-3, atol=1e-6)
+            assert not views["kbar_h"][0, h, nb:].float().abs().sum().item()     # zero padding rows
+            fn = sa.diag_threshold if thresh == "diag" else sa.exact_threshold
+            tau_ref = fn(qbar, kbar, 0.7, 1 / math.sqrt(128))[0]
+            np.testing.assert_allclose(views["tau_i"][0, h, :nb].cpu().double().numpy(), tau_ref, rtol=1e-4, atol=2e-5)
+
+
+def test_deterministic_and_stream_ordered():
+    q, k, v = _qkv(1, 3000, 2, 1800)
+    qg, kg, vg = to_gpu(q, k, v)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = bsa.sol_attn(qg, kg, vg, 0.9)
+        b = bsa.sol_attn(qg, kg, vg, 0.9)
+    s.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_python_binding_rejects_bad_tensors():
+    q, k, v = to_gpu(*_qkv(1, 128, 1, 1900))
+    with pytest.raises(ValueError):
+        bsa.sol_attn(q.float(), k, v)
+    with pytest.raises(ValueError):
+        bsa.sol_attn(q, k[:, :64].contiguous(), v)
+    with pytest.raises(ValueError):
+        bsa.sol_attn(q, k, v, tau=float("nan"))
+    with pytest.raises(bsa.SolAttnError):
+        bsa.sol_attn(q, k, v, sink_start=100, sink_tokens=100)
+
+
+# ---- workload shapes at full size: full routing, sampled outputs -------------------
+
+@pytest.mark.parametrize("tau", [0.0, 1.0])
+def test_wan21_dit_shape(tau):
+    """B=1, H=12, N=14040 (9x30x52 raster grid, last block 24 tokens), smooth random field."""
+    q, k, v = wan_dit().qkv()
+    run_case(q, k, v, tau, sample=6, seed=int(tau * 10))
+
+
+def test_operator_bench_shape():
+    """B=1, H=32, N=32768 block-offset data (the operator benchmark shape)."""
+    q, k, v = operator_bench().qkv()
+    run_case(q, k, v, 1.28, sample=3, seed=3)
+
+
+def test_long_sequence_with_text_sink():
+    """B=1, H=32, 512 text tokens (exact sink) + 65536 video tokens."""
+    w = long_sink(65536)
+    q, k, v = w.qkv()
+    run_case(q, k, v, 1.3, sink_start=0, sink_tokens=512, sample=2, seed=4)
