@@ -32,7 +32,7 @@ EXPORTED = [
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov",
-        "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi")]
+        "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc")]
 
 
 class SolAttnError(RuntimeError):
@@ -255,6 +255,7 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
             gv=view(L.gv, torch.bfloat16, (batch, heads, nbp, 2, 128)),
             glogn=view(L.glogn, torch.float32, (batch, heads, nbp, 2)),
             ghi=view(L.ghi, torch.int64, (batch, heads, nbp)),
+            qanc=view(L.qanc, torch.float32, (batch, heads, nbp, 2, 128)),
         )
     del bh
     return d

@@ -69,6 +69,7 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->gv = take(bh * nbp * 2 * kDim * 2);
     L->glogn = take(bh * nbp * 2 * 4);
     L->ghi = take(bh * nbp * 8);
+    L->qanc = take(bh * nbp * 2 * kDim * 4);
   }
   L->total_bytes = off;
   return SOL_OK;
@@ -96,6 +97,7 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.gv = (uint16_t*)at(L.gv);
   w.glogn = (float*)at(L.glogn);
   w.ghi = (uint64_t*)at(L.ghi);
+  w.qanc = (float*)at(L.qanc);
   return w;
 }
 

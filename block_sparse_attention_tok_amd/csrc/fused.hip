@@ -28,11 +28,11 @@
 //     selection does not depend on bf16 rounding of the pooled keys.
 #include "common.h"
 #include "kernels.h"
+#include "tile.h"
 
 namespace solattn {
 
 constexpr int kKsStride = 272;   // bytes per K row in LDS: 256 + 16 pad (conflict-free b128 reads)
-constexpr int kVtStride = 136;   // bytes per V^T row (one dim, 64 keys): 128 + 8 pad
 constexpr float kScale = 0.08838834764831845f;        // 1/sqrt(128)
 constexpr float kScaleLog2 = kScale * kLog2e;
 
@@ -59,29 +59,7 @@ __device__ __forceinline__ void load_tile(unsigned char* Ks, unsigned char* Vt, 
     if (r < valid) x = *(const uint4v*)(kb + (size_t)r * stride + cc * 8);
     *(uint4v*)(Ks + r * kKsStride + cc * 16) = x;
   }
-  // V: thread owns keys 4*(tid%16)..+3 and dims 8*c8..+7, c8 = tid/16 + 8p
-  const int r4 = 4 * (tid & 15);
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int c8 = (tid >> 4) + 8 * p;
-    uint4v R[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      R[rr] = uint4v{0u, 0u, 0u, 0u};
-      if (r4 + rr < valid) R[rr] = *(const uint4v*)(vb + (size_t)(r4 + rr) * stride + c8 * 8);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      // dims 2m (low halves) and 2m+1 (high halves)
-      uint2v lo, hi;
-      lo[0] = (R[0][m] & 0xffffu) | (R[1][m] << 16);
-      lo[1] = (R[2][m] & 0xffffu) | (R[3][m] << 16);
-      hi[0] = (R[0][m] >> 16) | (R[1][m] & 0xffff0000u);
-      hi[1] = (R[2][m] >> 16) | (R[3][m] & 0xffff0000u);
-      *(uint2v*)(Vt + (8 * c8 + 2 * m) * kVtStride + r4 * 2) = lo;
-      *(uint2v*)(Vt + (8 * c8 + 2 * m + 1) * kVtStride + r4 * 2) = hi;
-    }
-  }
+  load_v_transposed(Vt, vb, stride, valid, tid);
 }
 
 enum TileMode { kExactFull = 0, kExactPartial = 1, kProxy = 2 };
@@ -105,7 +83,6 @@ __device__ __forceinline__ void process_tile(const unsigned char* Ks, const unsi
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
   }
   // logits in log2 units; element idx of tile mt holds key 32 mt + 8 (idx/4) + 4 kg + idx%4
-  float mx = kNegInf;
 #pragma unroll
   for (int idx = 0; idx < 16; ++idx) {
     const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
@@ -121,42 +98,8 @@ __device__ __forceinline__ void process_tile(const unsigned char* Ks, const unsi
     }
     s0[idx] = x0;
     s1[idx] = x1;
-    mx = fmaxf(mx, fmaxf(x0, x1));
   }
-  mx = max_with_partner(mx);
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = m_new == kNegInf ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-  float psum = 0.f;
-  bf16x8 pa[4];
-#pragma unroll
-  for (int idx = 0; idx < 16; ++idx) {
-    const float p0 = __builtin_amdgcn_exp2f(s0[idx] - m_use);
-    const float p1 = __builtin_amdgcn_exp2f(s1[idx] - m_use);
-    psum += p0 + p1;
-    // k-step st covers keys 16 st .. 16 st + 15: tile st/2, elements 8 (st%2) .. +7
-    pa[(idx >> 3)][idx & 7] = (__bf16)p0;
-    pa[2 + (idx >> 3)][idx & 7] = (__bf16)p1;
-  }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int idx = 0; idx < 16; ++idx) o[mt][idx] *= alpha;
-  // O^T[dim][query] += V^T[dim][key] P^T[key][query]; logical k position (kg, e) of
-  // k-step st is key 16 st + 8 (e/4) + 4 kg + e%4 on both operands.
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const unsigned char* vrow = Vt + (32 * mt + l32) * kVtStride + kg * 8;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint2v lo = *(const uint2v*)(vrow + st * 32);
-      uint2v hi = *(const uint2v*)(vrow + st * 32 + 16);
-      uint4v av = {lo[0], lo[1], hi[0], hi[1]};
-      o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], o[mt], 0, 0, 0);
-    }
-  }
+  softmax_pv(s0, s1, Vt, o, m_run, l_run, l32, kg);
 }
 
 template <bool kExport>
@@ -201,17 +144,9 @@ __global__ __launch_bounds__(128) void sol_fused_kernel(FusedArgs a) {
   const size_t pooled_off = (size_t)bh * a.nbp * kDim;
   const int nchunks = a.nbp / 64;
   for (int c = 0; c < nchunks; ++c) {
-    // ---- routing: s_ij for the 64 pooled keys of this chunk (fp32; wave w sums dims 64w..64w+63)
+    // ---- routing: s_ij for the 64 pooled keys of this chunk (fp32)
     const int j = c * 64 + lane;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int d4 = 16 * w; d4 < 16 * w + 16; ++d4) {
-      const float4 kk = kt[(size_t)d4 * a.nbp + j];
-      acc += qb_s[4 * d4] * kk.x + qb_s[4 * d4 + 1] * kk.y + qb_s[4 * d4 + 2] * kk.z + qb_s[4 * d4 + 3] * kk.w;
-    }
-    part[w][lane] = acc;
-    __syncthreads();
-    const float s_hat = (part[0][lane] + part[1][lane]) * kScale;
+    const float s_hat = routing_scores(kt, a.nbp, c, qb_s, part, w, lane);
     const bool valid = j < a.nb;
     const bool sel = valid && (s_hat > tau_i || (j >= a.sink_b0 && j <= a.sink_b1));
     uint64_t selm = __ballot(sel);

@@ -24,6 +24,7 @@ struct Workspace {
   uint16_t* gv;
   float* glogn;     // [B][H][nbp][2]
   uint64_t* ghi;    // [B][H][nbp]
+  float* qanc;      // [B][H][nbp][2][128]
 };
 
 struct Shape {

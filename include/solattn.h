@@ -68,12 +68,13 @@ typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
  *   gk, gv   bf16  [B][H][nbp][2][128] group mean keys / values (Sol-Attn2)
  *   glogn    float [B][H][nbp][2]     ln n_g, -inf for an empty group (Sol-Attn2)
  *   ghi      uint64 [B][H][nbp]       bit u set iff token u of the block is in G_hi (Sol-Attn2)
+ *   qanc     float [B][H][nbp][2][128] 32-token anchor means of dequantized Q (Sol-Attn2)
  */
 typedef struct {
     int64_t total_bytes;
     int64_t nb, nbp;
     int64_t qbar, kbar_t, kbar_h, vbar_h, tau_i, kstat, kcov;
-    int64_t q8, k8, qscale, kscale, qhat, gk, gv, glogn, ghi;
+    int64_t q8, k8, qscale, kscale, qhat, gk, gv, glogn, ghi, qanc;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */
