@@ -58,6 +58,7 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   L->tau_i = take(bh * nbp * 4);
   L->kstat = take(bh * 2 * kDim * 4);
   L->kcov = take(bh * kDim * kDim * 4);
+  L->kpart = take(bh * 16 * 2 * kDim * 8);
   if (variant == SOL_VARIANT_SOL2) {
     const int64_t tp = nbp * kBlock;
     L->q8 = take(bh * tp * kDim);
@@ -88,6 +89,7 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.tau_i = (float*)at(L.tau_i);
   w.kstat = (float*)at(L.kstat);
   w.kcov = (float*)at(L.kcov);
+  w.kpart = (double*)at(L.kpart);
   w.q8 = (uint8_t*)at(L.q8);
   w.k8 = (uint8_t*)at(L.k8);
   w.qscale = (float*)at(L.qscale);

@@ -60,3 +60,47 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 }
 
 }  // namespace solattn
+
+namespace solattn {
+
+// s_waitcnt immediates for the gfx9 encoding (vmcnt in bits 3:0 and 15:14,
+// expcnt in 6:4, lgkmcnt in 11:8); the counters not named are left at max.
+constexpr int kWaitVm0 = 0x0F70;      // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;    // lgkmcnt(0)
+
+// Workgroup barrier for LDS hand-offs that must not wait for in-flight global
+// loads (unlike __syncthreads, whose fence drains vmcnt): completes this
+// wave's LDS reads, then s_barrier; the signal fences keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ void wait_vm0() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l's
+// 16 bytes land at lds_base + 16 l; lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* gsrc, unsigned char* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_base, 16, 0, 0);
+}
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element (i % 4)
+// of the 8-byte rows addressed by lanes 4 e + i / 4, e = 0..3.
+__device__ __forceinline__ uint2v lds_read_tr16(const unsigned char* p) {
+  shortx4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(__attribute__((address_space(3))) unsigned char*)p);
+  return __builtin_bit_cast(uint2v, r);
+}
+
+}  // namespace solattn

@@ -2,39 +2,41 @@
 //
 // Sol-Attn paper (arXiv 2607.24027) §3.2, Figure 4 and "Hardware-Aligned
 // Implementation": each program keeps one query block and its threshold
-// tau_i on chip and one online-softmax state in registers; an outer loop
-// streams chunks of pooled keys / values, compares each block's proxy score
+// tau_i on chip and one online-softmax state in registers; it streams the
+// pooled keys / values in chunks, compares each block's proxy score
 // s_ij = Q-bar_i . K-bar_j / sqrt(d) with tau_i (Eq. (4), Eq. (6)), folds every
 // unselected block in through its proxy (token-to-block tile Q_i K-bar^T with
-// weight n_j and the V sum V-hat_j), and an inner loop runs exact attention on
-// the original K/V blocks of the selected indices.  No proxy or routing map is
-// written to memory (only the optional test export below).
+// weight n_j and the V sum V-hat_j) and runs exact attention on the original
+// K/V blocks of the selected indices.  No proxy or routing map is written to
+// memory (only the optional test export).
 //
-// gfx950 mapping (one workgroup = one (batch, head, 64-row query block),
-// two wave64s of 32 query rows each):
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K tile rows from LDS,
-//     B = the wave's 32 query rows held in registers.  The accumulator puts
-//     one query per lane (lane % 32) and 16 keys per lane, so the row max and
-//     row sum are in-lane plus one v_permlane32_swap with the partner lane.
-//   * O^T += V^T P^T on the same MFMA: A = V^T read from a transposed LDS
-//     copy, B = P taken straight from the S^T accumulator (the k order inside
-//     one MFMA is permuted consistently on both operands), so O^T also keeps
-//     one query per lane and the softmax rescale is a per-lane multiply.
-//   * A proxy chunk is the same tile computation with K-bar / V-bar (V-hat_j/n_j)
-//     as keys / values and an additive log2(n_j) logit bias, selected and
-//     padding columns masked to -inf: sum_u e^{q.K-bar} v_u style algebra,
-//     n_j e^{q.K-bar_j} V-bar_j = e^{q.K-bar_j} V-hat_j, shares the softmax state.
-//   * Routing dot products run in fp32 from fp32 block means (VALU), so the
-//     selection does not depend on bf16 rounding of the pooled keys.
+// gfx950 mapping: one workgroup = one (batch, head, 64-row query block), two
+// wave64s of 32 query rows; __launch_bounds__(128, 2) keeps two waves per SIMD.
+//   * Routing runs first, in fp32 from the fp32 block means (VALU), for every
+//     chunk of 64 pooled keys; the per-chunk selection words stay in LDS.
+//   * The tile stream is, per chunk, one proxy tile (K-bar / V-bar = V-hat/n
+//     rows with logit bias log2 n_j; selected and padding columns masked) then
+//     the chunk's selected exact blocks.  All tiles share one online softmax.
+//   * Tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into
+//     one K and one V buffer whose 16-byte slots are XOR-swizzled per row; the
+//     V load of tile t overlaps S_t and its softmax, the K load of tile t+1
+//     overlaps PV_t.  Two LDS barriers per tile.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
+//     wave's query rows in registers): one query per lane, so row max / sum are
+//     in-lane plus one v_permlane32_swap.
+//   * O^T += V^T P^T: A = V^T gathered from the row-major V tile with
+//     ds_read_b64_tr_b16, B = P straight from the S^T accumulator (the k order
+//     inside each MFMA is permuted identically on both operands).
 #include "common.h"
 #include "kernels.h"
 #include "tile.h"
 
 namespace solattn {
 
-constexpr int kKsStride = 272;   // bytes per K row in LDS: 256 + 16 pad (conflict-free b128 reads)
 constexpr float kScale = 0.08838834764831845f;        // 1/sqrt(128)
 constexpr float kScaleLog2 = kScale * kLog2e;
+constexpr int kMaxChunks = 128;                         // nbp / 64 <= 128 (tokens <= 524288)
+constexpr int kEnd = -0x7fffffff;
 
 struct FusedArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; uint16_t* out;
@@ -45,76 +47,78 @@ struct FusedArgs {
   uint64_t* mask_out;
 };
 
-// Stage a 64-row K tile (row-major) and V tile (transposed) into LDS.
-// Rows r >= valid are zero-filled.  `stride` is the element distance between
-// consecutive rows in global memory.
-__device__ __forceinline__ void load_tile(unsigned char* Ks, unsigned char* Vt, const uint16_t* kb,
-                                          const uint16_t* vb, size_t stride, int valid, int tid) {
-  // K: thread owns 16-byte chunk cc of rows r0, r0 + 8, ...
-  const int cc = tid & 15, r0 = tid >> 4;
+// 16-byte slot swizzles of the 64 x 256-byte K and V tiles (row r, logical chunk
+// lc lives in physical slot lc ^ swz(r)): the K pattern spreads the 8 rows of a
+// b128 read phase over all banks, the V pattern the 4 rows x 2 chunks of a
+// transposed-read lane group.
+__device__ __forceinline__ int swz_k(int r) { return r & 7; }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+
+// DMA a 64 x 128 bf16 tile into LDS (16 KB, two waves x 8 instructions).  Rows
+// r >= valid re-read row valid - 1 (their logits are masked; finite values keep
+// 0 * V finite).
+template <bool kIsV>
+__device__ __forceinline__ void dma_tile(unsigned char* lds, const uint16_t* src, size_t stride, int valid,
+                                         int w, int lane) {
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int r = r0 + 8 * p;
-    uint4v x = {0u, 0u, 0u, 0u};
-    if (r < valid) x = *(const uint4v*)(kb + (size_t)r * stride + cc * 8);
-    *(uint4v*)(Ks + r * kKsStride + cc * 16) = x;
+  for (int n = 0; n < 8; ++n) {
+    const int seg = w * 8 + n;                          // 1 KB segment = rows 4 seg .. 4 seg + 3
+    const int r = 4 * seg + (lane >> 4);
+    const int lc = (lane & 15) ^ (kIsV ? swz_v(r) : swz_k(r));
+    const int rr = r < valid ? r : valid - 1;
+    dma16(src + (size_t)rr * stride + lc * 8, lds + seg * 1024);
   }
-  load_v_transposed(Vt, vb, stride, valid, tid);
+}
+
+// Tile order: per chunk c, the proxy tile (code -(c + 1)) if any block of the
+// chunk is unselected, then its selected blocks (code = block index).
+struct TileIter {
+  int c;
+  int phase;           // 0: proxy not yet considered for chunk c
+  uint64_t bits;
+};
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, const uint64_t* prox_s,
+                                         int nchunks) {
+  while (it.c < nchunks) {
+    if (it.phase == 0) {
+      it.phase = 1;
+      it.bits = uniform64(sel_s[it.c]);
+      if (uniform64(prox_s[it.c])) return -(it.c + 1);
+    }
+    if (it.bits) {
+      const int jb = it.c * 64 + __builtin_ctzll(it.bits);
+      it.bits &= it.bits - 1;
+      return jb;
+    }
+    ++it.c;
+    it.phase = 0;
+  }
+  return kEnd;
 }
 
 enum TileMode { kExactFull = 0, kExactPartial = 1, kProxy = 2 };
 
-// One 64-key tile against the wave's 32 query rows: S^T, online softmax, O^T += V^T P^T.
-// kProxy: key r carries bias log2(n_j) when bit r of `colmask` is set, else -inf.
-// kExactPartial: keys r >= `valid` are masked.
-template <int MODE>
-__device__ __forceinline__ void process_tile(const unsigned char* Ks, const unsigned char* Vt,
-                                             const bf16x8 (&qreg)[8], floatx16 (&o)[4], float& m_run,
-                                             float& l_run, uint64_t colmask, int valid, float last_bias,
-                                             int last_key, int l32, int kg) {
-  floatx16 s0 = {}, s1 = {};
-  const unsigned char* k0 = Ks + l32 * kKsStride + kg * 16;
-  const unsigned char* k1 = Ks + (32 + l32) * kKsStride + kg * 16;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    bf16x8 a0 = *(const bf16x8*)(k0 + ks * 32);
-    bf16x8 a1 = *(const bf16x8*)(k1 + ks * 32);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
-  }
-  // logits in log2 units; element idx of tile mt holds key 32 mt + 8 (idx/4) + 4 kg + idx%4
-#pragma unroll
-  for (int idx = 0; idx < 16; ++idx) {
-    const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
-    float x0 = s0[idx] * kScaleLog2, x1 = s1[idx] * kScaleLog2;
-    if (MODE == kProxy) {
-      const float b0 = key0 == last_key ? last_bias : 6.0f;        // log2(64) for full blocks
-      const float b1 = key0 + 32 == last_key ? last_bias : 6.0f;
-      x0 = ((colmask >> key0) & 1) ? x0 + b0 : kNegInf;
-      x1 = ((colmask >> (key0 + 32)) & 1) ? x1 + b1 : kNegInf;
-    } else if (MODE == kExactPartial) {
-      if (key0 >= valid) x0 = kNegInf;
-      if (key0 + 32 >= valid) x1 = kNegInf;
-    }
-    s0[idx] = x0;
-    s1[idx] = x1;
-  }
-  softmax_pv(s0, s1, Vt, o, m_run, l_run, l32, kg);
-}
-
-template <bool kExport>
-__global__ __launch_bounds__(128) void sol_fused_kernel(FusedArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[64 * kKsStride];
-  __shared__ __attribute__((aligned(16))) unsigned char Vt[128 * kVtStride];
+__global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char Kl[64 * 256];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vl[64 * 256];
   __shared__ __attribute__((aligned(16))) float qb_s[kDim];
-  __shared__ float part[2][64];
+  __shared__ float part[2][2][64];
+  __shared__ uint64_t sel_s[kMaxChunks], prox_s[kMaxChunks];
 
   const int total = a.B * a.H * a.nb;
   const int item = xcd_remap(blockIdx.x, total);
   const int i = item % a.nb;
   const int bh = item / a.nb;
   const int h = bh % a.H, b = bh / a.H;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t rs = (size_t)a.H * kDim;                      // elements between tokens (BTHD)
   const size_t head_off = (size_t)b * a.N * rs + (size_t)h * kDim;
 
@@ -123,61 +127,172 @@ __global__ __launch_bounds__(128) void sol_fused_kernel(FusedArgs a) {
 
   const int qrow = i * kBlock + w * 32 + l32;
   bf16x8 qreg[8];
-  if (qrow < a.N) {
-    const uint4v* src = (const uint4v*)(a.q + head_off + (size_t)qrow * rs);
+  {
+    const uint4v* src = (const uint4v*)(a.q + head_off + (size_t)(qrow < a.N ? qrow : a.N - 1) * rs);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, src[2 * ks + kg]);
-  } else {
+  }
+  __syncthreads();
+
+  // ---- routing for every chunk (fp32); wave w sums dims 64 w .. 64 w + 63
+  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
+  const int nchunks = a.nbp / 64;
+  for (int c = 0; c < nchunks; ++c) {
+    const int j = c * 64 + lane;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int d4 = 16 * w; d4 < 16 * w + 16; ++d4) {
+      const float4 kk = kt[(size_t)d4 * a.nbp + j];
+      acc += qb_s[4 * d4] * kk.x + qb_s[4 * d4 + 1] * kk.y + qb_s[4 * d4 + 2] * kk.z + qb_s[4 * d4 + 3] * kk.w;
+    }
+    part[c & 1][w][lane] = acc;
+    __syncthreads();
+    const float s_hat = (part[c & 1][0][lane] + part[c & 1][1][lane]) * kScale;
+    const bool valid = j < a.nb;
+    const bool sel = valid && (s_hat > tau_i || (j >= a.sink_b0 && j <= a.sink_b1));
+    const uint64_t selm = __ballot(sel);
+    const uint64_t proxm = __ballot(valid) & ~selm;
+    if (tid == 0) {
+      sel_s[c] = selm;
+      prox_s[c] = proxm;
+      if (a.mask_out) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
+    }
+  }
+  __syncthreads();
+
+  // ---- per-lane LDS offsets
+  // S^T A operand: key row 32 mt + l32, k-step ks reads logical chunk 2 ks + kg
+  int koff[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, uint4v{0u, 0u, 0u, 0u});
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = l32 * 256 + (((2 * ks + kg) ^ swz_k(l32)) << 4);
+  // V^T A operand (transposed read): lane group G = lane / 16, i' = lane % 16 addresses
+  // key 4 kg + i'/4 (+ 16 st + 8 half), dims 32 mt + 16 (G % 2) + 4 (i' % 4)
+  int voff[4];
+  {
+    const int ip = lane & 15, gm = (lane >> 4) & 1;
+    const int key = 4 * kg + (ip >> 2);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int lc = 4 * mt + 2 * gm + ((ip & 3) >> 1);
+      voff[mt] = key * 256 + ((lc ^ swz_v(key)) << 4) + (ip & 1) * 8;
+    }
   }
 
   floatx16 o[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
   float m_run = kNegInf, l_run = 0.f;
-  const int last_n = a.N - (a.nb - 1) * kBlock;               // valid tokens of the last block
+  const int last_n = a.N - (a.nb - 1) * kBlock;
   const float last_bias = __log2f((float)last_n);
-  __syncthreads();
-
-  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
   const size_t pooled_off = (size_t)bh * a.nbp * kDim;
-  const int nchunks = a.nbp / 64;
-  for (int c = 0; c < nchunks; ++c) {
-    // ---- routing: s_ij for the 64 pooled keys of this chunk (fp32)
-    const int j = c * 64 + lane;
-    const float s_hat = routing_scores(kt, a.nbp, c, qb_s, part, w, lane);
-    const bool valid = j < a.nb;
-    const bool sel = valid && (s_hat > tau_i || (j >= a.sink_b0 && j <= a.sink_b1));
-    uint64_t selm = __ballot(sel);
-    const uint64_t proxym = __ballot(valid) & ~selm;
-    if (kExport && tid == 0) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
 
-    // ---- proxy update for the unselected blocks of the chunk
-    if (proxym) {
-      load_tile(Ks, Vt, a.kbar_h + pooled_off + (size_t)c * 64 * kDim,
-                a.vbar_h + pooled_off + (size_t)c * 64 * kDim, kDim, 64, tid);
-      __syncthreads();
-      process_tile<kProxy>(Ks, Vt, qreg, o, m_run, l_run, proxym, 64, last_bias, a.nb - 1 - c * 64,
-                           l32, kg);
+  TileIter it{0, 0, 0};
+  int cur = next_tile(it, sel_s, prox_s, nchunks);
+  auto src_of = [&](int code, bool is_v, size_t& stride, int& valid) -> const uint16_t* {
+    if (code < 0) {
+      stride = kDim;
+      valid = 64;
+      return (is_v ? a.vbar_h : a.kbar_h) + pooled_off + (size_t)(-code - 1) * 64 * kDim;
     }
-    __syncthreads();
+    stride = rs;
+    valid = min(kBlock, a.N - code * kBlock);
+    return (is_v ? a.v : a.k) + head_off + (size_t)code * kBlock * rs;
+  };
+  if (cur != kEnd) {
+    size_t st; int vr;
+    const uint16_t* src = src_of(cur, false, st, vr);
+    dma_tile<false>(Kl, src, st, vr, w, lane);
+  }
 
-    // ---- exact update for the selected blocks of the chunk
-    while (selm) {
-      const int jb = c * 64 + __builtin_ctzll(selm);
-      selm &= selm - 1;
-      const int t0 = jb * kBlock;
-      const int valid_rows = min(kBlock, a.N - t0);
-      load_tile(Ks, Vt, a.k + head_off + (size_t)t0 * rs, a.v + head_off + (size_t)t0 * rs, rs,
-                valid_rows, tid);
-      __syncthreads();
-      if (valid_rows == kBlock)
-        process_tile<kExactFull>(Ks, Vt, qreg, o, m_run, l_run, 0, kBlock, 0.f, -1, l32, kg);
-      else
-        process_tile<kExactPartial>(Ks, Vt, qreg, o, m_run, l_run, 0, valid_rows, 0.f, -1, l32, kg);
-      __syncthreads();
+  while (cur != kEnd) {
+    const int nxt = next_tile(it, sel_s, prox_s, nchunks);
+    size_t stride; int valid;
+    const uint16_t* vsrc = src_of(cur, true, stride, valid);
+    wait_vm0();
+    lds_barrier();                                           // K(cur) landed; V buffer free
+    dma_tile<true>(Vl, vsrc, stride, valid, w, lane);
+
+    // ---- S^T = K Q^T
+    floatx16 s0 = {}, s1 = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a0 = *(const bf16x8*)(Kl + koff[ks]);
+      const bf16x8 a1 = *(const bf16x8*)(Kl + 32 * 256 + koff[ks]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
     }
+    // ---- logits (log2 units) with the tile's mask / bias, online softmax
+    const int mode = cur < 0 ? kProxy : (valid == kBlock ? kExactFull : kExactPartial);
+    if (mode == kExactFull) {
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) { s0[idx] *= kScaleLog2; s1[idx] *= kScaleLog2; }
+    } else if (mode == kExactPartial) {
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+        s0[idx] = key0 < valid ? s0[idx] * kScaleLog2 : kNegInf;
+        s1[idx] = key0 + 32 < valid ? s1[idx] * kScaleLog2 : kNegInf;
+      }
+    } else {
+      const int c = -cur - 1;
+      const uint64_t colmask = prox_s[c];
+      const int last_key = a.nb - 1 - c * 64;
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+        const float b0 = key0 == last_key ? last_bias : 6.0f;   // log2(64) for full blocks
+        const float b1 = key0 + 32 == last_key ? last_bias : 6.0f;
+        s0[idx] = ((colmask >> key0) & 1) ? s0[idx] * kScaleLog2 + b0 : kNegInf;
+        s1[idx] = ((colmask >> (key0 + 32)) & 1) ? s1[idx] * kScaleLog2 + b1 : kNegInf;
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
+    mx = max_with_partner(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    // Unconditional rescale: skipping it behind a wave-uniform branch made results
+    // depend on timing with two waves per SIMD (MFMA accumulators rewritten under
+    // a branch), so O and l are always multiplied by alpha (1 when the max is unchanged).
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) o[mt][idx] *= alpha;
+    m_run = m_new;
+    bf16x8 pa[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const float p0 = __builtin_amdgcn_exp2f(s0[idx] - m_use);
+      const float p1 = __builtin_amdgcn_exp2f(s1[idx] - m_use);
+      psum += p0 + p1;
+      pa[(idx >> 3)][idx & 7] = (__bf16)p0;              // k-step st = keys 16 st .. 16 st + 15
+      pa[2 + (idx >> 3)][idx & 7] = (__bf16)p1;
+    }
+    l_run += psum;
+
+    wait_vm0();
+    lds_barrier();                                           // V(cur) landed; K buffer free
+    if (nxt != kEnd) {
+      size_t st; int vr;
+      const uint16_t* src = src_of(nxt, false, st, vr);
+      dma_tile<false>(Kl, src, st, vr, w, lane);
+    }
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint2v lo = lds_read_tr16(Vl + voff[mt] + st * 16 * 256);
+        const uint2v hi = lds_read_tr16(Vl + voff[mt] + st * 16 * 256 + 8 * 256);
+        const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], o[mt], 0, 0, 0);
+      }
+    }
+    cur = nxt;
   }
 
   // ---- epilogue: O / l, bf16 RNE, BTHD store
@@ -200,16 +315,14 @@ __global__ __launch_bounds__(128) void sol_fused_kernel(FusedArgs a) {
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                         Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* mask_out,
                         hipStream_t stream) {
+  if (ws.nbp / 64 > kMaxChunks) return hipErrorInvalidValue;
   FusedArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = (ws.nb + 63) / 64;
   a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h; a.tau_i = ws.tau_i;
   a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
   const int total = s.B * s.H * ws.nb;
-  if (mask_out)
-    hipLaunchKernelGGL(sol_fused_kernel<true>, dim3(total), dim3(128), 0, stream, a);
-  else
-    hipLaunchKernelGGL(sol_fused_kernel<false>, dim3(total), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(sol_fused_kernel, dim3(total), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ struct Workspace {
   float* tau_i;     // [B][H][nbp]
   float* kstat;     // [B][H][2][128]
   float* kcov;      // [B][H][128][128]
+  double* kpart;    // [B][H][16][2][128] partial key-mean statistics
   uint8_t* q8;      // [B][H][tp][128]
   uint8_t* k8;
   float* qscale;    // [B][H][nbp]

@@ -254,7 +254,6 @@ struct Fused2Args {
   uint64_t* mask_out;
 };
 
-template <bool kExport>
 __global__ __launch_bounds__(128) void sol2_fused_kernel(Fused2Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char K8s[64 * kK8Stride];
   __shared__ __attribute__((aligned(16))) unsigned char Vt[128 * kVtStride];
@@ -304,7 +303,7 @@ __global__ __launch_bounds__(128) void sol2_fused_kernel(Fused2Args a) {
     const bool sel = valid && (s_hat > tau_i || (j >= a.sink_b0 && j <= a.sink_b1));
     uint64_t selm = __ballot(sel);
     const uint64_t tailm = __ballot(valid) & ~selm;
-    if (kExport && tid == 0) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
+    if (a.mask_out && tid == 0) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
 
     // ---- tail: groups of the unselected blocks of this chunk, against anchor w
     if (tailm) {
@@ -454,10 +453,7 @@ hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Worksp
   a.gk = ws.gk; a.gv = ws.gv; a.glogn = ws.glogn;
   a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
   const int total = s.B * s.H * ws.nb;
-  if (mask_out)
-    hipLaunchKernelGGL(sol2_fused_kernel<true>, dim3(total), dim3(128), 0, stream, a);
-  else
-    hipLaunchKernelGGL(sol2_fused_kernel<false>, dim3(total), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(sol2_fused_kernel, dim3(total), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -187,9 +187,80 @@ __global__ __launch_bounds__(256) void threshold_kernel(
   }
 }
 
+// Diagonal threshold in two wide passes (the single-workgroup-per-head kernel
+// above is latency-bound on long sequences).  Pass 1: per (b, h, slice of key
+// blocks) the sums of K-bar_j and K-bar_j (.) K-bar_j in fp64.  Pass 2: mu_K and
+// v_K = mean of squares - squared mean (the printed estimator, in fp64), then
+// tau_i for 32 query blocks per workgroup.
+constexpr int kStatSlices = 16;
+
+__global__ __launch_bounds__(256) void kstat_partial_kernel(const float* __restrict__ kbar_t, int nb, int nbp,
+                                                            double* __restrict__ part) {
+  __shared__ double s_sum[2][kDim], s_sq[2][kDim];
+  const int bh = blockIdx.x, sl = blockIdx.y, tid = threadIdx.x;
+  const int d = tid & 127, half = tid >> 7;
+  const int per = (nb + kStatSlices - 1) / kStatSlices;
+  const int j0 = sl * per, j1 = min(nb, j0 + per);
+  const float* kt = kbar_t + (size_t)bh * 32 * nbp * 4 + (size_t)(d >> 2) * nbp * 4 + (d & 3);
+  double a = 0.0, q = 0.0;
+  for (int jj = j0 + half; jj < j1; jj += 2) {
+    const double x = kt[(size_t)jj * 4];
+    a += x;
+    q += x * x;
+  }
+  s_sum[half][d] = a;
+  s_sq[half][d] = q;
+  __syncthreads();
+  if (tid < kDim) {
+    double* o = part + ((size_t)bh * kStatSlices + sl) * 2 * kDim;
+    o[tid] = s_sum[0][tid] + s_sum[1][tid];
+    o[kDim + tid] = s_sq[0][tid] + s_sq[1][tid];
+  }
+}
+
+__global__ __launch_bounds__(256) void tau_diag_kernel(const double* __restrict__ part, const float* __restrict__ qbar,
+                                                       int nb, int nbp, float tau, float* __restrict__ kstat,
+                                                       float* __restrict__ tau_i) {
+  __shared__ float s_mu[kDim], s_var[kDim];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  if (tid < kDim) {
+    double a = 0.0, q = 0.0;
+    const double* p = part + (size_t)bh * kStatSlices * 2 * kDim;
+    for (int sl = 0; sl < kStatSlices; ++sl) { a += p[sl * 2 * kDim + tid]; q += p[sl * 2 * kDim + kDim + tid]; }
+    const double mu = a / nb;
+    const float var = (float)(q / nb - mu * mu);
+    s_mu[tid] = (float)mu;
+    s_var[tid] = var;
+    if (blockIdx.y == 0) {
+      kstat[(size_t)bh * 256 + tid] = (float)mu;
+      kstat[(size_t)bh * 256 + 128 + tid] = var;
+    }
+  }
+  __syncthreads();
+  const float scale = 0.08838834764831845f;             // 1/sqrt(128)
+  const int wave = tid >> 6, lane = tid & 63;
+  const int i0 = blockIdx.y * 32 + wave * 8;
+  for (int i = i0; i < min(nb, i0 + 8); ++i) {
+    const float* qi = qbar + ((size_t)bh * nbp + i) * kDim;
+    const float q0 = qi[lane], q1 = qi[lane + 64];
+    float m = q0 * s_mu[lane] + q1 * s_mu[lane + 64];
+    float var = q0 * q0 * s_var[lane] + q1 * q1 * s_var[lane + 64];
+    m = wave_sum(m);
+    var = wave_sum(var);
+    if (lane == 0) tau_i[(size_t)bh * nbp + i] = m * scale + tau * sqrtf(fmaxf(var, 0.f)) * scale;
+  }
+}
+
 hipError_t launch_threshold(Shape s, const Workspace& ws, float tau, int exact, hipStream_t stream) {
-  hipLaunchKernelGGL(threshold_kernel, dim3(s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t, ws.nb,
-                     ws.nbp, tau, exact, ws.kstat, ws.kcov, ws.tau_i);
+  if (exact) {
+    hipLaunchKernelGGL(threshold_kernel, dim3(s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t, ws.nb,
+                       ws.nbp, tau, exact, ws.kstat, ws.kcov, ws.tau_i);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(kstat_partial_kernel, dim3(s.B * s.H, kStatSlices), dim3(256), 0, stream, ws.kbar_t, ws.nb,
+                     ws.nbp, ws.kpart);
+  hipLaunchKernelGGL(tau_diag_kernel, dim3(s.B * s.H, (ws.nb + 31) / 32), dim3(256), 0, stream, ws.kpart, ws.qbar,
+                     ws.nb, ws.nbp, tau, ws.kstat, ws.tau_i);
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
  *   tau_i    float [B][H][nbp]        per-query-block threshold tau_i
  *   kstat    float [B][H][2][128]     mu_K and v_K
  *   kcov     float [B][H][128][128]   covariance of the K block means (EXACT only)
+ *   kpart    double [B][H][16][2][128] partial sums of K block means and their squares
  *   q8, k8   uint8 [B][H][tp][128]    E4M3FN codes (Sol-Attn2)
  *   qscale, kscale float [B][H][nbp]  E4M3 block scales (Sol-Attn2)
  *   qhat     float [B][H][128]        mean-query direction (Sol-Attn2)
@@ -73,7 +74,7 @@ typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
 typedef struct {
     int64_t total_bytes;
     int64_t nb, nbp;
-    int64_t qbar, kbar_t, kbar_h, vbar_h, tau_i, kstat, kcov;
+    int64_t qbar, kbar_t, kbar_h, vbar_h, tau_i, kstat, kcov, kpart;
     int64_t q8, k8, qscale, kscale, qhat, gk, gv, glogn, ghi, qanc;
 } sol_ws_layout;
 

@@ -32,7 +32,9 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, thresh="diag", sample
     _, masks, ws = bsa.debug_routing(1, qg, kg, vg, tau, thresh, sink_start, sink_tokens, out=out)
     out2 = bsa.sol_attn(qg, kg, vg, tau, thresh, sink_start, sink_tokens)
     torch.cuda.synchronize()
-    assert torch.equal(out, out2), "export build and product build disagree"
+    assert torch.equal(out, out2), (f"export and product calls disagree: max diff "
+                                    f"{(out.float() - out2.float()).abs().max().item():.3e} in "
+                                    f"{int((out != out2).sum())} elements")
     ref = sa.routing_only(q, k, tau, sink_start, sink_tokens, thresh)
     nb = (N + 63) // 64
     forced = np.zeros((B, H, nb, nb), dtype=bool)

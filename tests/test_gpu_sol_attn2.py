@@ -40,7 +40,7 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, sample=No
     _, masks, ws = bsa.debug_routing(2, qg, kg, vg, tau, "diag", sink_start, sink_tokens, out=out)
     out2 = bsa.sol_attn2(qg, kg, vg, tau, "diag", sink_start, sink_tokens)
     torch.cuda.synchronize()
-    assert torch.equal(out, out2)
+    assert torch.equal(out, out2), "export and product calls disagree"
     views = bsa.workspace_views(2, ws, B, N, H)
     nb = (N + 63) // 64
     out_c = out.float().cpu().numpy()
