@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense-baselines", action="store_true")
     p.add_argument("--cpu-sample-blocks", type=int, default=24)
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (scales FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -55,6 +57,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     B, H, D = 1, args.heads, 128
     N = args.tokens + args.text_sink
     variant = 1 if args.variant == "sol1" else 2

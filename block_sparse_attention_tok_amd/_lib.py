@@ -237,8 +237,8 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
         nb=L.nb, nbp=nbp,
         qbar=view(L.qbar, torch.float32, (batch, heads, nbp, 128)),
         kbar_t=view(L.kbar_t, torch.float32, (batch, heads, 32, nbp, 4)),
-        kbar_h=view(L.kbar_h, torch.bfloat16, (batch, heads, nbp, 128)),
-        vbar_h=view(L.vbar_h, torch.bfloat16, (batch, heads, nbp, 128)),
+        kbar_h=view(L.kbar_h, torch.bfloat16, (batch, nbp, heads, 128)).transpose(1, 2),
+        vbar_h=view(L.vbar_h, torch.bfloat16, (batch, nbp, heads, 128)).transpose(1, 2),
         tau_i=view(L.tau_i, torch.float32, (batch, heads, nbp)),
         kstat=view(L.kstat, torch.float32, (batch, heads, 2, 128)),
         kcov=view(L.kcov, torch.float32, (batch, heads, 128, 128)),

@@ -89,8 +89,29 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l's
 // 16 bytes land at lds_base + 16 l; lds_base must be wave-uniform.
+typedef __attribute__((address_space(1))) const char global_char;
+
 __device__ __forceinline__ void dma16(const void* gsrc, unsigned char* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((global_char*)gsrc, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Same, with the address split into a wave-uniform base and a 32-bit per-lane
+// byte offset (selects the SGPR-base + VGPR-offset addressing form).
+__device__ __forceinline__ void dma16_off(const void* uniform_base, uint32_t lane_off, unsigned char* lds_base) {
+  __builtin_amdgcn_global_load_lds((global_char*)uniform_base + lane_off, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zeros
+// instead of faulting (gfx9 word 3: default data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + soffset + voffset to
+// lds_base + 16 lane (lds_base wave-uniform).
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset,
+                                          unsigned char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 16, voffset, soffset, 0, 0);
 }
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));

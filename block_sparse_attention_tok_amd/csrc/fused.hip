@@ -48,26 +48,38 @@ struct FusedArgs {
 };
 
 // 16-byte slot swizzles of the 64 x 256-byte K and V tiles (row r, logical chunk
-// lc lives in physical slot lc ^ swz(r)): the K pattern spreads the 8 rows of a
-// b128 read phase over all banks, the V pattern the 4 rows x 2 chunks of a
-// transposed-read lane group.
-__device__ __forceinline__ int swz_k(int r) { return r & 7; }
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+// lc lives in physical slot lc ^ swz(r)), chosen conflict-free for both 32- and
+// 64-bank LDS: K spreads 16 consecutive rows of a b128 read over distinct slots;
+// V spreads the 4 rows x 4 chunks touched by 32 lanes of a transposed read.
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return (0xEA40 >> (4 * (r & 3))) & 15; }   // 0, 4, 10, 14
 
-// DMA a 64 x 128 bf16 tile into LDS (16 KB, two waves x 8 instructions).  Rows
-// r >= valid re-read row valid - 1 (their logits are masked; finite values keep
-// 0 * V finite).
-template <bool kIsV>
-__device__ __forceinline__ void dma_tile(unsigned char* lds, const uint16_t* src, size_t stride, int valid,
-                                         int w, int lane) {
+// DMA of a 64 x 128 bf16 tile into LDS (16 KB, two waves x 8 instructions)
+// through a buffer resource.  Wave w, instruction n fills the 1 KB segment
+// 8 w + n, i.e. rows r = 32 w + 4 n + lane / 16; lane's 16 bytes go to slot
+// lane % 16 of row r, which holds logical chunk (lane % 16) ^ swz(r).  The
+// per-lane byte offset depends on n only through swz_k(r) = 4 (n % 4) + lane / 16
+// (four K variants, one V variant); 4 n rows are added through the uniform
+// soffset.  Rows past the end of the tensor read as zeros (buffer bounds).
+struct DmaOffsets {
+  uint32_t k[4], v;
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(uint32_t row_bytes, int w, int lane) {
+  const uint32_t row = 32 * w + (lane >> 4);
+  DmaOffsets d;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int seg = w * 8 + n;                          // 1 KB segment = rows 4 seg .. 4 seg + 3
-    const int r = 4 * seg + (lane >> 4);
-    const int lc = (lane & 15) ^ (kIsV ? swz_v(r) : swz_k(r));
-    const int rr = r < valid ? r : valid - 1;
-    dma16(src + (size_t)rr * stride + lc * 8, lds + seg * 1024);
-  }
+  for (int n = 0; n < 4; ++n) d.k[n] = row * row_bytes + (((lane & 15) ^ swz_k(row + 4 * n)) << 4);
+  d.v = row * row_bytes + (((lane & 15) ^ swz_v(row)) << 4);
+  return d;
+}
+
+template <bool kIsV>
+__device__ __forceinline__ void dma_tile(unsigned char* lds, __amdgpu_buffer_rsrc_t rsrc, uint32_t tile_off,
+                                         uint32_t row_bytes, const DmaOffsets& off, int w) {
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+    dma16_buf(rsrc, kIsV ? off.v : off.k[n & 3], tile_off + (uint32_t)n * 4 * row_bytes, lds + (w * 8 + n) * 1024);
 }
 
 // Tile order: per chunk c, the proxy tile (code -(c + 1)) if any block of the
@@ -82,6 +94,10 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
   return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  return (const void*)uniform64((uint64_t)p);
 }
 
 __device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, const uint64_t* prox_s,
@@ -114,9 +130,11 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 
   const int total = a.B * a.H * a.nb;
   const int item = xcd_remap(blockIdx.x, total);
-  const int i = item % a.nb;
-  const int bh = item / a.nb;
-  const int h = bh % a.H, b = bh / a.H;
+  // The divisions run on the VALU; readfirstlane keeps the (uniform) indices in
+  // SGPRs so addresses and buffer resources derived from them stay scalar.
+  const int i = __builtin_amdgcn_readfirstlane(item % a.nb);
+  const int bh = __builtin_amdgcn_readfirstlane(item / a.nb);
+  const int h = __builtin_amdgcn_readfirstlane(bh % a.H), b = __builtin_amdgcn_readfirstlane(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t rs = (size_t)a.H * kDim;                      // elements between tokens (BTHD)
@@ -161,12 +179,14 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   __syncthreads();
 
   // ---- per-lane LDS offsets
-  // S^T A operand: key row 32 mt + l32, k-step ks reads logical chunk 2 ks + kg
+  // S^T A operand: key row 32 mt + l32, k-step ks reads logical chunk 2 ks + kg, physical slot
+  // (2 ks + kg) ^ swz_k(row) (row & 15 = l32 & 15 for both m-tiles).
   int koff[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koff[ks] = l32 * 256 + (((2 * ks + kg) ^ swz_k(l32)) << 4);
-  // V^T A operand (transposed read): lane group G = lane / 16, i' = lane % 16 addresses
-  // key 4 kg + i'/4 (+ 16 st + 8 half), dims 32 mt + 16 (G % 2) + 4 (i' % 4)
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = l32 * 256 + 16 * ((2 * ks + kg) ^ swz_k(l32));
+  // V^T A operand (transposed read): lane group G = lane / 16, i' = lane % 16 addresses key
+  // 4 kg + i'/4 (+ 16 st + 8 half; the swizzle depends on key & 3 only), dims
+  // 32 mt + 16 (G % 2) + 4 (i' % 4) = logical chunk 4 mt + 2 (G % 2) + (i' % 4) / 2.
   int voff[4];
   {
     const int ip = lane & 15, gm = (lane >> 4) & 1;
@@ -174,7 +194,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int lc = 4 * mt + 2 * gm + ((ip & 3) >> 1);
-      voff[mt] = key * 256 + ((lc ^ swz_v(key)) << 4) + (ip & 1) * 8;
+      voff[mt] = key * 256 + 16 * (lc ^ swz_v(key)) + (ip & 1) * 8;
     }
   }
 
@@ -184,33 +204,38 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   float m_run = kNegInf, l_run = 0.f;
   const int last_n = a.N - (a.nb - 1) * kBlock;
   const float last_bias = __log2f((float)last_n);
-  const size_t pooled_off = (size_t)bh * a.nbp * kDim;
 
   TileIter it{0, 0, 0};
   int cur = next_tile(it, sel_s, prox_s, nchunks);
-  auto src_of = [&](int code, bool is_v, size_t& stride, int& valid) -> const uint16_t* {
+  // Buffer resources over this head's rows of k / v and of the pooled K-bar / V-bar
+  // (stored with the same row stride), so one set of lane offsets serves every
+  // tile; built at each use from kernel arguments so they stay in SGPRs.
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const uint32_t span_in = (uint32_t)((a.N - 1) * rs + kDim) * 2;
+  const uint32_t span_pool = (uint32_t)((a.nbp - 1) * rs + kDim) * 2;
+  const size_t pooled_head = ((size_t)b * a.nbp * a.H + h) * kDim;
+  const DmaOffsets doff = dma_offsets(row_bytes, w, lane);
+  // Issue the DMA of one buffer (K or V) of tile `code`; returns the tile's valid rows.
+  auto issue = [&](int code_in, bool is_v) -> int {
+    const int code = __builtin_amdgcn_readfirstlane(code_in);
     if (code < 0) {
-      stride = kDim;
-      valid = 64;
-      return (is_v ? a.vbar_h : a.kbar_h) + pooled_off + (size_t)(-code - 1) * 64 * kDim;
+      const uint32_t tile_off = (uint32_t)(-code - 1) * 64 * row_bytes;
+      if (is_v) dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.vbar_h + pooled_head), span_pool), tile_off, row_bytes, doff, w);
+      else dma_tile<false>(Kl, make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool), tile_off, row_bytes, doff, w);
+      return kBlock;
     }
-    stride = rs;
-    valid = min(kBlock, a.N - code * kBlock);
-    return (is_v ? a.v : a.k) + head_off + (size_t)code * kBlock * rs;
+    const uint32_t tile_off = (uint32_t)code * 64 * row_bytes;
+    if (is_v) dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.v + head_off), span_in), tile_off, row_bytes, doff, w);
+    else dma_tile<false>(Kl, make_rsrc(uniform_ptr(a.k + head_off), span_in), tile_off, row_bytes, doff, w);
+    return min(kBlock, a.N - code * kBlock);
   };
-  if (cur != kEnd) {
-    size_t st; int vr;
-    const uint16_t* src = src_of(cur, false, st, vr);
-    dma_tile<false>(Kl, src, st, vr, w, lane);
-  }
+  if (cur != kEnd) issue(cur, false);
 
   while (cur != kEnd) {
     const int nxt = next_tile(it, sel_s, prox_s, nchunks);
-    size_t stride; int valid;
-    const uint16_t* vsrc = src_of(cur, true, stride, valid);
     wait_vm0();
     lds_barrier();                                           // K(cur) landed; V buffer free
-    dma_tile<true>(Vl, vsrc, stride, valid, w, lane);
+    const int valid = issue(cur, true);
 
     // ---- S^T = K Q^T
     floatx16 s0 = {}, s1 = {};
@@ -223,19 +248,18 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     }
     // ---- logits (log2 units) with the tile's mask / bias, online softmax
     const int mode = cur < 0 ? kProxy : (valid == kBlock ? kExactFull : kExactPartial);
-    if (mode == kExactFull) {
-#pragma unroll
-      for (int idx = 0; idx < 16; ++idx) { s0[idx] *= kScaleLog2; s1[idx] *= kScaleLog2; }
-    } else if (mode == kExactPartial) {
+    float scale = kScaleLog2;                               // applied inside the exp argument
+    if (mode == kExactPartial) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
         s0[idx] = key0 < valid ? s0[idx] * kScaleLog2 : kNegInf;
         s1[idx] = key0 + 32 < valid ? s1[idx] * kScaleLog2 : kNegInf;
       }
-    } else {
+      scale = 1.f;
+    } else if (mode == kProxy) {
       const int c = -cur - 1;
-      const uint64_t colmask = prox_s[c];
+      const uint64_t colmask = uniform64(prox_s[c]);
       const int last_key = a.nb - 1 - c * 64;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
@@ -245,11 +269,12 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
         s0[idx] = ((colmask >> key0) & 1) ? s0[idx] * kScaleLog2 + b0 : kNegInf;
         s1[idx] = ((colmask >> (key0 + 32)) & 1) ? s1[idx] * kScaleLog2 + b1 : kNegInf;
       }
+      scale = 1.f;
     }
-    float mx = kNegInf;
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
-    mx = max_with_partner(mx);
+    for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
+    mx = max_with_partner(mx) * scale;                      // scale > 0 commutes with max
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     // Unconditional rescale: skipping it behind a wave-uniform branch made results
@@ -266,8 +291,8 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     float psum = 0.f;
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
-      const float p0 = __builtin_amdgcn_exp2f(s0[idx] - m_use);
-      const float p1 = __builtin_amdgcn_exp2f(s1[idx] - m_use);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], scale, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], scale, -m_use));
       psum += p0 + p1;
       pa[(idx >> 3)][idx & 7] = (__bf16)p0;              // k-step st = keys 16 st .. 16 st + 15
       pa[2 + (idx >> 3)][idx & 7] = (__bf16)p1;
@@ -276,18 +301,15 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 
     wait_vm0();
     lds_barrier();                                           // V(cur) landed; K buffer free
-    if (nxt != kEnd) {
-      size_t st; int vr;
-      const uint16_t* src = src_of(nxt, false, st, vr);
-      dma_tile<false>(Kl, src, st, vr, w, lane);
-    }
+    if (nxt != kEnd) issue(nxt, false);
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const uint2v lo = lds_read_tr16(Vl + voff[mt] + st * 16 * 256);
-        const uint2v hi = lds_read_tr16(Vl + voff[mt] + st * 16 * 256 + 8 * 256);
+        const int vo = voff[mt] + st * 16 * 256;
+        const uint2v lo = lds_read_tr16(Vl + vo);
+        const uint2v hi = lds_read_tr16(Vl + vo + 8 * 256);
         const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
         o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], o[mt], 0, 0, 0);
       }

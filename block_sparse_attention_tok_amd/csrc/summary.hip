@@ -82,8 +82,9 @@ __global__ __launch_bounds__(256) void summary_kernel(
         kh[m] = pack_bf16x2(kb[2 * m], kb[2 * m + 1]);
         vh[m] = pack_bf16x2(vs[2 * m] * inv_n, vs[2 * m + 1] * inv_n);
       }
-      kbar_h[(bh * nbp + j) * 16 + d8] = kh;
-      vbar_h[(bh * nbp + j) * 16 + d8] = vh;
+      const size_t prow = ((size_t)b * nbp + j) * H + h;       // [B][nbp][H][128]
+      kbar_h[prow * 16 + d8] = kh;
+      vbar_h[prow * 16 + d8] = vh;
     }
   }
 }

@@ -53,12 +53,12 @@ typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
 /* Byte offsets into the workspace of the intermediate arrays (for tests and
  * tooling; the kernels own these arrays during a call).  nbp = number of
  * 64-token blocks rounded up to a multiple of 64; tp = nbp * 64.  An offset
- * of -1 means the array does not exist for the variant.  All arrays are
- * indexed [batch][head][...].
+ * of -1 means the array does not exist for the variant.  Arrays are indexed
+ * [batch][head][...] unless shown otherwise.
  *   qbar     float [B][H][nbp][128]   Q block means (Sol-Attn2: of dequantized Q)
  *   kbar_t   float [B][H][32][nbp][4] K block means, 4-dim-interleaved
- *   kbar_h   bf16  [B][H][nbp][128]   K block means (MFMA operand)
- *   vbar_h   bf16  [B][H][nbp][128]   V block means V-hat_j / n_j (MFMA operand)
+ *   kbar_h   bf16  [B][nbp][H][128]   K block means (MFMA operand; token-major like the inputs)
+ *   vbar_h   bf16  [B][nbp][H][128]   V block means V-hat_j / n_j (MFMA operand)
  *   tau_i    float [B][H][nbp]        per-query-block threshold tau_i
  *   kstat    float [B][H][2][128]     mu_K and v_K
  *   kcov     float [B][H][128][128]   covariance of the K block means (EXACT only)
