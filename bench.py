@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense-baselines", action="store_true")
     p.add_argument("--cpu-sample-blocks", type=int, default=24)
+    p.add_argument("--kv-splits", type=int, default=0, help="key-range splits of the fused pass (0 = automatic)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (scales FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
@@ -79,7 +80,7 @@ def main():
     qc, kc, vc = q, k, v
     q, k, v = (t.to(dev) for t in (q, k, v))
     out = torch.empty_like(q)
-    ws = bsa.alloc_workspace(variant, q)
+    ws = bsa.alloc_workspace(variant, q, args.kv_splits if variant == 1 else 0)
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; workspace {ws.numel() / 2**20:.1f} MiB")
 
     nb = (N + 63) // 64
@@ -88,7 +89,8 @@ def main():
     pair_w = np.outer(counts, counts)
 
     def routing(tau):
-        _, m, _ = bsa.debug_routing(variant, q, k, v, tau, "diag", sink_start, sink_tokens, out=None, workspace=ws)
+        _, m, _ = bsa.debug_routing(variant, q, k, v, tau, "diag", sink_start, sink_tokens, out=None, workspace=ws,
+                                    kv_splits=args.kv_splits if variant == 1 else 0)
         return m.numpy()
 
     def sparsity(m):
@@ -122,7 +124,7 @@ def main():
 
     def step():
         bsa.prepare(variant, q, k, v, tau, ws)
-        bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens)
+        bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens, args.kv_splits)
 
     for _ in range(args.warmup):
         step()
@@ -134,7 +136,7 @@ def main():
         ev[s][0].record(stream)
         bsa.prepare(variant, q, k, v, tau, ws)
         ev[s][1].record(stream)
-        bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens)
+        bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens, args.kv_splits)
         ev[s][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -155,7 +157,7 @@ def main():
         # (i) this library with every block exact (a sink over [0, N))
         def dense_own():
             bsa.prepare(1, q, k, v, tau, ws)
-            bsa.fused(1, q, k, v, out, ws, 0, N)
+            bsa.fused(1, q, k, v, out, ws, 0, N, args.kv_splits)
         # (ii) torch SDPA on ROCm, for comparison only
         qt, kt, vt = (t.transpose(1, 2) for t in (q, k, v))
 
@@ -203,6 +205,7 @@ def main():
         "config": {"workload": workload, "batch": B, "heads": H, "head_dim": D, "tokens": N,
                    "tau": round(tau, 5), "realised_sparsity": round(real_sp, 5),
                    "sink": [sink_start, sink_tokens], "median_event_ms": round(med_step, 4),
+                   "kv_splits": bsa.kv_splits_for(B, N, H, args.kv_splits) if variant == 1 else 1,
                    "prepare_ms": round(float(np.mean(prep_ms)), 4), "fused_ms": round(fused_avg, 4),
                    "exact_work_mfma_frac": round(flops_exact / (fused_avg * 1e-3) / (peak * 1e12), 4),
                    "dense_baselines": baselines},

@@ -24,7 +24,8 @@ THRESH = {"diag": 0, "exact": 1}
 
 EXPORTED = [
     "sol_status_string", "sol_attn_validate", "sol_attn_workspace_bytes", "sol_attn_workspace_layout",
-    "sol_attn", "sol_attn_prepare", "sol_attn_fused", "sol_attn_debug_routing",
+    "sol_attn_kv_splits", "sol_attn_workspace_bytes_kv", "sol_attn_workspace_layout_kv",
+    "sol_attn", "sol_attn_prepare", "sol_attn_fused", "sol_attn_fused_kv", "sol_attn_debug_routing",
     "sol_attn2", "sol_attn2_prepare", "sol_attn2_fused", "sol_attn2_debug_routing",
 ]
 
@@ -32,7 +33,7 @@ EXPORTED = [
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov", "kpart",
-        "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc")]
+        "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse")]
 
 
 class SolAttnError(RuntimeError):
@@ -61,6 +62,14 @@ def lib() -> ctypes.CDLL:
     L.sol_attn_workspace_bytes.restype = sz
     L.sol_attn_workspace_layout.argtypes = [i32, i64, i64, i64, i64, ctypes.POINTER(WsLayout)]
     L.sol_attn_workspace_layout.restype = i32
+    L.sol_attn_kv_splits.argtypes = [i64, i64, i64, i32]
+    L.sol_attn_kv_splits.restype = i32
+    L.sol_attn_workspace_bytes_kv.argtypes = [i32, i64, i64, i64, i64, i32]
+    L.sol_attn_workspace_bytes_kv.restype = sz
+    L.sol_attn_workspace_layout_kv.argtypes = [i32, i64, i64, i64, i64, i32, ctypes.POINTER(WsLayout)]
+    L.sol_attn_workspace_layout_kv.restype = i32
+    L.sol_attn_fused_kv.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    L.sol_attn_fused_kv.restype = i32
     full = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp]
     for name in ("sol_attn", "sol_attn2"):
         getattr(L, name).argtypes = full
@@ -73,7 +82,7 @@ def lib() -> ctypes.CDLL:
     for name in ("sol_attn_fused", "sol_attn2_fused"):
         getattr(L, name).argtypes = fused
         getattr(L, name).restype = i32
-    dbg = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp, vp]
+    dbg = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, i32, vp, sz, vp, vp]
     for name in ("sol_attn_debug_routing", "sol_attn2_debug_routing"):
         getattr(L, name).argtypes = dbg
         getattr(L, name).restype = i32
@@ -112,24 +121,31 @@ def _check_tensors(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
         raise ValueError("k and v must have the same shape and device as q")
 
 
-def workspace_bytes(variant: int, batch: int, tokens: int, heads: int, head_dim: int = 128) -> int:
-    n = lib().sol_attn_workspace_bytes(variant, batch, tokens, heads, head_dim)
+def kv_splits_for(batch: int, tokens: int, heads: int, kv_splits: int = 0) -> int:
+    """Effective key-range split count (0 = automatic)."""
+    return int(lib().sol_attn_kv_splits(batch, tokens, heads, kv_splits))
+
+
+def workspace_bytes(variant: int, batch: int, tokens: int, heads: int, head_dim: int = 128,
+                    kv_splits: int = 0) -> int:
+    n = lib().sol_attn_workspace_bytes_kv(variant, batch, tokens, heads, head_dim, kv_splits)
     if n == 0:
         st = lib().sol_attn_validate(batch, tokens, heads, head_dim, 1.0, -1, 0, 0)
         _check(st if st != SOL_OK else 2, "sol_attn_workspace_bytes")
     return int(n)
 
 
-def workspace_layout(variant: int, batch: int, tokens: int, heads: int, head_dim: int = 128) -> WsLayout:
+def workspace_layout(variant: int, batch: int, tokens: int, heads: int, head_dim: int = 128,
+                     kv_splits: int = 0) -> WsLayout:
     L = WsLayout()
-    _check(lib().sol_attn_workspace_layout(variant, batch, tokens, heads, head_dim, ctypes.byref(L)),
-           "sol_attn_workspace_layout")
+    _check(lib().sol_attn_workspace_layout_kv(variant, batch, tokens, heads, head_dim, kv_splits, ctypes.byref(L)),
+           "sol_attn_workspace_layout_kv")
     return L
 
 
-def alloc_workspace(variant: int, q: torch.Tensor) -> torch.Tensor:
+def alloc_workspace(variant: int, q: torch.Tensor, kv_splits: int = 0) -> torch.Tensor:
     B, N, H, D = q.shape
-    return torch.empty(workspace_bytes(variant, B, N, H, D), dtype=torch.uint8, device=q.device)
+    return torch.empty(workspace_bytes(variant, B, N, H, D, kv_splits), dtype=torch.uint8, device=q.device)
 
 
 def validate(batch: int, tokens: int, heads: int, head_dim: int, tau: float, sink_start: Optional[int],
@@ -161,13 +177,24 @@ def _full_call(fn_name: str, variant: int, q, k, v, tau, sink_start, sink_tokens
 
 def sol_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
              sink_start: Optional[int] = None, sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+             workspace: Optional[torch.Tensor] = None, kv_splits: int = 0) -> torch.Tensor:
     """Sol-Attn forward on contiguous bf16 [batch, tokens, heads, 128] GPU tensors.
 
     tau: threshold coefficient (higher selects fewer KV blocks; 0 is not dense).
     sink_start None with sink_tokens > 0 keeps the last sink_tokens tokens exact.
+    kv_splits: key-range splits of the fused pass (0 = automatic).
     """
-    return _full_call("sol_attn", SOL_VARIANT_SOL1, q, k, v, tau, sink_start, sink_tokens, thresh, out, workspace)
+    if kv_splits == 0:
+        return _full_call("sol_attn", SOL_VARIANT_SOL1, q, k, v, tau, sink_start, sink_tokens, thresh, out,
+                          workspace)
+    _check_tensors(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(SOL_VARIANT_SOL1, q, kv_splits)
+    prepare(SOL_VARIANT_SOL1, q, k, v, tau, workspace, thresh)
+    fused(SOL_VARIANT_SOL1, q, k, v, out, workspace, sink_start, sink_tokens, kv_splits)
+    return out
 
 
 def sol_attn2(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
@@ -187,17 +214,22 @@ def prepare(variant: int, q, k, v, tau: float, workspace: torch.Tensor, thresh: 
 
 
 def fused(variant: int, q, k, v, out, workspace: torch.Tensor, sink_start: Optional[int] = None,
-          sink_tokens: int = 0):
-    """Stage 2 (the fused kernel) reading a workspace prepared for the same inputs."""
+          sink_tokens: int = 0, kv_splits: int = 0):
+    """Stage 2 (the fused kernel [+ split merge]) reading a workspace prepared for the same inputs."""
     B, N, H, D = q.shape
-    name = "sol_attn_fused" if variant == SOL_VARIANT_SOL1 else "sol_attn2_fused"
-    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
-                                int(sink_tokens), _ptr(workspace), workspace.numel(), _stream(q.device)), name)
+    if variant == SOL_VARIANT_SOL1:
+        _check(lib().sol_attn_fused_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
+                                       int(sink_tokens), int(kv_splits), _ptr(workspace), workspace.numel(),
+                                       _stream(q.device)), "sol_attn_fused_kv")
+        return
+    _check(lib().sol_attn2_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
+                                 int(sink_tokens), _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "sol_attn2_fused")
 
 
 def debug_routing(variant: int, q, k, v, tau: float = 1.0, thresh: str = "diag", sink_start: Optional[int] = None,
                   sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None, kv_splits: int = 0):
     """Run the full call and return (out, masks [B, H, nb, nb] bool on the CPU, workspace).
 
     The masks are the decisions the fused kernel itself made (test export)."""
@@ -206,12 +238,12 @@ def debug_routing(variant: int, q, k, v, tau: float = 1.0, thresh: str = "diag",
     nb = (N + 63) // 64
     nbw = (nb + 63) // 64
     if workspace is None:
-        workspace = alloc_workspace(variant, q)
+        workspace = alloc_workspace(variant, q, kv_splits)
     words = torch.zeros(B * H * nb * nbw, dtype=torch.int64, device=q.device)
     name = "sol_attn_debug_routing" if variant == SOL_VARIANT_SOL1 else "sol_attn2_debug_routing"
     _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, float(tau),
-                                _sink_start(sink_start), int(sink_tokens), THRESH[thresh], _ptr(workspace),
-                                workspace.numel(), _ptr(words), _stream(q.device)), name)
+                                _sink_start(sink_start), int(sink_tokens), THRESH[thresh], int(kv_splits),
+                                _ptr(workspace), workspace.numel(), _ptr(words), _stream(q.device)), name)
     w = words.view(B, H, nb, nbw).cpu()
     bits = torch.arange(64, dtype=torch.int64)
     m = ((w.unsqueeze(-1) >> bits) & 1).bool().reshape(B, H, nb, nbw * 64)[..., :nb]

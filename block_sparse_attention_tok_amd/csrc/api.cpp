@@ -14,6 +14,7 @@ namespace {
 constexpr int64_t kBlock = 64;
 constexpr int64_t kDim = 128;
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+constexpr int64_t kMaxTokens = (int64_t)1 << 19;   // 524288: 128 routing chunks
 
 int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
@@ -22,8 +23,10 @@ int check_shape(int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim) 
   if (head_dim != kDim) return SOL_ERR_HEAD_DIM;
   // element offsets and grid sizes stay inside 32-bit block counts / 64-bit offsets
   const int64_t nb = (tokens + kBlock - 1) / kBlock;
-  if (tokens >= kMaxIndex || heads >= 65536 || batch >= 65536) return SOL_ERR_SHAPE;
-  if (batch * heads * nb >= kMaxIndex) return SOL_ERR_SHAPE;
+  if (tokens > kMaxTokens || heads >= 65536 || batch >= 65536) return SOL_ERR_SHAPE;
+  if (batch * heads * nb * 16 >= kMaxIndex) return SOL_ERR_SHAPE;
+  // one head's rows of one batch must fit a 32-bit buffer range
+  if ((tokens - 1) * heads * kDim * 2 + kDim * 2 > (int64_t)0xFFFFFFFF) return SOL_ERR_SHAPE;
   return SOL_OK;
 }
 
@@ -39,7 +42,23 @@ int sink_range(int64_t tokens, int64_t sink_start, int64_t sink_tokens, int* b0,
   return SOL_OK;
 }
 
-int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim, sol_ws_layout* L) {
+constexpr int kMaxSplits = 16;
+
+// Effective split count: splits cover whole 64-block routing chunks.
+int effective_splits(int64_t tokens, int requested) {
+  const int64_t nb = (tokens + kBlock - 1) / kBlock;
+  const int nchunks = (int)((nb + 63) / 64);
+  int want = requested;
+  if (want <= 0) want = (nchunks + 3) / 4;                 // automatic: one split per four chunks
+  if (want > kMaxSplits) want = kMaxSplits;
+  if (want > nchunks) want = nchunks;
+  if (want < 1) want = 1;
+  const int cps = (nchunks + want - 1) / want;            // chunks per split
+  return (nchunks + cps - 1) / cps;
+}
+
+int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim, sol_ws_layout* L,
+           int kv_splits = 0) {
   int st = check_shape(batch, tokens, heads, head_dim);
   if (st != SOL_OK) return st;
   if (variant != SOL_VARIANT_SOL1 && variant != SOL_VARIANT_SOL2) return SOL_ERR_ARG;
@@ -72,6 +91,12 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->ghi = take(bh * nbp * 8);
     L->qanc = take(bh * nbp * 2 * kDim * 4);
   }
+  // split-KV partials (Sol-Attn only)
+  L->kv_splits = variant == SOL_VARIANT_SOL1 ? effective_splits(tokens, kv_splits) : 1;
+  if (L->kv_splits > 1) {
+    L->opart = take(L->kv_splits * bh * tokens * kDim * 2);
+    L->olse = take(L->kv_splits * bh * tokens * 4);
+  }
   L->total_bytes = off;
   return SOL_OK;
 }
@@ -100,6 +125,9 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.glogn = (float*)at(L.glogn);
   w.ghi = (uint64_t*)at(L.ghi);
   w.qanc = (float*)at(L.qanc);
+  w.kv_splits = (int)L.kv_splits;
+  w.opart = (uint16_t*)at(L.opart);
+  w.olse = (float*)at(L.olse);
   return w;
 }
 
@@ -107,9 +135,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Common argument checks; fills the layout on success.
 int prologue(int variant, const void* q, const void* k, const void* v, int64_t batch, int64_t tokens,
-             int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes, sol_ws_layout* L) {
+             int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes, sol_ws_layout* L,
+             int kv_splits = 0) {
   if (!q || !k || !v || !workspace) return SOL_ERR_NULL;
-  int st = layout(variant, batch, tokens, heads, head_dim, L);
+  int st = layout(variant, batch, tokens, heads, head_dim, L, kv_splits);
   if (st != SOL_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || ((uintptr_t)workspace & 255)) return SOL_ERR_ARG;
   if ((int64_t)workspace_bytes < L->total_bytes) return SOL_ERR_WORKSPACE;
@@ -121,6 +150,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SOL_OK : SOL_ERR_HIP; }
 solattn::Shape shape_of(int64_t batch, int64_t tokens, int64_t heads) {
   return solattn::Shape{(int)batch, (int)tokens, (int)heads};
 }
+
+int check_kv(int kv_splits) { return (kv_splits >= 0 && kv_splits <= kMaxSplits) ? SOL_OK : SOL_ERR_ARG; }
 
 int check_thresh(int thresh) { return (thresh == SOL_THRESH_DIAG || thresh == SOL_THRESH_EXACT) ? SOL_OK : SOL_ERR_ARG; }
 
@@ -166,11 +197,32 @@ int sol_attn_workspace_layout(int variant, int64_t batch, int64_t tokens, int64_
   return layout(variant, batch, tokens, heads, head_dim, out);
 }
 
+int sol_attn_kv_splits(int64_t batch, int64_t tokens, int64_t heads, int kv_splits) {
+  if (check_shape(batch, tokens, heads, kDim) != SOL_OK || check_kv(kv_splits) != SOL_OK) return 0;
+  return effective_splits(tokens, kv_splits);
+}
+
+size_t sol_attn_workspace_bytes_kv(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                                   int kv_splits) {
+  sol_ws_layout L;
+  if (check_kv(kv_splits) != SOL_OK) return 0;
+  if (layout(variant, batch, tokens, heads, head_dim, &L, kv_splits) != SOL_OK) return 0;
+  return (size_t)L.total_bytes;
+}
+
+int sol_attn_workspace_layout_kv(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                                 int kv_splits, sol_ws_layout* out) {
+  if (!out) return SOL_ERR_NULL;
+  if (check_kv(kv_splits) != SOL_OK) return SOL_ERR_ARG;
+  return layout(variant, batch, tokens, heads, head_dim, out, kv_splits);
+}
+
 int sol_attn_prepare(const void* q, const void* k, const void* v, int64_t batch, int64_t tokens, int64_t heads,
                      int64_t head_dim, float tau, int thresh, void* workspace, size_t workspace_bytes,
                      void* stream) {
   sol_ws_layout L;
-  int st = prologue(SOL_VARIANT_SOL1, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  // the split-KV partials sit at the end of the layout and stage 1 does not use them
+  int st = prologue(SOL_VARIANT_SOL1, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L, 1);
   if (st != SOL_OK) return st;
   if (!std::isfinite(tau)) return SOL_ERR_TAU;
   if ((st = check_thresh(thresh)) != SOL_OK) return st;
@@ -185,9 +237,10 @@ int sol_attn_prepare(const void* q, const void* k, const void* v, int64_t batch,
 static int fused_common(int variant, const void* q, const void* k, const void* v, void* out, int64_t batch,
                         int64_t tokens, int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens,
                         void* workspace, size_t workspace_bytes, uint64_t* mask_bits, void* stream,
-                        bool out_required) {
+                        bool out_required, int kv_splits = 0) {
   sol_ws_layout L;
-  int st = prologue(variant, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  if (check_kv(kv_splits) != SOL_OK) return SOL_ERR_ARG;
+  int st = prologue(variant, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L, kv_splits);
   if (st != SOL_OK) return st;
   if (out_required && !out) return SOL_ERR_NULL;
   if (out && !aligned16(out)) return SOL_ERR_ARG;
@@ -209,6 +262,13 @@ int sol_attn_fused(const void* q, const void* k, const void* v, void* out, int64
                       workspace, workspace_bytes, nullptr, stream, true);
 }
 
+int sol_attn_fused_kv(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                      int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens, int kv_splits,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return fused_common(SOL_VARIANT_SOL1, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
+                      workspace, workspace_bytes, nullptr, stream, true, kv_splits);
+}
+
 int sol_attn(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens, int64_t heads,
              int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens, int thresh, void* workspace,
              size_t workspace_bytes, void* stream) {
@@ -223,15 +283,16 @@ int sol_attn(const void* q, const void* k, const void* v, void* out, int64_t bat
 
 int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
                            int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens,
-                           int thresh, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
+                           int thresh, int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
                            void* stream) {
   if (!mask_bits) return SOL_ERR_NULL;
   int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
   if (st != SOL_OK) return st;
+  if ((st = check_kv(kv_splits)) != SOL_OK) return st;
   st = sol_attn_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);
   if (st != SOL_OK) return st;
   return fused_common(SOL_VARIANT_SOL1, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
-                      workspace, workspace_bytes, mask_bits, stream, false);
+                      workspace, workspace_bytes, mask_bits, stream, false, kv_splits);
 }
 
 int sol_attn2_prepare(const void* q, const void* k, const void* v, int64_t batch, int64_t tokens, int64_t heads,
@@ -275,9 +336,10 @@ int sol_attn2(const void* q, const void* k, const void* v, void* out, int64_t ba
 
 int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
                             int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens,
-                            int thresh, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
+                            int thresh, int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
                             void* stream) {
   if (!mask_bits) return SOL_ERR_NULL;
+  if (kv_splits != 0 && kv_splits != 1) return SOL_ERR_ARG;
   int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
   if (st != SOL_OK) return st;
   st = sol_attn2_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);

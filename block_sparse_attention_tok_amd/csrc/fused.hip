@@ -41,6 +41,8 @@ constexpr int kEnd = -0x7fffffff;
 struct FusedArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; uint16_t* out;
   int B, N, H, nb, nbp, nbw;
+  int S, cps;                   // key-range splits and routing chunks per split
+  uint16_t* opart; float* olse; // split partials (S > 1)
   const float* qbar; const float* kbar_t; const uint16_t* kbar_h; const uint16_t* vbar_h;
   const float* tau_i;
   int sink_b0, sink_b1;
@@ -100,16 +102,17 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)uniform64((uint64_t)p);
 }
 
+// Chunks are numbered locally from c0 (the split's first chunk); returned codes are global.
 __device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, const uint64_t* prox_s,
-                                         int nchunks) {
+                                         int nchunks, int c0) {
   while (it.c < nchunks) {
     if (it.phase == 0) {
       it.phase = 1;
       it.bits = uniform64(sel_s[it.c]);
-      if (uniform64(prox_s[it.c])) return -(it.c + 1);
+      if (uniform64(prox_s[it.c])) return -(c0 + it.c + 1);
     }
     if (it.bits) {
-      const int jb = it.c * 64 + __builtin_ctzll(it.bits);
+      const int jb = (c0 + it.c) * 64 + __builtin_ctzll(it.bits);
       it.bits &= it.bits - 1;
       return jb;
     }
@@ -128,12 +131,16 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   __shared__ float part[2][2][64];
   __shared__ uint64_t sel_s[kMaxChunks], prox_s[kMaxChunks];
 
-  const int total = a.B * a.H * a.nb;
+  // Work item order: query block fastest, then key split, then (batch, head), so the
+  // workgroups that run together on one XCD share a head and a key range.
+  const int total = a.B * a.H * a.S * a.nb;
   const int item = xcd_remap(blockIdx.x, total);
   // The divisions run on the VALU; readfirstlane keeps the (uniform) indices in
   // SGPRs so addresses and buffer resources derived from them stay scalar.
   const int i = __builtin_amdgcn_readfirstlane(item % a.nb);
-  const int bh = __builtin_amdgcn_readfirstlane(item / a.nb);
+  const int rest = __builtin_amdgcn_readfirstlane(item / a.nb);
+  const int split = __builtin_amdgcn_readfirstlane(rest % a.S);
+  const int bh = __builtin_amdgcn_readfirstlane(rest / a.S);
   const int h = __builtin_amdgcn_readfirstlane(bh % a.H), b = __builtin_amdgcn_readfirstlane(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,8 +161,10 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 
   // ---- routing for every chunk (fp32); wave w sums dims 64 w .. 64 w + 63
   const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
-  const int nchunks = a.nbp / 64;
-  for (int c = 0; c < nchunks; ++c) {
+  const int c_begin = split * a.cps;                        // this split's routing chunks
+  const int c_end = min(a.nbp / 64, c_begin + a.cps);
+  const int nchunks = c_end - c_begin;
+  for (int c = c_begin; c < c_end; ++c) {
     const int j = c * 64 + lane;
     float acc = 0.f;
 #pragma unroll 4
@@ -171,8 +180,8 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     const uint64_t selm = __ballot(sel);
     const uint64_t proxm = __ballot(valid) & ~selm;
     if (tid == 0) {
-      sel_s[c] = selm;
-      prox_s[c] = proxm;
+      sel_s[c - c_begin] = selm;
+      prox_s[c - c_begin] = proxm;
       if (a.mask_out) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
     }
   }
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   const float last_bias = __log2f((float)last_n);
 
   TileIter it{0, 0, 0};
-  int cur = next_tile(it, sel_s, prox_s, nchunks);
+  int cur = next_tile(it, sel_s, prox_s, nchunks, c_begin);
   // Buffer resources over this head's rows of k / v and of the pooled K-bar / V-bar
   // (stored with the same row stride), so one set of lane offsets serves every
   // tile; built at each use from kernel arguments so they stay in SGPRs.
@@ -232,7 +241,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   if (cur != kEnd) issue(cur, false);
 
   while (cur != kEnd) {
-    const int nxt = next_tile(it, sel_s, prox_s, nchunks);
+    const int nxt = next_tile(it, sel_s, prox_s, nchunks, c_begin);
     wait_vm0();
     lds_barrier();                                           // K(cur) landed; V buffer free
     const int valid = issue(cur, true);
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
       scale = 1.f;
     } else if (mode == kProxy) {
       const int c = -cur - 1;
-      const uint64_t colmask = uniform64(prox_s[c]);
+      const uint64_t colmask = uniform64(prox_s[c - c_begin]);
       const int last_key = a.nb - 1 - c * 64;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
@@ -317,11 +326,13 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     cur = nxt;
   }
 
-  // ---- epilogue: O / l, bf16 RNE, BTHD store
+  // ---- epilogue: O / l, bf16 RNE, BTHD store (or this split's partial row and its
+  // log2-sum-exp m + log2 l for the merge)
   const float l_tot = sum_with_partner(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (qrow < a.N && a.out != nullptr) {
-    uint16_t* dst = a.out + head_off + (size_t)qrow * rs;
+  uint16_t* dst_base = a.S > 1 ? a.opart + (size_t)split * a.B * a.N * rs : a.out;
+  if (qrow < a.N && dst_base != nullptr) {
+    uint16_t* dst = dst_base + head_off + (size_t)qrow * rs;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -331,20 +342,62 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
         pk[1] = pack_bf16x2(o[mt][4 * g + 2] * inv, o[mt][4 * g + 3] * inv);
         *(uint2v*)(dst + 32 * mt + 8 * g + 4 * kg) = pk;
       }
+    if (a.S > 1 && kg == 0)
+      a.olse[((size_t)split * a.B * a.N + (size_t)b * a.N + qrow) * a.H + h] =
+          l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
   }
+}
+
+// Merge of the key-range splits: o = sum_s 2^(lse_s - lse) o_s with lse = log2 sum_s 2^lse_s.
+// One thread per (row, 8 dims); partials are BTHD like the output.
+__global__ __launch_bounds__(256) void merge_splits_kernel(const uint4v* __restrict__ opart,
+                                                           const float* __restrict__ olse, int S,
+                                                           size_t rows, uint4v* __restrict__ out) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * 16) return;
+  const size_t row = t >> 4;
+  float m = kNegInf;
+  for (int sp = 0; sp < S; ++sp) m = fmaxf(m, olse[sp * rows + row]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    const float ls = olse[sp * rows + row];
+    const float wt = ls == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ls - m);
+    const uint4v x = opart[sp * rows * 16 + t];
+    wsum += wt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += wt * bf16_lo(x[e]);
+      acc[2 * e + 1] += wt * bf16_hi(x[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint4v r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  out[t] = r;
 }
 
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                         Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* mask_out,
                         hipStream_t stream) {
-  if (ws.nbp / 64 > kMaxChunks) return hipErrorInvalidValue;
+  const int nchunks = ws.nbp / 64;
+  const int S = ws.kv_splits;
+  const int cps = (nchunks + S - 1) / S;
+  if (cps > kMaxChunks || (S > 1 && (!ws.opart || !ws.olse))) return hipErrorInvalidValue;
   FusedArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = (ws.nb + 63) / 64;
+  a.S = S; a.cps = cps; a.opart = ws.opart; a.olse = ws.olse;
   a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h; a.tau_i = ws.tau_i;
   a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
-  const int total = s.B * s.H * ws.nb;
+  const int total = s.B * s.H * S * ws.nb;
   hipLaunchKernelGGL(sol_fused_kernel, dim3(total), dim3(128), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1 || out == nullptr) return e;
+  const size_t rows = (size_t)s.B * s.N * s.H;
+  hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
+                     (const uint4v*)ws.opart, ws.olse, S, rows, (uint4v*)out);
   return hipGetLastError();
 }
 

@@ -26,6 +26,9 @@ struct Workspace {
   float* glogn;     // [B][H][nbp][2]
   uint64_t* ghi;    // [B][H][nbp]
   float* qanc;      // [B][H][nbp][2][128]
+  int kv_splits;    // key-range splits of the fused Sol-Attn pass (1 = none)
+  uint16_t* opart;  // [S][B][N][H][128] bf16 normalized partial outputs
+  float* olse;      // [S][B][N][H] log2-sum-exp of the partial rows
 };
 
 struct Shape {

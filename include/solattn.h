@@ -34,7 +34,8 @@ extern "C" {
 typedef enum {
     SOL_OK = 0,
     SOL_ERR_NULL = 1,        /* a required pointer is NULL */
-    SOL_ERR_SHAPE = 2,       /* batch/tokens/heads < 1, or sizes overflow the index range */
+    SOL_ERR_SHAPE = 2,       /* batch/tokens/heads < 1, tokens > 524288, or one head's rows
+                                of one batch span more than 4 GiB */
     SOL_ERR_HEAD_DIM = 3,    /* head_dim != 128 */
     SOL_ERR_TAU = 4,         /* tau is NaN or infinite */
     SOL_ERR_SINK = 5,        /* sink_tokens < 0, or the sink range leaves [0, tokens) */
@@ -70,12 +71,15 @@ typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
  *   glogn    float [B][H][nbp][2]     ln n_g, -inf for an empty group (Sol-Attn2)
  *   ghi      uint64 [B][H][nbp]       bit u set iff token u of the block is in G_hi (Sol-Attn2)
  *   qanc     float [B][H][nbp][2][128] 32-token anchor means of dequantized Q (Sol-Attn2)
+ *   opart    bf16  [S][B][N][H][128]   per-key-split normalized partial outputs (S = kv_splits > 1)
+ *   olse     float [S][B][N][H]        per-key-split log2-sum-exp of the partial rows
  */
 typedef struct {
     int64_t total_bytes;
     int64_t nb, nbp;
     int64_t qbar, kbar_t, kbar_h, vbar_h, tau_i, kstat, kcov, kpart;
     int64_t q8, k8, qscale, kscale, qhat, gk, gv, glogn, ghi, qanc;
+    int64_t kv_splits, opart, olse;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */
@@ -96,6 +100,24 @@ size_t sol_attn_workspace_bytes(int variant, int64_t batch, int64_t tokens, int6
 /* Fill *layout (host pointer) with the workspace offsets; host-only. */
 int sol_attn_workspace_layout(int variant, int64_t batch, int64_t tokens, int64_t heads,
                               int64_t head_dim, sol_ws_layout* layout);
+
+/* Split-KV (Sol-Attn README, "Long-sequence tuning on H100": kv_splits).  The
+ * fused Sol-Attn pass can split each query block's key range into S parts run by
+ * separate workgroups and merged afterwards (partial outputs in bf16 with an fp32
+ * log-sum-exp); on MI355X this keeps the K/V working set of the workgroups that
+ * run together on one XCD inside its L2.  kv_splits = 0 means automatic: one
+ * split per 256 key blocks (four 64-block routing chunks), at most 16.  Splits
+ * cover whole routing chunks: a request r becomes ceil(C / ceil(C / r)) for C
+ * chunks (never above C).
+ * Host-only; returns the effective split count (>= 1), or 0 on a shape error. */
+int sol_attn_kv_splits(int64_t batch, int64_t tokens, int64_t heads, int kv_splits);
+
+/* Workspace size / layout for an explicit kv_splits (0 = automatic); the
+ * functions above use the automatic value. */
+size_t sol_attn_workspace_bytes_kv(int variant, int64_t batch, int64_t tokens, int64_t heads,
+                                   int64_t head_dim, int kv_splits);
+int sol_attn_workspace_layout_kv(int variant, int64_t batch, int64_t tokens, int64_t heads,
+                                 int64_t head_dim, int kv_splits, sol_ws_layout* layout);
 
 /*
  * Sol-Attn forward (Sol-Attn paper §3, Figure 4; Sol-Attn README "Core API",
@@ -129,7 +151,16 @@ int sol_attn_fused(const void* q, const void* k, const void* v, void* out,
                    int64_t sink_start, int64_t sink_tokens,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Test and tooling export, not part of the hot path: like sol_attn, and the
+/* Stage 2 with an explicit kv_splits (0 = automatic); the workspace must be
+ * sized by sol_attn_workspace_bytes_kv for the same kv_splits.  Runs the fused
+ * kernel and, for more than one split, the merge kernel. */
+int sol_attn_fused_kv(const void* q, const void* k, const void* v, void* out,
+                      int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                      int64_t sink_start, int64_t sink_tokens, int kv_splits,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test and tooling export, not part of the hot path: like sol_attn (with an
+ * explicit kv_splits, 0 = automatic, and a workspace sized for it), and the
  * fused kernel also writes the routing decision it made, as bit masks
  * mask_bits[b][h][i][w] (device, uint64, nbw = ceil(nb/64) words per query
  * block; bit (j % 64) of word j / 64 set iff KV block j was exact for query
@@ -137,7 +168,7 @@ int sol_attn_fused(const void* q, const void* k, const void* v, void* out,
 int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* out,
                            int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                            float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
-                           void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
+                           int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
                            void* stream);
 
 /*
@@ -167,11 +198,12 @@ int sol_attn2_fused(const void* q, const void* k, const void* v, void* out,
                     int64_t sink_start, int64_t sink_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Sol-Attn2 routing export, as sol_attn_debug_routing. */
+/* Sol-Attn2 routing export, as sol_attn_debug_routing (kv_splits must be 0 or 1:
+ * the Sol-Attn2 pass is not split). */
 int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* out,
                             int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                             float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
-                            void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
+                            int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
                             void* stream);
 
 #ifdef __cplusplus

@@ -75,7 +75,8 @@ def test_workspace_sizes_and_layout(L):
             assert n == lay.total_bytes > 0
             nb = (N + 63) // 64
             assert lay.nb == nb and lay.nbp % 64 == 0 and lay.nbp >= nb
-            offs = sorted(o for name, _ in _lib.WsLayout._fields_ if name not in ("total_bytes", "nb", "nbp")
+            offs = sorted(o for name, _ in _lib.WsLayout._fields_
+                          if name not in ("total_bytes", "nb", "nbp", "kv_splits")
                           for o in [getattr(lay, name)] if o >= 0)
             assert all(o % 256 == 0 for o in offs)
             assert offs[-1] < n
@@ -83,6 +84,25 @@ def test_workspace_sizes_and_layout(L):
                 assert lay.q8 == -1 and lay.gk == -1
     assert L.sol_attn_workspace_bytes(1, 1, 1024, 2, 64) == 0
     assert L.sol_attn_workspace_bytes(3, 1, 1024, 2, 128) == 0
+
+
+@pytest.mark.parametrize("tokens,req,expect", [
+    (1024, 0, 1), (8192, 0, 1), (8193, 0, 1), (14040, 0, 1), (16385, 0, 2), (32768, 0, 2), (66048, 0, 5), (131584, 0, 9),
+    (32768, 1, 1), (32768, 2, 2), (32768, 3, 3), (32768, 8, 8), (32768, 16, 8), (1024, 4, 1), (131584, 16, 11),
+])
+def test_kv_split_rule(L, tokens, req, expect):
+    """Splits cover whole 64-block routing chunks; automatic = one split per four chunks."""
+    assert L.sol_attn_kv_splits(1, tokens, 32, req) == expect
+    lay = __import__("block_sparse_attention_tok_amd")._lib.workspace_layout(1, 1, tokens, 32, kv_splits=req)
+    assert lay.kv_splits == expect
+    assert (lay.opart >= 0) == (expect > 1)
+    assert L.sol_attn_kv_splits(1, tokens, 32, 17) == 0       # out of range
+
+
+def test_shape_limits(L):
+    assert L.sol_attn_validate(1, 524288, 32, 128, 1.0, -1, 0, 0) == 0
+    assert L.sol_attn_validate(1, 524289, 1, 128, 1.0, -1, 0, 0) == 2
+    assert L.sol_attn_validate(1, 524288, 64, 128, 1.0, -1, 0, 0) == 2      # a head's rows exceed 4 GiB
 
 
 def test_entry_points_reject_bad_arguments_before_any_launch(L):
@@ -104,8 +124,10 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
     # unknown threshold type
     assert L.sol_attn(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 9, fake, 1 << 30, None) == 8
     # missing mask buffer for the debug export
-    assert L.sol_attn_debug_routing(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, 1 << 30,
+    assert L.sol_attn_debug_routing(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, 0, fake, 1 << 30,
                                     None, None) == 1
+    # kv_splits out of range
+    assert L.sol_attn_fused_kv(fake, fake, fake, fake, 1, 1024, 2, 128, -1, 0, 17, fake, 1 << 30, None) == 8
 
 
 def test_python_validate_wrapper():

@@ -178,3 +178,31 @@ def test_long_sequence_with_text_sink():
     w = long_sink(65536)
     q, k, v = w.qkv()
     run_case(q, k, v, 1.3, sink_start=0, sink_tokens=512, sample=2, seed=4)
+
+
+@pytest.mark.parametrize("N", [32768, 32768 + 13])
+def test_kv_splits_match_oracle(N):
+    """Split-KV (README "Long-sequence tuning": kv_splits): 1, 2, 4 and 8 key-range splits all match
+    the oracle, and agree with each other to bf16 rounding."""
+    q, k, v = _qkv(1, N, 2, 2500)
+    tau = 1.0
+    qg, kg, vg = to_gpu(q, k, v)
+    _, masks, _ = bsa.debug_routing(1, qg, kg, vg, tau)
+    gsel = masks.numpy()
+    ref = sa.routing_only(q, k, tau)
+    mask_check(gsel, ref["sel"], ref["s_hat"], ref["tau_i"])
+    nb = (N + 63) // 64
+    want = np.concatenate([oracle_rows(q, k, v, 0, h, i, gsel[0, h, i]) for h in range(2) for i in range(nb)])
+    outs = {}
+    for kv in (1, 2, 4, 8):
+        eff = bsa.kv_splits_for(1, N, 2, kv)
+        out = bsa.sol_attn(qg, kg, vg, tau, kv_splits=kv)
+        torch.cuda.synchronize()
+        oc = out.float().cpu().numpy()
+        got = np.concatenate([oc[0, i * 64:min(N, i * 64 + 64), h, :] for h in range(2) for i in range(nb)])
+        err, mx = compare_out(got, want, what=f"kv_splits={kv}")
+        say(f"   kv_splits {kv} (effective {eff}): rel L2 {err:.2e} max abs {mx:.2e}")
+        outs[kv] = out.float()
+    for kv in (2, 4, 8):
+        d = (outs[kv] - outs[1]).norm() / outs[1].norm()
+        assert d < 1e-2, f"kv_splits={kv} vs 1: {d:.3e}"
