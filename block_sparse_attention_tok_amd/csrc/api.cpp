@@ -25,8 +25,9 @@ int check_shape(int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim) 
   const int64_t nb = (tokens + kBlock - 1) / kBlock;
   if (tokens > kMaxTokens || heads >= 65536 || batch >= 65536) return SOL_ERR_SHAPE;
   if (batch * heads * nb * 16 >= kMaxIndex) return SOL_ERR_SHAPE;
-  // one head's rows of one batch must fit a 32-bit buffer range
-  if ((tokens - 1) * heads * kDim * 2 + kDim * 2 > (int64_t)0xFFFFFFFF) return SOL_ERR_SHAPE;
+  // one head's rows of one batch, padded to whole 64-row blocks, must fit a 32-bit
+  // buffer range (tile loads address up to 63 rows past the last token)
+  if ((nb * kBlock - 1) * heads * kDim * 2 + kDim * 2 > (int64_t)0xFFFFFFFF) return SOL_ERR_SHAPE;
   return SOL_OK;
 }
 

@@ -66,6 +66,7 @@ namespace solattn {
 // s_waitcnt immediates for the gfx9 encoding (vmcnt in bits 3:0 and 15:14,
 // expcnt in 6:4, lgkmcnt in 11:8); the counters not named are left at max.
 constexpr int kWaitVm0 = 0x0F70;      // vmcnt(0)
+constexpr int kWaitVm8 = 0x0F78;      // vmcnt(8)
 constexpr int kWaitLgkm0 = 0xC07F;    // lgkmcnt(0)
 
 // Workgroup barrier for LDS hand-offs that must not wait for in-flight global
@@ -82,6 +83,14 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ void wait_vm0() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most 8 of this wave's vector-memory operations are in flight
+// (they complete in issue order): all but the last 8 DMA instructions have landed.
+__device__ __forceinline__ void wait_vm8() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVm8);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 

@@ -61,8 +61,9 @@ __device__ __forceinline__ int swz_v(int r) { return (0xEA40 >> (4 * (r & 3))) &
 // 8 w + n, i.e. rows r = 32 w + 4 n + lane / 16; lane's 16 bytes go to slot
 // lane % 16 of row r, which holds logical chunk (lane % 16) ^ swz(r).  The
 // per-lane byte offset depends on n only through swz_k(r) = 4 (n % 4) + lane / 16
-// (four K variants, one V variant); 4 n rows are added through the uniform
-// soffset.  Rows past the end of the tensor read as zeros (buffer bounds).
+// (four K variants, one V variant).  The whole offset (tile, 4 n rows, lane) is
+// in the VGPR operand, the one the buffer range check covers, so rows past the
+// end of the tensor read as zeros.
 struct DmaOffsets {
   uint32_t k[4], v;
 };
@@ -81,7 +82,7 @@ __device__ __forceinline__ void dma_tile(unsigned char* lds, __amdgpu_buffer_rsr
                                          uint32_t row_bytes, const DmaOffsets& off, int w) {
 #pragma unroll
   for (int n = 0; n < 8; ++n)
-    dma16_buf(rsrc, kIsV ? off.v : off.k[n & 3], tile_off + (uint32_t)n * 4 * row_bytes, lds + (w * 8 + n) * 1024);
+    dma16_buf(rsrc, (kIsV ? off.v : off.k[n & 3]) + tile_off + (uint32_t)n * 4 * row_bytes, 0, lds + (w * 8 + n) * 1024);
 }
 
 // Tile order: per chunk c, the proxy tile (code -(c + 1)) if any block of the
@@ -124,12 +125,29 @@ __device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, co
 
 enum TileMode { kExactFull = 0, kExactPartial = 1, kProxy = 2 };
 
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the 8 bf16 values of a packed P fragment into acc (v_dot2c_f32_bf16 with ones).
+// The pairs are taken with shufflevector: extracting them from a bit_cast to
+// 4 x uint32 lowers, with the ROCm 7.2 compiler, to four reads of the first pair.
+__device__ __forceinline__ float add_bf16x8(bf16x8 x, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+  return acc;
+}
+
 __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Kl[64 * 256];
   __shared__ __attribute__((aligned(1024))) unsigned char Vl[64 * 256];
   __shared__ __attribute__((aligned(16))) float qb_s[kDim];
   __shared__ float part[2][2][64];
   __shared__ uint64_t sel_s[kMaxChunks], prox_s[kMaxChunks];
+  __shared__ int redo_s[2];
 
   // Work item order: query block fastest, then key split, then (batch, head), so the
   // workgroups that run together on one XCD share a head and a key range.
@@ -207,15 +225,6 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     }
   }
 
-  floatx16 o[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
-  float m_run = kNegInf, l_run = 0.f;
-  const int last_n = a.N - (a.nb - 1) * kBlock;
-  const float last_bias = __log2f((float)last_n);
-
-  TileIter it{0, 0, 0};
-  int cur = next_tile(it, sel_s, prox_s, nchunks, c_begin);
   // Buffer resources over this head's rows of k / v and of the pooled K-bar / V-bar
   // (stored with the same row stride), so one set of lane offsets serves every
   // tile; built at each use from kernel arguments so they stay in SGPRs.
@@ -224,6 +233,66 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   const uint32_t span_pool = (uint32_t)((a.nbp - 1) * rs + kDim) * 2;
   const size_t pooled_head = ((size_t)b * a.nbp * a.H + h) * kDim;
   const DmaOffsets doff = dma_offsets(row_bytes, w, lane);
+
+  // S^T = K Q^T for the 64-row K tile at LDS `kl` (two 32-key m-tiles).
+  auto scores = [&](const unsigned char* kl, floatx16& s0, floatx16& s1) {
+    s0 = floatx16{};
+    s1 = floatx16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a0 = *(const bf16x8*)(kl + koff[ks]);
+      const bf16x8 a1 = *(const bf16x8*)(kl + 32 * 256 + koff[ks]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
+    }
+  };
+
+  // ---- reference max.  Every unselected block j contributes n_j 2^(x_j) with
+  // x_j = log2(e) q . K-bar_j / sqrt(d), and every selected block at least as much
+  // (the mean of exp over a block is >= exp of the mean logit), so with
+  // m_ref = max_j x_j over the split's blocks the softmax denominator is >= 1 and
+  // needs no running maximum: P = 2^(x - m_ref) is taken directly.  Exact logits
+  // above m_ref are representable up to ~2^127; a row that still overflows sends
+  // the workgroup through the rescaling loop below.
+  float m_ref;
+  {
+    auto pool = [&]() { return make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool); };
+    dma_tile<false>(Kl, pool(), (uint32_t)c_begin * 64 * row_bytes, row_bytes, doff, w);
+    float mx = kNegInf;
+    for (int c = 0; c < nchunks; ++c) {
+      const unsigned char* buf = (c & 1) ? Vl : Kl;
+      if (c + 1 < nchunks) {
+        dma_tile<false>((c & 1) ? Kl : Vl, pool(), (uint32_t)(c_begin + c + 1) * 64 * row_bytes, row_bytes, doff, w);
+        wait_vm8();
+      } else {
+        wait_vm0();
+      }
+      lds_barrier();                                         // pooled tile c landed
+      floatx16 s0, s1;
+      scores(buf, s0, s1);
+      const int nvalid = __builtin_amdgcn_readfirstlane(a.nb - (c_begin + c) * 64);
+      if (nvalid >= kBlock) {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
+      } else {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+          const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+          mx = fmaxf(mx, fmaxf(key0 < nvalid ? s0[idx] : kNegInf, key0 + 32 < nvalid ? s1[idx] : kNegInf));
+        }
+      }
+      lds_barrier();                                         // buffer free for tile c + 2
+    }
+    m_ref = max_with_partner(mx) * kScaleLog2;
+  }
+
+  floatx16 o[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
+  float m_run = kNegInf, l_run = 0.f;
+  const int last_n = a.N - (a.nb - 1) * kBlock;
+  const float last_bias = __log2f((float)last_n);
+
   // Issue the DMA of one buffer (K or V) of tile `code`; returns the tile's valid rows.
   auto issue = [&](int code_in, bool is_v) -> int {
     const int code = __builtin_amdgcn_readfirstlane(code_in);
@@ -238,97 +307,165 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     else dma_tile<false>(Kl, make_rsrc(uniform_ptr(a.k + head_off), span_in), tile_off, row_bytes, doff, w);
     return min(kBlock, a.N - code * kBlock);
   };
-  if (cur != kEnd) issue(cur, false);
 
-  while (cur != kEnd) {
-    const int nxt = next_tile(it, sel_s, prox_s, nchunks, c_begin);
-    wait_vm0();
-    lds_barrier();                                           // K(cur) landed; V buffer free
-    const int valid = issue(cur, true);
+  // The tile stream of this split.  kSafe = false: fixed reference max, no
+  // rescaling; kSafe = true: running max with the usual rescale of O and l.
+  auto run_tiles = [&](auto safe_tag) {
+    constexpr bool kSafe = decltype(safe_tag)::value;
+    TileIter it{0, 0, 0};
+    int cur = next_tile(it, sel_s, prox_s, nchunks, c_begin);
+    if (cur != kEnd) issue(cur, false);
+    const float neg_ref = -m_ref;
+    while (cur != kEnd) {
+      const int nxt = next_tile(it, sel_s, prox_s, nchunks, c_begin);
+      wait_vm0();
+      lds_barrier();                                         // K(cur) landed; V buffer free
+      const int valid = issue(cur, true);
 
-    // ---- S^T = K Q^T
-    floatx16 s0 = {}, s1 = {};
+      floatx16 s0, s1;
+      scores(Kl, s0, s1);
+      const int mode = cur < 0 ? kProxy : (valid == kBlock ? kExactFull : kExactPartial);
+      bf16x8 pa[4];
+      if constexpr (!kSafe) {
+        // ---- P = 2^(x - m_ref) with the tile's mask / proxy weight n_j
+        float p0[16], p1[16];
+        if (mode == kExactFull) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(Kl + koff[ks]);
-      const bf16x8 a1 = *(const bf16x8*)(Kl + 32 * 256 + koff[ks]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
-    }
-    // ---- logits (log2 units) with the tile's mask / bias, online softmax
-    const int mode = cur < 0 ? kProxy : (valid == kBlock ? kExactFull : kExactPartial);
-    float scale = kScaleLog2;                               // applied inside the exp argument
-    if (mode == kExactPartial) {
+          for (int idx = 0; idx < 16; ++idx) {
+            p0[idx] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], kScaleLog2, neg_ref));
+            p1[idx] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], kScaleLog2, neg_ref));
+          }
+        } else if (mode == kExactPartial) {
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
-        s0[idx] = key0 < valid ? s0[idx] * kScaleLog2 : kNegInf;
-        s1[idx] = key0 + 32 < valid ? s1[idx] * kScaleLog2 : kNegInf;
+          for (int idx = 0; idx < 16; ++idx) {
+            const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], kScaleLog2, neg_ref));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], kScaleLog2, neg_ref));
+            p0[idx] = key0 < valid ? e0 : 0.f;
+            p1[idx] = key0 + 32 < valid ? e1 : 0.f;
+          }
+        } else {
+          const int c = -cur - 1;
+          const uint64_t colmask = uniform64(prox_s[c - c_begin]);
+          const int last_key = a.nb - 1 - c * 64;
+          const float off_full = 6.0f - m_ref;                  // log2(64) for full blocks
+          const float off_last = last_bias - m_ref;
+#pragma unroll
+          for (int idx = 0; idx < 16; ++idx) {
+            const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+            const float e0 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(s0[idx], kScaleLog2, key0 == last_key ? off_last : off_full));
+            const float e1 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(s1[idx], kScaleLog2, key0 + 32 == last_key ? off_last : off_full));
+            p0[idx] = ((colmask >> key0) & 1) ? e0 : 0.f;
+            p1[idx] = ((colmask >> (key0 + 32)) & 1) ? e1 : 0.f;
+          }
+        }
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+          pa[(idx >> 3)][idx & 7] = (__bf16)p0[idx];            // k-step st = keys 16 st .. 16 st + 15
+          pa[2 + (idx >> 3)][idx & 7] = (__bf16)p1[idx];
+        }
+        // l sums the bf16 P that the PV product consumes.
+#pragma unroll
+        for (int st = 0; st < 4; ++st) l_run = add_bf16x8(pa[st], l_run);
+      } else {
+        // ---- logits (log2 units) with the tile's mask / bias, online softmax
+        float scale = kScaleLog2;                             // applied inside the exp argument
+        if (mode == kExactPartial) {
+#pragma unroll
+          for (int idx = 0; idx < 16; ++idx) {
+            const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+            s0[idx] = key0 < valid ? s0[idx] * kScaleLog2 : kNegInf;
+            s1[idx] = key0 + 32 < valid ? s1[idx] * kScaleLog2 : kNegInf;
+          }
+          scale = 1.f;
+        } else if (mode == kProxy) {
+          const int c = -cur - 1;
+          const uint64_t colmask = uniform64(prox_s[c - c_begin]);
+          const int last_key = a.nb - 1 - c * 64;
+#pragma unroll
+          for (int idx = 0; idx < 16; ++idx) {
+            const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+            const float b0 = key0 == last_key ? last_bias : 6.0f;
+            const float b1 = key0 + 32 == last_key ? last_bias : 6.0f;
+            s0[idx] = ((colmask >> key0) & 1) ? s0[idx] * kScaleLog2 + b0 : kNegInf;
+            s1[idx] = ((colmask >> (key0 + 32)) & 1) ? s1[idx] * kScaleLog2 + b1 : kNegInf;
+          }
+          scale = 1.f;
+        }
+        float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
+        mx = max_with_partner(mx) * scale;                    // scale > 0 commutes with max
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        // Unconditional rescale (skipping it behind a wave-uniform branch made results
+        // timing-dependent with two waves per SIMD).
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int idx = 0; idx < 16; ++idx) o[mt][idx] *= alpha;
+        m_run = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+          const float q0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], scale, -m_use));
+          const float q1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], scale, -m_use));
+          psum += q0 + q1;
+          pa[(idx >> 3)][idx & 7] = (__bf16)q0;
+          pa[2 + (idx >> 3)][idx & 7] = (__bf16)q1;
+        }
+        l_run += psum;
       }
-      scale = 1.f;
-    } else if (mode == kProxy) {
-      const int c = -cur - 1;
-      const uint64_t colmask = uniform64(prox_s[c - c_begin]);
-      const int last_key = a.nb - 1 - c * 64;
+
+      wait_vm0();
+      lds_barrier();                                         // V(cur) landed; K buffer free
+      if (nxt != kEnd) issue(nxt, false);
+      // ---- O^T += V^T P^T
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
-        const float b0 = key0 == last_key ? last_bias : 6.0f;   // log2(64) for full blocks
-        const float b1 = key0 + 32 == last_key ? last_bias : 6.0f;
-        s0[idx] = ((colmask >> key0) & 1) ? s0[idx] * kScaleLog2 + b0 : kNegInf;
-        s1[idx] = ((colmask >> (key0 + 32)) & 1) ? s1[idx] * kScaleLog2 + b1 : kNegInf;
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int vo = voff[mt] + st * 16 * 256;
+          const uint2v lo = lds_read_tr16(Vl + vo);
+          const uint2v hi = lds_read_tr16(Vl + vo + 8 * 256);
+          const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], o[mt], 0, 0, 0);
+        }
       }
-      scale = 1.f;
+      cur = nxt;
     }
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
-    mx = max_with_partner(mx) * scale;                      // scale > 0 commutes with max
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    // Unconditional rescale: skipping it behind a wave-uniform branch made results
-    // depend on timing with two waves per SIMD (MFMA accumulators rewritten under
-    // a branch), so O and l are always multiplied by alpha (1 when the max is unchanged).
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    l_run *= alpha;
+  };
+
+  run_tiles(BoolTag<false>{});
+  float l_tot = sum_with_partner(l_run);
+  float m_fin = m_ref;
+  {
+    // Any non-finite O or l in the workgroup: rerun its tiles with rescaling.
+    float chk = l_tot * 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) o[mt][idx] *= alpha;
-    m_run = m_new;
-    bf16x8 pa[4];
-    float psum = 0.f;
+      for (int idx = 0; idx < 16; ++idx) chk = __builtin_fmaf(o[mt][idx], 0.f, chk);
+    const uint64_t bad = __ballot(!(chk == 0.f));
+    if (lane == 0) redo_s[w] = bad != 0;
+    __syncthreads();
+    if (redo_s[0] | redo_s[1]) {
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], scale, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], scale, -m_use));
-      psum += p0 + p1;
-      pa[(idx >> 3)][idx & 7] = (__bf16)p0;              // k-step st = keys 16 st .. 16 st + 15
-      pa[2 + (idx >> 3)][idx & 7] = (__bf16)p1;
+      for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
+      l_run = 0.f;
+      m_run = kNegInf;
+      run_tiles(BoolTag<true>{});
+      l_tot = sum_with_partner(l_run);
+      m_fin = m_run;
     }
-    l_run += psum;
-
-    wait_vm0();
-    lds_barrier();                                           // V(cur) landed; K buffer free
-    if (nxt != kEnd) issue(nxt, false);
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int vo = voff[mt] + st * 16 * 256;
-        const uint2v lo = lds_read_tr16(Vl + vo);
-        const uint2v hi = lds_read_tr16(Vl + vo + 8 * 256);
-        const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], o[mt], 0, 0, 0);
-      }
-    }
-    cur = nxt;
   }
 
   // ---- epilogue: O / l, bf16 RNE, BTHD store (or this split's partial row and its
   // log2-sum-exp m + log2 l for the merge)
-  const float l_tot = sum_with_partner(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   uint16_t* dst_base = a.S > 1 ? a.opart + (size_t)split * a.B * a.N * rs : a.out;
   if (qrow < a.N && dst_base != nullptr) {
@@ -344,7 +481,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
       }
     if (a.S > 1 && kg == 0)
       a.olse[((size_t)split * a.B * a.N + (size_t)b * a.N + qrow) * a.H + h] =
-          l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+          l_tot > 0.f ? m_fin + __log2f(l_tot) : kNegInf;
   }
 }
 

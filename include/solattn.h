@@ -35,7 +35,7 @@ typedef enum {
     SOL_OK = 0,
     SOL_ERR_NULL = 1,        /* a required pointer is NULL */
     SOL_ERR_SHAPE = 2,       /* batch/tokens/heads < 1, tokens > 524288, or one head's rows
-                                of one batch span more than 4 GiB */
+                                of one batch, padded to a multiple of 64, span more than 4 GiB */
     SOL_ERR_HEAD_DIM = 3,    /* head_dim != 128 */
     SOL_ERR_TAU = 4,         /* tau is NaN or infinite */
     SOL_ERR_SINK = 5,        /* sink_tokens < 0, or the sink range leaves [0, tokens) */

@@ -103,6 +103,9 @@ def test_shape_limits(L):
     assert L.sol_attn_validate(1, 524288, 32, 128, 1.0, -1, 0, 0) == 0
     assert L.sol_attn_validate(1, 524289, 1, 128, 1.0, -1, 0, 0) == 2
     assert L.sol_attn_validate(1, 524288, 64, 128, 1.0, -1, 0, 0) == 2      # a head's rows exceed 4 GiB
+    # H = 48: 349526 rows fit 4 GiB, but padded to 349568 (whole 64-row blocks) they do not
+    assert L.sol_attn_validate(1, 349526, 48, 128, 1.0, -1, 0, 0) == 2
+    assert L.sol_attn_validate(1, 349504, 48, 128, 1.0, -1, 0, 0) == 0
 
 
 def test_entry_points_reject_bad_arguments_before_any_launch(L):
