@@ -33,7 +33,8 @@ EXPORTED = [
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov", "kpart",
-        "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse")]
+        "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse",
+        "sel", "tmu", "tnu", "tlz")]
 
 
 class SolAttnError(RuntimeError):

@@ -91,6 +91,10 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->glogn = take(bh * nbp * 2 * 4);
     L->ghi = take(bh * nbp * 8);
     L->qanc = take(bh * nbp * 2 * kDim * 4);
+    L->sel = take(bh * nb * (nbp / 64) * 8);
+    L->tmu = take(bh * nbp * 2 * kDim * 4);
+    L->tnu = take(bh * nbp * 2 * kDim * 4);
+    L->tlz = take(bh * nbp * 2 * 4);
   }
   // split-KV partials (Sol-Attn only)
   L->kv_splits = variant == SOL_VARIANT_SOL1 ? effective_splits(tokens, kv_splits) : 1;
@@ -129,6 +133,10 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.kv_splits = (int)L.kv_splits;
   w.opart = (uint16_t*)at(L.opart);
   w.olse = (float*)at(L.olse);
+  w.sel = (uint64_t*)at(L.sel);
+  w.tmu = (float*)at(L.tmu);
+  w.tnu = (float*)at(L.tnu);
+  w.tlz = (float*)at(L.tlz);
   return w;
 }
 
@@ -252,8 +260,13 @@ static int fused_common(int variant, const void* q, const void* k, const void* v
   if (variant == SOL_VARIANT_SOL1)
     return hip_status(solattn::launch_fused((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                             (uint16_t*)out, s, w, b0, b1, mask_bits, (hipStream_t)stream));
-  return hip_status(solattn::launch_fused2((const uint16_t*)v, (uint16_t*)out, s, w, b0, b1, mask_bits,
-                                           (hipStream_t)stream));
+  hipStream_t hs = (hipStream_t)stream;
+  if ((st = hip_status(solattn::launch_tail2(s, w, b0, b1, hs))) != SOL_OK) return st;
+  if (mask_bits) {
+    const size_t bytes = (size_t)batch * heads * w.nb * (w.nbp / 64) * sizeof(uint64_t);
+    if ((st = hip_status(hipMemcpyAsync(mask_bits, w.sel, bytes, hipMemcpyDeviceToDevice, hs))) != SOL_OK) return st;
+  }
+  return hip_status(solattn::launch_fused2((const uint16_t*)v, (uint16_t*)out, s, w, hs));
 }
 
 int sol_attn_fused(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,

@@ -29,7 +29,7 @@
 //     inside each MFMA is permuted identically on both operands).
 #include "common.h"
 #include "kernels.h"
-#include "tile.h"
+#include "pipe.h"
 
 namespace solattn {
 
@@ -49,42 +49,6 @@ struct FusedArgs {
   uint64_t* mask_out;
 };
 
-// 16-byte slot swizzles of the 64 x 256-byte K and V tiles (row r, logical chunk
-// lc lives in physical slot lc ^ swz(r)), chosen conflict-free for both 32- and
-// 64-bank LDS: K spreads 16 consecutive rows of a b128 read over distinct slots;
-// V spreads the 4 rows x 4 chunks touched by 32 lanes of a transposed read.
-__device__ __forceinline__ int swz_k(int r) { return r & 15; }
-__device__ __forceinline__ int swz_v(int r) { return (0xEA40 >> (4 * (r & 3))) & 15; }   // 0, 4, 10, 14
-
-// DMA of a 64 x 128 bf16 tile into LDS (16 KB, two waves x 8 instructions)
-// through a buffer resource.  Wave w, instruction n fills the 1 KB segment
-// 8 w + n, i.e. rows r = 32 w + 4 n + lane / 16; lane's 16 bytes go to slot
-// lane % 16 of row r, which holds logical chunk (lane % 16) ^ swz(r).  The
-// per-lane byte offset depends on n only through swz_k(r) = 4 (n % 4) + lane / 16
-// (four K variants, one V variant).  The whole offset (tile, 4 n rows, lane) is
-// in the VGPR operand, the one the buffer range check covers, so rows past the
-// end of the tensor read as zeros.
-struct DmaOffsets {
-  uint32_t k[4], v;
-};
-
-__device__ __forceinline__ DmaOffsets dma_offsets(uint32_t row_bytes, int w, int lane) {
-  const uint32_t row = 32 * w + (lane >> 4);
-  DmaOffsets d;
-#pragma unroll
-  for (int n = 0; n < 4; ++n) d.k[n] = row * row_bytes + (((lane & 15) ^ swz_k(row + 4 * n)) << 4);
-  d.v = row * row_bytes + (((lane & 15) ^ swz_v(row)) << 4);
-  return d;
-}
-
-template <bool kIsV>
-__device__ __forceinline__ void dma_tile(unsigned char* lds, __amdgpu_buffer_rsrc_t rsrc, uint32_t tile_off,
-                                         uint32_t row_bytes, const DmaOffsets& off, int w) {
-#pragma unroll
-  for (int n = 0; n < 8; ++n)
-    dma16_buf(rsrc, (kIsV ? off.v : off.k[n & 3]) + tile_off + (uint32_t)n * 4 * row_bytes, 0, lds + (w * 8 + n) * 1024);
-}
-
 // Tile order: per chunk c, the proxy tile (code -(c + 1)) if any block of the
 // chunk is unselected, then its selected blocks (code = block index).
 struct TileIter {
@@ -92,16 +56,6 @@ struct TileIter {
   int phase;           // 0: proxy not yet considered for chunk c
   uint64_t bits;
 };
-
-__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  return (const void*)uniform64((uint64_t)p);
-}
 
 // Chunks are numbered locally from c0 (the split's first chunk); returned codes are global.
 __device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, const uint64_t* prox_s,
@@ -124,22 +78,6 @@ __device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, co
 }
 
 enum TileMode { kExactFull = 0, kExactPartial = 1, kProxy = 2 };
-
-template <bool B> struct BoolTag { static constexpr bool value = B; };
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Sum of the 8 bf16 values of a packed P fragment into acc (v_dot2c_f32_bf16 with ones).
-// The pairs are taken with shufflevector: extracting them from a bit_cast to
-// 4 x uint32 lowers, with the ROCm 7.2 compiler, to four reads of the first pair.
-__device__ __forceinline__ float add_bf16x8(bf16x8 x, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
-  return acc;
-}
 
 __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Kl[64 * 256];
@@ -211,19 +149,8 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   int koff[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) koff[ks] = l32 * 256 + 16 * ((2 * ks + kg) ^ swz_k(l32));
-  // V^T A operand (transposed read): lane group G = lane / 16, i' = lane % 16 addresses key
-  // 4 kg + i'/4 (+ 16 st + 8 half; the swizzle depends on key & 3 only), dims
-  // 32 mt + 16 (G % 2) + 4 (i' % 4) = logical chunk 4 mt + 2 (G % 2) + (i' % 4) / 2.
-  int voff[4];
-  {
-    const int ip = lane & 15, gm = (lane >> 4) & 1;
-    const int key = 4 * kg + (ip >> 2);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int lc = 4 * mt + 2 * gm + ((ip & 3) >> 1);
-      voff[mt] = key * 256 + 16 * (lc ^ swz_v(key)) + (ip & 1) * 8;
-    }
-  }
+  int voff[4];                                               // V^T operand (transposed read)
+  v_operand_offsets(lane, voff);
 
   // Buffer resources over this head's rows of k / v and of the pooled K-bar / V-bar
   // (stored with the same row stride), so one set of lane offsets serves every
@@ -424,18 +351,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
       wait_vm0();
       lds_barrier();                                         // V(cur) landed; K buffer free
       if (nxt != kEnd) issue(nxt, false);
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int vo = voff[mt] + st * 16 * 256;
-          const uint2v lo = lds_read_tr16(Vl + vo);
-          const uint2v hi = lds_read_tr16(Vl + vo + 8 * 256);
-          const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], o[mt], 0, 0, 0);
-        }
-      }
+      pv_tile(o, Vl, voff, pa);                              // O^T += V^T P^T
       cur = nxt;
     }
   };

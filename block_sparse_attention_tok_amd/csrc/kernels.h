@@ -29,6 +29,10 @@ struct Workspace {
   int kv_splits;    // key-range splits of the fused Sol-Attn pass (1 = none)
   uint16_t* opart;  // [S][B][N][H][128] bf16 normalized partial outputs
   float* olse;      // [S][B][N][H] log2-sum-exp of the partial rows
+  uint64_t* sel;    // [B][H][nb][nbp / 64] Sol-Attn2 routing bits
+  float* tmu;       // [B][H][nbp][2][128] Sol-Attn2 tail key means per anchor
+  float* tnu;       // [B][H][nbp][2][128] Sol-Attn2 tail value means per anchor
+  float* tlz;       // [B][H][nbp][2] log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d)
 };
 
 struct Shape {
@@ -51,8 +55,9 @@ hipError_t launch_quant_summary(const uint16_t* q, const uint16_t* k, const uint
                                 const Workspace& ws, hipStream_t stream);
 hipError_t launch_qhat(Shape s, const Workspace& ws, hipStream_t stream);
 hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream);
-// Sol-Attn2 stage 2.
-hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws,
-                         int sink_b0, int sink_b1, uint64_t* mask_out, hipStream_t stream);
+// Sol-Attn2 stage 2: routing and the complementary tail per anchor (writes sel, tmu, tnu, tlz),
+// then the exact FP8 pass combined with the tail.
+hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream);
+hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, hipStream_t stream);
 
 }  // namespace solattn

@@ -1,0 +1,102 @@
+// Tile pipeline pieces shared by the fused Sol-Attn and Sol-Attn2 kernels on gfx950:
+// swizzled 64-row tiles moved HBM -> LDS by buffer DMA, and the PV product read
+// back through ds_read_b64_tr_b16.
+#pragma once
+#include "common.h"
+
+namespace solattn {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
+// 16-byte slot swizzles of the 64 x 256-byte K and V tiles (row r, logical chunk
+// lc lives in physical slot lc ^ swz(r)), chosen conflict-free for both 32- and
+// 64-bank LDS: K spreads 16 consecutive rows of a b128 read over distinct slots;
+// V spreads the 4 rows x 4 chunks touched by 32 lanes of a transposed read.
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return (0xEA40 >> (4 * (r & 3))) & 15; }   // 0, 4, 10, 14
+
+// DMA of a 64 x 128 bf16 tile into LDS (16 KB, two waves x 8 instructions)
+// through a buffer resource.  Wave w, instruction n fills the 1 KB segment
+// 8 w + n, i.e. rows r = 32 w + 4 n + lane / 16; lane's 16 bytes go to slot
+// lane % 16 of row r, which holds logical chunk (lane % 16) ^ swz(r).  The
+// per-lane byte offset depends on n only through swz_k(r) = 4 (n % 4) + lane / 16
+// (four K variants, one V variant).  The whole offset (tile, 4 n rows, lane) is
+// in the VGPR operand, the one the buffer range check covers, so rows past the
+// end of the tensor read as zeros.
+struct DmaOffsets {
+  uint32_t k[4], v;
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(uint32_t row_bytes, int w, int lane) {
+  const uint32_t row = 32 * w + (lane >> 4);
+  DmaOffsets d;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) d.k[n] = row * row_bytes + (((lane & 15) ^ swz_k(row + 4 * n)) << 4);
+  d.v = row * row_bytes + (((lane & 15) ^ swz_v(row)) << 4);
+  return d;
+}
+
+template <bool kIsV>
+__device__ __forceinline__ void dma_tile(unsigned char* lds, __amdgpu_buffer_rsrc_t rsrc, uint32_t tile_off,
+                                         uint32_t row_bytes, const DmaOffsets& off, int w) {
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+    dma16_buf(rsrc, (kIsV ? off.v : off.k[n & 3]) + tile_off + (uint32_t)n * 4 * row_bytes, 0, lds + (w * 8 + n) * 1024);
+}
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  return (const void*)uniform64((uint64_t)p);
+}
+
+// Sum of the 8 bf16 values of a packed P fragment into acc (v_dot2c_f32_bf16 with ones).
+// The pairs are taken with shufflevector: extracting them from a bit_cast to
+// 4 x uint32 lowers, with the ROCm 7.2 compiler, to four reads of the first pair.
+__device__ __forceinline__ float add_bf16x8(bf16x8 x, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+  return acc;
+}
+
+// V^T A-operand offsets of the transposed read (v_mfma_f32_32x32x16_bf16): lane group
+// G = lane / 16, i' = lane % 16 addresses key 4 kg + i'/4 (+ 16 st + 8 half; the
+// swizzle depends on key & 3 only), dims 32 mt + 16 (G % 2) + 4 (i' % 4) = logical
+// chunk 4 mt + 2 (G % 2) + (i' % 4) / 2.
+__device__ __forceinline__ void v_operand_offsets(int lane, int (&voff)[4]) {
+  const int ip = lane & 15, gm = (lane >> 4) & 1, kg = lane >> 5;
+  const int key = 4 * kg + (ip >> 2);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int lc = 4 * mt + 2 * gm + ((ip & 3) >> 1);
+    voff[mt] = key * 256 + 16 * (lc ^ swz_v(key)) + (ip & 1) * 8;
+  }
+}
+
+// O^T += V^T P^T for one 64-key tile: pa[st] holds keys 16 st + 8 (e / 4) + 4 kg + e % 4
+// (e = 0..7) of the lane's query column, the same key order as the transposed V read.
+__device__ __forceinline__ void pv_tile(floatx16 (&o)[4], const unsigned char* Vl, const int (&voff)[4],
+                                        const bf16x8 (&pa)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int vo = voff[mt] + st * 16 * 256;
+      const uint2v lo = lds_read_tr16(Vl + vo);
+      const uint2v hi = lds_read_tr16(Vl + vo + 8 * 256);
+      const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
+      o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], o[mt], 0, 0, 0);
+    }
+  }
+}
+
+}  // namespace solattn

@@ -12,7 +12,7 @@
 // ties joining the upper group; V stays bf16; an empty block uses scale 1.
 #include "common.h"
 #include "kernels.h"
-#include "tile.h"
+#include "pipe.h"
 
 namespace solattn {
 
@@ -234,49 +234,260 @@ hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStr
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: fused FP8 exact attention + complementary tail.
-// One workgroup per (b, h, query block i); wave w owns query rows 32 w .. 32 w + 31,
-// which are exactly anchor a = (i, w).
-//   exact: S^T = K8 Q8^T on v_mfma_f32_32x32x64_f8f6f4 (OCP E4M3), times s_q s_k;
-//          online softmax and O^T += V^T P^T in bf16 as in Sol-Attn.
-//   tail:  per chunk, lane jj scores the two groups of block 64 c + jj against the
-//          anchor mean (Eq. (1), online log-sum-exp in log2 units) and the wave
-//          accumulates sum w (k-bar_g, v-bar_g) with lane-owned dims.
-//   end:   mu_a, nu_a, ln Z_a; delta_t (Eq. (2)); Eq. (3) with the exact state.
+// Stage 2a: routing and the complementary tail of every anchor (draft, Method,
+// Eq. (1)).  One workgroup (two waves) per (b, h, 32 consecutive query blocks);
+// wave w's lane column n = lane % 32 is anchor n of query blocks i0 + 16 w ..
+// i0 + 16 w + 15 (query block i0 + 16 w + n / 2, half n % 2).  Tiles of 16 key
+// blocks (32 groups) stream through LDS, each row a group's bf16 mean key then
+// mean value:
+//   routing  s-hat_ij = Q-bar_i . K-bar_j / sqrt(d) (fp32, dequantized means) for the
+//            32 x 16 (query block, key block) pairs; the bits are written to `sel`
+//            for the exact pass;
+//   scores   l_ga = ln n_g + q-bar_a . k-bar_g / sqrt(d) on v_mfma_f32_32x32x16_bf16
+//            (A = the group rows, B = the anchors), masked to groups of blocks the
+//            anchor's query block did not select; online log-sum-exp per anchor;
+//   means    [mu_a; nu_a]^T += [Gk | Gv]^T W^T on the same MFMA (A = the group rows
+//            through ds_read_b64_tr_b16, B = the bf16 weights).
+// The anchor results (mu_a, nu_a, log2 Z_a - log2(e) q-bar_a . mu_a / sqrt(d)) go to
+// the workspace; the exact pass adds delta_t and combines (Eqs. (2), (3)).
 // ---------------------------------------------------------------------------
+constexpr int kTailStride = 528;       // bytes per LDS group row: 256 (k-bar) + 256 (v-bar) + 16 pad
+
+struct Tail2Args {
+  int B, N, H, nb, nbp, nbw;
+  const float* qbar; const float* kbar_t; const float* tau_i; const float* qanc;
+  const uint16_t* gk; const uint16_t* gv; const float* glogn;
+  int sink_b0, sink_b1;
+  uint64_t* sel; float* tmu; float* tnu; float* tlz;
+};
+
+__global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
+  __shared__ __attribute__((aligned(16))) float qb_s[32][kDim];
+  __shared__ __attribute__((aligned(16))) unsigned char G_s[32 * kTailStride];
+  __shared__ float tau_s[32];
+  __shared__ uint32_t selw_s[32];        // routing bits of the tile (16 key blocks) per query block
+  __shared__ uint64_t selacc_s[32];      // routing bits of the current 64-block chunk
+  __shared__ float gl_s[32];             // ln n_g of the tile's groups (-inf: empty or padding)
+
+  const int bh = blockIdx.y, i0 = blockIdx.x * 32;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
+  const int nqb = min(32, a.nb - i0);
+
+  for (int e = tid; e < 32 * 32; e += 128) {
+    const int r = e >> 5, c4 = e & 31;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < nqb) x = ((const float4*)(a.qbar + ((size_t)bh * a.nbp + i0 + r) * kDim))[c4];
+    ((float4*)qb_s[r])[c4] = x;
+  }
+  if (tid < 32) {
+    tau_s[tid] = tid < nqb ? a.tau_i[(size_t)bh * a.nbp + i0 + tid] : 0.f;
+    selacc_s[tid] = 0ull;
+  }
+
+  // Anchor means as the bf16 B operand: qa[ks] = dims 16 ks + 8 kg .. + 7 of anchor l32.
+  const int qr = 16 * w + (l32 >> 1);                    // local query block of the anchor
+  const int qi = i0 + qr;                                 // < nbp always (nbp is a multiple of 64)
+  const size_t arow = ((size_t)bh * a.nbp + qi) * 2 + (l32 & 1);
+  bf16x8 qa[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const float4 x0 = ((const float4*)(a.qanc + arow * kDim))[4 * ks + 2 * kg];
+    const float4 x1 = ((const float4*)(a.qanc + arow * kDim))[4 * ks + 2 * kg + 1];
+    qa[ks] = bf16x8{(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
+                    (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
+  }
+  // Transposed-read offsets of the group rows (the Sol-Attn V^T pattern over 32 rows,
+  // row stride kTailStride, no swizzle): dims 32 mt + 16 (G % 2) + 4 (i' % 4).
+  int toff[8];
+  {
+    const int ip = lane & 15, gm = (lane >> 4) & 1;
+    const int row = 4 * kg + (ip >> 2);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) toff[mt] = row * kTailStride + 64 * mt + 32 * gm + 8 * (ip & 3);
+  }
+
+  floatx16 num[8];                                        // rows: dims (0..127 mu, 128..255 nu); cols: anchors
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) num[mt] = floatx16{};
+  float m_run = kNegInf, z_run = 0.f;
+  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
+  const int ntiles = a.nbp / 16;
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = 16 * t;
+    __syncthreads();                                      // previous tile's LDS reads are done
+    for (int e = tid; e < 32 * 32; e += 128) {
+      const int r = e >> 5, c = e & 31;
+      const uint16_t* src = (c < 16 ? a.gk : a.gv) + (((size_t)bh * a.nbp + j0) * 2 + r) * kDim + (c & 15) * 8;
+      *(uint4v*)(G_s + r * kTailStride + c * 16) = *(const uint4v*)src;
+    }
+    if (tid < 32) {
+      gl_s[tid] = j0 + (tid >> 1) < a.nb ? a.glogn[((size_t)bh * a.nbp + j0) * 2 + tid] : kNegInf;
+      selw_s[tid] = 0u;
+    }
+    __syncthreads();
+    // ---- routing: key block j0 + (tid % 16) against query blocks tid / 16 + 8 p
+    {
+      const int jl = tid & 15, j = j0 + jl;
+      float acc[4][2];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) acc[p][0] = acc[p][1] = 0.f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll 4
+        for (int d4 = 16 * half; d4 < 16 * half + 16; ++d4) {
+          const float4 kk = kt[(size_t)d4 * a.nbp + j];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const float* qv = qb_s[(tid >> 4) + 8 * p] + 4 * d4;
+            acc[p][half] += qv[0] * kk.x + qv[1] * kk.y + qv[2] * kk.z + qv[3] * kk.w;
+          }
+        }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = (tid >> 4) + 8 * p;
+        const float s_hat = (acc[p][0] + acc[p][1]) * kScale2;
+        const bool sel = r < nqb && j < a.nb && (s_hat > tau_s[r] || (j >= a.sink_b0 && j <= a.sink_b1));
+        if (sel) atomicOr(&selw_s[r], 1u << jl);
+      }
+    }
+    __syncthreads();
+    if (tid < 32) {
+      selacc_s[tid] |= (uint64_t)selw_s[tid] << (j0 & 63);
+      if ((t & 3) == 3) {
+        if (tid < nqb) a.sel[((size_t)bh * a.nb + i0 + tid) * a.nbw + (j0 >> 6)] = selacc_s[tid];
+        selacc_s[tid] = 0ull;
+      }
+    }
+    // ---- tail scores of the tile's 32 groups against the wave's 32 anchors
+    floatx16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(G_s + l32 * kTailStride + 32 * ks + 16 * kg),
+                                                  qa[ks], s, 0, 0, 0);
+    const uint32_t mine = selw_s[qr];
+    float mx = kNegInf;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const int g = 8 * (idx >> 2) + 4 * kg + (idx & 3);  // group row of the tile
+      const bool tail = !((mine >> (g >> 1)) & 1);
+      s[idx] = tail ? (s[idx] * kScale2 + gl_s[g]) * kLog2e : kNegInf;
+      mx = fmaxf(mx, s[idx]);
+    }
+    mx = max_with_partner(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    z_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) num[mt][idx] *= alpha;
+    m_run = m_new;
+    bf16x8 pa[2];
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) pa[idx >> 3][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s[idx] - m_use);
+    z_run = add_bf16x8(pa[1], add_bf16x8(pa[0], z_run));  // the bf16 weights of the numerators
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int vo = toff[mt] + st * 16 * kTailStride;
+        const uint2v lo = lds_read_tr16(G_s + vo);
+        const uint2v hi = lds_read_tr16(G_s + vo + 8 * kTailStride);
+        const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
+        num[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], num[mt], 0, 0, 0);
+      }
+  }
+
+  // ---- anchor results: mu_a, nu_a and log2 Z_a - log2(e) q-bar_a . mu_a / sqrt(d)
+  const float z = sum_with_partner(z_run);
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  if (qi < a.nb) {
+    float qmu = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * (mt & 3) + 8 * gq + 4 * kg;   // dims d .. d + 3 of mu (mt < 4) or nu
+        float4 r4 = make_float4(num[mt][4 * gq] * inv, num[mt][4 * gq + 1] * inv, num[mt][4 * gq + 2] * inv,
+                                num[mt][4 * gq + 3] * inv);
+        if (mt < 4) {
+          *(float4*)(a.tmu + arow * kDim + d) = r4;
+          const float4 q4 = *(const float4*)(a.qanc + arow * kDim + d);
+          qmu += q4.x * r4.x + q4.y * r4.y + q4.z * r4.z + q4.w * r4.w;
+        } else {
+          *(float4*)(a.tnu + arow * kDim + d) = r4;
+        }
+      }
+    qmu = sum_with_partner(qmu);
+    if (kg == 0) a.tlz[arow] = z > 0.f ? m_run + __log2f(z) - qmu * kScale2 * kLog2e : kNegInf;
+  }
+}
+
+hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream) {
+  Tail2Args a;
+  a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = ws.nbp / 64;
+  a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.tau_i = ws.tau_i; a.qanc = ws.qanc;
+  a.gk = ws.gk; a.gv = ws.gv; a.glogn = ws.glogn;
+  a.sink_b0 = sink_b0; a.sink_b1 = sink_b1;
+  a.sel = ws.sel; a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
+  hipLaunchKernelGGL(sol2_tail_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2b: exact FP8 attention over the selected blocks, combined with the tail.
+// One workgroup per (b, h, query block i), two wave64s; wave w owns query rows
+// 32 w .. 32 w + 31, which are exactly anchor a = (i, w).
+//   * The selected blocks (the routing bits of stage 2a) stream through LDS: the
+//     FP8 K tile (64 x 128 B) and the bf16 V tile (64 x 256 B) by buffer DMA
+//     (buffer_load ... lds), V of tile t overlapping S_t, K of tile t + 1
+//     overlapping PV_t.
+//   * S^T = K8 Q8^T on v_mfma_f32_32x32x64_f8f6f4 (OCP E4M3; issued through the
+//     scaled form with unit scales), times s_q s_k / sqrt(d); online softmax; O^T +=
+//     V^T P^T in bf16 exactly as in the Sol-Attn pass.
+//   * Epilogue: delta_t = (q'_t - q-bar_a) . mu_a / sqrt(d) from the dequantized query
+//     codes, lambda_t = ln Z_a + delta_t, and Eq. (3) with the exact state.
+// ---------------------------------------------------------------------------
+constexpr int kMaxChunks2 = 128;
+
 struct Fused2Args {
   const uint16_t* v; uint16_t* out;
   int B, N, H, nb, nbp, nbw, tp;
   const uint8_t* q8; const uint8_t* k8; const float* qscale; const float* kscale;
-  const float* qbar; const float* kbar_t; const float* tau_i; const float* qanc;
-  const uint16_t* gk; const uint16_t* gv; const float* glogn;
-  int sink_b0, sink_b1;
-  uint64_t* mask_out;
+  const uint64_t* sel; const float* tmu; const float* tnu; const float* tlz;
 };
 
-__global__ __launch_bounds__(128) void sol2_fused_kernel(Fused2Args a) {
-  __shared__ __attribute__((aligned(16))) unsigned char K8s[64 * kK8Stride];
-  __shared__ __attribute__((aligned(16))) unsigned char Vt[128 * kVtStride];
-  __shared__ __attribute__((aligned(16))) float qb_s[kDim];
-  __shared__ float part[2][64];
-  __shared__ __attribute__((aligned(16))) float qa_s[2][kDim];
-  __shared__ float w_s[2][128];
+// 16-byte slot swizzle of the 64 x 128-byte FP8 K tile: 16 consecutive rows reading one
+// logical chunk land on 16 distinct (row parity, slot) bank groups with 64 banks, and
+// 8 consecutive rows on 8 distinct slots with 32 banks.
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char K8l[64 * 128];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vl[64 * 256];
+  __shared__ uint64_t sel_s[kMaxChunks2];
   __shared__ __attribute__((aligned(16))) float mu_s[2][kDim];
   __shared__ __attribute__((aligned(16))) float nu_s[2][kDim];
 
   const int total = a.B * a.H * a.nb;
   const int item = xcd_remap(blockIdx.x, total);
-  const int i = item % a.nb;
-  const int bh = item / a.nb;
-  const int h = bh % a.H, b = bh / a.H;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
+  const int i = __builtin_amdgcn_readfirstlane(item % a.nb);
+  const int bh = __builtin_amdgcn_readfirstlane(item / a.nb);
+  const int h = __builtin_amdgcn_readfirstlane(bh % a.H), b = __builtin_amdgcn_readfirstlane(bh / a.H);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t rs = (size_t)a.H * kDim;
   const size_t head_off = (size_t)b * a.N * rs + (size_t)h * kDim;
   const size_t qrow_blk = (size_t)bh * a.nbp + i;
 
-  if (tid < 32) ((float4*)qb_s)[tid] = ((const float4*)(a.qbar + qrow_blk * kDim))[tid];
-  if (lane < 32) ((float4*)qa_s[w])[lane] = ((const float4*)(a.qanc + (qrow_blk * 2 + w) * kDim))[lane];
-  const float tau_i = a.tau_i[qrow_blk];
+  for (int c = tid; c < a.nbw; c += 128) sel_s[c] = a.sel[((size_t)bh * a.nb + i) * a.nbw + c];
+  const size_t arow = qrow_blk * 2 + w;
+  if (lane < 32) {
+    ((float4*)mu_s[w])[lane] = ((const float4*)(a.tmu + arow * kDim))[lane];
+    ((float4*)nu_s[w])[lane] = ((const float4*)(a.tnu + arow * kDim))[lane];
+  }
+  const float tlz = a.tlz[arow];
   const float sq = a.qscale[qrow_blk];
 
   const int qrow = i * kBlock + w * 32 + l32;           // < tp always; rows >= N hold zero codes
@@ -286,127 +497,115 @@ __global__ __launch_bounds__(128) void sol2_fused_kernel(Fused2Args a) {
     qf[0] = src[kg];          // dims 32 kg .. 32 kg + 31
     qf[1] = src[2 + kg];      // dims 64 + 32 kg .. + 31
   }
+  __syncthreads();
+
+  // K8 operand reads: row 32 mt + l32, logical chunks 4 ks + 2 kg (+1); swz8 depends on l32 only.
+  const int sz = swz8(l32);
+  int k8off[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) k8off[ks][hf] = l32 * 128 + 16 * ((4 * ks + 2 * kg + hf) ^ sz);
+  int voff[4];
+  v_operand_offsets(lane, voff);
+  // K8 DMA, wave w instruction n: 1 KB segment 4 w + n = rows 8 (4 w + n) + lane / 8, slot
+  // lane % 8 holding logical chunk (lane % 8) ^ swz8(row); swz8(row) = lane / 8 ^ (n & 1).
+  uint32_t k8dma[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) k8dma[par] = (lane >> 3) * 128 + 16 * ((lane & 7) ^ (lane >> 3) ^ par);
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const uint32_t span_in = (uint32_t)(((size_t)a.N - 1) * rs + kDim) * 2;
+  const DmaOffsets doff = dma_offsets(row_bytes, w, lane);
+  const uint8_t* k8_head = a.k8 + (size_t)bh * a.tp * kDim;
+  const uint32_t span_k8 = (uint32_t)a.tp * kDim;
+  auto issue_k = [&](int jb) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(uniform_ptr(k8_head), span_k8);
+    const uint32_t tile_off = (uint32_t)jb * 64 * 128;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      dma16_buf(rsrc, tile_off + 1024 * (4 * w + n) + k8dma[n & 1], 0, K8l + 1024 * (4 * w + n));
+  };
+  auto issue_v = [&](int jb) {
+    dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.v + head_off), span_in), (uint32_t)jb * 64 * row_bytes, row_bytes,
+                   doff, w);
+  };
+  // Selected blocks in order.
+  int c_it = 0;
+  uint64_t bits = 0;
+  auto next_sel = [&]() -> int {
+    while (!bits) {
+      if (c_it >= a.nbw) return -1;
+      bits = uniform64(sel_s[c_it++]);
+    }
+    const int jb = (c_it - 1) * 64 + __builtin_ctzll(bits);
+    bits &= bits - 1;
+    return __builtin_amdgcn_readfirstlane(jb);
+  };
+
   floatx16 o[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
   float m_run = kNegInf, l_run = 0.f;
-  // tail state (log2 units), lane owns dims 2 lane, 2 lane + 1
-  float m_t = kNegInf, z_t = 0.f, tk0 = 0.f, tk1 = 0.f, tv0 = 0.f, tv1 = 0.f;
-  __syncthreads();
-
-  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
-  const int nchunks = a.nbp / 64;
-  for (int c = 0; c < nchunks; ++c) {
-    const int j = c * 64 + lane;
-    const float s_hat = routing_scores(kt, a.nbp, c, qb_s, part, w, lane);
-    const bool valid = j < a.nb;
-    const bool sel = valid && (s_hat > tau_i || (j >= a.sink_b0 && j <= a.sink_b1));
-    uint64_t selm = __ballot(sel);
-    const uint64_t tailm = __ballot(valid) & ~selm;
-    if (a.mask_out && tid == 0) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
-
-    // ---- tail: groups of the unselected blocks of this chunk, against anchor w
-    if (tailm) {
-      float l0 = kNegInf, l1 = kNegInf;
-      const size_t grow = ((size_t)bh * a.nbp + j) * 2;
-      if ((tailm >> lane) & 1) {
-        const uint4v* g0 = (const uint4v*)(a.gk + grow * kDim);
-        float d0 = 0.f, d1 = 0.f;
-#pragma unroll 4
-        for (int cc = 0; cc < 16; ++cc) {
-          const uint4v x0 = g0[cc], x1 = g0[16 + cc];
+  const float qs = sq * kScale2 * kLog2e;
+  int cur = next_sel();
+  if (cur >= 0) issue_k(cur);
+  while (cur >= 0) {
+    const int nxt = next_sel();
+    wait_vm0();
+    lds_barrier();                                         // K8(cur) landed; V buffer free
+    issue_v(cur);
+    floatx16 s0 = {}, s1 = {};
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const float q0 = qa_s[w][8 * cc + 2 * m], q1 = qa_s[w][8 * cc + 2 * m + 1];
-            d0 += bf16_lo(x0[m]) * q0 + bf16_hi(x0[m]) * q1;
-            d1 += bf16_lo(x1[m]) * q0 + bf16_hi(x1[m]) * q1;
-          }
-        }
-        const float gl0 = a.glogn[grow], gl1 = a.glogn[grow + 1];
-        l0 = gl0 == kNegInf ? kNegInf : (gl0 + d0 * kScale2) * kLog2e;
-        l1 = gl1 == kNegInf ? kNegInf : (gl1 + d1 * kScale2) * kLog2e;
-      }
-      const float mc = wave_max(fmaxf(l0, l1));
-      if (mc != kNegInf) {
-        const float m_new = fmaxf(m_t, mc);
-        const float sc = __builtin_amdgcn_exp2f(m_t - m_new);
-        const float w0 = __builtin_amdgcn_exp2f(l0 - m_new), w1 = __builtin_amdgcn_exp2f(l1 - m_new);
-        w_s[w][2 * lane] = w0;
-        w_s[w][2 * lane + 1] = w1;
-        z_t = z_t * sc + wave_sum(w0 + w1);
-        m_t = m_new;
-        tk0 *= sc; tk1 *= sc; tv0 *= sc; tv1 *= sc;
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-        const uint32_t* gkc = (const uint32_t*)(a.gk + ((size_t)bh * a.nbp + c * 64) * 2 * kDim) + lane;
-        const uint32_t* gvc = (const uint32_t*)(a.gv + ((size_t)bh * a.nbp + c * 64) * 2 * kDim) + lane;
-        uint64_t tm = tailm;
-        while (tm) {
-          const int jj = __builtin_ctzll(tm);
-          tm &= tm - 1;
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            const float wg = w_s[w][2 * jj + g];
-            if (wg == 0.f) continue;
-            const uint32_t kw = gkc[(2 * jj + g) * 64], vw = gvc[(2 * jj + g) * 64];
-            tk0 += wg * bf16_lo(kw); tk1 += wg * bf16_hi(kw);
-            tv0 += wg * bf16_lo(vw); tv1 += wg * bf16_hi(vw);
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4v a0l = *(const uint4v*)(K8l + k8off[ks][0]), a0h = *(const uint4v*)(K8l + k8off[ks][1]);
+      const uint4v a1l = *(const uint4v*)(K8l + 32 * 128 + k8off[ks][0]);
+      const uint4v a1h = *(const uint4v*)(K8l + 32 * 128 + k8off[ks][1]);
+      const intx8 a0 = {(int)a0l[0], (int)a0l[1], (int)a0l[2], (int)a0l[3], (int)a0h[0], (int)a0h[1], (int)a0h[2], (int)a0h[3]};
+      const intx8 a1 = {(int)a1l[0], (int)a1l[1], (int)a1l[2], (int)a1l[3], (int)a1h[0], (int)a1h[1], (int)a1h[2], (int)a1h[3]};
+      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qf[ks], s0, 0, 0, 0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qf[ks], s1, 0, 0, 0, 0, 0, 0);
     }
-    __syncthreads();
-
-    // ---- exact blocks of this chunk: FP8 S^T, bf16 PV
-    while (selm) {
-      const int jb = c * 64 + __builtin_ctzll(selm);
-      selm &= selm - 1;
-      const int t0 = jb * kBlock;
-      const int valid_rows = min(kBlock, a.N - t0);
-      {
-        // K8 tile: 64 rows x 128 B (rows >= N hold zero codes), 8 x 16 B per row
-        const uint8_t* src = a.k8 + ((size_t)bh * a.tp + t0) * kDim;
-        const int cc = tid & 7, r0 = tid >> 3;
+    // logits in log2 units; rows past the end of the last block are masked
+    const float f = qs * a.kscale[(size_t)bh * a.nbp + cur];
+    const int valid = min(kBlock, a.N - cur * kBlock);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int r = r0 + 16 * p;
-          *(uint4v*)(K8s + r * kK8Stride + cc * 16) = *(const uint4v*)(src + (size_t)r * kDim + cc * 16);
-        }
-      }
-      load_v_transposed(Vt, a.v + head_off + (size_t)t0 * rs, rs, valid_rows, tid);
-      __syncthreads();
-      const float f = sq * a.kscale[(size_t)bh * a.nbp + jb] * kScale2 * kLog2e;
-      floatx16 s0 = {}, s1 = {};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const intx8 a0 = *(const intx8*)(K8s + l32 * kK8Stride + 64 * ks + 32 * kg);
-        const intx8 a1 = *(const intx8*)(K8s + (32 + l32) * kK8Stride + 64 * ks + 32 * kg);
-        s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qf[ks], s0, 0, 0, 0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qf[ks], s1, 0, 0, 0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
-        s0[idx] = key0 < valid_rows ? s0[idx] * f : kNegInf;
-        s1[idx] = key0 + 32 < valid_rows ? s1[idx] * f : kNegInf;
-      }
-      softmax_pv(s0, s1, Vt, o, m_run, l_run, l32, kg);
-      __syncthreads();
+    for (int idx = 0; idx < 16; ++idx) {
+      const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+      s0[idx] = key0 < valid ? s0[idx] * f : kNegInf;
+      s1[idx] = key0 + 32 < valid ? s1[idx] * f : kNegInf;
     }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
+    mx = max_with_partner(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    // Unconditional rescale (skipping it behind a wave-uniform branch made results
+    // timing-dependent with two waves per SIMD).
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) o[mt][idx] *= alpha;
+    m_run = m_new;
+    bf16x8 pa[4];
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      pa[idx >> 3][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[idx] - m_use);   // keys 16 st ..
+      pa[2 + (idx >> 3)][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[idx] - m_use);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) l_run = add_bf16x8(pa[st], l_run);
+    wait_vm0();
+    lds_barrier();                                         // V(cur) landed; K buffer free
+    if (nxt >= 0) issue_k(nxt);
+    pv_tile(o, Vl, voff, pa);
+    cur = nxt;
   }
 
-  // ---- tail finalisation: mu_a, nu_a, ln Z_a (log2), delta_t, Eq. (3)
-  const float inv_z = z_t > 0.f ? 1.f / z_t : 0.f;
-  mu_s[w][2 * lane] = tk0 * inv_z;
-  mu_s[w][2 * lane + 1] = tk1 * inv_z;
-  nu_s[w][2 * lane] = tv0 * inv_z;
-  nu_s[w][2 * lane + 1] = tv1 * inv_z;
-  const float qa_mu = wave_sum(qa_s[w][2 * lane] * tk0 * inv_z + qa_s[w][2 * lane + 1] * tk1 * inv_z);
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  const float lnz2 = z_t > 0.f ? m_t + __log2f(z_t) : kNegInf;
-  // q'_t . mu over this lane's 64 dims (32 kg .. +31 and 64 + 32 kg .. +31), then with the partner
+  // ---- epilogue: tail logit lambda_t = log2 Z_a + log2(e) q'_t . mu_a / sqrt(d) (the
+  // q-bar_a term is in tlz), then Eq. (3) with one shared denominator.
   float qmu = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
@@ -418,7 +617,7 @@ __global__ __launch_bounds__(128) void sol2_fused_kernel(Fused2Args a) {
       for (int e = 0; e < 4; ++e) qmu += f4[e] * mu_s[w][64 * ks + 32 * kg + 4 * m + e];
     }
   qmu = sum_with_partner(qmu) * sq;
-  const float lam2 = lnz2 == kNegInf ? kNegInf : lnz2 + (qmu - qa_mu) * kScale2 * kLog2e;
+  const float lam2 = tlz == kNegInf ? kNegInf : tlz + qmu * kScale2 * kLog2e;
   const float m_fin = fmaxf(m_run, lam2);
   const float m_use = m_fin == kNegInf ? 0.f : m_fin;
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -443,15 +642,13 @@ __global__ __launch_bounds__(128) void sol2_fused_kernel(Fused2Args a) {
   }
 }
 
-hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, int sink_b0, int sink_b1,
-                         uint64_t* mask_out, hipStream_t stream) {
+hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, hipStream_t stream) {
+  if (ws.nbp / 64 > kMaxChunks2) return hipErrorInvalidValue;
   Fused2Args a;
   a.v = v; a.out = out;
-  a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = (ws.nb + 63) / 64; a.tp = ws.nbp * kBlock;
+  a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = ws.nbp / 64; a.tp = ws.nbp * kBlock;
   a.q8 = ws.q8; a.k8 = ws.k8; a.qscale = ws.qscale; a.kscale = ws.kscale;
-  a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.tau_i = ws.tau_i; a.qanc = ws.qanc;
-  a.gk = ws.gk; a.gv = ws.gv; a.glogn = ws.glogn;
-  a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
+  a.sel = ws.sel; a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
   const int total = s.B * s.H * ws.nb;
   hipLaunchKernelGGL(sol2_fused_kernel, dim3(total), dim3(128), 0, stream, a);
   return hipGetLastError();

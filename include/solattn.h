@@ -73,6 +73,11 @@ typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
  *   qanc     float [B][H][nbp][2][128] 32-token anchor means of dequantized Q (Sol-Attn2)
  *   opart    bf16  [S][B][N][H][128]   per-key-split normalized partial outputs (S = kv_splits > 1)
  *   olse     float [S][B][N][H]        per-key-split log2-sum-exp of the partial rows
+ *   sel      uint64 [B][H][nb][nbp/64] routing bits, bit j % 64 of word j / 64 set iff block j
+ *                                      is exact for query block i (Sol-Attn2)
+ *   tmu, tnu float [B][H][nbp][2][128] per-anchor tail key / value means mu_a, nu_a (Sol-Attn2)
+ *   tlz      float [B][H][nbp][2]     log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d); -inf if the
+ *                                      anchor's tail is empty (Sol-Attn2)
  */
 typedef struct {
     int64_t total_bytes;
@@ -80,6 +85,7 @@ typedef struct {
     int64_t qbar, kbar_t, kbar_h, vbar_h, tau_i, kstat, kcov, kpart;
     int64_t q8, k8, qscale, kscale, qhat, gk, gv, glogn, ghi, qanc;
     int64_t kv_splits, opart, olse;
+    int64_t sel, tmu, tnu, tlz;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */
