@@ -115,21 +115,38 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // ---- routing for every chunk (fp32); wave w sums dims 64 w .. 64 w + 63
-  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
+  // Buffer resources over this head's rows of k / v and of the pooled K-bar / V-bar
+  // (stored with the same row stride), so one set of lane offsets serves every
+  // tile; built at each use from kernel arguments so they stay in SGPRs.
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const uint32_t span_in = (uint32_t)((a.N - 1) * rs + kDim) * 2;
+  const uint32_t span_pool = (uint32_t)((a.nbp - 1) * rs + kDim) * 2;
+  const size_t pooled_head = ((size_t)b * a.nbp * a.H + h) * kDim;
+  const DmaOffsets doff = dma_offsets(row_bytes, w, lane);
   const int c_begin = split * a.cps;                        // this split's routing chunks
   const int c_end = min(a.nbp / 64, c_begin + a.cps);
   const int nchunks = c_end - c_begin;
+  // The reference pass below reads the pooled K-bar tiles; its first DMA is issued
+  // now and lands while the routing runs (the routing barriers do not wait for it).
+  auto pool = [&]() { return make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool); };
+  dma_tile<false>(Kl, pool(), (uint32_t)c_begin * 64 * row_bytes, row_bytes, doff, w);
+
+  // ---- routing for every chunk (fp32); wave w sums dims 64 w .. 64 w + 63
+  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
   for (int c = c_begin; c < c_end; ++c) {
     const int j = c * 64 + lane;
+    float4 kk[16];                                           // all 16 loads in flight at once
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kk[e] = kt[(size_t)(16 * w + e) * a.nbp + j];
     float acc = 0.f;
-#pragma unroll 4
-    for (int d4 = 16 * w; d4 < 16 * w + 16; ++d4) {
-      const float4 kk = kt[(size_t)d4 * a.nbp + j];
-      acc += qb_s[4 * d4] * kk.x + qb_s[4 * d4 + 1] * kk.y + qb_s[4 * d4 + 2] * kk.z + qb_s[4 * d4 + 3] * kk.w;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int d4 = 16 * w + e;
+      acc += qb_s[4 * d4] * kk[e].x + qb_s[4 * d4 + 1] * kk[e].y + qb_s[4 * d4 + 2] * kk[e].z +
+             qb_s[4 * d4 + 3] * kk[e].w;
     }
     part[c & 1][w][lane] = acc;
-    __syncthreads();
+    lds_barrier();
     const float s_hat = (part[c & 1][0][lane] + part[c & 1][1][lane]) * kScale;
     const bool valid = j < a.nb;
     const bool sel = valid && (s_hat > tau_i || (j >= a.sink_b0 && j <= a.sink_b1));
@@ -141,7 +158,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
       if (a.mask_out) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- per-lane LDS offsets
   // S^T A operand: key row 32 mt + l32, k-step ks reads logical chunk 2 ks + kg, physical slot
@@ -152,14 +169,6 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   int voff[4];                                               // V^T operand (transposed read)
   v_operand_offsets(lane, voff);
 
-  // Buffer resources over this head's rows of k / v and of the pooled K-bar / V-bar
-  // (stored with the same row stride), so one set of lane offsets serves every
-  // tile; built at each use from kernel arguments so they stay in SGPRs.
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
-  const uint32_t span_in = (uint32_t)((a.N - 1) * rs + kDim) * 2;
-  const uint32_t span_pool = (uint32_t)((a.nbp - 1) * rs + kDim) * 2;
-  const size_t pooled_head = ((size_t)b * a.nbp * a.H + h) * kDim;
-  const DmaOffsets doff = dma_offsets(row_bytes, w, lane);
 
   // S^T = K Q^T for the 64-row K tile at LDS `kl` (two 32-key m-tiles).
   auto scores = [&](const unsigned char* kl, floatx16& s0, floatx16& s1) {
@@ -183,8 +192,6 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   // the workgroup through the rescaling loop below.
   float m_ref;
   {
-    auto pool = [&]() { return make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool); };
-    dma_tile<false>(Kl, pool(), (uint32_t)c_begin * 64 * row_bytes, row_bytes, doff, w);
     float mx = kNegInf;
     for (int c = 0; c < nchunks; ++c) {
       const unsigned char* buf = (c & 1) ? Vl : Kl;
