@@ -116,9 +116,10 @@ def main():
     exact_pairs = float((masks * pair_w).sum())
     proxy_units = float(((~masks) * counts[:, None]).sum())       # (query token, unselected block)
     flops_exact = 4.0 * D * exact_pairs
-    flops_proxy = 4.0 * D * proxy_units
+    flops_proxy = 4.0 * D * proxy_units if variant == 1 else 0.0   # Sol-Attn2 has a tail pass instead
     dense_flops = 4.0 * B * H * float(N) ** 2 * D
-    log(f"[bench] realised sparsity {real_sp:.4f}; exact {flops_exact / 1e12:.3f} TFLOP, proxy {flops_proxy / 1e12:.3f} TFLOP")
+    log(f"[bench] realised sparsity {real_sp:.4f}; exact {flops_exact / 1e12:.3f} TFLOP"
+        + (f", proxy {flops_proxy / 1e12:.3f} TFLOP" if variant == 1 else ""))
 
     stream = torch.cuda.current_stream(dev)
 
@@ -147,10 +148,38 @@ def main():
     med_step = float(np.median(step_ms))
     fused_avg = float(np.mean(fused_ms))
     value = dense_flops / (ms_per_step * 1e-3) / 1e12
-    peak = 2500.0 if variant == 1 else 5000.0
-    achieved = (flops_exact + flops_proxy) / (fused_avg * 1e-3) / 1e12
+
+    # Roofline of the dominant kernel, timed alone with events on its own stream: the
+    # fused Sol-Attn kernel (called without an output: no split merge, no final store),
+    # or the exact Sol-Attn2 kernel (after the tail pass of the last step).
+    if variant == 1:
+        kernel = "sol_fused_kernel"
+        run_kernel = lambda: bsa.fused(1, q, k, v, None, ws, sink_start, sink_tokens, args.kv_splits)  # noqa: E731
+        kernel_flops = flops_exact + flops_proxy
+        peak = 2500.0                                          # dense bf16 MFMA
+    else:
+        kernel = "sol2_fused_kernel"
+        run_kernel = lambda: bsa.exact2(q, k, v, out, ws)    # noqa: E731
+        kernel_flops = flops_exact
+        # QK^T on FP8 (5.0 PF) and PV on bf16 (2.5 PF), half the exact FLOPs each
+        peak = kernel_flops / (0.5 * kernel_flops / 5000.0 + 0.5 * kernel_flops / 2500.0)
+    for _ in range(2):
+        run_kernel()
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        kev[s][0].record(stream)
+        run_kernel()
+        kev[s][1].record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
+    achieved = kernel_flops / (kernel_ms * 1e-3) / 1e12
     log(f"[bench] step {ms_per_step:.3f} ms (median event {med_step:.3f}); prepare {np.mean(prep_ms):.3f} ms, "
-        f"fused {fused_avg:.3f} ms -> {achieved:.1f} TFLOP/s algorithmic")
+        f"stage 2 {fused_avg:.3f} ms; {kernel} alone {kernel_ms:.3f} ms -> {achieved:.1f} TFLOP/s algorithmic")
+    from block_sparse_attention_tok_amd.profsum import read_traffic
+    tag = ("op_bench" if not args.text_sink else "long_sink") + f"_{N // 1024}k_{round(100 * args.sparsity)}pct"
+    traffic_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{kernel}_{tag}_traffic.md")
+    traffic = read_traffic(traffic_file, kernel)
 
     baselines = {}
     if not args.no_dense_baselines and variant == 1:
@@ -206,13 +235,17 @@ def main():
                    "tau": round(tau, 5), "realised_sparsity": round(real_sp, 5),
                    "sink": [sink_start, sink_tokens], "median_event_ms": round(med_step, 4),
                    "kv_splits": bsa.kv_splits_for(B, N, H, args.kv_splits) if variant == 1 else 1,
-                   "prepare_ms": round(float(np.mean(prep_ms)), 4), "fused_ms": round(fused_avg, 4),
-                   "exact_work_mfma_frac": round(flops_exact / (fused_avg * 1e-3) / (peak * 1e12), 4),
+                   "prepare_ms": round(float(np.mean(prep_ms)), 4), "stage2_ms": round(fused_avg, 4),
+                   "kernel_ms": round(kernel_ms, 4),
+                   "exact_work_mfma_frac": round(flops_exact / (kernel_ms * 1e-3) / (peak * 1e12), 4),
                    "dense_baselines": baselines},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "sol_fused_kernel" if variant == 1 else "sol2_fused_kernel",
-                     "work_per_launch": {"exact_flop": flops_exact, "proxy_flop": flops_proxy}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": kernel,
+                     "work_per_launch": {"exact_flop": flops_exact, "proxy_flop": flops_proxy},
+                     "traffic_source": os.path.relpath(traffic_file, os.path.dirname(os.path.abspath(__file__)))
+                     if traffic is not None else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

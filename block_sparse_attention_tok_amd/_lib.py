@@ -26,7 +26,8 @@ EXPORTED = [
     "sol_status_string", "sol_attn_validate", "sol_attn_workspace_bytes", "sol_attn_workspace_layout",
     "sol_attn_kv_splits", "sol_attn_workspace_bytes_kv", "sol_attn_workspace_layout_kv",
     "sol_attn", "sol_attn_prepare", "sol_attn_fused", "sol_attn_fused_kv", "sol_attn_debug_routing",
-    "sol_attn2", "sol_attn2_prepare", "sol_attn2_fused", "sol_attn2_debug_routing",
+    "sol_attn2", "sol_attn2_prepare", "sol_attn2_fused", "sol_attn2_tail", "sol_attn2_exact",
+    "sol_attn2_debug_routing",
 ]
 
 
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.sol_attn_workspace_layout_kv.restype = i32
     L.sol_attn_fused_kv.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     L.sol_attn_fused_kv.restype = i32
+    L.sol_attn2_tail.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
+    L.sol_attn2_tail.restype = i32
+    L.sol_attn2_exact.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+    L.sol_attn2_exact.restype = i32
     full = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp]
     for name in ("sol_attn", "sol_attn2"):
         getattr(L, name).argtypes = full
@@ -226,6 +231,20 @@ def fused(variant: int, q, k, v, out, workspace: torch.Tensor, sink_start: Optio
     _check(lib().sol_attn2_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
                                  int(sink_tokens), _ptr(workspace), workspace.numel(), _stream(q.device)),
            "sol_attn2_fused")
+
+
+def tail2(q, k, v, workspace: torch.Tensor, sink_start: Optional[int] = None, sink_tokens: int = 0):
+    """Sol-Attn2 stage 2a: routing bits and the per-anchor tail, into the workspace."""
+    B, N, H, D = q.shape
+    _check(lib().sol_attn2_tail(_ptr(q), _ptr(k), _ptr(v), B, N, H, D, _sink_start(sink_start), int(sink_tokens),
+                                _ptr(workspace), workspace.numel(), _stream(q.device)), "sol_attn2_tail")
+
+
+def exact2(q, k, v, out, workspace: torch.Tensor):
+    """Sol-Attn2 stage 2b: the exact FP8 pass combined with the tail of stage 2a."""
+    B, N, H, D = q.shape
+    _check(lib().sol_attn2_exact(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _ptr(workspace),
+                                 workspace.numel(), _stream(q.device)), "sol_attn2_exact")
 
 
 def debug_routing(variant: int, q, k, v, tau: float = 1.0, thresh: str = "diag", sink_start: Optional[int] = None,

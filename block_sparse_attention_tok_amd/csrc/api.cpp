@@ -243,10 +243,13 @@ int sol_attn_prepare(const void* q, const void* k, const void* v, int64_t batch,
   return hip_status(solattn::launch_threshold(s, w, tau, thresh == SOL_THRESH_EXACT, hs));
 }
 
+// Sol-Attn2 stage 2 parts: the routing + tail pass, the exact pass, or both in order.
+enum { kStage2Tail = 1, kStage2Exact = 2, kStage2Both = 3 };
+
 static int fused_common(int variant, const void* q, const void* k, const void* v, void* out, int64_t batch,
                         int64_t tokens, int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens,
                         void* workspace, size_t workspace_bytes, uint64_t* mask_bits, void* stream,
-                        bool out_required, int kv_splits = 0) {
+                        bool out_required, int kv_splits = 0, int stage2 = kStage2Both) {
   sol_ws_layout L;
   if (check_kv(kv_splits) != SOL_OK) return SOL_ERR_ARG;
   int st = prologue(variant, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L, kv_splits);
@@ -261,11 +264,15 @@ static int fused_common(int variant, const void* q, const void* k, const void* v
     return hip_status(solattn::launch_fused((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                             (uint16_t*)out, s, w, b0, b1, mask_bits, (hipStream_t)stream));
   hipStream_t hs = (hipStream_t)stream;
-  if ((st = hip_status(solattn::launch_tail2(s, w, b0, b1, hs))) != SOL_OK) return st;
-  if (mask_bits) {
-    const size_t bytes = (size_t)batch * heads * w.nb * (w.nbp / 64) * sizeof(uint64_t);
-    if ((st = hip_status(hipMemcpyAsync(mask_bits, w.sel, bytes, hipMemcpyDeviceToDevice, hs))) != SOL_OK) return st;
+  if (stage2 & kStage2Tail) {
+    if ((st = hip_status(solattn::launch_tail2(s, w, b0, b1, hs))) != SOL_OK) return st;
+    if (mask_bits) {
+      const size_t bytes = (size_t)batch * heads * w.nb * (w.nbp / 64) * sizeof(uint64_t);
+      if ((st = hip_status(hipMemcpyAsync(mask_bits, w.sel, bytes, hipMemcpyDeviceToDevice, hs))) != SOL_OK)
+        return st;
+    }
   }
+  if (!(stage2 & kStage2Exact)) return SOL_OK;
   return hip_status(solattn::launch_fused2((const uint16_t*)v, (uint16_t*)out, s, w, hs));
 }
 
@@ -280,7 +287,7 @@ int sol_attn_fused_kv(const void* q, const void* k, const void* v, void* out, in
                       int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens, int kv_splits,
                       void* workspace, size_t workspace_bytes, void* stream) {
   return fused_common(SOL_VARIANT_SOL1, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
-                      workspace, workspace_bytes, nullptr, stream, true, kv_splits);
+                      workspace, workspace_bytes, nullptr, stream, false, kv_splits);
 }
 
 int sol_attn(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens, int64_t heads,
@@ -334,6 +341,19 @@ int sol_attn2_fused(const void* q, const void* k, const void* v, void* out, int6
                     size_t workspace_bytes, void* stream) {
   return fused_common(SOL_VARIANT_SOL2, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
                       workspace, workspace_bytes, nullptr, stream, true);
+}
+
+int sol_attn2_tail(const void* q, const void* k, const void* v, int64_t batch, int64_t tokens, int64_t heads,
+                   int64_t head_dim, int64_t sink_start, int64_t sink_tokens, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return fused_common(SOL_VARIANT_SOL2, q, k, v, nullptr, batch, tokens, heads, head_dim, sink_start, sink_tokens,
+                      workspace, workspace_bytes, nullptr, stream, false, 0, kStage2Tail);
+}
+
+int sol_attn2_exact(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                    int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes, void* stream) {
+  return fused_common(SOL_VARIANT_SOL2, q, k, v, out, batch, tokens, heads, head_dim, -1, 0, workspace,
+                      workspace_bytes, nullptr, stream, true, 0, kStage2Exact);
 }
 
 int sol_attn2(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens, int64_t heads,

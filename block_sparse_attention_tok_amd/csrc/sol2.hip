@@ -263,6 +263,7 @@ struct Tail2Args {
 
 __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   __shared__ __attribute__((aligned(16))) float qb_s[32][kDim];
+  __shared__ __attribute__((aligned(16))) float kb_s[16][kDim];   // key block means of the tile
   __shared__ __attribute__((aligned(16))) unsigned char G_s[32 * kTailStride];
   __shared__ float tau_s[32];
   __shared__ uint32_t selw_s[32];        // routing bits of the tile (16 key blocks) per query block
@@ -306,24 +307,50 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
     for (int mt = 0; mt < 8; ++mt) toff[mt] = row * kTailStride + 64 * mt + 32 * gm + 8 * (ip & 3);
   }
 
+  // Tile t's group rows (8 x 16 B per thread), key block means (4 x 16 B) and ln n_g are
+  // loaded into registers one tile ahead, all loads in flight together.
+  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
+  uint4v gr[8];
+  floatx4 kr4[4];
+  float glr = kNegInf;
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 128 * u, r = e >> 5, c = e & 31;
+      gr[u] = *(const uint4v*)((c < 16 ? a.gk : a.gv) + (((size_t)bh * a.nbp + j0) * 2 + r) * kDim + (c & 15) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 128 * u, d4 = e >> 4, jl = e & 15;   // kb_s[jl][4 d4 .. 4 d4 + 3]
+      kr4[u] = *(const floatx4*)(kt + (size_t)d4 * a.nbp + j0 + jl);
+    }
+    if (tid < 32) glr = j0 + (tid >> 1) < a.nb ? a.glogn[((size_t)bh * a.nbp + j0) * 2 + tid] : kNegInf;
+  };
+
   floatx16 num[8];                                        // rows: dims (0..127 mu, 128..255 nu); cols: anchors
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) num[mt] = floatx16{};
   float m_run = kNegInf, z_run = 0.f;
-  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
   const int ntiles = a.nbp / 16;
+  load_tile(0);
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = 16 * t;
     __syncthreads();                                      // previous tile's LDS reads are done
-    for (int e = tid; e < 32 * 32; e += 128) {
-      const int r = e >> 5, c = e & 31;
-      const uint16_t* src = (c < 16 ? a.gk : a.gv) + (((size_t)bh * a.nbp + j0) * 2 + r) * kDim + (c & 15) * 8;
-      *(uint4v*)(G_s + r * kTailStride + c * 16) = *(const uint4v*)src;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 128 * u, r = e >> 5, c = e & 31;
+      *(uint4v*)(G_s + r * kTailStride + c * 16) = gr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 128 * u, d4 = e >> 4, jl = e & 15;
+      *(floatx4*)(kb_s[jl] + 4 * d4) = kr4[u];
     }
     if (tid < 32) {
-      gl_s[tid] = j0 + (tid >> 1) < a.nb ? a.glogn[((size_t)bh * a.nbp + j0) * 2 + tid] : kNegInf;
+      gl_s[tid] = glr;
       selw_s[tid] = 0u;
     }
+    load_tile(t + 1 < ntiles ? j0 + 16 : j0);             // lands while this tile computes (last: reload)
     __syncthreads();
     // ---- routing: key block j0 + (tid % 16) against query blocks tid / 16 + 8 p
     {
@@ -335,11 +362,11 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
       for (int half = 0; half < 2; ++half)
 #pragma unroll 4
         for (int d4 = 16 * half; d4 < 16 * half + 16; ++d4) {
-          const float4 kk = kt[(size_t)d4 * a.nbp + j];
+          const float4 kk = *(const float4*)(kb_s[jl] + 4 * d4);
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const float* qv = qb_s[(tid >> 4) + 8 * p] + 4 * d4;
-            acc[p][half] += qv[0] * kk.x + qv[1] * kk.y + qv[2] * kk.z + qv[3] * kk.w;
+            const float4 qv = *(const float4*)(qb_s[(tid >> 4) + 8 * p] + 4 * d4);
+            acc[p][half] += qv.x * kk.x + qv.y * kk.y + qv.z * kk.z + qv.w * kk.w;
           }
         }
 #pragma unroll

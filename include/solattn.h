@@ -159,7 +159,9 @@ int sol_attn_fused(const void* q, const void* k, const void* v, void* out,
 
 /* Stage 2 with an explicit kv_splits (0 = automatic); the workspace must be
  * sized by sol_attn_workspace_bytes_kv for the same kv_splits.  Runs the fused
- * kernel and, for more than one split, the merge kernel. */
+ * kernel and, for more than one split, the merge kernel.  out may be NULL: then
+ * only the fused kernel runs (split partials are still written to the workspace,
+ * the final output store and the merge are skipped), e.g. to time that kernel. */
 int sol_attn_fused_kv(const void* q, const void* k, const void* v, void* out,
                       int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                       int64_t sink_start, int64_t sink_tokens, int kv_splits,
@@ -198,10 +200,29 @@ int sol_attn2_prepare(const void* q, const void* k, const void* v,
                       int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                       float tau, int thresh, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 2 of sol_attn2: the fused FP8 exact + complementary-tail kernel. */
+/* Stage 2 of sol_attn2 (Sol-Attn2 draft, Method, Eqs. (1)-(3)): sol_attn2_tail
+ * then sol_attn2_exact on the same workspace and stream. */
 int sol_attn2_fused(const void* q, const void* k, const void* v, void* out,
                     int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                     int64_t sink_start, int64_t sink_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2a (Sol-Attn2 draft, Method, Eq. (1)): routing of every (query block, key
+ * block) pair on the dequantized block means (bits into the workspace array sel),
+ * and per 32-token anchor the tail over the groups of the unselected blocks:
+ * log2 Z_a, mu_a, nu_a (workspace arrays tmu, tnu, tlz).  Needs stage 1 on this
+ * workspace.  q, k, v are only validated (the pass reads the workspace). */
+int sol_attn2_tail(const void* q, const void* k, const void* v,
+                   int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                   int64_t sink_start, int64_t sink_tokens,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2b (Sol-Attn2 draft, Eqs. (2), (3); "FP8 quantization and ExpCast"): exact
+ * attention over the selected blocks with FP8 Q K^T and bf16 P V, combined with
+ * the anchor tail through delta_t and one shared denominator; writes out (device,
+ * bf16 BTHD, non-NULL).  Needs stage 2a on this workspace. */
+int sol_attn2_exact(const void* q, const void* k, const void* v, void* out,
+                    int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sol-Attn2 routing export, as sol_attn_debug_routing (kv_splits must be 0 or 1:

@@ -131,6 +131,10 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
                                     None, None) == 1
     # kv_splits out of range
     assert L.sol_attn_fused_kv(fake, fake, fake, fake, 1, 1024, 2, 128, -1, 0, 17, fake, 1 << 30, None) == 8
+    # Sol-Attn2 stage 2 parts: sink out of range, missing output, workspace too small
+    assert L.sol_attn2_tail(fake, fake, fake, 1, 1024, 2, 128, 1000, 100, fake, 1 << 30, None) == 5
+    assert L.sol_attn2_exact(fake, fake, fake, None, 1, 1024, 2, 128, fake, 1 << 30, None) == 1
+    assert L.sol_attn2_exact(fake, fake, fake, fake, 1, 1024, 2, 128, fake, 16, None) == 6
 
 
 def test_python_validate_wrapper():
