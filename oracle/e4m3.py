@@ -75,3 +75,26 @@ def quantize_block_fp32(x_block: np.ndarray):
     s = np.float32(amax / np.float32(MAX_FINITE)) if amax > 0 else np.float32(1.0)
     y = (xf / s).astype(np.float32)           # correctly rounded fp32 division
     return encode_rne(y), s
+
+
+# ----------------------------------------------------------------------------
+# ExpCast (Sol-Attn2 draft, "FP8 quantization and ExpCast", after VC-Attention):
+# a base-2 score u = (s - m) log2 e maps straight to an E4M3 probability byte,
+#     c(u) = clip_[0,120]( RNE(8 u + 55.65) ),   p-hat(u) = decode(c(u)) ~ 2^u.
+# For u = k + phi the byte is 8 (k + 7) + j with mantissa j ~ 8 phi, i.e. the
+# exponent field carries k and the mantissa a linear stand-in for 2^phi; the
+# 55.65 (not 56) offset shifts the rounding points to balance that stand-in.
+# The rounding decides an integer, so it is done in IEEE fp32, as the kernel does.
+# ----------------------------------------------------------------------------
+
+def expcast_code(u) -> np.ndarray:
+    """ExpCast codes of base-2 scores u (float array): uint8 in [0, 120]."""
+    uf = np.asarray(u, dtype=np.float32)
+    t = (np.float32(8.0) * uf + np.float32(55.65)).astype(np.float32)   # 8 u is exact in fp32
+    c = np.rint(t)                                                       # nearest, ties to even
+    return np.clip(c, 0.0, 120.0).astype(np.uint8)
+
+
+def expcast_weight(u) -> np.ndarray:
+    """p-hat(u) = decode(c(u)), float64."""
+    return decode(expcast_code(u))

@@ -37,6 +37,13 @@ Steps, per (batch, head):
 The oracle is parameterised by anchor size, grouping ("split2", "whole",
 "singleton") and quantization on/off so that the reductions used as pins
 (tests/test_oracle_sol_attn2.py) can be run.
+
+FP8 PV option (pv="expcast"; draft "FP8 quantization and ExpCast"): V is
+quantized with one E4M3 scale per (b, h) (s_V = max|V| / 448), and the exact
+weights are ExpCast bytes, p-hat = decode(c((z - m) log2 e)), with the pivot m
+the row's largest exact logit (the final value of the kernel's online pivot);
+the same p-hat weights form the exact numerator (with the dequantized V) and the
+exact part of the denominator.  The tail keeps the bf16 group means of V.
 """
 from __future__ import annotations
 
@@ -47,10 +54,12 @@ from typing import Iterable, Optional
 import numpy as np
 
 from . import e4m3
+from .e4m3 import expcast_weight
 from .sol_attn import (BLOCK, block_counts, block_means, block_ranges, route,
                        sink_block_mask, _head)
 
 ANCHOR = 32
+LOG2E = 1.0 / math.log(2.0)
 
 
 # ----------------------------------------------------------------------------
@@ -147,11 +156,13 @@ def tail_stats(qbar_a: np.ndarray, groups: list, scale: float):
 
 def attend_query_block2(q: np.ndarray, k: np.ndarray, v: np.ndarray, i: int, sel_row: np.ndarray,
                         groups: list, scale: float, anchor: int = ANCHOR, block: int = BLOCK,
-                        return_parts: bool = False):
+                        return_parts: bool = False, pv: str = "bf16", v_exact: Optional[np.ndarray] = None):
     """Output rows of query block i: exact blocks plus the first-order-corrected tail.
 
     return_parts also returns, per anchor, (range, ln Z_a, mu_a, nu_a) and
     per-token alpha_t = Z_E / (Z_E + Z-hat) (output table, Sol-Attn2 row).
+    pv="expcast" uses ExpCast weights for the exact tokens and v_exact (the
+    per-head FP8-dequantized V) as their values; the tail still uses `groups`.
     """
     n, d = q.shape
     s, e = i * block, min(i * block + block, n)
@@ -171,11 +182,21 @@ def attend_query_block2(q: np.ndarray, k: np.ndarray, v: np.ndarray, i: int, sel
         m = np.full(a1 - a0, -np.inf)
         if z.shape[1]:
             m = np.maximum(m, z.max(axis=1))
-        m = np.maximum(m, lam)
-        ez = np.exp(z - m[:, None])
-        zhat = np.exp(lam - m)
-        ze = ez.sum(axis=1)
-        num = ez @ v[ex_idx] + zhat[:, None] * nu[None, :]
+        if pv == "expcast" and z.shape[1]:
+            # ExpCast against the row pivot p = max exact logit: e^{z} ~ e^{p} p-hat((z - p) log2 e)
+            p = z.max(axis=1)
+            w = expcast_weight((z - p[:, None]) * LOG2E)
+            mm = np.maximum(p, lam)
+            ez_scale = np.exp(p - mm)
+            zhat = np.exp(lam - mm)
+            ze = w.sum(axis=1) * ez_scale
+            num = (w @ v_exact[ex_idx]) * ez_scale[:, None] + zhat[:, None] * nu[None, :]
+        else:
+            m = np.maximum(m, lam)
+            ez = np.exp(z - m[:, None])
+            zhat = np.exp(lam - m)
+            ze = ez.sum(axis=1)
+            num = ez @ v[ex_idx] + zhat[:, None] * nu[None, :]
         den = ze + zhat
         out[a0 - s:a1 - s] = num / den[:, None]
         alpha[a0 - s:a1 - s] = ze / den
@@ -201,10 +222,18 @@ class Head2Result:
     groups: list
 
 
+def quantize_head_v(v: np.ndarray):
+    """One E4M3 scale for a whole (b, h) of V (draft "FP8 quantization": "V with one
+    scale per head").  Returns (codes uint8 [N, d], scale float32, dequantized float64)."""
+    c, s = e4m3.quantize_block_fp32(v)
+    return c, s, np.float64(s) * e4m3.decode(c)
+
+
 def sol_attn2_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float = 1.0,
                    sink_start: Optional[int] = None, sink_tokens: int = 0, thresh: str = "diag",
                    anchor: int = ANCHOR, grouping: str = "split2", quantize: bool = True,
-                   query_blocks: Optional[Iterable[int]] = None, block: int = BLOCK) -> Head2Result:
+                   query_blocks: Optional[Iterable[int]] = None, block: int = BLOCK,
+                   pv: str = "bf16") -> Head2Result:
     """Sol-Attn2 for one (batch, head): q, k, v [N, d] holding the exact input values."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -224,15 +253,16 @@ def sol_attn2_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float = 1.0
     groups = all_key_groups(kd, v, qhat, grouping, block)
     out = np.full((n, d), np.nan)
     nb = len(block_counts(n, block))
+    v_exact = quantize_head_v(v)[2] if pv == "expcast" else None
     for i in (range(nb) if query_blocks is None else query_blocks):
         s, e = i * block, min(i * block + block, n)
-        out[s:e] = attend_query_block2(qd, kd, v, i, sel[i], groups, scale, anchor, block)
+        out[s:e] = attend_query_block2(qd, kd, v, i, sel[i], groups, scale, anchor, block, pv=pv, v_exact=v_exact)
     return Head2Result(out, sel, s_hat, tau_i, qd, kd, qc, kc, qs, ks, qhat, groups)
 
 
 def sol_attn2(q, k, v, tau: float = 1.0, sink_start: Optional[int] = None, sink_tokens: int = 0,
               thresh: str = "diag", anchor: int = ANCHOR, grouping: str = "split2",
-              quantize: bool = True, query_blocks=None):
+              quantize: bool = True, query_blocks=None, pv: str = "bf16"):
     """Sol-Attn2 over BTHD inputs [B, N, H, d].
 
     Returns dict(out [B,N,H,d], sel [B,H,nb,nb], s_hat, tau_i, q_codes/k_codes
@@ -252,7 +282,7 @@ def sol_attn2(q, k, v, tau: float = 1.0, sink_start: Optional[int] = None, sink_
     for b in range(B):
         for h in range(H):
             r = sol_attn2_head(_head(q, b, h), _head(k, b, h), _head(v, b, h), tau, sink_start,
-                               sink_tokens, thresh, anchor, grouping, quantize, qb)
+                               sink_tokens, thresh, anchor, grouping, quantize, qb, pv=pv)
             res["out"][b, :, h, :] = r.out
             res["sel"][b, h], res["s_hat"][b, h], res["tau_i"][b, h] = r.sel, r.s_hat, r.tau_i
             res["qhat"][b, h] = r.qhat

@@ -1,0 +1,108 @@
+"""Pins for the ExpCast / FP8-PV part of the Sol-Attn2 oracle (no GPU).
+
+Sol-Attn2 draft, "FP8 quantization and ExpCast": c(u) = clip_[0,120](RNE(8u + 55.65)),
+p-hat(u) = decode_E4M3(c(u)) ~ 2^u, V quantized with one E4M3 scale per head, and the
+same decoded weights in the PV product and the denominator.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import e4m3
+from oracle import sol_attn2 as s2
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+@pytest.mark.parametrize("u,code", [
+    (0.0, 56),      # 55.65 -> 56: exponent field 7, mantissa 0 -> 1.0
+    (1.0, 64),      # 63.65 -> 64 -> 2.0
+    (-1.0, 48),     # 47.65 -> 48 -> 0.5
+    (0.5, 60),      # 59.65 -> 60: 1.5 (2^0.5 = 1.414 on the linear mantissa)
+    (-6.5, 4),      # 3.65 -> 4: subnormal 4/8 * 2^-6
+    (-7.0, 0),      # -0.35 -> 0
+    (8.05, 120),    # 120.05 -> 120 = 2^8
+    (10.0, 120),    # clipped
+    (-math.inf, 0),
+])
+def test_code_table(u, code):
+    assert int(e4m3.expcast_code(np.float32(u))) == code
+
+
+def test_integer_scores_decode_to_exact_powers_of_two():
+    for k in range(-6, 9):
+        assert float(e4m3.expcast_weight(np.float32(k))) == 2.0 ** k
+
+
+def test_ratio_to_two_to_the_u_matches_closed_form():
+    """Within an octave u = k + phi the byte's mantissa is j = RNE(8 phi - 0.35), so
+    p-hat / 2^u = (1 + j/8) / 2^phi, decreasing in phi on each j-interval; its extremes
+    are the interval ends (j + 0.5 + 0.35)/8 (just below) and (j - 0.5 + 0.35)/8."""
+    lo_c, hi_c = math.inf, -math.inf
+    for j in range(0, 9):
+        a = max(0.0, (j - 0.5 + 0.35) / 8.0)
+        b = min(1.0, (j + 0.5 + 0.35) / 8.0)
+        if a >= b:
+            continue
+        mant = 1.0 + j / 8.0 if j < 8 else 2.0
+        hi_c = max(hi_c, mant / 2.0 ** a)
+        lo_c = min(lo_c, mant / 2.0 ** b)
+    u = np.linspace(-6.0, 0.0, 240001)[:-1]
+    r = e4m3.expcast_weight(u) / 2.0 ** u
+    assert r.max() <= hi_c + 1e-6 and r.max() >= hi_c - 1e-3
+    assert r.min() >= lo_c - 1e-6 and r.min() <= lo_c + 1e-3
+    assert 0.92 < lo_c < 0.94 and 1.07 < hi_c < 1.08
+    # the 55.65 offset centres the linear mantissa: mean ratio within 1% of 1
+    assert abs(r.mean() - 1.0) < 0.01
+
+
+def _block_offset(n, d, seed):
+    g = np.random.default_rng(seed)
+    nb = (n + 63) // 64
+    off = g.standard_normal((nb, d))
+    x = g.standard_normal((n, d)) + off[np.arange(n) // 64]
+    return x.astype(np.float32).astype(np.float64)
+
+
+def test_constant_values_come_back_exactly():
+    """With every block exact, o = sum p-hat v' / sum p-hat; for V rows all equal to c the
+    output is the per-head-quantized c exactly, which holds only if the same weights
+    form the numerator and the denominator."""
+    n, d = 200, 128
+    q, k = _block_offset(n, d, 1), _block_offset(n, d, 2)
+    c = np.random.default_rng(3).standard_normal(d).astype(np.float32).astype(np.float64)
+    v = np.tile(c, (n, 1))
+    r = s2.sol_attn2_head(q, k, v, tau=1.0, sink_start=0, sink_tokens=n, pv="expcast")
+    c8 = s2.quantize_head_v(v)[2][0]
+    np.testing.assert_allclose(r.out, np.tile(c8, (n, 1)), rtol=1e-12, atol=1e-12)
+    assert not np.allclose(c8, c)          # the quantization is visible
+
+
+def test_integer_gaps_reduce_to_softmax_over_quantized_v():
+    """Logits whose base-2 gaps to the row maximum are integers in [-6, 0] get exact
+    powers of two, so the oracle equals softmax attention over the per-head FP8 V."""
+    n, d = 128, 128
+    rng = np.random.default_rng(5)
+    gaps = rng.integers(0, 7, size=n).astype(np.float64)        # 0..6
+    q = np.zeros((n, d))
+    q[:, 0] = math.sqrt(d) * math.log(2.0)                       # z_u = ln 2 * k_u[0]
+    k = np.zeros((n, d))
+    k[:, 0] = -gaps
+    v = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+    r = s2.sol_attn2_head(q, k, v, tau=1.0, sink_start=0, sink_tokens=n, quantize=False, pv="expcast")
+    v8 = s2.quantize_head_v(v)[2]
+    w = 2.0 ** (-gaps)
+    want = (w @ v8) / w.sum()
+    np.testing.assert_allclose(r.out, np.tile(want, (n, 1)), rtol=1e-12, atol=1e-13)
+
+
+def test_fp8_pv_stays_close_to_the_bf16_reading():
+    """ExpCast and the per-head V scale are approximations of the same output: on the
+    block-offset data the two readings agree to a few percent (rel L2)."""
+    n, d = 256, 128
+    q, k, v = (_block_offset(n, d, s) for s in (11, 12, 13))
+    a = s2.sol_attn2_head(q, k, v, tau=1.0).out
+    b = s2.sol_attn2_head(q, k, v, tau=1.0, pv="expcast").out
+    err = np.linalg.norm(a - b) / np.linalg.norm(a)
+    assert 1e-4 < err < 0.05

@@ -109,3 +109,38 @@ PINS_SOL2 = [
 def test_sol_attn2_mutation_is_caught(name, monkeypatch):
     MUTATIONS_SOL2[name](monkeypatch)
     assert any(_fails(fn, *args) for fn, args in PINS_SOL2), f"mutation {name} not caught"
+
+
+import test_oracle_expcast as p3  # noqa: E402
+from oracle import e4m3  # noqa: E402
+
+
+def _code_with_offset(offset):
+    def code(u):
+        t = (np.float32(8.0) * np.asarray(u, dtype=np.float32) + np.float32(offset)).astype(np.float32)
+        return np.clip(np.rint(t), 0.0, 120.0).astype(np.uint8)
+    return code
+
+
+MUTATIONS_EXPCAST = {
+    # the plain 56 offset (no centring of the linear mantissa)
+    "offset_56": lambda mp: mp.setattr(e4m3, "expcast_code", _code_with_offset(56.0)),
+    # the exact tokens use the unquantized V
+    "v_not_quantized": lambda mp: mp.setattr(s2, "quantize_head_v", lambda v: (None, np.float32(1.0), v)),
+    # the mantissa is read as the next octave (off-by-one exponent)
+    "exponent_off_by_one": lambda mp: mp.setattr(
+        e4m3, "expcast_weight", lambda u: 2.0 * e4m3.decode(e4m3.expcast_code(u))),
+}
+
+PINS_EXPCAST = [
+    (p3.test_ratio_to_two_to_the_u_matches_closed_form, ()),
+    (p3.test_integer_scores_decode_to_exact_powers_of_two, ()),
+    (p3.test_constant_values_come_back_exactly, ()),
+    (p3.test_integer_gaps_reduce_to_softmax_over_quantized_v, ()),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_EXPCAST))
+def test_expcast_mutation_is_caught(name, monkeypatch):
+    MUTATIONS_EXPCAST[name](monkeypatch)
+    assert any(_fails(fn, *args) for fn, args in PINS_EXPCAST), f"mutation {name} not caught"
