@@ -40,10 +40,14 @@ The oracle is parameterised by anchor size, grouping ("split2", "whole",
 
 FP8 PV option (pv="expcast"; draft "FP8 quantization and ExpCast"): V is
 quantized with one E4M3 scale per (b, h) (s_V = max|V| / 448), and the exact
-weights are ExpCast bytes, p-hat = decode(c((z - m) log2 e)), with the pivot m
-the row's largest exact logit (the final value of the kernel's online pivot);
-the same p-hat weights form the exact numerator (with the dequantized V) and the
-exact part of the denominator.  The tail keeps the bf16 group means of V.
+weights are ExpCast bytes, p-hat = decode(c((z - m) log2 e)), against the shared
+online pivot m: the selected key blocks are taken in ascending order, m is
+raised to each block's largest logit before that block's bytes are formed, and
+the sums so far are rescaled by e^{m_old - m} (the pages give the pivot as
+online; the reading takes the order and granularity of the tiled pass, one
+64-token block at a time).  The same p-hat weights form the exact numerator
+(with the dequantized V) and the exact part of the denominator.  The tail keeps
+the bf16 group means of V.
 """
 from __future__ import annotations
 
@@ -183,14 +187,28 @@ def attend_query_block2(q: np.ndarray, k: np.ndarray, v: np.ndarray, i: int, sel
         if z.shape[1]:
             m = np.maximum(m, z.max(axis=1))
         if pv == "expcast" and z.shape[1]:
-            # ExpCast against the row pivot p = max exact logit: e^{z} ~ e^{p} p-hat((z - p) log2 e)
-            p = z.max(axis=1)
-            w = expcast_weight((z - p[:, None]) * LOG2E)
+            # ExpCast with the shared online pivot: the selected blocks in ascending order,
+            # the pivot p raised to each block's largest logit before its bytes are taken,
+            # e^{z} ~ e^{p} p-hat((z - p) log2 e), earlier sums rescaled by e^{p_old - p}.
+            p = np.full(a1 - a0, -np.inf)
+            wnum = np.zeros((a1 - a0, d))
+            wden = np.zeros(a1 - a0)
+            col = 0
+            for j in np.flatnonzero(sel_row):
+                bs, be = ranges[j]
+                zj = z[:, col:col + (be - bs)]
+                col += be - bs
+                p_new = np.maximum(p, zj.max(axis=1))
+                keep = np.where(np.isfinite(p), np.exp(p - p_new), 0.0)
+                w = expcast_weight((zj - p_new[:, None]) * LOG2E)
+                wnum = wnum * keep[:, None] + w @ v_exact[bs:be]
+                wden = wden * keep + w.sum(axis=1)
+                p = p_new
             mm = np.maximum(p, lam)
             ez_scale = np.exp(p - mm)
             zhat = np.exp(lam - mm)
-            ze = w.sum(axis=1) * ez_scale
-            num = (w @ v_exact[ex_idx]) * ez_scale[:, None] + zhat[:, None] * nu[None, :]
+            ze = wden * ez_scale
+            num = wnum * ez_scale[:, None] + zhat[:, None] * nu[None, :]
         else:
             m = np.maximum(m, lam)
             ez = np.exp(z - m[:, None])

@@ -106,3 +106,40 @@ def test_fp8_pv_stays_close_to_the_bf16_reading():
     b = s2.sol_attn2_head(q, k, v, tau=1.0, pv="expcast").out
     err = np.linalg.norm(a - b) / np.linalg.norm(a)
     assert 1e-4 < err < 0.05
+
+
+def test_online_pivot_that_never_moves_equals_the_direct_formula():
+    """If the first selected block holds every row's largest logit, the online pivot is
+    fixed from the start and the output is sum p-hat((z - max) log2 e) v' / sum p-hat."""
+    n, d = 192, 128
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((n, d)) * 0.1
+    k = rng.standard_normal((n, d)) * 0.1
+    q[:, 0] = 1.0
+    k[:64, 0] = 3.0                                    # block 0 holds every row's largest logit
+    k[64:, 0] = 0.0
+    v = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+    r = s2.sol_attn2_head(q, k, v, tau=1.0, sink_start=0, sink_tokens=n, quantize=False, pv="expcast")
+    z = (q @ k.T) / math.sqrt(d)
+    assert (z[:, :64].max(axis=1) >= z.max(axis=1)).all()
+    w = e4m3.expcast_weight((z - z.max(axis=1, keepdims=True)) / math.log(2.0))
+    want = (w @ s2.quantize_head_v(v)[2]) / w.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(r.out, want, rtol=1e-10, atol=1e-12)
+
+
+def test_online_pivot_keeps_blocks_seen_before_the_maximum():
+    """Block 0 with base-2 logits 0, then block 1 with logits 10: block 0's bytes are taken
+    against pivot 0 (weight 1 each) and rescaled by 2^-10 when the pivot moves, so
+    o = (2^-10 sum_0 v' + sum_1 v') / (64 2^-10 + 64).  A final-maximum pivot would put
+    block 0 at u = -10, byte 0, weight 0."""
+    n, d = 128, 128
+    q = np.zeros((n, d))
+    q[:, 0] = math.sqrt(d) * math.log(2.0)
+    k = np.zeros((n, d))
+    k[64:, 0] = 10.0
+    v = np.random.default_rng(4).standard_normal((n, d)).astype(np.float32).astype(np.float64)
+    r = s2.sol_attn2_head(q, k, v, tau=1.0, sink_start=0, sink_tokens=n, quantize=False, pv="expcast")
+    v8 = s2.quantize_head_v(v)[2]
+    want = (2.0 ** -10 * v8[:64].sum(axis=0) + v8[64:].sum(axis=0)) / (64 * 2.0 ** -10 + 64)
+    np.testing.assert_allclose(r.out, np.tile(want, (n, 1)), rtol=1e-12, atol=1e-13)
+    assert not np.allclose(want, v8[64:].mean(axis=0), rtol=1e-6, atol=0)
