@@ -29,7 +29,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--variant", choices=["sol1", "sol2"], default="sol1")
+    p.add_argument("--variant", choices=["sol1", "sol2", "sol2pv8"], default="sol1",
+                   help="sol1: Sol-Attn; sol2: Sol-Attn2 (FP8 Q/K); sol2pv8: Sol-Attn2 with ExpCast FP8 PV")
     p.add_argument("--tokens", type=int, default=32768, help="video tokens (32768 = operator benchmark shape)")
     p.add_argument("--heads", type=int, default=32)
     p.add_argument("--text-sink", type=int, default=0, help="exact text-prefix tokens (long-sequence shape: 512)")
@@ -69,7 +70,7 @@ def main():
         return
     B, H, D = 1, args.heads, 128
     N = args.tokens + args.text_sink
-    variant = 1 if args.variant == "sol1" else 2
+    variant = {"sol1": 1, "sol2": 2, "sol2pv8": 3}[args.variant]
     sink_start, sink_tokens = (0, args.text_sink) if args.text_sink else (None, 0)
     log(f"[bench] generating B={B} N={N} H={H} d={D} ({args.variant})")
     t0 = time.time()
@@ -89,8 +90,9 @@ def main():
     pair_w = np.outer(counts, counts)
 
     def routing(tau):
-        _, m, _ = bsa.debug_routing(variant, q, k, v, tau, "diag", sink_start, sink_tokens, out=None, workspace=ws,
-                                    kv_splits=args.kv_splits if variant == 1 else 0)
+        # (the FP8-PV workspace extends the Sol-Attn2 one and routes the same way)
+        _, m, _ = bsa.debug_routing(min(variant, 2), q, k, v, tau, "diag", sink_start, sink_tokens, out=None,
+                                    workspace=ws, kv_splits=args.kv_splits if variant == 1 else 0)
         return m.numpy()
 
     def sparsity(m):
@@ -157,12 +159,17 @@ def main():
         run_kernel = lambda: bsa.fused(1, q, k, v, None, ws, sink_start, sink_tokens, args.kv_splits)  # noqa: E731
         kernel_flops = flops_exact + flops_proxy
         peak = 2500.0                                          # dense bf16 MFMA
-    else:
+    elif variant == 2:
         kernel = "sol2_fused_kernel"
         run_kernel = lambda: bsa.exact2(q, k, v, out, ws)    # noqa: E731
         kernel_flops = flops_exact
         # QK^T on FP8 (5.0 PF) and PV on bf16 (2.5 PF), half the exact FLOPs each
         peak = kernel_flops / (0.5 * kernel_flops / 5000.0 + 0.5 * kernel_flops / 2500.0)
+    else:
+        kernel = "sol2_fused_kernel"
+        run_kernel = lambda: bsa.exact2(q, k, v, out, ws, pv8=True)  # noqa: E731
+        kernel_flops = flops_exact
+        peak = 5000.0                                          # QK^T and PV both on FP8
     for _ in range(2):
         run_kernel()
     kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -215,7 +222,8 @@ def main():
         cpu = cpu_baseline(qc, kc, vc, tau, sink_start, sink_tokens, variant, args.cpu_sample_blocks, dense_flops)
         log(f"[bench] cpu oracle {cpu}")
 
-    workload = (f"{'Sol-Attn' if variant == 1 else 'Sol-Attn2 (FP8 Q/K)'} forward, B={B} H={H} d={D} "
+    workload = (f"{ {1: 'Sol-Attn', 2: 'Sol-Attn2 (FP8 Q/K)', 3: 'Sol-Attn2 (FP8 Q/K, ExpCast FP8 PV)'}[variant] } "
+                f"forward, B={B} H={H} d={D} "
                 f"N={N}{' (512 text sink + ' + str(args.tokens) + ' video)' if args.text_sink else ''}, "
                 f"block-offset synthetic data, {100 * args.sparsity:.0f}% target token-pair sparsity")
     rec = {
@@ -229,7 +237,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if variant == 1 else "fp8(e4m3 QK)+bf16(PV)",
+        "dtype": {1: "bf16", 2: "fp8(e4m3 QK)+bf16(PV)", 3: "fp8(e4m3 QK, ExpCast P, e4m3 V)"}[variant],
         "data": "synthetic (seeded block-offset Gaussian Q/K/V, bf16)",
         "config": {"workload": workload, "batch": B, "heads": H, "head_dim": D, "tokens": N,
                    "tau": round(tau, 5), "realised_sparsity": round(real_sp, 5),
@@ -276,11 +284,14 @@ def cpu_baseline(q, k, v, tau, sink_start, sink_tokens, variant, sample_blocks, 
             sa.attend_query_block(qh, kh, vh, i, r.sel[i], kbar, vsum, counts, 1 / math.sqrt(D))
         t_blocks = time.perf_counter() - t1
     else:
+        pv = "expcast" if variant == 3 else "bf16"
         r = s2.sol_attn2_head(qh, kh, vh, tau, sink_start, sink_tokens, query_blocks=[])
+        v_exact = s2.quantize_head_v(vh)[2] if variant == 3 else None
         t_route = time.perf_counter() - t0
         t1 = time.perf_counter()
         for i in blocks:
-            s2.attend_query_block2(r.q_deq, r.k_deq, vh, i, r.sel[i], r.groups, 1 / math.sqrt(D))
+            s2.attend_query_block2(r.q_deq, r.k_deq, vh, i, r.sel[i], r.groups, 1 / math.sqrt(D), pv=pv,
+                                   v_exact=v_exact)
         t_blocks = time.perf_counter() - t1
     t_full = B * H * (t_route + t_blocks * nb / len(blocks))
     return {"value": round(dense_flops / t_full / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",

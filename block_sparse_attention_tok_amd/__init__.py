@@ -5,11 +5,10 @@ include/solattn.h); this package is its thin ctypes binding.  Tensors are
 contiguous bf16 [batch, tokens, heads, 128] on the GPU (Sol-Attn README,
 "Core API").
 """
-from ._lib import (SOL_VARIANT_SOL1, SOL_VARIANT_SOL2, SolAttnError, alloc_workspace,  # noqa: F401
-                   debug_routing, exact2, fused, kv_splits_for, lib, prepare, sol_attn, sol_attn2, tail2, validate,
-                   workspace_bytes,
-                   workspace_layout, workspace_views)
+from ._lib import (SOL_VARIANT_SOL1, SOL_VARIANT_SOL2, SOL_VARIANT_SOL2_PV8, SolAttnError,  # noqa: F401
+                   alloc_workspace, debug_routing, exact2, fused, kv_splits_for, lib, prepare, sol_attn, sol_attn2,
+                   sol_attn2_pv8, tail2, validate, workspace_bytes, workspace_layout, workspace_views)
 
-__all__ = ["sol_attn", "sol_attn2", "validate", "workspace_bytes", "workspace_layout", "prepare", "fused",
-           "debug_routing", "tail2", "exact2", "alloc_workspace", "kv_splits_for", "workspace_views", "SolAttnError", "lib",
-           "SOL_VARIANT_SOL1", "SOL_VARIANT_SOL2"]
+__all__ = ["sol_attn", "sol_attn2", "sol_attn2_pv8", "validate", "workspace_bytes", "workspace_layout", "prepare",
+           "fused", "tail2", "exact2", "debug_routing", "alloc_workspace", "kv_splits_for", "workspace_views",
+           "SolAttnError", "lib", "SOL_VARIANT_SOL1", "SOL_VARIANT_SOL2", "SOL_VARIANT_SOL2_PV8"]

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libsolattn.so")
 SOL_OK = 0
 SOL_VARIANT_SOL1 = 1
 SOL_VARIANT_SOL2 = 2
+SOL_VARIANT_SOL2_PV8 = 3
 THRESH = {"diag": 0, "exact": 1}
 
 EXPORTED = [
@@ -27,7 +28,7 @@ EXPORTED = [
     "sol_attn_kv_splits", "sol_attn_workspace_bytes_kv", "sol_attn_workspace_layout_kv",
     "sol_attn", "sol_attn_prepare", "sol_attn_fused", "sol_attn_fused_kv", "sol_attn_debug_routing",
     "sol_attn2", "sol_attn2_prepare", "sol_attn2_fused", "sol_attn2_tail", "sol_attn2_exact",
-    "sol_attn2_debug_routing",
+    "sol_attn2_debug_routing", "sol_attn2_pv8", "sol_attn2_pv8_prepare", "sol_attn2_pv8_exact",
 ]
 
 
@@ -35,7 +36,7 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov", "kpart",
         "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse",
-        "sel", "tmu", "tnu", "tlz")]
+        "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale")]
 
 
 class SolAttnError(RuntimeError):
@@ -74,14 +75,15 @@ def lib() -> ctypes.CDLL:
     L.sol_attn_fused_kv.restype = i32
     L.sol_attn2_tail.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
     L.sol_attn2_tail.restype = i32
-    L.sol_attn2_exact.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
-    L.sol_attn2_exact.restype = i32
+    for name in ("sol_attn2_exact", "sol_attn2_pv8_exact"):
+        getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        getattr(L, name).restype = i32
     full = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp]
-    for name in ("sol_attn", "sol_attn2"):
+    for name in ("sol_attn", "sol_attn2", "sol_attn2_pv8"):
         getattr(L, name).argtypes = full
         getattr(L, name).restype = i32
     prep = [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp, sz, vp]
-    for name in ("sol_attn_prepare", "sol_attn2_prepare"):
+    for name in ("sol_attn_prepare", "sol_attn2_prepare", "sol_attn2_pv8_prepare"):
         getattr(L, name).argtypes = prep
         getattr(L, name).restype = i32
     fused = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
@@ -210,11 +212,20 @@ def sol_attn2(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.
     return _full_call("sol_attn2", SOL_VARIANT_SOL2, q, k, v, tau, sink_start, sink_tokens, thresh, out, workspace)
 
 
+def sol_attn2_pv8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
+                  sink_start: Optional[int] = None, sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sol-Attn2 with ExpCast P and per-head FP8 V (FP8 PV)."""
+    return _full_call("sol_attn2_pv8", SOL_VARIANT_SOL2_PV8, q, k, v, tau, sink_start, sink_tokens, thresh, out,
+                      workspace)
+
+
 def prepare(variant: int, q, k, v, tau: float, workspace: torch.Tensor, thresh: str = "diag"):
     """Stage 1 (summaries + threshold [+ Sol-Attn2 quantization and groups]) into `workspace`."""
     _check_tensors(q, k, v)
     B, N, H, D = q.shape
-    name = "sol_attn_prepare" if variant == SOL_VARIANT_SOL1 else "sol_attn2_prepare"
+    name = {SOL_VARIANT_SOL1: "sol_attn_prepare", SOL_VARIANT_SOL2: "sol_attn2_prepare",
+            SOL_VARIANT_SOL2_PV8: "sol_attn2_pv8_prepare"}[variant]
     _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), B, N, H, D, float(tau), THRESH[thresh],
                                 _ptr(workspace), workspace.numel(), _stream(q.device)), name)
 
@@ -228,6 +239,10 @@ def fused(variant: int, q, k, v, out, workspace: torch.Tensor, sink_start: Optio
                                        int(sink_tokens), int(kv_splits), _ptr(workspace), workspace.numel(),
                                        _stream(q.device)), "sol_attn_fused_kv")
         return
+    if variant == SOL_VARIANT_SOL2_PV8:
+        tail2(q, k, v, workspace, sink_start, sink_tokens)
+        exact2(q, k, v, out, workspace, pv8=True)
+        return
     _check(lib().sol_attn2_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
                                  int(sink_tokens), _ptr(workspace), workspace.numel(), _stream(q.device)),
            "sol_attn2_fused")
@@ -240,11 +255,12 @@ def tail2(q, k, v, workspace: torch.Tensor, sink_start: Optional[int] = None, si
                                 _ptr(workspace), workspace.numel(), _stream(q.device)), "sol_attn2_tail")
 
 
-def exact2(q, k, v, out, workspace: torch.Tensor):
-    """Sol-Attn2 stage 2b: the exact FP8 pass combined with the tail of stage 2a."""
+def exact2(q, k, v, out, workspace: torch.Tensor, pv8: bool = False):
+    """Sol-Attn2 stage 2b: the exact FP8 pass (FP8 PV with pv8) combined with the tail of stage 2a."""
     B, N, H, D = q.shape
-    _check(lib().sol_attn2_exact(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _ptr(workspace),
-                                 workspace.numel(), _stream(q.device)), "sol_attn2_exact")
+    name = "sol_attn2_pv8_exact" if pv8 else "sol_attn2_exact"
+    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _ptr(workspace),
+                                workspace.numel(), _stream(q.device)), name)
 
 
 def debug_routing(variant: int, q, k, v, tau: float = 1.0, thresh: str = "diag", sink_start: Optional[int] = None,
@@ -295,7 +311,7 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
         kstat=view(L.kstat, torch.float32, (batch, heads, 2, 128)),
         kcov=view(L.kcov, torch.float32, (batch, heads, 128, 128)),
     )
-    if variant == SOL_VARIANT_SOL2:
+    if variant in (SOL_VARIANT_SOL2, SOL_VARIANT_SOL2_PV8):
         tp = nbp * 64
         d.update(
             q8=view(L.q8, torch.uint8, (batch, heads, tp, 128)),
@@ -308,6 +324,17 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
             glogn=view(L.glogn, torch.float32, (batch, heads, nbp, 2)),
             ghi=view(L.ghi, torch.int64, (batch, heads, nbp)),
             qanc=view(L.qanc, torch.float32, (batch, heads, nbp, 2, 128)),
+            sel=view(L.sel, torch.int64, (batch, heads, L.nb, nbp // 64)),
+            tmu=view(L.tmu, torch.float32, (batch, heads, nbp, 2, 128)),
+            tnu=view(L.tnu, torch.float32, (batch, heads, nbp, 2, 128)),
+            tlz=view(L.tlz, torch.float32, (batch, heads, nbp, 2)),
+        )
+    if variant == SOL_VARIANT_SOL2_PV8:
+        tp = nbp * 64
+        d.update(
+            v8t=view(L.v8t, torch.uint8, (batch, heads, 128, tp)),
+            vbmax=view(L.vbmax, torch.float32, (batch, heads, nbp)),
+            vscale=view(L.vscale, torch.float32, (batch, heads)),
         )
     del bh
     return d

@@ -62,7 +62,8 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
            int kv_splits = 0) {
   int st = check_shape(batch, tokens, heads, head_dim);
   if (st != SOL_OK) return st;
-  if (variant != SOL_VARIANT_SOL1 && variant != SOL_VARIANT_SOL2) return SOL_ERR_ARG;
+  if (variant != SOL_VARIANT_SOL1 && variant != SOL_VARIANT_SOL2 && variant != SOL_VARIANT_SOL2_PV8)
+    return SOL_ERR_ARG;
   std::memset(L, 0xff, sizeof(*L));          // every offset -1
   const int64_t nb = (tokens + kBlock - 1) / kBlock;
   const int64_t nbp = (nb + 63) / 64 * 64;
@@ -79,7 +80,7 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   L->kstat = take(bh * 2 * kDim * 4);
   L->kcov = take(bh * kDim * kDim * 4);
   L->kpart = take(bh * 16 * 2 * kDim * 8);
-  if (variant == SOL_VARIANT_SOL2) {
+  if (variant == SOL_VARIANT_SOL2 || variant == SOL_VARIANT_SOL2_PV8) {
     const int64_t tp = nbp * kBlock;
     L->q8 = take(bh * tp * kDim);
     L->k8 = take(bh * tp * kDim);
@@ -95,6 +96,11 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->tmu = take(bh * nbp * 2 * kDim * 4);
     L->tnu = take(bh * nbp * 2 * kDim * 4);
     L->tlz = take(bh * nbp * 2 * 4);
+    if (variant == SOL_VARIANT_SOL2_PV8) {
+      L->v8t = take(bh * kDim * tp);
+      L->vbmax = take(bh * nbp * 4);
+      L->vscale = take(bh * 4);
+    }
   }
   // split-KV partials (Sol-Attn only)
   L->kv_splits = variant == SOL_VARIANT_SOL1 ? effective_splits(tokens, kv_splits) : 1;
@@ -137,6 +143,9 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.tmu = (float*)at(L.tmu);
   w.tnu = (float*)at(L.tnu);
   w.tlz = (float*)at(L.tlz);
+  w.v8t = (uint8_t*)at(L.v8t);
+  w.vbmax = (float*)at(L.vbmax);
+  w.vscale = (float*)at(L.vscale);
   return w;
 }
 
@@ -273,7 +282,8 @@ static int fused_common(int variant, const void* q, const void* k, const void* v
     }
   }
   if (!(stage2 & kStage2Exact)) return SOL_OK;
-  return hip_status(solattn::launch_fused2((const uint16_t*)v, (uint16_t*)out, s, w, hs));
+  return hip_status(solattn::launch_fused2((const uint16_t*)v, (uint16_t*)out, s, w,
+                                           variant == SOL_VARIANT_SOL2_PV8, hs));
 }
 
 int sol_attn_fused(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
@@ -316,11 +326,11 @@ int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* ou
                       workspace, workspace_bytes, mask_bits, stream, false, kv_splits);
 }
 
-int sol_attn2_prepare(const void* q, const void* k, const void* v, int64_t batch, int64_t tokens, int64_t heads,
-                      int64_t head_dim, float tau, int thresh, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+static int prepare2(int variant, const void* q, const void* k, const void* v, int64_t batch, int64_t tokens,
+                    int64_t heads, int64_t head_dim, float tau, int thresh, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   sol_ws_layout L;
-  int st = prologue(SOL_VARIANT_SOL2, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  int st = prologue(variant, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
   if (st != SOL_OK) return st;
   if (!std::isfinite(tau)) return SOL_ERR_TAU;
   if ((st = check_thresh(thresh)) != SOL_OK) return st;
@@ -333,7 +343,42 @@ int sol_attn2_prepare(const void* q, const void* k, const void* v, int64_t batch
   if (st != SOL_OK) return st;
   st = hip_status(solattn::launch_qhat(s, w, hs));
   if (st != SOL_OK) return st;
-  return hip_status(solattn::launch_groups((const uint16_t*)v, s, w, hs));
+  st = hip_status(solattn::launch_groups((const uint16_t*)v, s, w, hs));
+  if (st != SOL_OK || variant != SOL_VARIANT_SOL2_PV8) return st;
+  return hip_status(solattn::launch_vquant((const uint16_t*)v, s, w, hs));
+}
+
+int sol_attn2_prepare(const void* q, const void* k, const void* v, int64_t batch, int64_t tokens, int64_t heads,
+                      int64_t head_dim, float tau, int thresh, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return prepare2(SOL_VARIANT_SOL2, q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace,
+                  workspace_bytes, stream);
+}
+
+int sol_attn2_pv8_prepare(const void* q, const void* k, const void* v, int64_t batch, int64_t tokens,
+                          int64_t heads, int64_t head_dim, float tau, int thresh, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return prepare2(SOL_VARIANT_SOL2_PV8, q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace,
+                  workspace_bytes, stream);
+}
+
+int sol_attn2_pv8_exact(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                        int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes, void* stream) {
+  return fused_common(SOL_VARIANT_SOL2_PV8, q, k, v, out, batch, tokens, heads, head_dim, -1, 0, workspace,
+                      workspace_bytes, nullptr, stream, true, 0, kStage2Exact);
+}
+
+int sol_attn2_pv8(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                  int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return SOL_ERR_NULL;
+  int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
+  if (st != SOL_OK) return st;
+  st = sol_attn2_pv8_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes,
+                             stream);
+  if (st != SOL_OK) return st;
+  return fused_common(SOL_VARIANT_SOL2_PV8, q, k, v, out, batch, tokens, heads, head_dim, sink_start,
+                      sink_tokens, workspace, workspace_bytes, nullptr, stream, true, 0, kStage2Both);
 }
 
 int sol_attn2_fused(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,

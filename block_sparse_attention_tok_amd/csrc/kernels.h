@@ -33,6 +33,9 @@ struct Workspace {
   float* tmu;       // [B][H][nbp][2][128] Sol-Attn2 tail key means per anchor
   float* tnu;       // [B][H][nbp][2][128] Sol-Attn2 tail value means per anchor
   float* tlz;       // [B][H][nbp][2] log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d)
+  uint8_t* v8t;     // [B][H][128][tp] E4M3 V codes, PV operand order within each 64-token block
+  float* vbmax;     // [B][H][nbp] max |V| per block
+  float* vscale;    // [B][H] per-head V scale
 };
 
 struct Shape {
@@ -58,6 +61,9 @@ hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStr
 // Sol-Attn2 stage 2: routing and the complementary tail per anchor (writes sel, tmu, tnu, tlz),
 // then the exact FP8 pass combined with the tail.
 hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream);
-hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, hipStream_t stream);
+hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, bool pv8,
+                         hipStream_t stream);
+// FP8 PV variant, stage 1 addition: per-head V scale and the E4M3 V codes (v8t).
+hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream);
 
 }  // namespace solattn

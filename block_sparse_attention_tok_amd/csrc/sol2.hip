@@ -164,7 +164,8 @@ __global__ __launch_bounds__(256) void groups_kernel(const uint16_t* __restrict_
                                                      const float* __restrict__ kscale, const float* __restrict__ qhat,
                                                      int N, int H, int nb, int nbp, int tp, int total,
                                                      uint16_t* __restrict__ gk, uint16_t* __restrict__ gv,
-                                                     float* __restrict__ glogn, uint64_t* __restrict__ ghi) {
+                                                     float* __restrict__ glogn, uint64_t* __restrict__ ghi,
+                                                     float* __restrict__ vbmax) {
   __shared__ float qh_s[4][kDim];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + wv;
@@ -203,11 +204,13 @@ __global__ __launch_bounds__(256) void groups_kernel(const uint16_t* __restrict_
   const size_t rs = (size_t)H * kDim;
   const uint16_t* vb = v + ((size_t)b * N + t0) * rs + (size_t)h * kDim + 2 * lane;
   const uint8_t* kb = k8 + ((size_t)bh * tp + t0) * kDim + 2 * lane;
+  float vmax = 0.f;
   for (int u = 0; u < n; ++u) {
     const uint32_t vw = *(const uint32_t*)(vb + (size_t)u * rs);
     const uint32_t kw = *(const uint16_t*)(kb + (size_t)u * kDim);
     const auto kf = __builtin_amdgcn_cvt_pk_f32_fp8(kw, false);
     const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
+    vmax = fmaxf(vmax, fmaxf(fabsf(v0), fabsf(v1)));
     if ((hi >> u) & 1) { kh[0] += kf[0]; kh[1] += kf[1]; vh[0] += v0; vh[1] += v1; }
     else               { kl[0] += kf[0]; kl[1] += kf[1]; vl[0] += v0; vl[1] += v1; }
   }
@@ -219,17 +222,88 @@ __global__ __launch_bounds__(256) void groups_kernel(const uint16_t* __restrict_
   gko[64 + lane] = pack_bf16x2(sk * kl[0] * il, sk * kl[1] * il);
   gvo[lane] = pack_bf16x2(vh[0] * ih, vh[1] * ih);
   gvo[64 + lane] = pack_bf16x2(vl[0] * il, vl[1] * il);
+  vmax = wave_max(vmax);
   if (lane == 0) {
     glogn[row * 2] = nh > 0 ? __logf((float)nh) : kNegInf;
     glogn[row * 2 + 1] = nl > 0 ? __logf((float)nl) : kNegInf;
     ghi[row] = hi;
+    if (vbmax) vbmax[row] = vmax;
   }
 }
 
 hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream) {
   const int total = s.B * s.H * ws.nbp;
   hipLaunchKernelGGL(groups_kernel, dim3((total + 3) / 4), dim3(256), 0, stream, v, ws.k8, ws.kscale, ws.qhat, s.N,
-                     s.H, ws.nb, ws.nbp, ws.nbp * kBlock, total, ws.gk, ws.gv, ws.glogn, ws.ghi);
+                     s.H, ws.nb, ws.nbp, ws.nbp * kBlock, total, ws.gk, ws.gv, ws.glogn, ws.ghi, ws.vbmax);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1e (FP8 PV only): per-head V scale s_V = max |V| / 448 (draft "FP8
+// quantization": V with one scale per head) and the E4M3 codes of V / s_V, written
+// dim-major with each 64-token block in the FP8 PV operand order: token
+// 32 h + 8 q + 4 g + r at position 32 g + 16 h + 4 q + r (g is the MFMA k-half a
+// lane of the score tile holds; h, q, r index its accumulator registers).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void vscale_kernel(const float* __restrict__ vbmax, int nbp,
+                                                     float* __restrict__ vscale) {
+  __shared__ float red[4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  float m = 0.f;
+  for (int j = tid; j < nbp; j += 256) m = fmaxf(m, vbmax[(size_t)bh * nbp + j]);
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    vscale[bh] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  }
+}
+
+__device__ __forceinline__ int pv_token(int p) {         // inverse of the operand-order permutation
+  const int g = p >> 5, e = p & 31;
+  return 32 * (e >> 4) + 8 * ((e >> 2) & 3) + 4 * g + (e & 3);
+}
+
+__global__ __launch_bounds__(256) void v8t_kernel(const uint16_t* __restrict__ v, const float* __restrict__ vscale,
+                                                  int N, int H, int tp, uint8_t* __restrict__ v8t) {
+  __shared__ uint16_t vs[64][kDim + 8];
+  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int b = bh / H, h = bh % H;
+  const int t0 = j * kBlock, n = max(0, min(kBlock, N - t0));
+  const size_t rs = (size_t)H * kDim;
+  for (int e = tid; e < 64 * 16; e += 256) {
+    const int r = e >> 4, c = e & 15;
+    uint4v x = {0u, 0u, 0u, 0u};
+    if (r < n) x = *(const uint4v*)(v + ((size_t)b * N + t0 + r) * rs + (size_t)h * kDim + 8 * c);
+    *(uint4v*)(&vs[r][8 * c]) = x;
+  }
+  __syncthreads();
+  const float s = vscale[bh];
+  const int d = tid >> 1, p0 = 32 * (tid & 1);
+  uint32_t w[8];
+#pragma unroll
+  for (int q4 = 0; q4 < 8; ++q4) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = bf16_bits_to_f32(vs[pv_token(p0 + 4 * q4 + e)][d]);
+      y[e] = fminf(fmaxf(__fdiv_rn(x, s), -448.f), 448.f);
+    }
+    w[q4] = fp8x2(y[0], y[1]) | (fp8x2(y[2], y[3]) << 16);
+  }
+  uint4v* dst = (uint4v*)(v8t + ((size_t)bh * kDim + d) * tp + (size_t)j * kBlock + p0);
+  dst[0] = uint4v{w[0], w[1], w[2], w[3]};
+  dst[1] = uint4v{w[4], w[5], w[6], w[7]};
+}
+
+hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream) {
+  if (!ws.v8t || !ws.vbmax || !ws.vscale) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(vscale_kernel, dim3(s.B * s.H), dim3(256), 0, stream, ws.vbmax, ws.nbp, ws.vscale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(v8t_kernel, dim3(ws.nbp, s.B * s.H), dim3(256), 0, stream, v, ws.vscale, s.N, s.H,
+                     ws.nbp * kBlock, ws.v8t);
   return hipGetLastError();
 }
 
@@ -483,13 +557,19 @@ struct Fused2Args {
   int B, N, H, nb, nbp, nbw, tp;
   const uint8_t* q8; const uint8_t* k8; const float* qscale; const float* kscale;
   const uint64_t* sel; const float* tmu; const float* tnu; const float* tlz;
+  const uint8_t* v8t; const float* vscale;   // FP8 PV only
 };
+
+// 16-byte slot swizzle of the 128 x 64-byte FP8 V^T tile (rows = dims): 16 consecutive
+// rows reading one logical chunk cover all 16 bank groups of a 64-bank LDS.
+__device__ __forceinline__ int swz8v(int r) { return (r >> 2) & 3; }
 
 // 16-byte slot swizzle of the 64 x 128-byte FP8 K tile: 16 consecutive rows reading one
 // logical chunk land on 16 distinct (row parity, slot) bank groups with 64 banks, and
 // 8 consecutive rows on 8 distinct slots with 32 banks.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+template <bool kPv8>
 __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   __shared__ __attribute__((aligned(1024))) unsigned char K8l[64 * 128];
   __shared__ __attribute__((aligned(1024))) unsigned char Vl[64 * 256];
@@ -552,10 +632,26 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
     for (int n = 0; n < 4; ++n)
       dma16_buf(rsrc, tile_off + 1024 * (4 * w + n) + k8dma[n & 1], 0, K8l + 1024 * (4 * w + n));
   };
+  // FP8 V^T tile DMA, wave w instruction n: 1 KB segment 4 w + n = dims 16 (4 w + n) + lane / 4,
+  // slot lane % 4 holding logical chunk (lane % 4) ^ swz8v(dim) (swz8v depends on lane / 4 only).
+  const uint32_t v8dma = (uint32_t)(lane >> 2) * a.tp + 16 * ((lane & 3) ^ swz8v(lane >> 2));
+  const uint8_t* v8_head = a.v8t + (size_t)bh * kDim * a.tp;
   auto issue_v = [&](int jb) {
-    dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.v + head_off), span_in), (uint32_t)jb * 64 * row_bytes, row_bytes,
-                   doff, w);
+    if constexpr (kPv8) {
+      const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(uniform_ptr(v8_head), (uint32_t)kDim * a.tp);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        dma16_buf(rsrc, (uint32_t)(16 * (4 * w + n)) * a.tp + (uint32_t)jb * 64 + v8dma, 0, Vl + 1024 * (4 * w + n));
+    } else {
+      dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.v + head_off), span_in), (uint32_t)jb * 64 * row_bytes, row_bytes,
+                     doff, w);
+    }
   };
+  // FP8 V^T operand reads: row (dim) 32 mt + l32, logical chunks 2 kg, 2 kg + 1.
+  int v8off[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) v8off[hf] = l32 * 64 + 16 * ((2 * kg + hf) ^ swz8v(l32));
+  floatx16 ol = {};                                        // FP8 PV: sum of the decoded P bytes (all rows)
   // Selected blocks in order.
   int c_it = 0;
   uint64_t bits = 0;
@@ -616,18 +712,48 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) o[mt][idx] *= alpha;
     m_run = m_new;
-    bf16x8 pa[4];
+    if constexpr (kPv8) {
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      pa[idx >> 3][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[idx] - m_use);   // keys 16 st ..
-      pa[2 + (idx >> 3)][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[idx] - m_use);
+      for (int idx = 0; idx < 16; ++idx) ol[idx] *= alpha;
+      // ExpCast bytes c = RNE(8 (x - m) + 55.65) (<= 56 since x <= m; v_cvt_pk_u8_f32
+      // rounds to nearest even and saturates below at 0, which is the clip), in the PV
+      // operand order: byte e = idx of s0, 16 + idx of s1.
+      const float c0 = 55.65f - 8.f * m_use;
+      uint32_t pw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        pw[idx >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s0[idx], 8.f, c0), idx & 3, pw[idx >> 2]);
+        pw[4 + (idx >> 2)] =
+            __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s1[idx], 8.f, c0), idx & 3, pw[4 + (idx >> 2)]);
+      }
+      const intx8 pc = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+      const intx8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,   // E4M3 1.0
+                          0x38383838, 0x38383838, 0x38383838, 0x38383838};
+      wait_vm0();
+      lds_barrier();                                       // V(cur) landed; K buffer free
+      if (nxt >= 0) issue_k(nxt);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint4v lo = *(const uint4v*)(Vl + mt * 32 * 64 + v8off[0]);
+        const uint4v hi = *(const uint4v*)(Vl + mt * 32 * 64 + v8off[1]);
+        const intx8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        o[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pc, o[mt], 0, 0, 0, 0, 0, 0);
+      }
+      ol = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pc, ol, 0, 0, 0, 0, 0, 0);
+    } else {
+      bf16x8 pa[4];
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        pa[idx >> 3][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[idx] - m_use);   // keys 16 st ..
+        pa[2 + (idx >> 3)][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[idx] - m_use);
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) l_run = add_bf16x8(pa[st], l_run);
+      wait_vm0();
+      lds_barrier();                                       // V(cur) landed; K buffer free
+      if (nxt >= 0) issue_k(nxt);
+      pv_tile(o, Vl, voff, pa);
     }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) l_run = add_bf16x8(pa[st], l_run);
-    wait_vm0();
-    lds_barrier();                                         // V(cur) landed; K buffer free
-    if (nxt >= 0) issue_k(nxt);
-    pv_tile(o, Vl, voff, pa);
     cur = nxt;
   }
 
@@ -649,7 +775,11 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   const float m_use = m_fin == kNegInf ? 0.f : m_fin;
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
   const float wt = __builtin_amdgcn_exp2f(lam2 - m_use);
-  const float l_tot = sum_with_partner(l_run) * alpha + wt;
+  // FP8 PV: the exact sums come from the MFMA (already over both k-halves) and the
+  // numerator carries the per-head V scale.
+  const float l_ex = kPv8 ? ol[0] : sum_with_partner(l_run);
+  const float vs = kPv8 ? a.vscale[bh] : 1.f;
+  const float l_tot = l_ex * alpha + wt;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (qrow < a.N && a.out != nullptr) {
     uint16_t* dst = a.out + head_off + (size_t)qrow * rs;
@@ -660,7 +790,7 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
         const int d0 = 32 * mt + 8 * g + 4 * kg;
         float r4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r4[e] = (o[mt][4 * g + e] * alpha + wt * nu_s[w][d0 + e]) * inv;
+        for (int e = 0; e < 4; ++e) r4[e] = (o[mt][4 * g + e] * (alpha * vs) + wt * nu_s[w][d0 + e]) * inv;
         uint2v pk;
         pk[0] = pack_bf16x2(r4[0], r4[1]);
         pk[1] = pack_bf16x2(r4[2], r4[3]);
@@ -669,15 +799,18 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   }
 }
 
-hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, hipStream_t stream) {
-  if (ws.nbp / 64 > kMaxChunks2) return hipErrorInvalidValue;
+hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, bool pv8,
+                         hipStream_t stream) {
+  if (ws.nbp / 64 > kMaxChunks2 || (pv8 && (!ws.v8t || !ws.vscale))) return hipErrorInvalidValue;
   Fused2Args a;
   a.v = v; a.out = out;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = ws.nbp / 64; a.tp = ws.nbp * kBlock;
   a.q8 = ws.q8; a.k8 = ws.k8; a.qscale = ws.qscale; a.kscale = ws.kscale;
   a.sel = ws.sel; a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
+  a.v8t = ws.v8t; a.vscale = ws.vscale;
   const int total = s.B * s.H * ws.nb;
-  hipLaunchKernelGGL(sol2_fused_kernel, dim3(total), dim3(128), 0, stream, a);
+  if (pv8) hipLaunchKernelGGL(sol2_fused_kernel<true>, dim3(total), dim3(128), 0, stream, a);
+  else hipLaunchKernelGGL(sol2_fused_kernel<false>, dim3(total), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

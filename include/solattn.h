@@ -49,7 +49,11 @@ typedef enum {
 typedef enum { SOL_THRESH_DIAG = 0, SOL_THRESH_EXACT = 1 } sol_thresh;
 
 /* Variants for sol_attn_workspace_bytes / sol_attn_workspace_layout. */
-typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
+typedef enum {
+    SOL_VARIANT_SOL1 = 1,      /* Sol-Attn */
+    SOL_VARIANT_SOL2 = 2,      /* Sol-Attn2: FP8 Q/K, bf16 V */
+    SOL_VARIANT_SOL2_PV8 = 3   /* Sol-Attn2 with ExpCast P and per-head FP8 V (FP8 PV) */
+} sol_variant;
 
 /* Byte offsets into the workspace of the intermediate arrays (for tests and
  * tooling; the kernels own these arrays during a call).  nbp = number of
@@ -78,6 +82,14 @@ typedef enum { SOL_VARIANT_SOL1 = 1, SOL_VARIANT_SOL2 = 2 } sol_variant;
  *   tmu, tnu float [B][H][nbp][2][128] per-anchor tail key / value means mu_a, nu_a (Sol-Attn2)
  *   tlz      float [B][H][nbp][2]     log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d); -inf if the
  *                                      anchor's tail is empty (Sol-Attn2)
+ *   v8t      uint8 [B][H][128][tp]    E4M3 codes of V / s_V, dim-major; within each 64-token
+ *                                      block, token 32 h + 8 q + 4 g + r sits at position
+ *                                      32 g + 16 h + 4 q + r (the FP8 PV operand order;
+ *                                      SOL_VARIANT_SOL2_PV8 only, like vbmax and vscale)
+ *   vbmax    float [B][H][nbp]        max |V| per 64-token block
+ *   vscale   float [B][H]             s_V = max |V| / 448 per head (1 for an all-zero head)
+ * The SOL_VARIANT_SOL2_PV8 layout is the SOL_VARIANT_SOL2 layout with v8t, vbmax and
+ * vscale appended, so the Sol-Attn2 stage calls accept either workspace.
  */
 typedef struct {
     int64_t total_bytes;
@@ -86,6 +98,7 @@ typedef struct {
     int64_t q8, k8, qscale, kscale, qhat, gk, gv, glogn, ghi, qanc;
     int64_t kv_splits, opart, olse;
     int64_t sel, tmu, tnu, tlz;
+    int64_t v8t, vbmax, vscale;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */
@@ -224,6 +237,31 @@ int sol_attn2_tail(const void* q, const void* k, const void* v,
 int sol_attn2_exact(const void* q, const void* k, const void* v, void* out,
                     int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sol-Attn2 with FP8 PV (Sol-Attn2 draft, "FP8 quantization and ExpCast"): as
+ * sol_attn2, but V is quantized with one E4M3 scale per head and the exact
+ * weights are ExpCast bytes c(u) = clip(RNE(8u + 55.65), 0, 120), u the base-2
+ * score minus the online pivot; the same decoded bytes weight V (FP8 MFMA) and
+ * form the exact part of the denominator.  Workspace >=
+ * sol_attn_workspace_bytes(SOL_VARIANT_SOL2_PV8, ...).
+ */
+int sol_attn2_pv8(const void* q, const void* k, const void* v, void* out,
+                  int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                  float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 1 of sol_attn2_pv8: sol_attn2_prepare plus the per-head V scale and the
+ * E4M3 V codes (workspace arrays vbmax, vscale, v8t). */
+int sol_attn2_pv8_prepare(const void* q, const void* k, const void* v,
+                          int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                          float tau, int thresh, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2b of sol_attn2_pv8 (after sol_attn2_tail on the same workspace): exact
+ * attention with FP8 Q K^T and FP8 P V (ExpCast P), combined with the tail. */
+int sol_attn2_pv8_exact(const void* q, const void* k, const void* v, void* out,
+                        int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sol-Attn2 routing export, as sol_attn_debug_routing (kv_splits must be 0 or 1:
  * the Sol-Attn2 pass is not split). */

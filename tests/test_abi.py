@@ -83,7 +83,23 @@ def test_workspace_sizes_and_layout(L):
             if variant == 1:
                 assert lay.q8 == -1 and lay.gk == -1
     assert L.sol_attn_workspace_bytes(1, 1, 1024, 2, 64) == 0
-    assert L.sol_attn_workspace_bytes(3, 1, 1024, 2, 128) == 0
+    assert L.sol_attn_workspace_bytes(4, 1, 1024, 2, 128) == 0
+
+
+@pytest.mark.parametrize("B,N,H", [(1, 1024, 2), (1, 14040, 12), (2, 333, 3)])
+def test_fp8_pv_layout_extends_the_sol2_layout(L, B, N, H):
+    """The FP8-PV workspace is the Sol-Attn2 one with v8t / vbmax / vscale appended, so the
+    shared Sol-Attn2 stage calls (tail pass) run on it unchanged."""
+    from block_sparse_attention_tok_amd import _lib
+    l2 = _lib.workspace_layout(2, B, N, H)
+    l3 = _lib.workspace_layout(3, B, N, H)
+    for name, _ in _lib.WsLayout._fields_:
+        if name in ("total_bytes", "v8t", "vbmax", "vscale"):
+            continue
+        assert getattr(l2, name) == getattr(l3, name), name
+    assert l2.v8t == l2.vbmax == l2.vscale == -1
+    assert l3.v8t >= l2.total_bytes and l3.total_bytes > l3.vscale > l3.vbmax > l3.v8t
+    assert l3.vbmax - l3.v8t >= B * H * 128 * l3.nbp * 64
 
 
 @pytest.mark.parametrize("tokens,req,expect", [
