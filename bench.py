@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--tau", type=float, default=None, help="fixed tau instead of the search")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense-baselines", action="store_true")
-    p.add_argument("--cpu-sample-blocks", type=int, default=24)
+    p.add_argument("--cpu-sample-heads", type=int, default=16, help="heads the CPU oracle is timed on")
+    p.add_argument("--cpu-sample-blocks", type=int, default=256, help="query blocks per sampled head")
     p.add_argument("--kv-splits", type=int, default=0, help="key-range splits of the fused pass (0 = automatic)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (scales FETCH_SIZE / WRITE_SIZE counters)")
@@ -184,7 +185,8 @@ def main():
     log(f"[bench] step {ms_per_step:.3f} ms (median event {med_step:.3f}); prepare {np.mean(prep_ms):.3f} ms, "
         f"stage 2 {fused_avg:.3f} ms; {kernel} alone {kernel_ms:.3f} ms -> {achieved:.1f} TFLOP/s algorithmic")
     from block_sparse_attention_tok_amd.profsum import read_traffic
-    tag = ("op_bench" if not args.text_sink else "long_sink") + f"_{N // 1024}k_{round(100 * args.sparsity)}pct"
+    tag = (("op_bench" if not args.text_sink else "long_sink") + f"_{N // 1024}k_{round(100 * args.sparsity)}pct"
+           + ("_pv8" if variant == 3 else ""))
     traffic_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{kernel}_{tag}_traffic.md")
     traffic = read_traffic(traffic_file, kernel)
 
@@ -219,7 +221,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(qc, kc, vc, tau, sink_start, sink_tokens, variant, args.cpu_sample_blocks, dense_flops)
+        cpu = cpu_baseline(qc, kc, vc, tau, sink_start, sink_tokens, variant, args.cpu_sample_heads,
+                           args.cpu_sample_blocks, dense_flops)
         log(f"[bench] cpu oracle {cpu}")
 
     workload = (f"{ {1: 'Sol-Attn', 2: 'Sol-Attn2 (FP8 Q/K)', 3: 'Sol-Attn2 (FP8 Q/K, ExpCast FP8 PV)'}[variant] } "
@@ -259,8 +262,10 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(q, k, v, tau, sink_start, sink_tokens, variant, sample_blocks, dense_flops):
-    """Time the oracle (as written, untuned) on a bounded sample of the workload and extrapolate."""
+def cpu_baseline(q, k, v, tau, sink_start, sink_tokens, variant, sample_heads, sample_blocks, dense_flops):
+    """Time the oracle (as written, untuned) on a bounded sample of the workload and extrapolate:
+    full routing and summaries of `sample_heads` heads plus `sample_blocks` seeded query blocks
+    of each, scaled to every head and block of the call."""
     import numpy as np
     import oracle.sol_attn as sa
     import oracle.sol_attn2 as s2
@@ -272,33 +277,37 @@ def cpu_baseline(q, k, v, tau, sink_start, sink_tokens, variant, sample_blocks, 
     B, N, H, D = q.shape
     nb = (N + 63) // 64
     rng = np.random.default_rng(7)
-    blocks = sorted(rng.choice(nb, size=min(sample_blocks, nb), replace=False).tolist())
-    t0 = time.perf_counter()
-    qh, kh, vh = (t[0, :, 0, :].double().numpy() for t in (q, k, v))
-    if variant == 1:
-        r = sa.sol_attn_head(qh, kh, vh, tau, sink_start, sink_tokens, query_blocks=[])
-        t_route = time.perf_counter() - t0
-        kbar, vsum, counts = sa.block_means(kh), sa.block_sums(vh), sa.block_counts(N)
-        t1 = time.perf_counter()
-        for i in blocks:
-            sa.attend_query_block(qh, kh, vh, i, r.sel[i], kbar, vsum, counts, 1 / math.sqrt(D))
-        t_blocks = time.perf_counter() - t1
-    else:
-        pv = "expcast" if variant == 3 else "bf16"
-        r = s2.sol_attn2_head(qh, kh, vh, tau, sink_start, sink_tokens, query_blocks=[])
-        v_exact = s2.quantize_head_v(vh)[2] if variant == 3 else None
-        t_route = time.perf_counter() - t0
-        t1 = time.perf_counter()
-        for i in blocks:
-            s2.attend_query_block2(r.q_deq, r.k_deq, vh, i, r.sel[i], r.groups, 1 / math.sqrt(D), pv=pv,
-                                   v_exact=v_exact)
-        t_blocks = time.perf_counter() - t1
-    t_full = B * H * (t_route + t_blocks * nb / len(blocks))
+    heads = sorted(rng.choice(H, size=min(sample_heads, H), replace=False).tolist())
+    t_route = t_blocks = 0.0
+    n_blocks = 0
+    for h in heads:
+        blocks = sorted(rng.choice(nb, size=min(sample_blocks, nb), replace=False).tolist())
+        t0 = time.perf_counter()
+        qh, kh, vh = (t[0, :, h, :].double().numpy() for t in (q, k, v))
+        if variant == 1:
+            r = sa.sol_attn_head(qh, kh, vh, tau, sink_start, sink_tokens, query_blocks=[])
+            kbar, vsum, counts = sa.block_means(kh), sa.block_sums(vh), sa.block_counts(N)
+            t1 = time.perf_counter()
+            for i in blocks:
+                sa.attend_query_block(qh, kh, vh, i, r.sel[i], kbar, vsum, counts, 1 / math.sqrt(D))
+        else:
+            pv = "expcast" if variant == 3 else "bf16"
+            r = s2.sol_attn2_head(qh, kh, vh, tau, sink_start, sink_tokens, query_blocks=[])
+            v_exact = s2.quantize_head_v(vh)[2] if variant == 3 else None
+            t1 = time.perf_counter()
+            for i in blocks:
+                s2.attend_query_block2(r.q_deq, r.k_deq, vh, i, r.sel[i], r.groups, 1 / math.sqrt(D), pv=pv,
+                                       v_exact=v_exact)
+        t2 = time.perf_counter()
+        t_route += t1 - t0
+        t_blocks += t2 - t1
+        n_blocks += len(blocks)
+    t_full = B * H * (t_route / len(heads) + t_blocks / n_blocks * nb)
     return {"value": round(dense_flops / t_full / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",
             "cores": int(cores), "kind": "oracle",
-            "sample": (f"head 0 of batch 0: full routing/summaries ({t_route:.2f} s) + {len(blocks)} of {nb} query "
-                       f"blocks ({t_blocks:.2f} s), extrapolated to all {B * H} heads x {nb} blocks = "
-                       f"{t_full:.1f} s per call (float64 numpy)")}
+            "sample": (f"batch 0, {len(heads)} of {H} heads: full routing/summaries ({t_route:.1f} s) + "
+                       f"{n_blocks // len(heads)} of {nb} query blocks each ({t_blocks:.1f} s), extrapolated to "
+                       f"{B * H} heads x {nb} blocks = {t_full:.1f} s per call (float64 numpy)")}
 
 
 if __name__ == "__main__":
