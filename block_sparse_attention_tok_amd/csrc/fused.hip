@@ -10,23 +10,32 @@
 // K/V blocks of the selected indices.  No proxy or routing map is written to
 // memory (only the optional test export).
 //
-// gfx950 mapping: one workgroup = one (batch, head, 64-row query block), two
-// wave64s of 32 query rows; __launch_bounds__(128, 2) keeps two waves per SIMD.
+// gfx950 mapping: one workgroup = one (batch, head, 64-row query block, key
+// split), two wave64s of 32 query rows; __launch_bounds__(128, 2) keeps two
+// waves per SIMD; workgroups are ordered so that each XCD walks its own heads.
 //   * Routing runs first, in fp32 from the fp32 block means (VALU), for every
 //     chunk of 64 pooled keys; the per-chunk selection words stay in LDS.
+//   * A reference pass over the pooled K-bar tiles gives each query row
+//     m_ref = max_j log2(e) q . K-bar_j / sqrt(d).  Because a block's mean of
+//     exponentials is at least the exponential of its mean logit, the softmax
+//     denominator measured against m_ref is >= 1, so the main pass takes
+//     P = 2^(x - m_ref) with no running maximum and no O rescale; a workgroup
+//     whose O or l overflows reruns its tiles with the usual rescaling.
 //   * The tile stream is, per chunk, one proxy tile (K-bar / V-bar = V-hat/n
 //     rows with logit bias log2 n_j; selected and padding columns masked) then
-//     the chunk's selected exact blocks.  All tiles share one online softmax.
-//   * Tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into
-//     one K and one V buffer whose 16-byte slots are XOR-swizzled per row; the
-//     V load of tile t overlaps S_t and its softmax, the K load of tile t+1
-//     overlaps PV_t.  Two LDS barriers per tile.
+//     the chunk's selected exact blocks.
+//   * Tiles move HBM -> LDS with buffer_load ... lds (no VGPR staging; the
+//     buffer's range check covers every lane offset) into one K and one V
+//     buffer whose 16-byte slots are XOR-swizzled per row; the V load of tile t
+//     overlaps S_t and its exponentials, the K load of tile t+1 overlaps PV_t.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
-//     wave's query rows in registers): one query per lane, so row max / sum are
-//     in-lane plus one v_permlane32_swap.
+//     wave's query rows in registers): one query per lane, so the row max is
+//     in-lane plus one v_permlane32_swap; row sums use v_dot2 on the bf16 P.
 //   * O^T += V^T P^T: A = V^T gathered from the row-major V tile with
 //     ds_read_b64_tr_b16, B = P straight from the S^T accumulator (the k order
 //     inside each MFMA is permuted identically on both operands).
+//   * Several key splits write bf16 partial rows and their log2-sum-exp; a
+//     small merge kernel combines them.
 #include "common.h"
 #include "kernels.h"
 #include "pipe.h"

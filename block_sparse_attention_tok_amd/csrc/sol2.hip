@@ -9,7 +9,12 @@
 // Readings where the draft is open (documented with the oracle): the
 // mean-query direction is the per-(batch, head) mean of the dequantized
 // queries; a key block splits at its mean projection onto that direction,
-// ties joining the upper group; V stays bf16; an empty block uses scale 1.
+// ties joining the upper group; an empty block uses scale 1.  V is bf16 in the
+// default path; the FP8-PV path ("FP8 quantization and ExpCast") stores V once
+// per head as E4M3 with one scale and feeds the exact blocks' probabilities as
+// ExpCast bytes c(u) = clip(RNE(8 u + 55.65), 0, 120) taken against the running
+// per-row pivot, so the same decoded weights enter the PV product and the
+// denominator.
 #include "common.h"
 #include "kernels.h"
 #include "pipe.h"
@@ -546,7 +551,11 @@ hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, 
 //     overlapping PV_t.
 //   * S^T = K8 Q8^T on v_mfma_f32_32x32x64_f8f6f4 (OCP E4M3; issued through the
 //     scaled form with unit scales), times s_q s_k / sqrt(d); online softmax; O^T +=
-//     V^T P^T in bf16 exactly as in the Sol-Attn pass.
+//     V^T P^T in bf16 exactly as in the Sol-Attn pass.  The FP8-PV instance instead
+//     streams the per-head E4M3 V^T tile (128 x 64 B), turns each score into its
+//     ExpCast byte against the running row maximum, and runs PV and the row sums
+//     (an all-ones B operand) on the same FP8 MFMA, so the denominator is the sum
+//     of exactly the decoded weights that multiply V.
 //   * Epilogue: delta_t = (q'_t - q-bar_a) . mu_a / sqrt(d) from the dequantized query
 //     codes, lambda_t = ln Z_a + delta_t, and Eq. (3) with the exact state.
 // ---------------------------------------------------------------------------

@@ -5,6 +5,7 @@ p-hat(u) = decode_E4M3(c(u)) ~ 2^u, V quantized with one E4M3 scale per head, an
 same decoded weights in the PV product and the denominator.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -15,19 +16,23 @@ from oracle import sol_attn2 as s2
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 
-@pytest.mark.parametrize("u,code", [
-    (0.0, 56),      # 55.65 -> 56: exponent field 7, mantissa 0 -> 1.0
-    (1.0, 64),      # 63.65 -> 64 -> 2.0
-    (-1.0, 48),     # 47.65 -> 48 -> 0.5
-    (0.5, 60),      # 59.65 -> 60: 1.5 (2^0.5 = 1.414 on the linear mantissa)
-    (-6.5, 4),      # 3.65 -> 4: subnormal 4/8 * 2^-6
-    (-7.0, 0),      # -0.35 -> 0
-    (8.05, 120),    # 120.05 -> 120 = 2^8
-    (10.0, 120),    # clipped
-    (-math.inf, 0),
-])
-def test_code_table(u, code):
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "expcast_codes.txt")
+
+
+def _golden_rows():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.split("#", 1)[0].split()
+        if line:
+            rows.append((float(line[0]), int(line[1]), float(line[2])))
+    return rows
+
+
+@pytest.mark.parametrize("u,code,weight", _golden_rows())
+def test_code_table(u, code, weight):
+    """Hand-worked (u, code, weight) rows of the Draft's ExpCast definition."""
     assert int(e4m3.expcast_code(np.float32(u))) == code
+    assert float(e4m3.expcast_weight(np.float32(u))) == weight
 
 
 def test_integer_scores_decode_to_exact_powers_of_two():
