@@ -144,3 +144,30 @@ PINS_EXPCAST = [
 def test_expcast_mutation_is_caught(name, monkeypatch):
     MUTATIONS_EXPCAST[name](monkeypatch)
     assert any(_fails(fn, *args) for fn, args in PINS_EXPCAST), f"mutation {name} not caught"
+
+
+import test_oracle_backward as p4  # noqa: E402
+from oracle import sol_attn_bwd as sb  # noqa: E402
+
+MUTATIONS_BACKWARD = {
+    # softmax backward without the D_t = dO . o term
+    "no_D_term": lambda mp: mp.setattr(sb, "_logit_grad", lambda p, dp, D: p * dp),
+    # the pooled key's gradient reaches every token whole instead of 1/n_j of it
+    "mean_chain_rule_dropped": lambda mp: mp.setattr(sb, "_per_token", lambda g, count: g),
+    # the pooled keys lose their ln n_j bias (forward weight and chain rule both)
+    "no_count_bias": lambda mp: mp.setattr(sb, "block_counts", lambda n, block=64: np.ones((n + block - 1) // block)),
+    # pooled values taken as block sums
+    "pooled_value_sum": lambda mp: mp.setattr(sb, "block_means", sa.block_sums),
+}
+
+PINS_BACKWARD = [
+    (p4.test_directional_derivatives_match_central_differences, (130, 32, 4, 0.4)),
+    (p4.test_single_coordinates_in_exact_pooled_and_partial_blocks, ()),
+    (p4.test_identical_keys_agree_with_dense_gradients, ()),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_BACKWARD))
+def test_backward_mutation_is_caught(name, monkeypatch):
+    MUTATIONS_BACKWARD[name](monkeypatch)
+    assert any(_fails(fn, *args) for fn, args in PINS_BACKWARD), f"mutation {name} not caught"
