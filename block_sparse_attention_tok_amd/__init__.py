@@ -1,14 +1,17 @@
-"""Sol-Attn / Sol-Attn2 forward passes for AMD Instinct MI355X (gfx950).
+"""Sol-Attn / Sol-Attn2 for AMD Instinct MI355X (gfx950): the forward passes and the
+Sol-Attn backward with fixed routing.
 
 The compute lives in libsolattn.so (hand-written HIP kernels behind a C ABI,
 include/solattn.h); this package is its thin ctypes binding.  Tensors are
 contiguous bf16 [batch, tokens, heads, 128] on the GPU (Sol-Attn README,
 "Core API").
 """
-from ._lib import (SOL_VARIANT_SOL1, SOL_VARIANT_SOL2, SOL_VARIANT_SOL2_PV8, SolAttnError,  # noqa: F401
-                   alloc_workspace, debug_routing, exact2, fused, kv_splits_for, lib, prepare, sol_attn, sol_attn2,
-                   sol_attn2_pv8, tail2, validate, workspace_bytes, workspace_layout, workspace_views)
+from ._lib import (SOL_VARIANT_SOL1, SOL_VARIANT_SOL1_TRAIN, SOL_VARIANT_SOL2, SOL_VARIANT_SOL2_PV8,  # noqa: F401
+                   SolAttnError, SolAttnFunction, alloc_workspace, backward, debug_routing, exact2, forward_train,
+                   fused, kv_splits_for, lib, prepare, sol_attn, sol_attn2, sol_attn2_pv8, sol_attn_train, tail2,
+                   validate, workspace_bytes, workspace_layout, workspace_views)
 
 __all__ = ["sol_attn", "sol_attn2", "sol_attn2_pv8", "validate", "workspace_bytes", "workspace_layout", "prepare",
            "fused", "tail2", "exact2", "debug_routing", "alloc_workspace", "kv_splits_for", "workspace_views",
-           "SolAttnError", "lib", "SOL_VARIANT_SOL1", "SOL_VARIANT_SOL2", "SOL_VARIANT_SOL2_PV8"]
+           "SolAttnError", "lib", "SOL_VARIANT_SOL1", "SOL_VARIANT_SOL2", "SOL_VARIANT_SOL2_PV8",
+           "SOL_VARIANT_SOL1_TRAIN", "forward_train", "backward", "sol_attn_train", "SolAttnFunction"]

@@ -21,6 +21,7 @@ SOL_OK = 0
 SOL_VARIANT_SOL1 = 1
 SOL_VARIANT_SOL2 = 2
 SOL_VARIANT_SOL2_PV8 = 3
+SOL_VARIANT_SOL1_TRAIN = 4
 THRESH = {"diag": 0, "exact": 1}
 
 EXPORTED = [
@@ -29,6 +30,7 @@ EXPORTED = [
     "sol_attn", "sol_attn_prepare", "sol_attn_fused", "sol_attn_fused_kv", "sol_attn_debug_routing",
     "sol_attn2", "sol_attn2_prepare", "sol_attn2_fused", "sol_attn2_tail", "sol_attn2_exact",
     "sol_attn2_debug_routing", "sol_attn2_pv8", "sol_attn2_pv8_prepare", "sol_attn2_pv8_exact",
+    "sol_attn_forward_train", "sol_attn_backward",
 ]
 
 
@@ -36,7 +38,7 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov", "kpart",
         "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse",
-        "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale")]
+        "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale", "lse", "mrow", "mcol", "ld", "dkbar", "dvbar")]
 
 
 class SolAttnError(RuntimeError):
@@ -79,7 +81,7 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         getattr(L, name).restype = i32
     full = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp]
-    for name in ("sol_attn", "sol_attn2", "sol_attn2_pv8"):
+    for name in ("sol_attn", "sol_attn2", "sol_attn2_pv8", "sol_attn_forward_train"):
         getattr(L, name).argtypes = full
         getattr(L, name).restype = i32
     prep = [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp, sz, vp]
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
     for name in ("sol_attn_debug_routing", "sol_attn2_debug_routing"):
         getattr(L, name).argtypes = dbg
         getattr(L, name).restype = i32
+    L.sol_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+    L.sol_attn_backward.restype = i32
     _LIB = L
     return L
 
@@ -220,6 +224,59 @@ def sol_attn2_pv8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float 
                       workspace)
 
 
+def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
+                  sink_start: Optional[int] = None, sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Sol-Attn forward that keeps its routing and row log-sum-exp for `backward`;
+    returns (out, workspace)."""
+    if workspace is None:
+        workspace = alloc_workspace(SOL_VARIANT_SOL1_TRAIN, q)
+    out = _full_call("sol_attn_forward_train", SOL_VARIANT_SOL1_TRAIN, q, k, v, tau, sink_start, sink_tokens, thresh,
+                     out, workspace)
+    return out, workspace
+
+
+def backward(q, k, v, out, dout, workspace: torch.Tensor, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(dout * out) with the routing of the `forward_train` call
+    that filled `workspace` held fixed."""
+    _check_tensors(q, k, v)
+    for name, t in (("out", out), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor of q's shape on q's device")
+    B, N, H, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check(lib().sol_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   B, N, H, D, _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "sol_attn_backward")
+    return dq, dk, dv
+
+
+class SolAttnFunction(torch.autograd.Function):
+    """Sol-Attn as a differentiable op: forward_train, then backward with the routing fixed."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, tau, thresh, sink_start, sink_tokens):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        out, ws = forward_train(q, k, v, tau, thresh, sink_start, sink_tokens)
+        ctx.save_for_backward(q, k, v, out, ws)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, ws = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, out, dout.contiguous(), ws)
+        return dq, dk, dv, None, None, None, None
+
+
+def sol_attn_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
+                   sink_start: Optional[int] = None, sink_tokens: int = 0) -> torch.Tensor:
+    """Differentiable Sol-Attn (autograd): gradients flow through q, k, v with the forward's routing fixed."""
+    return SolAttnFunction.apply(q, k, v, tau, thresh, sink_start, sink_tokens)
+
+
 def prepare(variant: int, q, k, v, tau: float, workspace: torch.Tensor, thresh: str = "diag"):
     """Stage 1 (summaries + threshold [+ Sol-Attn2 quantization and groups]) into `workspace`."""
     _check_tensors(q, k, v)
@@ -328,6 +385,16 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
             tmu=view(L.tmu, torch.float32, (batch, heads, nbp, 2, 128)),
             tnu=view(L.tnu, torch.float32, (batch, heads, nbp, 2, 128)),
             tlz=view(L.tlz, torch.float32, (batch, heads, nbp, 2)),
+        )
+    if variant == SOL_VARIANT_SOL1_TRAIN:
+        tp = nbp * 64
+        d.update(
+            lse=view(L.lse, torch.float32, (batch, heads, tp)),
+            mrow=view(L.mrow, torch.int64, (batch, heads, L.nb, nbp // 64)),
+            mcol=view(L.mcol, torch.int64, (batch, heads, L.nb, nbp // 64)),
+            ld=view(L.ld, torch.float32, (batch, heads, tp, 2)),
+            dkbar=view(L.dkbar, torch.float32, (batch, heads, nbp, 128)),
+            dvbar=view(L.dvbar, torch.float32, (batch, heads, nbp, 128)),
         )
     if variant == SOL_VARIANT_SOL2_PV8:
         tp = nbp * 64

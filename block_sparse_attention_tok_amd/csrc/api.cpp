@@ -62,7 +62,8 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
            int kv_splits = 0) {
   int st = check_shape(batch, tokens, heads, head_dim);
   if (st != SOL_OK) return st;
-  if (variant != SOL_VARIANT_SOL1 && variant != SOL_VARIANT_SOL2 && variant != SOL_VARIANT_SOL2_PV8)
+  if (variant != SOL_VARIANT_SOL1 && variant != SOL_VARIANT_SOL2 && variant != SOL_VARIANT_SOL2_PV8 &&
+      variant != SOL_VARIANT_SOL1_TRAIN)
     return SOL_ERR_ARG;
   std::memset(L, 0xff, sizeof(*L));          // every offset -1
   const int64_t nb = (tokens + kBlock - 1) / kBlock;
@@ -103,10 +104,21 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     }
   }
   // split-KV partials (Sol-Attn only)
-  L->kv_splits = variant == SOL_VARIANT_SOL1 ? effective_splits(tokens, kv_splits) : 1;
+  const bool sol1 = variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN;
+  L->kv_splits = sol1 ? effective_splits(tokens, kv_splits) : 1;
   if (L->kv_splits > 1) {
     L->opart = take(L->kv_splits * bh * tokens * kDim * 2);
     L->olse = take(L->kv_splits * bh * tokens * 4);
+  }
+  // forward state for the backward, and backward scratch (Sol-Attn training)
+  if (variant == SOL_VARIANT_SOL1_TRAIN) {
+    const int64_t tp = nbp * kBlock;
+    L->lse = take(bh * tp * 4);
+    L->mrow = take(bh * nb * (nbp / 64) * 8);
+    L->mcol = take(bh * nb * (nbp / 64) * 8);
+    L->ld = take(bh * tp * 2 * 4);
+    L->dkbar = take(bh * nbp * kDim * 4);
+    L->dvbar = take(bh * nbp * kDim * 4);
   }
   L->total_bytes = off;
   return SOL_OK;
@@ -146,6 +158,12 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.v8t = (uint8_t*)at(L.v8t);
   w.vbmax = (float*)at(L.vbmax);
   w.vscale = (float*)at(L.vscale);
+  w.lse = (float*)at(L.lse);
+  w.mrow = (uint64_t*)at(L.mrow);
+  w.mcol = (uint64_t*)at(L.mcol);
+  w.ld = (float*)at(L.ld);
+  w.dkbar = (float*)at(L.dkbar);
+  w.dvbar = (float*)at(L.dvbar);
   return w;
 }
 
@@ -269,9 +287,10 @@ static int fused_common(int variant, const void* q, const void* k, const void* v
   if ((st = sink_range(tokens, sink_start, sink_tokens, &b0, &b1)) != SOL_OK) return st;
   solattn::Workspace w = resolve(L, workspace);
   solattn::Shape s = shape_of(batch, tokens, heads);
-  if (variant == SOL_VARIANT_SOL1)
+  if (variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN)
     return hip_status(solattn::launch_fused((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                            (uint16_t*)out, s, w, b0, b1, mask_bits, (hipStream_t)stream));
+                                            (uint16_t*)out, s, w, b0, b1, mask_bits ? mask_bits : w.mrow,
+                                            (hipStream_t)stream));
   hipStream_t hs = (hipStream_t)stream;
   if (stage2 & kStage2Tail) {
     if ((st = hip_status(solattn::launch_tail2(s, w, b0, b1, hs))) != SOL_OK) return st;
@@ -310,6 +329,36 @@ int sol_attn(const void* q, const void* k, const void* v, void* out, int64_t bat
   if (st != SOL_OK) return st;
   return sol_attn_fused(q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens, workspace,
                         workspace_bytes, stream);
+}
+
+int sol_attn_forward_train(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                           int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens,
+                           int thresh, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return SOL_ERR_NULL;
+  int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
+  if (st != SOL_OK) return st;
+  sol_ws_layout L;
+  st = prologue(SOL_VARIANT_SOL1_TRAIN, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  if (st != SOL_OK) return st;
+  st = sol_attn_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);
+  if (st != SOL_OK) return st;
+  return fused_common(SOL_VARIANT_SOL1_TRAIN, q, k, v, out, batch, tokens, heads, head_dim, sink_start,
+                      sink_tokens, workspace, workspace_bytes, nullptr, stream, true);
+}
+
+int sol_attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, void* dq,
+                      void* dk, void* dv, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out || !dout || !dq || !dk || !dv) return SOL_ERR_NULL;
+  sol_ws_layout L;
+  int st = prologue(SOL_VARIANT_SOL1_TRAIN, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  if (st != SOL_OK) return st;
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return SOL_ERR_ARG;
+  solattn::Workspace w = resolve(L, workspace);
+  return hip_status(solattn::launch_backward((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                             (const uint16_t*)out, (const uint16_t*)dout, (uint16_t*)dq,
+                                             (uint16_t*)dk, (uint16_t*)dv, shape_of(batch, tokens, heads), w,
+                                             (hipStream_t)stream));
 }
 
 int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,

@@ -56,6 +56,8 @@ struct FusedArgs {
   const float* tau_i;
   int sink_b0, sink_b1;
   uint64_t* mask_out;
+  float* lse;                   // [B][H][tp] base-2 log-sum-exp per query row (NULL = none)
+  int tp;
 };
 
 // Tile order: per chunk c, the proxy tile (code -(c + 1)) if any block of the
@@ -411,17 +413,19 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
         pk[1] = pack_bf16x2(o[mt][4 * g + 2] * inv, o[mt][4 * g + 3] * inv);
         *(uint2v*)(dst + 32 * mt + 8 * g + 4 * kg) = pk;
       }
-    if (a.S > 1 && kg == 0)
-      a.olse[((size_t)split * a.B * a.N + (size_t)b * a.N + qrow) * a.H + h] =
-          l_tot > 0.f ? m_fin + __log2f(l_tot) : kNegInf;
+    const float lse2 = l_tot > 0.f ? m_fin + __log2f(l_tot) : kNegInf;
+    if (a.S > 1 && kg == 0) a.olse[((size_t)split * a.B * a.N + (size_t)b * a.N + qrow) * a.H + h] = lse2;
+    if (a.S == 1 && a.lse != nullptr && kg == 0) a.lse[(size_t)bh * a.tp + qrow] = lse2;
   }
 }
 
 // Merge of the key-range splits: o = sum_s 2^(lse_s - lse) o_s with lse = log2 sum_s 2^lse_s.
-// One thread per (row, 8 dims); partials are BTHD like the output.
+// One thread per (row, 8 dims); partials are BTHD like the output.  With `lse` set, the
+// first thread of each row also stores the merged log2-sum-exp at [b][h][n] (row stride tp).
 __global__ __launch_bounds__(256) void merge_splits_kernel(const uint4v* __restrict__ opart,
                                                            const float* __restrict__ olse, int S,
-                                                           size_t rows, uint4v* __restrict__ out) {
+                                                           size_t rows, uint4v* __restrict__ out,
+                                                           float* __restrict__ lse, int N, int H, int tp) {
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= rows * 16) return;
   const size_t row = t >> 4;
@@ -441,6 +445,10 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const uint4v* __restr
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (lse != nullptr && (t & 15) == 0) {
+    const size_t n = (row / H) % N, bq = row / ((size_t)H * N);
+    lse[(bq * H + row % H) * tp + n] = wsum > 0.f ? m + __log2f(wsum) : kNegInf;
+  }
   uint4v r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
@@ -460,13 +468,14 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   a.S = S; a.cps = cps; a.opart = ws.opart; a.olse = ws.olse;
   a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h; a.tau_i = ws.tau_i;
   a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
+  a.lse = ws.lse; a.tp = ws.nbp * kBlock;
   const int total = s.B * s.H * S * ws.nb;
   hipLaunchKernelGGL(sol_fused_kernel, dim3(total), dim3(128), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1 || out == nullptr) return e;
   const size_t rows = (size_t)s.B * s.N * s.H;
   hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
-                     (const uint4v*)ws.opart, ws.olse, S, rows, (uint4v*)out);
+                     (const uint4v*)ws.opart, ws.olse, S, rows, (uint4v*)out, ws.lse, s.N, s.H, ws.nbp * kBlock);
   return hipGetLastError();
 }
 

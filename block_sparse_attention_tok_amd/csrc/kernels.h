@@ -36,6 +36,13 @@ struct Workspace {
   uint8_t* v8t;     // [B][H][128][tp] E4M3 V codes, PV operand order within each 64-token block
   float* vbmax;     // [B][H][nbp] max |V| per block
   float* vscale;    // [B][H] per-head V scale
+  // Sol-Attn training layout: state the forward leaves for the backward, and backward scratch
+  float* lse;       // [B][H][tp] base-2 log-sum-exp of each query row (forward output)
+  uint64_t* mrow;   // [B][H][nb][nbp / 64] routing bits of the forward, one row per query block
+  uint64_t* mcol;   // [B][H][nb][nbp / 64] the same bits transposed, one row per key block
+  float* ld;        // [B][H][tp][2] (lse, D = dO . O) per query row
+  float* dkbar;     // [B][H][nbp][128] gradient w.r.t. the pooled keys K-bar_j (times 1/sqrt(d))
+  float* dvbar;     // [B][H][nbp][128] gradient w.r.t. the pooled values V-bar_j
 };
 
 struct Shape {
@@ -63,6 +70,11 @@ hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStr
 hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream);
 hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, bool pv8,
                          hipStream_t stream);
+// Sol-Attn backward with the forward's routing fixed: D and the transposed masks, the
+// pooled-key gradients, dK / dV per key block, then dQ per query block.
+hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,
+                           const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, Shape s,
+                           const Workspace& ws, hipStream_t stream);
 // FP8 PV variant, stage 1 addition: per-head V scale and the E4M3 V codes (v8t).
 hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream);
 

@@ -52,7 +52,8 @@ typedef enum { SOL_THRESH_DIAG = 0, SOL_THRESH_EXACT = 1 } sol_thresh;
 typedef enum {
     SOL_VARIANT_SOL1 = 1,      /* Sol-Attn */
     SOL_VARIANT_SOL2 = 2,      /* Sol-Attn2: FP8 Q/K, bf16 V */
-    SOL_VARIANT_SOL2_PV8 = 3   /* Sol-Attn2 with ExpCast P and per-head FP8 V (FP8 PV) */
+    SOL_VARIANT_SOL2_PV8 = 3,  /* Sol-Attn2 with ExpCast P and per-head FP8 V (FP8 PV) */
+    SOL_VARIANT_SOL1_TRAIN = 4 /* Sol-Attn forward that keeps its state for sol_attn_backward */
 } sol_variant;
 
 /* Byte offsets into the workspace of the intermediate arrays (for tests and
@@ -88,8 +89,18 @@ typedef enum {
  *                                      SOL_VARIANT_SOL2_PV8 only, like vbmax and vscale)
  *   vbmax    float [B][H][nbp]        max |V| per 64-token block
  *   vscale   float [B][H]             s_V = max |V| / 448 per head (1 for an all-zero head)
+ *   lse      float [B][H][tp]         base-2 log of each query row's softmax denominator, in
+ *                                      units of log2(e) q.k / sqrt(d) (SOL_VARIANT_SOL1_TRAIN,
+ *                                      like the arrays below; written by sol_attn_forward_train)
+ *   mrow     uint64 [B][H][nb][nbp/64] the forward's routing bits, one row per query block
+ *   mcol     uint64 [B][H][nb][nbp/64] the same bits by key block (backward scratch)
+ *   ld       float [B][H][tp][2]      (lse, dO . O) per query row (backward scratch)
+ *   dkbar, dvbar float [B][H][nbp][128] gradients w.r.t. the pooled keys (times 1/sqrt(d))
+ *                                      and pooled values (backward scratch)
  * The SOL_VARIANT_SOL2_PV8 layout is the SOL_VARIANT_SOL2 layout with v8t, vbmax and
- * vscale appended, so the Sol-Attn2 stage calls accept either workspace.
+ * vscale appended, so the Sol-Attn2 stage calls accept either workspace; likewise the
+ * SOL_VARIANT_SOL1_TRAIN layout is the SOL_VARIANT_SOL1 one with the training arrays
+ * appended.
  */
 typedef struct {
     int64_t total_bytes;
@@ -99,6 +110,7 @@ typedef struct {
     int64_t kv_splits, opart, olse;
     int64_t sel, tmu, tnu, tlz;
     int64_t v8t, vbmax, vscale;
+    int64_t lse, mrow, mcol, ld, dkbar, dvbar;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */
@@ -179,6 +191,36 @@ int sol_attn_fused_kv(const void* q, const void* k, const void* v, void* out,
                       int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                       int64_t sink_start, int64_t sink_tokens, int kv_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Training forward (Sol-Attn paper §6 "Limitations and Future Work" names backward
+ * support as the missing piece; the Sol-Attn2 draft, Method, Stage A1 passage, fixes
+ * its meaning: the block selection stays fixed during the backward pass).  Same
+ * arguments, output and errors as sol_attn with automatic kv_splits, on a workspace
+ * of at least sol_attn_workspace_bytes(SOL_VARIANT_SOL1_TRAIN, ...) bytes; the call
+ * also leaves in the workspace the routing bits it used (mrow) and each query row's
+ * log-sum-exp (lse), which sol_attn_backward reads.  The workspace must then be left
+ * untouched until the backward call. */
+int sol_attn_forward_train(const void* q, const void* k, const void* v, void* out,
+                           int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                           float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of sol_attn_forward_train with its routing fixed: the gradients of
+ * sum(dout * out) w.r.t. q, k and v.  The forward is one softmax over the tokens of
+ * the exact blocks and one pooled key per unselected block (K mean, logit bias
+ * ln n_j, value V mean; Sol-Attn paper §3.2), so the gradient reaches every exact
+ * token directly and every token of an unselected block as 1/n_j of its pooled
+ * key's and value's gradient (the block means).  q, k, v, out: the tensors of the
+ * forward call (device, bf16 BTHD, unchanged since); dout: device bf16 BTHD, the
+ * gradient of the output; dq, dk, dv: device bf16 BTHD outputs, fully written.
+ * workspace: the forward's (SOL_VARIANT_SOL1_TRAIN layout), which this call also uses
+ * as scratch; the shape must be the forward's.  Errors: SOL_ERR_NULL for a NULL
+ * pointer, SOL_ERR_ARG for pointers not 16-byte aligned, shape and workspace errors as
+ * sol_attn; nothing is launched then.  The pooled-key gradients are summed with fp32
+ * atomics, so the last bits of dk and dv can differ between runs. */
+int sol_attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      void* dq, void* dk, void* dv, int64_t batch, int64_t tokens, int64_t heads,
+                      int64_t head_dim, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Test and tooling export, not part of the hot path: like sol_attn (with an
  * explicit kv_splits, 0 = automatic, and a workspace sized for it), and the

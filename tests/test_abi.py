@@ -68,7 +68,7 @@ def test_validate(L, args, status):
 
 def test_workspace_sizes_and_layout(L):
     from block_sparse_attention_tok_amd import _lib
-    for variant in (1, 2):
+    for variant in (1, 2, 4):
         for (B, N, H) in ((1, 1024, 2), (1, 14040, 12), (2, 333, 3), (1, 32768, 32)):
             n = L.sol_attn_workspace_bytes(variant, B, N, H, 128)
             lay = _lib.workspace_layout(variant, B, N, H)
@@ -83,7 +83,7 @@ def test_workspace_sizes_and_layout(L):
             if variant == 1:
                 assert lay.q8 == -1 and lay.gk == -1
     assert L.sol_attn_workspace_bytes(1, 1, 1024, 2, 64) == 0
-    assert L.sol_attn_workspace_bytes(4, 1, 1024, 2, 128) == 0
+    assert L.sol_attn_workspace_bytes(5, 1, 1024, 2, 128) == 0
 
 
 @pytest.mark.parametrize("B,N,H", [(1, 1024, 2), (1, 14040, 12), (2, 333, 3)])
@@ -100,6 +100,28 @@ def test_fp8_pv_layout_extends_the_sol2_layout(L, B, N, H):
     assert l2.v8t == l2.vbmax == l2.vscale == -1
     assert l3.v8t >= l2.total_bytes and l3.total_bytes > l3.vscale > l3.vbmax > l3.v8t
     assert l3.vbmax - l3.v8t >= B * H * 128 * l3.nbp * 64
+
+
+@pytest.mark.parametrize("B,N,H", [(1, 1024, 2), (1, 14040, 12), (2, 333, 3), (1, 32768, 32)])
+def test_training_layout_extends_the_sol_attn_layout(L, B, N, H):
+    """The training workspace is the Sol-Attn one (split partials included) with the forward
+    state and backward scratch appended, so the Sol-Attn stage calls run on it unchanged."""
+    from block_sparse_attention_tok_amd import _lib
+    l1 = _lib.workspace_layout(1, B, N, H)
+    l4 = _lib.workspace_layout(4, B, N, H)
+    extra = ("lse", "mrow", "mcol", "ld", "dkbar", "dvbar")
+    for name, _ in _lib.WsLayout._fields_:
+        if name in ("total_bytes",) + extra:
+            continue
+        assert getattr(l1, name) == getattr(l4, name), name
+    assert all(getattr(l1, n) == -1 for n in extra)
+    offs = [getattr(l4, n) for n in extra]
+    assert offs == sorted(offs) and offs[0] >= l1.total_bytes and l4.total_bytes > offs[-1]
+    tp = l4.nbp * 64
+    nbw = l4.nbp // 64
+    assert l4.mrow - l4.lse >= B * H * tp * 4
+    assert l4.mcol - l4.mrow >= B * H * l4.nb * nbw * 8
+    assert l4.dvbar - l4.dkbar >= B * H * l4.nbp * 128 * 4
 
 
 @pytest.mark.parametrize("tokens,req,expect", [
@@ -151,6 +173,19 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
     assert L.sol_attn2_tail(fake, fake, fake, 1, 1024, 2, 128, 1000, 100, fake, 1 << 30, None) == 5
     assert L.sol_attn2_exact(fake, fake, fake, None, 1, 1024, 2, 128, fake, 1 << 30, None) == 1
     assert L.sol_attn2_exact(fake, fake, fake, fake, 1, 1024, 2, 128, fake, 16, None) == 6
+    # training forward / backward: missing output or gradient, workspace sized for the plain forward,
+    # misaligned gradient
+    assert L.sol_attn_forward_train(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, 1 << 30, None) == 1
+    small = L.sol_attn_workspace_bytes(1, 1, 1024, 2, 128)
+    assert L.sol_attn_forward_train(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, small, None) == 6
+    assert L.sol_attn_backward(fake, fake, fake, fake, None, fake, fake, fake, 1, 1024, 2, 128, fake, 1 << 30,
+                               None) == 1
+    assert L.sol_attn_backward(fake, fake, fake, fake, fake, fake, fake, fake, 1, 1024, 2, 128, fake, small,
+                               None) == 6
+    assert L.sol_attn_backward(fake, fake, fake, fake, fake, vp(0x1008), fake, fake, 1, 1024, 2, 128, fake,
+                               1 << 30, None) == 8
+    assert L.sol_attn_backward(fake, fake, fake, fake, fake, fake, fake, fake, 1, 1024, 2, 64, fake, 1 << 30,
+                               None) == 3
 
 
 def test_python_validate_wrapper():
