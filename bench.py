@@ -29,8 +29,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--variant", choices=["sol1", "sol2", "sol2pv8"], default="sol1",
-                   help="sol1: Sol-Attn; sol2: Sol-Attn2 (FP8 Q/K); sol2pv8: Sol-Attn2 with ExpCast FP8 PV")
+    p.add_argument("--variant", choices=["sol1", "sol2", "sol2pv8", "sol1train"], default="sol1",
+                   help="sol1: Sol-Attn; sol2: Sol-Attn2 (FP8 Q/K); sol2pv8: Sol-Attn2 with ExpCast FP8 PV; "
+                        "sol1train: Sol-Attn training step (forward that keeps its routing + backward)")
     p.add_argument("--tokens", type=int, default=32768, help="video tokens (32768 = operator benchmark shape)")
     p.add_argument("--heads", type=int, default=32)
     p.add_argument("--text-sink", type=int, default=0, help="exact text-prefix tokens (long-sequence shape: 512)")
@@ -71,6 +72,8 @@ def main():
         return
     B, H, D = 1, args.heads, 128
     N = args.tokens + args.text_sink
+    if args.variant == "sol1train":
+        return bench_train(args)
     variant = {"sol1": 1, "sol2": 2, "sol2pv8": 3}[args.variant]
     sink_start, sink_tokens = (0, args.text_sink) if args.text_sink else (None, 0)
     log(f"[bench] generating B={B} N={N} H={H} d={D} ({args.variant})")
@@ -258,6 +261,94 @@ def main():
                      "traffic_source": os.path.relpath(traffic_file, os.path.dirname(os.path.abspath(__file__)))
                      if traffic is not None else None},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_train(args):
+    """Training step: sol_attn_forward_train + sol_attn_backward (routing fixed), timed as one
+    step.  value = dense-equivalent training TFLOP/s, 14 B H N^2 d per step (forward 4, backward
+    10: S recomputed, dP, dV, dK, dQ).  The roofline covers the backward call: algorithmic FLOP
+    are 14 d per selected token pair and per (query token, unselected block), 8 d in the dK / dV
+    kernels and 6 d in the dQ kernel."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_tok_amd as bsa
+    from workloads import block_offset_tensor, text_prefix_tensor
+    dev = torch.device("cuda:0")
+    B, H, D = 1, args.heads, 128
+    N = args.tokens + args.text_sink
+    sink_start, sink_tokens = (0, args.text_sink) if args.text_sink else (None, 0)
+    log(f"[bench] generating B={B} N={N} H={H} d={D} (training step)")
+    if args.text_sink:
+        q, k, v = (text_prefix_tensor(B, args.text_sink, args.tokens, H, D, 3000 + i) for i in range(3))
+    else:
+        q, k, v = (block_offset_tensor(B, N, H, D, 3000 + i) for i in range(3))
+    g = torch.Generator().manual_seed(3999)
+    dout = torch.randn(*q.shape, generator=g).to(torch.bfloat16)
+    q, k, v, dout = (t.to(dev) for t in (q, k, v, dout))
+    ws = bsa.alloc_workspace(bsa.SOL_VARIANT_SOL1_TRAIN, q)
+    out = torch.empty_like(q)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    tau = 1.28 if args.tau is None else args.tau
+    bsa.forward_train(q, k, v, tau, "diag", sink_start, sink_tokens, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    views = bsa.workspace_views(bsa.SOL_VARIANT_SOL1_TRAIN, ws, B, N, H)
+    nb = views["nb"]
+    w = views["mrow"].cpu()
+    bits = torch.arange(64, dtype=torch.int64)
+    masks = ((w.unsqueeze(-1) >> bits) & 1).bool().reshape(B, H, nb, -1)[..., :nb].numpy()
+    counts = np.full(nb, 64.0)
+    counts[-1] = N - 64 * (nb - 1)
+    exact_pairs = float((masks * np.outer(counts, counts)).sum())
+    proxy_units = float(((~masks) * counts[:, None]).sum())
+    real_sp = 1.0 - exact_pairs / (B * H * float(N) ** 2)
+    bwd_flops = 14.0 * D * (exact_pairs + proxy_units)
+    fwd_flops = 4.0 * D * (exact_pairs + proxy_units)
+    dense_flops = 14.0 * B * H * float(N) ** 2 * D
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        bsa.forward_train(q, k, v, tau, "diag", sink_start, sink_tokens, out=out, workspace=ws)
+
+    def bwd():
+        bsa.backward(q, k, v, out, dout, ws, dq, dk, dv)
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        ev[s_][0].record(stream)
+        fwd()
+        ev[s_][1].record(stream)
+        bwd()
+        ev[s_][2].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    achieved = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    log(f"[bench] training step {ms_per_step:.3f} ms: forward {fwd_ms:.3f} ms, backward {bwd_ms:.3f} ms "
+        f"-> backward {achieved:.1f} TFLOP/s algorithmic; realised sparsity {real_sp:.4f}")
+    rec = {
+        "metric": "dense-equiv attn TFLOP/s + MFMA util, H32 d128 N=32K-128K @80-90% sparsity",
+        "value": round(dense_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s (dense-equivalent training step, 14*B*H*N^2*d / t_step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded block-offset Gaussian Q/K/V and dO, bf16)",
+        "config": {"workload": f"Sol-Attn training step (forward + backward, routing fixed), B={B} H={H} d={D} "
+                               f"N={N}, block-offset synthetic data, tau {tau}",
+                   "tau": tau, "realised_sparsity": round(real_sp, 5), "forward_ms": round(fwd_ms, 4),
+                   "backward_ms": round(bwd_ms, 4), "forward_algorithmic_tflop": fwd_flops / 1e12,
+                   "backward_algorithmic_tflop": bwd_flops / 1e12},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(achieved / 2500.0, 4), "traffic": None, "kernel": "sol_attn_backward (all kernels)",
+                     "work_per_launch": {"backward_flop": bwd_flops}},
+        "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
 

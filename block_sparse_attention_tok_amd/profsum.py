@@ -83,7 +83,7 @@ def _stats_md(csv_path, title, cmd):
            f"    {cmd}", "", "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |",
            "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
-        name = r["Name"].split("(")[0]
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                    f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     return "\n".join(out) + "\n"
