@@ -146,16 +146,33 @@ hipError_t launch_quant_summary(const uint16_t* q, const uint16_t* k, const uint
 // ---------------------------------------------------------------------------
 // Stage 1c: mean-query direction q-hat = mean of the dequantized queries of the (b, h).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void qhat_kernel(const float* __restrict__ qbar, int N, int nb, int nbp,
-                                                   float* __restrict__ qhat) {
-  const int bh = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(1024) void qhat_kernel(const float* __restrict__ qbar, int N, int nb, int nbp,
+                                                    float* __restrict__ qhat) {
+  // thread (d, slice): dim d of the blocks slice, slice + 8, ...; the 8 slices meet in LDS
+  __shared__ float part[8][kDim];
+  const int bh = blockIdx.x, d = threadIdx.x & (kDim - 1), slice = threadIdx.x >> 7;
   float acc = 0.f;
-  for (int i = 0; i < nb; ++i) acc += (float)min(kBlock, N - i * kBlock) * qbar[((size_t)bh * nbp + i) * kDim + d];
-  qhat[(size_t)bh * kDim + d] = acc / (float)N;
+  int i = slice;
+  for (; i + 24 < nb - 1; i += 32) {                     // four loads in flight (before the last block)
+    const float x0 = qbar[((size_t)bh * nbp + i) * kDim + d];
+    const float x1 = qbar[((size_t)bh * nbp + i + 8) * kDim + d];
+    const float x2 = qbar[((size_t)bh * nbp + i + 16) * kDim + d];
+    const float x3 = qbar[((size_t)bh * nbp + i + 24) * kDim + d];
+    acc += 64.f * ((x0 + x1) + (x2 + x3));               // full blocks
+  }
+  for (; i < nb; i += 8) acc += (float)min(kBlock, N - i * kBlock) * qbar[((size_t)bh * nbp + i) * kDim + d];
+  part[slice][d] = acc;
+  __syncthreads();
+  if (slice == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) t += part[s8][d];
+    qhat[(size_t)bh * kDim + d] = t / (float)N;
+  }
 }
 
 hipError_t launch_qhat(Shape s, const Workspace& ws, hipStream_t stream) {
-  hipLaunchKernelGGL(qhat_kernel, dim3(s.B * s.H), dim3(kDim), 0, stream, ws.qbar, s.N, ws.nb, ws.nbp, ws.qhat);
+  hipLaunchKernelGGL(qhat_kernel, dim3(s.B * s.H), dim3(1024), 0, stream, ws.qbar, s.N, ws.nb, ws.nbp, ws.qhat);
   return hipGetLastError();
 }
 
@@ -210,14 +227,25 @@ __global__ __launch_bounds__(256) void groups_kernel(const uint16_t* __restrict_
   const uint16_t* vb = v + ((size_t)b * N + t0) * rs + (size_t)h * kDim + 2 * lane;
   const uint8_t* kb = k8 + ((size_t)bh * tp + t0) * kDim + 2 * lane;
   float vmax = 0.f;
-  for (int u = 0; u < n; ++u) {
-    const uint32_t vw = *(const uint32_t*)(vb + (size_t)u * rs);
-    const uint32_t kw = *(const uint16_t*)(kb + (size_t)u * kDim);
-    const auto kf = __builtin_amdgcn_cvt_pk_f32_fp8(kw, false);
-    const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
-    vmax = fmaxf(vmax, fmaxf(fabsf(v0), fabsf(v1)));
-    if ((hi >> u) & 1) { kh[0] += kf[0]; kh[1] += kf[1]; vh[0] += v0; vh[1] += v1; }
-    else               { kl[0] += kf[0]; kl[1] += kf[1]; vl[0] += v0; vl[1] += v1; }
+  for (int u0 = 0; u0 < n; u0 += 16) {                    // 16 tokens' loads in flight together
+    uint32_t vw[16], kw[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int u = u0 + e;
+      vw[e] = u < n ? *(const uint32_t*)(vb + (size_t)u * rs) : 0u;
+      kw[e] = u < n ? (uint32_t)*(const uint16_t*)(kb + (size_t)u * kDim) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int u = u0 + e;
+      if (u < n) {
+        const auto kf = __builtin_amdgcn_cvt_pk_f32_fp8(kw[e], false);
+        const float v0 = bf16_lo(vw[e]), v1 = bf16_hi(vw[e]);
+        vmax = fmaxf(vmax, fmaxf(fabsf(v0), fabsf(v1)));
+        if ((hi >> u) & 1) { kh[0] += kf[0]; kh[1] += kf[1]; vh[0] += v0; vh[1] += v1; }
+        else               { kl[0] += kf[0]; kl[1] += kf[1]; vl[0] += v0; vl[1] += v1; }
+      }
+    }
   }
   const int nh = __popcll(hi), nl = n - nh;
   const float ih = nh > 0 ? 1.f / (float)nh : 0.f, il = nl > 0 ? 1.f / (float)nl : 0.f;
@@ -341,8 +369,10 @@ struct Tail2Args {
 };
 
 __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
-  __shared__ __attribute__((aligned(16))) float qb_s[32][kDim];
-  __shared__ __attribute__((aligned(16))) float kb_s[16][kDim];   // key block means of the tile
+  // rows padded by 4 floats: the 16 key blocks (and 4 query blocks) a wave reads at one
+  // dim offset fall on distinct LDS banks
+  __shared__ __attribute__((aligned(16))) float qb_s[32][kDim + 4];
+  __shared__ __attribute__((aligned(16))) float kb_s[16][kDim + 4];   // key block means of the tile
   __shared__ __attribute__((aligned(16))) unsigned char G_s[32 * kTailStride];
   __shared__ float tau_s[32];
   __shared__ uint32_t selw_s[32];        // routing bits of the tile (16 key blocks) per query block
@@ -414,7 +444,7 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   load_tile(0);
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = 16 * t;
-    __syncthreads();                                      // previous tile's LDS reads are done
+    lds_barrier();                                        // previous tile's LDS reads are done
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = tid + 128 * u, r = e >> 5, c = e & 31;
@@ -425,12 +455,9 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
       const int e = tid + 128 * u, d4 = e >> 4, jl = e & 15;
       *(floatx4*)(kb_s[jl] + 4 * d4) = kr4[u];
     }
-    if (tid < 32) {
-      gl_s[tid] = glr;
-      selw_s[tid] = 0u;
-    }
+    if (tid < 32) gl_s[tid] = glr;
     load_tile(t + 1 < ntiles ? j0 + 16 : j0);             // lands while this tile computes (last: reload)
-    __syncthreads();
+    lds_barrier();                                        // LDS barriers: the prefetch stays in flight
     // ---- routing: key block j0 + (tid % 16) against query blocks tid / 16 + 8 p
     {
       const int jl = tid & 15, j = j0 + jl;
@@ -448,15 +475,18 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
             acc[p][half] += qv.x * kk.x + qv.y * kk.y + qv.z * kk.z + qv.w * kk.w;
           }
         }
+      // lanes 16 g .. 16 g + 15 of the wave hold key blocks 0..15 of query block r: the
+      // ballot's 16-bit field g is r's routing word for the tile
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int r = (tid >> 4) + 8 * p;
         const float s_hat = (acc[p][0] + acc[p][1]) * kScale2;
         const bool sel = r < nqb && j < a.nb && (s_hat > tau_s[r] || (j >= a.sink_b0 && j <= a.sink_b1));
-        if (sel) atomicOr(&selw_s[r], 1u << jl);
+        const uint64_t bits = __ballot(sel);
+        if (jl == 0) selw_s[r] = (uint32_t)(bits >> (lane & 48)) & 0xffffu;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < 32) {
       selacc_s[tid] |= (uint64_t)selw_s[tid] << (j0 & 63);
       if ((t & 3) == 3) {
