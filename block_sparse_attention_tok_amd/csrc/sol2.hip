@@ -709,13 +709,12 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
   float m_run = kNegInf, l_run = 0.f;
   const float qs = sq * kScale2 * kLog2e;
-  int cur = next_sel();
-  if (cur >= 0) issue_k(cur);
-  while (cur >= 0) {
-    const int nxt = next_sel();
-    wait_vm0();
-    lds_barrier();                                         // K8(cur) landed; V buffer free
-    issue_v(cur);
+  const int last_partial = a.N % kBlock ? a.nb - 1 : -1;   // the only block with masked rows
+  // One selected block: scores, running max, P (bf16 or ExpCast bytes), PV.  kPartial masks
+  // the rows past the end of the sequence (only the last block, which comes last in the
+  // ascending order); full blocks take the logits straight from the raw scores.
+  auto tile = [&](auto partial_tag, int cur, int nxt) {
+    constexpr bool kPartial = decltype(partial_tag)::value;
     floatx16 s0 = {}, s1 = {};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -727,19 +726,22 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
       s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qf[ks], s0, 0, 0, 0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qf[ks], s1, 0, 0, 0, 0, 0, 0);
     }
-    // logits in log2 units; rows past the end of the last block are masked
+    // logits in log2 units are f * s (f = s_q s_k log2(e) / sqrt(d) > 0, so the max of the
+    // raw scores gives the max of the logits)
     const float f = qs * a.kscale[(size_t)bh * a.nbp + cur];
-    const int valid = min(kBlock, a.N - cur * kBlock);
+    if constexpr (kPartial) {
+      const int valid = a.N - cur * kBlock;
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
-      s0[idx] = key0 < valid ? s0[idx] * f : kNegInf;
-      s1[idx] = key0 + 32 < valid ? s1[idx] * f : kNegInf;
+      for (int idx = 0; idx < 16; ++idx) {
+        const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+        s0[idx] = key0 < valid ? s0[idx] : kNegInf;
+        s1[idx] = key0 + 32 < valid ? s1[idx] : kNegInf;
+      }
     }
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
-    mx = max_with_partner(mx);
+    mx = max_with_partner(mx) * f;
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     // Unconditional rescale (skipping it behind a wave-uniform branch made results
@@ -755,15 +757,16 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) ol[idx] *= alpha;
       // ExpCast bytes c = RNE(8 (x - m) + 55.65) (<= 56 since x <= m; v_cvt_pk_u8_f32
-      // rounds to nearest even and saturates below at 0, which is the clip), in the PV
-      // operand order: byte e = idx of s0, 16 + idx of s1.
+      // rounds to nearest even and saturates below at 0, which is the clip; masked rows
+      // are -inf and give 0), in the PV operand order: byte e = idx of s0, 16 + idx of s1.
       const float c0 = 55.65f - 8.f * m_use;
+      const float f8 = 8.f * f;
       uint32_t pw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        pw[idx >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s0[idx], 8.f, c0), idx & 3, pw[idx >> 2]);
+        pw[idx >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s0[idx], f8, c0), idx & 3, pw[idx >> 2]);
         pw[4 + (idx >> 2)] =
-            __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s1[idx], 8.f, c0), idx & 3, pw[4 + (idx >> 2)]);
+            __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s1[idx], f8, c0), idx & 3, pw[4 + (idx >> 2)]);
       }
       const intx8 pc = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
       const intx8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,   // E4M3 1.0
@@ -780,11 +783,12 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
       }
       ol = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pc, ol, 0, 0, 0, 0, 0, 0);
     } else {
+      const float neg_m = -m_use;
       bf16x8 pa[4];
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        pa[idx >> 3][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[idx] - m_use);   // keys 16 st ..
-        pa[2 + (idx >> 3)][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[idx] - m_use);
+        pa[idx >> 3][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], f, neg_m));   // keys 16 st ..
+        pa[2 + (idx >> 3)][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], f, neg_m));
       }
 #pragma unroll
       for (int st = 0; st < 4; ++st) l_run = add_bf16x8(pa[st], l_run);
@@ -793,6 +797,16 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
       if (nxt >= 0) issue_k(nxt);
       pv_tile(o, Vl, voff, pa);
     }
+  };
+  int cur = next_sel();
+  if (cur >= 0) issue_k(cur);
+  while (cur >= 0) {
+    const int nxt = next_sel();
+    wait_vm0();
+    lds_barrier();                                         // K8(cur) landed; V buffer free
+    issue_v(cur);
+    if (cur == last_partial) tile(BoolTag<true>{}, cur, nxt);
+    else tile(BoolTag<false>{}, cur, nxt);
     cur = nxt;
   }
 
