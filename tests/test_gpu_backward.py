@@ -90,7 +90,7 @@ def test_tiny_workload(tau):
     run_case(*_qkv(1, 1024, 2, 1000), tau)
 
 
-@pytest.mark.parametrize("N", [40, 64, 65, 200, 1000, 4493])
+@pytest.mark.parametrize("N", [1, 40, 64, 65, 200, 1000, 4493])
 def test_ragged_lengths(N):
     run_case(*_qkv(1, N, 2, 1100 + N), 1.0, seed=N)
 

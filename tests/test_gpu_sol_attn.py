@@ -206,3 +206,38 @@ def test_kv_splits_match_oracle(N):
     for kv in (2, 4, 8):
         d = (outs[kv] - outs[1]).norm() / outs[1].norm()
         assert d < 1e-2, f"kv_splits={kv} vs 1: {d:.3e}"
+
+
+# ---- degenerate inputs and the maximum length ---------------------------------------
+
+@pytest.mark.parametrize("N", [1, 2])
+def test_single_block_shorter_than_a_tile(N):
+    """One partial block: its proxy equals its threshold (zero spread), a tie that either
+    decision satisfies; the oracle comparison uses the kernel's decision.  With one token both
+    branches give that token's value."""
+    q, k, v = _qkv(1, N, 2, 2600 + N)
+    out, _, _ = run_case(q, k, v, 1.0)
+    if N == 1:
+        compare_out(out.float().cpu().numpy(), v.float().numpy(), what="N=1")
+
+
+def test_zero_queries_give_the_value_mean():
+    """All-zero queries: every logit is 0 and every proxy equals the threshold, so nothing is
+    selected and the output is the mean of V over the whole sequence (closed form)."""
+    B, N, H = 1, 1000, 2
+    _, k, v = _qkv(B, N, H, 2700)
+    q = torch.zeros_like(k)
+    out, masks, _ = run_case(q, k, v, 0.5)
+    assert not masks.any()
+    want = v.float().mean(dim=1, keepdim=True).expand(B, N, H, 128)
+    compare_out(out.float().cpu().numpy(), want.numpy(), what="zero queries")
+
+
+def test_maximum_sequence_length():
+    """524288 tokens (128 routing chunks, the largest length the library accepts): full routing
+    against the oracle and a sample of query blocks including the last."""
+    N = 524288
+    q, k, v = _qkv(1, N, 1, 2800)
+    assert bsa.validate(1, N, 1, 128, 1.28, None, 0) == 0
+    assert bsa.validate(1, N + 1, 1, 128, 1.28, None, 0) != 0
+    run_case(q, k, v, 1.28, sample=3, seed=5)

@@ -138,3 +138,17 @@ def test_sol2_bench_shape():
     """B=1, H=32, N=32768, tau near 90% sparsity: 3 heads checked in full routing, sampled outputs."""
     q, k, v = sol2_bench().qkv()
     run_case(q, k, v, 1.28, heads=[0, 13, 31], sample=3, seed=6)
+
+
+def test_single_token():
+    """N = 1: one key, so exact and tail branches both return its value (up to the FP8 path)."""
+    q, k, v = _qkv(1, 1, 2, 2500)
+    out, _, _ = run_case(q, k, v, 1.0)
+    np.testing.assert_allclose(out.float().cpu().numpy(), v.float().numpy(), rtol=1e-2, atol=1e-2)
+
+
+def test_maximum_sequence_length():
+    """524288 tokens, the largest length the library accepts: codes, scales, groups and routing of
+    the head in full, sampled output rows including the last block."""
+    q, k, v = _qkv(1, 524288, 1, 2600)
+    run_case(q, k, v, 1.28, sample=2, seed=7)

@@ -128,3 +128,9 @@ def test_sol2_bench_shape():
     """B=1, H=32, N=32768 near 90% sparsity: codes of 3 heads in full, sampled outputs."""
     q, k, v = sol2_bench().qkv()
     run_case(q, k, v, 1.28, heads=[0, 13, 31], sample=3, seed=7)
+
+
+def test_maximum_sequence_length():
+    """524288 tokens with the FP8 PV path (V codes in their operand order at the largest length)."""
+    q, k, v = _qkv(1, 524288, 1, 2700)
+    run_case(q, k, v, 1.28, sample=2, seed=8)
