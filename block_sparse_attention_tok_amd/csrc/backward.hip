@@ -41,6 +41,7 @@ constexpr float kScaleB = 0.08838834764831845f;        // 1/sqrt(128)
 constexpr float kScaleLog2B = kScaleB * kLog2e;
 constexpr int kMaxChunksB = 128;
 constexpr int kEndB = -0x7fffffff;
+constexpr int kMaxRange = 512;                          // query blocks per pooled-key workgroup
 
 struct BwdArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* out; const uint16_t* dout;
@@ -209,6 +210,7 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char Ql[2][16384];
   __shared__ __attribute__((aligned(16))) unsigned char Gl[2][16384];
   __shared__ __attribute__((aligned(16))) float St[2][256];     // (lse, D) pairs of 64 rows + copy
+  __shared__ uint64_t mw_s[kPooled ? kMaxRange : 1];            // routing words of the range (pooled)
 
   const int nchunks = a.nbp / 64;
   const int total = kPooled ? a.B * a.H * nchunks * a.nrange : a.B * a.H * a.nb;
@@ -255,12 +257,18 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
   const uint64_t* mcol_j = a.mcol + ((size_t)bh * a.nb + jb) * a.nbw;
   int it_i = kPooled ? r * a.bpr : 0;
   const int it_end = kPooled ? min(a.nb, (r + 1) * a.bpr) : a.nbw;
+  if constexpr (kPooled) {
+    // the chunk's routing word of every query block of the range, loaded once (bpr <= kMaxRange)
+    for (int e = threadIdx.x; e < it_end - it_i; e += 128) mw_s[e] = mrow_bh[(size_t)(it_i + e) * a.nbw + c];
+    __syncthreads();
+  }
+  const int range0 = it_i;
   uint64_t it_bits = 0;
   auto next_query = [&]() -> int {
     if constexpr (kPooled) {
       while (it_i < it_end) {
         const int i = it_i++;
-        if (valid_chunk & ~uniform64(mrow_bh[(size_t)i * a.nbw + c])) return i;
+        if (valid_chunk & ~uniform64(mw_s[i - range0])) return i;
       }
       return kEndB;
     } else {
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
     const unsigned char* Q = Ql[buf];
     const unsigned char* G = Gl[buf];
     bool ok = key_ok;
-    if constexpr (kPooled) ok = ok && !((uniform64(mrow_bh[(size_t)cur * a.nbw + c]) >> (32 * w + l32)) & 1ull);
+    if constexpr (kPooled) ok = ok && !((uniform64(mw_s[cur - range0]) >> (32 * w + l32)) & 1ull);
     floatx16 s0, s1, d0, d1;
     row_product(Q, roff, kreg, s0, s1);                      // S = Q K^T (rows = queries)
     row_product(G, roff, vreg, d0, d1);                      // dP = dO V^T
@@ -545,6 +553,7 @@ hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t*
   // pooled keys: enough (chunk, query range) workgroups to fill the chip twice over
   const int bhc = s.B * s.H * nchunks;
   int nrange = (2048 + bhc - 1) / bhc;
+  if (nrange < (ws.nb + kMaxRange - 1) / kMaxRange) nrange = (ws.nb + kMaxRange - 1) / kMaxRange;
   if (nrange > ws.nb) nrange = ws.nb;
   if (nrange < 1) nrange = 1;
   a.bpr = (ws.nb + nrange - 1) / nrange;

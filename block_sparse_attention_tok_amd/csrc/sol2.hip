@@ -358,7 +358,10 @@ hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStr
 // The anchor results (mu_a, nu_a, log2 Z_a - log2(e) q-bar_a . mu_a / sqrt(d)) go to
 // the workspace; the exact pass adds delta_t and combines (Eqs. (2), (3)).
 // ---------------------------------------------------------------------------
-constexpr int kTailStride = 528;       // bytes per LDS group row: 256 (k-bar) + 256 (v-bar) + 16 pad
+// 16-byte slot swizzle of the 32 x 256-byte group tiles of the tail pass: 16 consecutive
+// rows at one logical slot (the scores' row reads) and 4 consecutive rows x 4 slots (the
+// means' transposed reads) both land on 16 distinct slots.
+__device__ __forceinline__ int swz_g(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 struct Tail2Args {
   int B, N, H, nb, nbp, nbw;
@@ -372,8 +375,13 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   // rows padded by 4 floats: the 16 key blocks (and 4 query blocks) a wave reads at one
   // dim offset fall on distinct LDS banks
   __shared__ __attribute__((aligned(16))) float qb_s[32][kDim + 4];
-  __shared__ __attribute__((aligned(16))) float kb_s[16][kDim + 4];   // key block means of the tile
-  __shared__ __attribute__((aligned(16))) unsigned char G_s[32 * kTailStride];
+  // Double-buffered tiles, filled by buffer DMA: the 32 group mean keys and mean values
+  // (32 rows x 256 B each, 16-byte slots swizzled by swz_g so that both the row reads of
+  // the scores and the transposed reads of the means are conflict-free) and the 16 key
+  // block means of the routing, stored [dim / 4][key block] (one 256-byte row per 4 dims).
+  __shared__ __attribute__((aligned(1024))) unsigned char Gk_s[2][32 * 256];
+  __shared__ __attribute__((aligned(1024))) unsigned char Gv_s[2][32 * 256];
+  __shared__ __attribute__((aligned(1024))) float4 kbT_s[2][32][16];
   __shared__ float tau_s[32];
   __shared__ uint32_t selw_s[32];        // routing bits of the tile (16 key blocks) per query block
   __shared__ uint64_t selacc_s[32];      // routing bits of the current 64-block chunk
@@ -406,34 +414,52 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
     qa[ks] = bf16x8{(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
                     (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
   }
-  // Transposed-read offsets of the group rows (the Sol-Attn V^T pattern over 32 rows,
-  // row stride kTailStride, no swizzle): dims 32 mt + 16 (G % 2) + 4 (i' % 4).
-  int toff[8];
+  // Transposed-read offsets of the group rows (the V^T pattern of the Sol-Attn pass over 32
+  // rows): row 4 kg + i'/4 (+ 8 for the upper half, + 16 per k-step), logical chunk
+  // 4 mt + 2 (G % 2) + (i' % 4) / 2 of the 16-chunk row.
+  int toff[4][2];
   {
     const int ip = lane & 15, gm = (lane >> 4) & 1;
-    const int row = 4 * kg + (ip >> 2);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) toff[mt] = row * kTailStride + 64 * mt + 32 * gm + 8 * (ip & 3);
+    for (int half = 0; half < 2; ++half) {
+      const int row = 4 * kg + (ip >> 2) + 8 * half;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        toff[mt][half] = row * 256 + 16 * ((4 * mt + 2 * gm + ((ip & 3) >> 1)) ^ swz_g(row)) + 8 * (ip & 1);
+    }
   }
+  // scores A operand: group row l32, logical chunk 2 ks + kg
+  int goff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) goff[ks] = l32 * 256 + 16 * ((2 * ks + kg) ^ swz_g(l32));
 
-  // Tile t's group rows (8 x 16 B per thread), key block means (4 x 16 B) and ln n_g are
-  // loaded into registers one tile ahead, all loads in flight together.
-  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
-  uint4v gr[8];
-  floatx4 kr4[4];
-  float glr = kNegInf;
-  auto load_tile = [&](int j0) {
+  // DMA of tile t (key blocks 16 t .. 16 t + 15) into buffer `buf`: wave w, instruction n
+  // fills 1 KB segment 4 w + n of each array.  Group rows r = 16 w + 4 n + lane / 16 (slot
+  // lane % 16 holds logical chunk (lane % 16) ^ swz_g(r)); key-block means: dims
+  // 4 (16 w + 4 n + lane / 16) .. + 3 of key block lane % 16.
+  const uint32_t grow = (uint32_t)(16 * w + (lane >> 4));
+  uint32_t gdma[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + 128 * u, r = e >> 5, c = e & 31;
-      gr[u] = *(const uint4v*)((c < 16 ? a.gk : a.gv) + (((size_t)bh * a.nbp + j0) * 2 + r) * kDim + (c & 15) * 8);
-    }
+  for (int n = 0; n < 4; ++n) gdma[n] = (grow + 4 * n) * 256 + 16 * ((lane & 15) ^ swz_g(grow + 4 * n));
+  const uint32_t kdma = (grow * a.nbp + (lane & 15)) * 16;
+  auto issue_tile = [&](int t, int buf) {
+    const uint32_t gbytes = (uint32_t)a.nbp * 2 * 256;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(a.gk + (size_t)bh * a.nbp * 2 * kDim), gbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(a.gv + (size_t)bh * a.nbp * 2 * kDim), gbytes);
+    const __amdgpu_buffer_rsrc_t rt =
+        make_rsrc(uniform_ptr(a.kbar_t + (size_t)bh * 32 * a.nbp * 4), (uint32_t)a.nbp * 32 * 16);
+    const uint32_t toff_g = (uint32_t)t * 32 * 256;          // 32 group rows per tile
+    const uint32_t toff_k = (uint32_t)t * 16 * 16;           // 16 key blocks per tile
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 128 * u, d4 = e >> 4, jl = e & 15;   // kb_s[jl][4 d4 .. 4 d4 + 3]
-      kr4[u] = *(const floatx4*)(kt + (size_t)d4 * a.nbp + j0 + jl);
+    for (int n = 0; n < 4; ++n) {
+      dma16_buf(rk, toff_g + gdma[n], 0, Gk_s[buf] + 1024 * (4 * w + n));
+      dma16_buf(rv, toff_g + gdma[n], 0, Gv_s[buf] + 1024 * (4 * w + n));
+      dma16_buf(rt, toff_k + kdma + (uint32_t)(4 * n) * a.nbp * 16, 0, (unsigned char*)kbT_s[buf] + 1024 * (4 * w + n));
     }
-    if (tid < 32) glr = j0 + (tid >> 1) < a.nb ? a.glogn[((size_t)bh * a.nbp + j0) * 2 + tid] : kNegInf;
+  };
+  float glr = kNegInf;                                    // ln n_g of the next tile (lanes 0..31)
+  auto load_gl = [&](int t) {
+    if (tid < 32) glr = 16 * t + (tid >> 1) < a.nb ? a.glogn[((size_t)bh * a.nbp + 16 * t) * 2 + tid] : kNegInf;
   };
 
   floatx16 num[8];                                        // rows: dims (0..127 mu, 128..255 nu); cols: anchors
@@ -441,23 +467,17 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   for (int mt = 0; mt < 8; ++mt) num[mt] = floatx16{};
   float m_run = kNegInf, z_run = 0.f;
   const int ntiles = a.nbp / 16;
-  load_tile(0);
+  issue_tile(0, 0);
+  load_gl(0);
   for (int t = 0; t < ntiles; ++t) {
-    const int j0 = 16 * t;
-    lds_barrier();                                        // previous tile's LDS reads are done
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + 128 * u, r = e >> 5, c = e & 31;
-      *(uint4v*)(G_s + r * kTailStride + c * 16) = gr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 128 * u, d4 = e >> 4, jl = e & 15;
-      *(floatx4*)(kb_s[jl] + 4 * d4) = kr4[u];
-    }
+    const int j0 = 16 * t, buf = t & 1;
+    wait_vm0();
+    lds_barrier();                                        // tile t landed; the other buffer is free
     if (tid < 32) gl_s[tid] = glr;
-    load_tile(t + 1 < ntiles ? j0 + 16 : j0);             // lands while this tile computes (last: reload)
-    lds_barrier();                                        // LDS barriers: the prefetch stays in flight
+    if (t + 1 < ntiles) {
+      issue_tile(t + 1, buf ^ 1);                         // lands while this tile computes
+      load_gl(t + 1);
+    }
     // ---- routing: key block j0 + (tid % 16) against query blocks tid / 16 + 8 p
     {
       const int jl = tid & 15, j = j0 + jl;
@@ -468,7 +488,7 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
       for (int half = 0; half < 2; ++half)
 #pragma unroll 4
         for (int d4 = 16 * half; d4 < 16 * half + 16; ++d4) {
-          const float4 kk = *(const float4*)(kb_s[jl] + 4 * d4);
+          const float4 kk = kbT_s[buf][d4][jl];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             const float4 qv = *(const float4*)(qb_s[(tid >> 4) + 8 * p] + 4 * d4);
@@ -498,8 +518,7 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
     floatx16 s = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(G_s + l32 * kTailStride + 32 * ks + 16 * kg),
-                                                  qa[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(Gk_s[buf] + goff[ks]), qa[ks], s, 0, 0, 0);
     const uint32_t mine = selw_s[qr];
     float mx = kNegInf;
 #pragma unroll
@@ -527,9 +546,9 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int vo = toff[mt] + st * 16 * kTailStride;
-        const uint2v lo = lds_read_tr16(G_s + vo);
-        const uint2v hi = lds_read_tr16(G_s + vo + 8 * kTailStride);
+        const unsigned char* gt = mt < 4 ? Gk_s[buf] : Gv_s[buf];   // m-tiles 0..3: mu dims, 4..7: nu
+        const uint2v lo = lds_read_tr16(gt + toff[mt & 3][0] + st * 16 * 256);
+        const uint2v hi = lds_read_tr16(gt + toff[mt & 3][1] + st * 16 * 256);
         const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
         num[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], num[mt], 0, 0, 0);
       }
