@@ -15,15 +15,15 @@
 // waves per SIMD; workgroups are ordered so that each XCD walks its own heads.
 //   * Routing runs first, in fp32 from the fp32 block means (VALU), for every
 //     chunk of 64 pooled keys; the per-chunk selection words stay in LDS.
-//   * A reference pass over the pooled K-bar tiles gives each query row
-//     m_ref = max_j log2(e) q . K-bar_j / sqrt(d).  Because a block's mean of
+//   * The tile stream is the pooled tile of every chunk (K-bar / V-bar = V-hat/n
+//     rows with logit bias log2 n_j; selected and padding columns masked), then
+//     the selected exact blocks chunk by chunk.
+//   * The first pooled tile fixes a per-row reference m_ref, the largest pooled
+//     logit log2(e) q . K-bar_j / sqrt(d) of its chunk.  Because a block's mean of
 //     exponentials is at least the exponential of its mean logit, the softmax
-//     denominator measured against m_ref is >= 1, so the main pass takes
+//     denominator measured against m_ref is >= 1, so every tile takes
 //     P = 2^(x - m_ref) with no running maximum and no O rescale; a workgroup
 //     whose O or l overflows reruns its tiles with the usual rescaling.
-//   * The tile stream is, per chunk, one proxy tile (K-bar / V-bar = V-hat/n
-//     rows with logit bias log2 n_j; selected and padding columns masked) then
-//     the chunk's selected exact blocks.
 //   * Tiles move HBM -> LDS with buffer_load ... lds (no VGPR staging; the
 //     buffer's range check covers every lane offset) into one K and one V
 //     buffer whose 16-byte slots are XOR-swizzled per row; the V load of tile t
@@ -60,30 +60,29 @@ struct FusedArgs {
   int tp;
 };
 
-// Tile order: per chunk c, the proxy tile (code -(c + 1)) if any block of the
-// chunk is unselected, then its selected blocks (code = block index).
+// Tile order: first the pooled tile of every chunk c (code -(c + 1)), then the selected
+// blocks chunk by chunk (code = block index).
 struct TileIter {
   int c;
-  int phase;           // 0: proxy not yet considered for chunk c
+  int phase;           // 0: pooled tiles, 1: exact blocks
   uint64_t bits;
 };
 
 // Chunks are numbered locally from c0 (the split's first chunk); returned codes are global.
-__device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, const uint64_t* prox_s,
-                                         int nchunks, int c0) {
+__device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, int nchunks, int c0) {
+  if (it.phase == 0) {
+    if (it.c < nchunks) return -(c0 + it.c++ + 1);
+    it.phase = 1;
+    it.c = 0;
+    it.bits = nchunks > 0 ? uniform64(sel_s[0]) : 0ull;
+  }
   while (it.c < nchunks) {
-    if (it.phase == 0) {
-      it.phase = 1;
-      it.bits = uniform64(sel_s[it.c]);
-      if (uniform64(prox_s[it.c])) return -(c0 + it.c + 1);
-    }
     if (it.bits) {
       const int jb = (c0 + it.c) * 64 + __builtin_ctzll(it.bits);
       it.bits &= it.bits - 1;
       return jb;
     }
-    ++it.c;
-    it.phase = 0;
+    if (++it.c < nchunks) it.bits = uniform64(sel_s[it.c]);
   }
   return kEnd;
 }
@@ -137,7 +136,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   const int c_begin = split * a.cps;                        // this split's routing chunks
   const int c_end = min(a.nbp / 64, c_begin + a.cps);
   const int nchunks = c_end - c_begin;
-  // The reference pass below reads the pooled K-bar tiles; its first DMA is issued
+  // The first tile is the pooled tile of the split's first chunk; its DMA is issued
   // now and lands while the routing runs (the routing barriers do not wait for it).
   auto pool = [&]() { return make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool); };
   dma_tile<false>(Kl, pool(), (uint32_t)c_begin * 64 * row_bytes, row_bytes, doff, w);
@@ -196,41 +195,12 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 
   // ---- reference max.  Every unselected block j contributes n_j 2^(x_j) with
   // x_j = log2(e) q . K-bar_j / sqrt(d), and every selected block at least as much
-  // (the mean of exp over a block is >= exp of the mean logit), so with
-  // m_ref = max_j x_j over the split's blocks the softmax denominator is >= 1 and
-  // needs no running maximum: P = 2^(x - m_ref) is taken directly.  Exact logits
-  // above m_ref are representable up to ~2^127; a row that still overflows sends
-  // the workgroup through the rescaling loop below.
-  float m_ref;
-  {
-    float mx = kNegInf;
-    for (int c = 0; c < nchunks; ++c) {
-      const unsigned char* buf = (c & 1) ? Vl : Kl;
-      if (c + 1 < nchunks) {
-        dma_tile<false>((c & 1) ? Kl : Vl, pool(), (uint32_t)(c_begin + c + 1) * 64 * row_bytes, row_bytes, doff, w);
-        wait_vm8();
-      } else {
-        wait_vm0();
-      }
-      lds_barrier();                                         // pooled tile c landed
-      floatx16 s0, s1;
-      scores(buf, s0, s1);
-      const int nvalid = __builtin_amdgcn_readfirstlane(a.nb - (c_begin + c) * 64);
-      if (nvalid >= kBlock) {
-#pragma unroll
-        for (int idx = 0; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
-      } else {
-#pragma unroll
-        for (int idx = 0; idx < 16; ++idx) {
-          const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
-          mx = fmaxf(mx, fmaxf(key0 < nvalid ? s0[idx] : kNegInf, key0 + 32 < nvalid ? s1[idx] : kNegInf));
-        }
-      }
-      lds_barrier();                                         // buffer free for tile c + 2
-    }
-    m_ref = max_with_partner(mx) * kScaleLog2;
-  }
-
+  // (the mean of exp over a block is >= exp of the mean logit), so with m_ref = x_j of
+  // any one block the softmax denominator is >= 1.  The first tile of the stream is the
+  // pooled tile of the split's first chunk; m_ref is the largest x_j over its valid
+  // blocks (selected or not), and every tile takes P = 2^(x - m_ref) with no running
+  // maximum.  Logits above m_ref are representable up to ~2^127; a row that still
+  // overflows sends the workgroup through the rescaling loop below.
   floatx16 o[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
@@ -253,16 +223,17 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     return min(kBlock, a.N - code * kBlock);
   };
 
-  // The tile stream of this split.  kSafe = false: fixed reference max, no
-  // rescaling; kSafe = true: running max with the usual rescale of O and l.
-  auto run_tiles = [&](auto safe_tag) {
+  // The tile stream of this split.  kSafe = false: the pooled tiles with a running
+  // maximum over all pooled logits, then the exact blocks against that maximum with no
+  // rescaling; kSafe = true: running max with the usual rescale of O and l throughout.
+  // first_issued: the K DMA of the first tile is already in flight.
+  auto run_tiles = [&](auto safe_tag, bool first_issued) {
     constexpr bool kSafe = decltype(safe_tag)::value;
     TileIter it{0, 0, 0};
-    int cur = next_tile(it, sel_s, prox_s, nchunks, c_begin);
-    if (cur != kEnd) issue(cur, false);
-    const float neg_ref = -m_ref;
+    int cur = next_tile(it, sel_s, nchunks, c_begin);
+    if (cur != kEnd && !first_issued) issue(cur, false);
     while (cur != kEnd) {
-      const int nxt = next_tile(it, sel_s, prox_s, nchunks, c_begin);
+      const int nxt = next_tile(it, sel_s, nchunks, c_begin);
       wait_vm0();
       lds_barrier();                                         // K(cur) landed; V buffer free
       const int valid = issue(cur, true);
@@ -272,8 +243,10 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
       const int mode = cur < 0 ? kProxy : (valid == kBlock ? kExactFull : kExactPartial);
       bf16x8 pa[4];
       if constexpr (!kSafe) {
-        // ---- P = 2^(x - m_ref) with the tile's mask / proxy weight n_j
+        // ---- P = 2^(x - m_ref) with the tile's mask / proxy weight n_j (m_ref is set by
+        // the first tile, a pooled one, below; the exact tiles come after it)
         float p0[16], p1[16];
+        const float neg_ref = -m_run;
         if (mode == kExactFull) {
 #pragma unroll
           for (int idx = 0; idx < 16; ++idx) {
@@ -290,11 +263,21 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
             p1[idx] = key0 + 32 < valid ? e1 : 0.f;
           }
         } else {
+          // pooled tile; the first one (the split's first chunk) fixes the reference
+          // m_ref = its maximum pooled logit over every valid key, selected or not
           const int c = -cur - 1;
+          const int nvalid = __builtin_amdgcn_readfirstlane(a.nb - c * 64);
+          float mx = kNegInf;
+#pragma unroll
+          for (int idx = 0; idx < 16; ++idx) {
+            const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+            mx = fmaxf(mx, fmaxf(key0 < nvalid ? s0[idx] : kNegInf, key0 + 32 < nvalid ? s1[idx] : kNegInf));
+          }
+          m_run = m_run == kNegInf ? max_with_partner(mx) * kScaleLog2 : m_run;
           const uint64_t colmask = uniform64(prox_s[c - c_begin]);
           const int last_key = a.nb - 1 - c * 64;
-          const float off_full = 6.0f - m_ref;                  // log2(64) for full blocks
-          const float off_last = last_bias - m_ref;
+          const float off_full = 6.0f - m_run;                  // log2(64) for full blocks
+          const float off_last = last_bias - m_run;
 #pragma unroll
           for (int idx = 0; idx < 16; ++idx) {
             const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
@@ -374,9 +357,9 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     }
   };
 
-  run_tiles(BoolTag<false>{});
+  run_tiles(BoolTag<false>{}, true);
   float l_tot = sum_with_partner(l_run);
-  float m_fin = m_ref;
+  float m_fin = m_run;
   {
     // Any non-finite O or l in the workgroup: rerun its tiles with rescaling.
     float chk = l_tot * 0.f;
@@ -392,7 +375,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
       for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
       l_run = 0.f;
       m_run = kNegInf;
-      run_tiles(BoolTag<true>{});
+      run_tiles(BoolTag<true>{}, false);
       l_tot = sum_with_partner(l_run);
       m_fin = m_run;
     }
