@@ -179,7 +179,6 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   int voff[4];                                               // V^T operand (transposed read)
   v_operand_offsets(lane, voff);
 
-
   // S^T = K Q^T for the 64-row K tile at LDS `kl` (two 32-key m-tiles).
   auto scores = [&](const unsigned char* kl, floatx16& s0, floatx16& s1) {
     s0 = floatx16{};
@@ -223,8 +222,8 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     return min(kBlock, a.N - code * kBlock);
   };
 
-  // The tile stream of this split.  kSafe = false: the pooled tiles with a running
-  // maximum over all pooled logits, then the exact blocks against that maximum with no
+  // The tile stream of this split (pooled tiles first, then the exact blocks).
+  // kSafe = false: every tile against m_ref, which the first pooled tile sets, with no
   // rescaling; kSafe = true: running max with the usual rescale of O and l throughout.
   // first_issued: the K DMA of the first tile is already in flight.
   auto run_tiles = [&](auto safe_tag, bool first_issued) {
