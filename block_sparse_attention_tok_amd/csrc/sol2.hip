@@ -34,6 +34,19 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
   f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
 }
 
+// x / s for an E4M3 scale s = RN(max|X| / 448), from one reciprocal r = RN(1 / s): q = x r,
+// then Markstein's correction q + (x - q s) r, both steps fused multiply-adds (P. Markstein,
+// "Computation of elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990).  For s >= 2^-60, every bf16 x with |x| <= 448 s and either quotient at
+// least 2^-12 it gives the IEEE quotient bit for bit (tests/host/div_by_scale.c checks every
+// bf16 max and every x); below 2^-12 both quotients round to the E4M3 code 0.  Smaller scales
+// take the IEEE division.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  const float q = x * r;
+  return fmaf(fmaf(-q, s, x), r, q);
+}
+constexpr float kMinReciprocalScale = 0x1p-60f;
+
 // ---------------------------------------------------------------------------
 // Stage 1a: quantization (draft "FP8 quantization": s = max|X| / 448, X8 = E4M3(X / s))
 // and block / anchor means of the dequantized values.  One workgroup per
@@ -80,6 +93,30 @@ __global__ __launch_bounds__(256) void quant_summary_kernel(
   ak = fmaxf(fmaxf(wmax[1][0], wmax[1][1]), fmaxf(wmax[1][2], wmax[1][3]));
   const float sq = aq > 0.f ? __fdiv_rn(aq, 448.0f) : 1.0f;
   const float sk = ak > 0.f ? __fdiv_rn(ak, 448.0f) : 1.0f;
+  const float rq = __fdiv_rn(1.0f, sq), rk = __fdiv_rn(1.0f, sk);
+
+  // E4M3 codes; rows t >= n hold zeros and encode to code 0
+  uint2v cq[4], ck[4];
+  auto encode = [&](auto recip_tag) {
+    constexpr bool kRecip = decltype(recip_tag)::value;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float yq[4], yk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = xq[p][4 * m + e], x1 = xk[p][4 * m + e];
+          yq[e] = fminf(fmaxf(kRecip ? div_by_scale(x0, sq, rq) : __fdiv_rn(x0, sq), -448.f), 448.f);
+          yk[e] = fminf(fmaxf(kRecip ? div_by_scale(x1, sk, rk) : __fdiv_rn(x1, sk), -448.f), 448.f);
+        }
+        cq[p][m] = fp8x2(yq[0], yq[1]) | (fp8x2(yq[2], yq[3]) << 16);
+        ck[p][m] = fp8x2(yk[0], yk[1]) | (fp8x2(yk[2], yk[3]) << 16);
+      }
+    }
+  };
+  if (sq >= kMinReciprocalScale && sk >= kMinReciprocalScale) encode(BoolTag<true>{});   // uniform branch
+  else encode(BoolTag<false>{});
 
   float sumq0[8], sumq1[8], sumk[8];
 #pragma unroll
@@ -88,32 +125,18 @@ __global__ __launch_bounds__(256) void quant_summary_kernel(
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int t = r + 16 * p;
-    uint2v cq = {0u, 0u}, ck = {0u, 0u};
-    if (t < n) {
+    // sums of the decoded codes (exact in fp32: multiples of 2^-9 below 2^15)
+    float dq[8], dk[8];
+    fp8x4_to_f32(cq[p][0], dq); fp8x4_to_f32(cq[p][1], dq + 4);
+    fp8x4_to_f32(ck[p][0], dk); fp8x4_to_f32(ck[p][1], dk + 4);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        float yq[4], yk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          yq[e] = fminf(fmaxf(__fdiv_rn(xq[p][4 * m + e], sq), -448.f), 448.f);
-          yk[e] = fminf(fmaxf(__fdiv_rn(xk[p][4 * m + e], sk), -448.f), 448.f);
-        }
-        cq[m] = fp8x2(yq[0], yq[1]) | (fp8x2(yq[2], yq[3]) << 16);
-        ck[m] = fp8x2(yk[0], yk[1]) | (fp8x2(yk[2], yk[3]) << 16);
-      }
-      // sums of the decoded codes (exact in fp32: multiples of 2^-9 below 2^15)
-      float dq[8], dk[8];
-      fp8x4_to_f32(cq[0], dq); fp8x4_to_f32(cq[1], dq + 4);
-      fp8x4_to_f32(ck[0], dk); fp8x4_to_f32(ck[1], dk + 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (p < 2) sumq0[e] += dq[e]; else sumq1[e] += dq[e];
-        sumk[e] += dk[e];
-      }
+    for (int e = 0; e < 8; ++e) {
+      if (p < 2) sumq0[e] += dq[e]; else sumq1[e] += dq[e];
+      sumk[e] += dk[e];
     }
     if (j < nb) {   // codes of rows t >= n inside the last block are written as zeros
-      *(uint2v*)(q8 + dst0 + (size_t)t * kDim) = cq;
-      *(uint2v*)(k8 + dst0 + (size_t)t * kDim) = ck;
+      *(uint2v*)(q8 + dst0 + (size_t)t * kDim) = cq[p];
+      *(uint2v*)(k8 + dst0 + (size_t)t * kDim) = ck[p];
     }
   }
 #pragma unroll
@@ -313,18 +336,24 @@ __global__ __launch_bounds__(256) void v8t_kernel(const uint16_t* __restrict__ v
   }
   __syncthreads();
   const float s = vscale[bh];
+  const float rinv = __fdiv_rn(1.0f, s);
   const int d = tid >> 1, p0 = 32 * (tid & 1);
   uint32_t w[8];
+  auto encode = [&](auto recip_tag) {
+    constexpr bool kRecip = decltype(recip_tag)::value;
 #pragma unroll
-  for (int q4 = 0; q4 < 8; ++q4) {
-    float y[4];
+    for (int q4 = 0; q4 < 8; ++q4) {
+      float y[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = bf16_bits_to_f32(vs[pv_token(p0 + 4 * q4 + e)][d]);
-      y[e] = fminf(fmaxf(__fdiv_rn(x, s), -448.f), 448.f);
+      for (int e = 0; e < 4; ++e) {
+        const float x = bf16_bits_to_f32(vs[pv_token(p0 + 4 * q4 + e)][d]);
+        y[e] = fminf(fmaxf(kRecip ? div_by_scale(x, s, rinv) : __fdiv_rn(x, s), -448.f), 448.f);
+      }
+      w[q4] = fp8x2(y[0], y[1]) | (fp8x2(y[2], y[3]) << 16);
     }
-    w[q4] = fp8x2(y[0], y[1]) | (fp8x2(y[2], y[3]) << 16);
-  }
+  };
+  if (s >= kMinReciprocalScale) encode(BoolTag<true>{});   // uniform branch
+  else encode(BoolTag<false>{});
   uint4v* dst = (uint4v*)(v8t + ((size_t)bh * kDim + d) * tp + (size_t)j * kBlock + p0);
   dst[0] = uint4v{w[0], w[1], w[2], w[3]};
   dst[1] = uint4v{w[4], w[5], w[6], w[7]};
