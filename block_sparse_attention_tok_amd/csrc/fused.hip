@@ -87,6 +87,9 @@ __device__ __forceinline__ int next_tile(TileIter& it, const uint64_t* sel_s, in
   return kEnd;
 }
 
+// K operand reads are issued this many score MFMAs ahead of the MFMA that consumes them.
+constexpr int kSAhead = 4;
+
 enum TileMode { kExactFull = 0, kExactPartial = 1, kProxy = 2 };
 
 __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
@@ -183,13 +186,25 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   auto scores = [&](const unsigned char* kl, floatx16& s0, floatx16& s1) {
     s0 = floatx16{};
     s1 = floatx16{};
+    bf16x8 ak[16];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(kl + koff[ks]);
-      const bf16x8 a1 = *(const bf16x8*)(kl + 32 * 256 + koff[ks]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
+      ak[2 * ks] = *(const bf16x8*)(kl + koff[ks]);
+      ak[2 * ks + 1] = *(const bf16x8*)(kl + 32 * 256 + koff[ks]);
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[2 * ks], qreg[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[2 * ks + 1], qreg[ks], s1, 0, 0, 0);
+    }
+    // each K operand read kSAhead products ahead of its MFMA
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kSAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 16 - kSAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kSAhead, 0);
   };
 
   // ---- reference max.  Every unselected block j contributes n_j 2^(x_j) with

@@ -82,21 +82,38 @@ __device__ __forceinline__ void v_operand_offsets(int lane, int (&voff)[4]) {
   }
 }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+// The V^T operand of each PV product is read this many products ahead, so that the LDS
+// latency overlaps the products before it (the scheduler otherwise places each read just
+// before its MFMA under the register limit of two waves per SIMD).
+constexpr int kPvAhead = 4;
+
 // O^T += V^T P^T for one 64-key tile: pa[st] holds keys 16 st + 8 (e / 4) + 4 kg + e % 4
 // (e = 0..7) of the lane's query column, the same key order as the transposed V read.
 __device__ __forceinline__ void pv_tile(floatx16 (&o)[4], const unsigned char* Vl, const int (&voff)[4],
                                         const bf16x8 (&pa)[4]) {
+  uint4v av[16];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int vo = voff[mt] + st * 16 * 256;
-      const uint2v lo = lds_read_tr16(Vl + vo);
-      const uint2v hi = lds_read_tr16(Vl + vo + 8 * 256);
-      const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
-      o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], o[mt], 0, 0, 0);
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int mt = i >> 2, st = i & 3;
+    const int vo = voff[mt] + st * 16 * 256;
+    const uint2v lo = lds_read_tr16(Vl + vo);
+    const uint2v hi = lds_read_tr16(Vl + vo + 8 * 256);
+    av[i] = uint4v{lo[0], lo[1], hi[0], hi[1]};
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int mt = i >> 2, st = i & 3;
+    o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]), pa[st], o[mt], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 16 - kPvAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvAhead, 0);
 }
 
 }  // namespace solattn
