@@ -94,6 +94,15 @@ __device__ __forceinline__ void wait_vm8() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l's
@@ -121,6 +130,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset,
                                           unsigned char* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 16, voffset, soffset, 0, 0);
+}
+
+// buffer_load_dword ... lds: 4 bytes per lane from rsrc + soffset + voffset to
+// lds_base + 4 lane (lds_base wave-uniform); lanes outside the buffer store zeros.
+__device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t soffset,
+                                         unsigned char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 4, voffset, soffset, 0, 0);
 }
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));

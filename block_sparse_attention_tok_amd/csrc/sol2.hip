@@ -370,15 +370,64 @@ hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStr
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2a: routing and the complementary tail of every anchor (draft, Method,
-// Eq. (1)).  One workgroup (two waves) per (b, h, 32 consecutive query blocks);
-// wave w's lane column n = lane % 32 is anchor n of query blocks i0 + 16 w ..
-// i0 + 16 w + 15 (query block i0 + 16 w + n / 2, half n % 2).  Tiles of 16 key
-// blocks (32 groups) stream through LDS, each row a group's bf16 mean key then
-// mean value:
-//   routing  s-hat_ij = Q-bar_i . K-bar_j / sqrt(d) (fp32, dequantized means) for the
-//            32 x 16 (query block, key block) pairs; the bits are written to `sel`
-//            for the exact pass;
+// Stage 2a: routing (draft, Method, Eq. (1) selection): s-hat_ij = Q-bar_i . K-bar_j /
+// sqrt(d) in fp32 from the dequantized block means, against tau_i, with the sink's
+// blocks forced exact.  One workgroup (four waves) per (b, h, 16 query blocks, 64-block
+// chunk c); wave w holds query blocks i0 + 4 w .. i0 + 4 w + 3 and lane l key block
+// 64 c + l, so each query block's routing word for the chunk is one ballot.
+// ---------------------------------------------------------------------------
+struct Route2Args {
+  int nb, nbp, nbw;
+  const float* qbar; const float* kbar_t; const float* tau_i;
+  int sink_b0, sink_b1;
+  uint64_t* sel;
+};
+
+__global__ __launch_bounds__(256) void sol2_route_kernel(Route2Args a) {
+  __shared__ __attribute__((aligned(16))) float qb_s[16][kDim];
+  const int c = blockIdx.x, i0 = blockIdx.y * 16, bh = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < 16 * 32; e += 256) {
+    const int r = e >> 5, c4 = e & 31;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i0 + r < a.nb) x = ((const float4*)(a.qbar + ((size_t)bh * a.nbp + i0 + r) * kDim))[c4];
+    ((float4*)qb_s[r])[c4] = x;
+  }
+  __syncthreads();
+  const int j = 64 * c + lane;
+  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp + j;   // dims 4 d4 .. 4 d4 + 3
+  float acc[4][2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) acc[p][0] = acc[p][1] = 0.f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll 4
+    for (int d4 = 16 * half; d4 < 16 * half + 16; ++d4) {
+      const float4 kk = kt[(size_t)d4 * a.nbp];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float4 qv = *(const float4*)(qb_s[4 * w + p] + 4 * d4);
+        acc[p][half] += qv.x * kk.x + qv.y * kk.y + qv.z * kk.z + qv.w * kk.w;
+      }
+    }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = i0 + 4 * w + p;
+    const float s_hat = (acc[p][0] + acc[p][1]) * kScale2;
+    const bool sel = i < a.nb && j < a.nb &&
+                     (s_hat > a.tau_i[(size_t)bh * a.nbp + min(i, a.nb - 1)] || (j >= a.sink_b0 && j <= a.sink_b1));
+    const uint64_t bits = __ballot(sel);
+    if (lane == 0 && i < a.nb) a.sel[((size_t)bh * a.nb + i) * a.nbw + c] = bits;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2b: the complementary tail of every anchor (draft, Method, Eq. (1)).  One
+// workgroup (two waves) per (b, h, 32 consecutive query blocks); wave w's lane column
+// n = lane % 32 is anchor n of query blocks i0 + 16 w .. i0 + 16 w + 15 (query block
+// i0 + 16 w + n / 2, half n % 2).  Tiles of 16 key blocks (32 groups) stream through
+// LDS two tiles ahead, each row a group's bf16 mean key then mean value, with ln n_g of
+// the tile's groups and the routing words of its chunk:
 //   scores   l_ga = ln n_g + q-bar_a . k-bar_g / sqrt(d) on v_mfma_f32_32x32x16_bf16
 //            (A = the group rows, B = the anchors), masked to groups of blocks the
 //            anchor's query block did not select; online log-sum-exp per anchor;
@@ -394,42 +443,30 @@ __device__ __forceinline__ int swz_g(int r) { return ((r & 3) << 2) | ((r >> 2) 
 
 struct Tail2Args {
   int B, N, H, nb, nbp, nbw;
-  const float* qbar; const float* kbar_t; const float* tau_i; const float* qanc;
+  const float* qanc;
   const uint16_t* gk; const uint16_t* gv; const float* glogn;
-  int sink_b0, sink_b1;
-  uint64_t* sel; float* tmu; float* tnu; float* tlz;
+  const uint64_t* sel;
+  float* tmu; float* tnu; float* tlz;
 };
 
+constexpr int kTailBufs = 3;               // tiles in flight: the one computed and two more
+constexpr int kTailDmaPerTile = 10;        // buffer loads per wave per tile
+
 __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
-  // rows padded by 4 floats: the 16 key blocks (and 4 query blocks) a wave reads at one
-  // dim offset fall on distinct LDS banks
-  __shared__ __attribute__((aligned(16))) float qb_s[32][kDim + 4];
-  // Double-buffered tiles, filled by buffer DMA: the 32 group mean keys and mean values
-  // (32 rows x 256 B each, 16-byte slots swizzled by swz_g so that both the row reads of
-  // the scores and the transposed reads of the means are conflict-free) and the 16 key
-  // block means of the routing, stored [dim / 4][key block] (one 256-byte row per 4 dims).
-  __shared__ __attribute__((aligned(1024))) unsigned char Gk_s[2][32 * 256];
-  __shared__ __attribute__((aligned(1024))) unsigned char Gv_s[2][32 * 256];
-  __shared__ __attribute__((aligned(1024))) float4 kbT_s[2][32][16];
-  __shared__ float tau_s[32];
-  __shared__ uint32_t selw_s[32];        // routing bits of the tile (16 key blocks) per query block
-  __shared__ uint64_t selacc_s[32];      // routing bits of the current 64-block chunk
-  __shared__ float gl_s[32];             // ln n_g of the tile's groups (-inf: empty or padding)
+  // Per buffer, filled by buffer DMA: the 32 group mean keys and mean values (32 rows x
+  // 256 B each, 16-byte slots swizzled by swz_g so that both the row reads of the scores
+  // and the transposed reads of the means are conflict-free); ln n_g of the tile's groups
+  // (wave w brings groups 16 w .. 16 w + 15 into gl_s[.][w]); the routing words of the
+  // tile's 64-block chunk as 32-bit halves (wave w brings query blocks 16 w .. 16 w + 15
+  // into sw_s[.][w]).  Lanes past those ranges read outside the buffer and store zeros
+  // in the unused tail of each row.
+  __shared__ __attribute__((aligned(1024))) unsigned char Gk_s[kTailBufs][32 * 256];
+  __shared__ __attribute__((aligned(1024))) unsigned char Gv_s[kTailBufs][32 * 256];
+  __shared__ __attribute__((aligned(256))) float gl_s[kTailBufs][2][64];
+  __shared__ __attribute__((aligned(256))) uint32_t sw_s[kTailBufs][2][64];
 
   const int bh = blockIdx.y, i0 = blockIdx.x * 32;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
-  const int nqb = min(32, a.nb - i0);
-
-  for (int e = tid; e < 32 * 32; e += 128) {
-    const int r = e >> 5, c4 = e & 31;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < nqb) x = ((const float4*)(a.qbar + ((size_t)bh * a.nbp + i0 + r) * kDim))[c4];
-    ((float4*)qb_s[r])[c4] = x;
-  }
-  if (tid < 32) {
-    tau_s[tid] = tid < nqb ? a.tau_i[(size_t)bh * a.nbp + i0 + tid] : 0.f;
-    selacc_s[tid] = 0ull;
-  }
 
   // Anchor means as the bf16 B operand: qa[ks] = dims 16 ks + 8 kg .. + 7 of anchor l32.
   const int qr = 16 * w + (l32 >> 1);                    // local query block of the anchor
@@ -463,98 +500,59 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   for (int ks = 0; ks < 8; ++ks) goff[ks] = l32 * 256 + 16 * ((2 * ks + kg) ^ swz_g(l32));
 
   // DMA of tile t (key blocks 16 t .. 16 t + 15) into buffer `buf`: wave w, instruction n
-  // fills 1 KB segment 4 w + n of each array.  Group rows r = 16 w + 4 n + lane / 16 (slot
-  // lane % 16 holds logical chunk (lane % 16) ^ swz_g(r)); key-block means: dims
-  // 4 (16 w + 4 n + lane / 16) .. + 3 of key block lane % 16.
+  // fills 1 KB segment 4 w + n of each group array (rows r = 16 w + 4 n + lane / 16; slot
+  // lane % 16 holds logical chunk (lane % 16) ^ swz_g(r)), then one dword per lane of
+  // ln n_g and of the routing words.
   const uint32_t grow = (uint32_t)(16 * w + (lane >> 4));
   uint32_t gdma[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) gdma[n] = (grow + 4 * n) * 256 + 16 * ((lane & 15) ^ swz_g(grow + 4 * n));
-  const uint32_t kdma = (grow * a.nbp + (lane & 15)) * 16;
+  constexpr uint32_t kPastEnd = 0x80000000u;             // beyond every buffer's range: reads zero
+  const uint32_t gldma = lane < 16 ? (uint32_t)(16 * w + lane) * 4 : kPastEnd;
+  const uint32_t swdma = lane < 32 ? ((uint32_t)(i0 + 16 * w + (lane >> 1)) * a.nbw * 8 + 4 * (lane & 1)) : kPastEnd;
+  const int ntiles = a.nbp / 16;
   auto issue_tile = [&](int t, int buf) {
     const uint32_t gbytes = (uint32_t)a.nbp * 2 * 256;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(a.gk + (size_t)bh * a.nbp * 2 * kDim), gbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(a.gv + (size_t)bh * a.nbp * 2 * kDim), gbytes);
-    const __amdgpu_buffer_rsrc_t rt =
-        make_rsrc(uniform_ptr(a.kbar_t + (size_t)bh * 32 * a.nbp * 4), (uint32_t)a.nbp * 32 * 16);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(uniform_ptr(a.glogn + (size_t)bh * a.nbp * 2), (uint32_t)a.nbp * 2 * 4);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(uniform_ptr(a.sel + (size_t)bh * a.nb * a.nbw), (uint32_t)a.nb * a.nbw * 8);
     const uint32_t toff_g = (uint32_t)t * 32 * 256;          // 32 group rows per tile
-    const uint32_t toff_k = (uint32_t)t * 16 * 16;           // 16 key blocks per tile
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       dma16_buf(rk, toff_g + gdma[n], 0, Gk_s[buf] + 1024 * (4 * w + n));
       dma16_buf(rv, toff_g + gdma[n], 0, Gv_s[buf] + 1024 * (4 * w + n));
-      dma16_buf(rt, toff_k + kdma + (uint32_t)(4 * n) * a.nbp * 16, 0, (unsigned char*)kbT_s[buf] + 1024 * (4 * w + n));
     }
-  };
-  float glr = kNegInf;                                    // ln n_g of the next tile (lanes 0..31)
-  auto load_gl = [&](int t) {
-    if (tid < 32) glr = 16 * t + (tid >> 1) < a.nb ? a.glogn[((size_t)bh * a.nbp + 16 * t) * 2 + tid] : kNegInf;
+    dma4_buf(rl, lane < 16 ? (uint32_t)t * 32 * 4 + gldma : kPastEnd, 0, (unsigned char*)gl_s[buf][w]);
+    dma4_buf(rs, lane < 32 ? (uint32_t)(t >> 2) * 8 + swdma : kPastEnd, 0, (unsigned char*)sw_s[buf][w]);
   };
 
   floatx16 num[8];                                        // rows: dims (0..127 mu, 128..255 nu); cols: anchors
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) num[mt] = floatx16{};
   float m_run = kNegInf, z_run = 0.f;
-  const int ntiles = a.nbp / 16;
   issue_tile(0, 0);
-  load_gl(0);
+  if (ntiles > 1) issue_tile(1, 1);
   for (int t = 0; t < ntiles; ++t) {
-    const int j0 = 16 * t, buf = t & 1;
-    wait_vm0();
-    lds_barrier();                                        // tile t landed; the other buffer is free
-    if (tid < 32) gl_s[tid] = glr;
-    if (t + 1 < ntiles) {
-      issue_tile(t + 1, buf ^ 1);                         // lands while this tile computes
-      load_gl(t + 1);
-    }
-    // ---- routing: key block j0 + (tid % 16) against query blocks tid / 16 + 8 p
-    {
-      const int jl = tid & 15, j = j0 + jl;
-      float acc[4][2];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) acc[p][0] = acc[p][1] = 0.f;
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll 4
-        for (int d4 = 16 * half; d4 < 16 * half + 16; ++d4) {
-          const float4 kk = kbT_s[buf][d4][jl];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const float4 qv = *(const float4*)(qb_s[(tid >> 4) + 8 * p] + 4 * d4);
-            acc[p][half] += qv.x * kk.x + qv.y * kk.y + qv.z * kk.z + qv.w * kk.w;
-          }
-        }
-      // lanes 16 g .. 16 g + 15 of the wave hold key blocks 0..15 of query block r: the
-      // ballot's 16-bit field g is r's routing word for the tile
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int r = (tid >> 4) + 8 * p;
-        const float s_hat = (acc[p][0] + acc[p][1]) * kScale2;
-        const bool sel = r < nqb && j < a.nb && (s_hat > tau_s[r] || (j >= a.sink_b0 && j <= a.sink_b1));
-        const uint64_t bits = __ballot(sel);
-        if (jl == 0) selw_s[r] = (uint32_t)(bits >> (lane & 48)) & 0xffffu;
-      }
-    }
-    lds_barrier();
-    if (tid < 32) {
-      selacc_s[tid] |= (uint64_t)selw_s[tid] << (j0 & 63);
-      if ((t & 3) == 3) {
-        if (tid < nqb) a.sel[((size_t)bh * a.nb + i0 + tid) * a.nbw + (j0 >> 6)] = selacc_s[tid];
-        selacc_s[tid] = 0ull;
-      }
-    }
+    const int j0 = 16 * t, buf = t % kTailBufs;
+    if (t + 1 < ntiles) wait_vm<kTailDmaPerTile>();         // tile t landed (tile t + 1 may be in flight)
+    else wait_vm0();
+    lds_barrier();                                        // every wave's part of tile t; buffer of t - 1 free
+    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % kTailBufs);
     // ---- tail scores of the tile's 32 groups against the wave's 32 anchors
     floatx16 s = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(Gk_s[buf] + goff[ks]), qa[ks], s, 0, 0, 0);
-    const uint32_t mine = selw_s[qr];
+    // routing bits of the anchor's query block for the tile's 16 key blocks
+    const uint32_t mine = (sw_s[buf][w][2 * (qr & 15) + ((t >> 1) & 1)] >> (16 * (t & 1))) & 0xffffu;
     float mx = kNegInf;
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       const int g = 8 * (idx >> 2) + 4 * kg + (idx & 3);  // group row of the tile
-      const bool tail = !((mine >> (g >> 1)) & 1);
-      s[idx] = tail ? (s[idx] * kScale2 + gl_s[g]) * kLog2e : kNegInf;
+      const bool tail = !((mine >> (g >> 1)) & 1) && j0 + (g >> 1) < a.nb;
+      s[idx] = tail ? (s[idx] * kScale2 + gl_s[buf][g >> 4][g & 15]) * kLog2e : kNegInf;
       mx = fmaxf(mx, s[idx]);
     }
     mx = max_with_partner(mx);
@@ -609,18 +607,25 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
 }
 
 hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream) {
+  Route2Args r;
+  r.nb = ws.nb; r.nbp = ws.nbp; r.nbw = ws.nbp / 64;
+  r.qbar = ws.qbar; r.kbar_t = ws.kbar_t; r.tau_i = ws.tau_i;
+  r.sink_b0 = sink_b0; r.sink_b1 = sink_b1;
+  r.sel = ws.sel;
+  hipLaunchKernelGGL(sol2_route_kernel, dim3(ws.nbp / 64, (ws.nb + 15) / 16, s.B * s.H), dim3(256), 0, stream, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   Tail2Args a;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = ws.nbp / 64;
-  a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.tau_i = ws.tau_i; a.qanc = ws.qanc;
+  a.qanc = ws.qanc;
   a.gk = ws.gk; a.gv = ws.gv; a.glogn = ws.glogn;
-  a.sink_b0 = sink_b0; a.sink_b1 = sink_b1;
   a.sel = ws.sel; a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
   hipLaunchKernelGGL(sol2_tail_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2b: exact FP8 attention over the selected blocks, combined with the tail.
+// Stage 2c: exact FP8 attention over the selected blocks, combined with the tail.
 // One workgroup per (b, h, query block i), two wave64s; wave w owns query rows
 // 32 w .. 32 w + 31, which are exactly anchor a = (i, w).
 //   * The selected blocks (the routing bits of stage 2a) stream through LDS: the
