@@ -464,6 +464,7 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Gv_s[kTailBufs][32 * 256];
   __shared__ __attribute__((aligned(256))) float gl_s[kTailBufs][2][64];
   __shared__ __attribute__((aligned(256))) uint32_t sw_s[kTailBufs][2][64];
+  __shared__ int redo_s[2];
 
   const int bh = blockIdx.y, i0 = blockIdx.x * 32;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
@@ -529,56 +530,84 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   };
 
   floatx16 num[8];                                        // rows: dims (0..127 mu, 128..255 nu); cols: anchors
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) num[mt] = floatx16{};
   float m_run = kNegInf, z_run = 0.f;
-  issue_tile(0, 0);
-  if (ntiles > 1) issue_tile(1, 1);
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = 16 * t, buf = t % kTailBufs;
-    if (t + 1 < ntiles) wait_vm<kTailDmaPerTile>();         // tile t landed (tile t + 1 may be in flight)
-    else wait_vm0();
-    lds_barrier();                                        // every wave's part of tile t; buffer of t - 1 free
-    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % kTailBufs);
-    // ---- tail scores of the tile's 32 groups against the wave's 32 anchors
-    floatx16 s = {};
+  // One pass over the tiles.  kSafe = false: the anchor's first tile with a tail group
+  // fixes the reference m (its largest tail logit) and every weight is 2^(l - m) with no
+  // rescaling of the 128 accumulators; kSafe = true: running maximum with the rescale.
+  auto run_tiles = [&](auto safe_tag) {
+    constexpr bool kSafe = decltype(safe_tag)::value;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(Gk_s[buf] + goff[ks]), qa[ks], s, 0, 0, 0);
-    // routing bits of the anchor's query block for the tile's 16 key blocks
-    const uint32_t mine = (sw_s[buf][w][2 * (qr & 15) + ((t >> 1) & 1)] >> (16 * (t & 1))) & 0xffffu;
-    float mx = kNegInf;
+    for (int mt = 0; mt < 8; ++mt) num[mt] = floatx16{};
+    m_run = kNegInf;
+    z_run = 0.f;
+    issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(1, 1);
+    for (int t = 0; t < ntiles; ++t) {
+      const int j0 = 16 * t, buf = t % kTailBufs;
+      if (t + 1 < ntiles) wait_vm<kTailDmaPerTile>();     // tile t landed (tile t + 1 may be in flight)
+      else wait_vm0();
+      lds_barrier();                                      // every wave's part of tile t; buffer of t - 1 free
+      if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % kTailBufs);
+      // ---- tail scores of the tile's 32 groups against the wave's 32 anchors
+      floatx16 s = {};
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const int g = 8 * (idx >> 2) + 4 * kg + (idx & 3);  // group row of the tile
-      const bool tail = !((mine >> (g >> 1)) & 1) && j0 + (g >> 1) < a.nb;
-      s[idx] = tail ? (s[idx] * kScale2 + gl_s[buf][g >> 4][g & 15]) * kLog2e : kNegInf;
-      mx = fmaxf(mx, s[idx]);
-    }
-    mx = max_with_partner(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    z_run *= alpha;
+      for (int ks = 0; ks < 8; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(Gk_s[buf] + goff[ks]), qa[ks], s, 0, 0, 0);
+      // routing bits of the anchor's query block for the tile's 16 key blocks
+      const uint32_t mine = (sw_s[buf][w][2 * (qr & 15) + ((t >> 1) & 1)] >> (16 * (t & 1))) & 0xffffu;
+      float mx = kNegInf;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int idx = 0; idx < 16; ++idx) num[mt][idx] *= alpha;
-    m_run = m_new;
-    bf16x8 pa[2];
-#pragma unroll
-    for (int idx = 0; idx < 16; ++idx) pa[idx >> 3][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s[idx] - m_use);
-    z_run = add_bf16x8(pa[1], add_bf16x8(pa[0], z_run));  // the bf16 weights of the numerators
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const unsigned char* gt = mt < 4 ? Gk_s[buf] : Gv_s[buf];   // m-tiles 0..3: mu dims, 4..7: nu
-        const uint2v lo = lds_read_tr16(gt + toff[mt & 3][0] + st * 16 * 256);
-        const uint2v hi = lds_read_tr16(gt + toff[mt & 3][1] + st * 16 * 256);
-        const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
-        num[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], num[mt], 0, 0, 0);
+      for (int idx = 0; idx < 16; ++idx) {
+        const int g = 8 * (idx >> 2) + 4 * kg + (idx & 3);  // group row of the tile
+        const bool tail = !((mine >> (g >> 1)) & 1) && j0 + (g >> 1) < a.nb;
+        s[idx] = tail ? (s[idx] * kScale2 + gl_s[buf][g >> 4][g & 15]) * kLog2e : kNegInf;
+        mx = fmaxf(mx, s[idx]);
       }
+      mx = max_with_partner(mx);
+      float m_use;
+      if constexpr (kSafe) {
+        const float m_new = fmaxf(m_run, mx);
+        m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        z_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int idx = 0; idx < 16; ++idx) num[mt][idx] *= alpha;
+        m_run = m_new;
+      } else {
+        m_run = m_run == kNegInf ? mx : m_run;
+        m_use = m_run == kNegInf ? 0.f : m_run;
+      }
+      bf16x8 pa[2];
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) pa[idx >> 3][idx & 7] = (__bf16)__builtin_amdgcn_exp2f(s[idx] - m_use);
+      z_run = add_bf16x8(pa[1], add_bf16x8(pa[0], z_run));  // the bf16 weights of the numerators
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const unsigned char* gt = mt < 4 ? Gk_s[buf] : Gv_s[buf];   // m-tiles 0..3: mu dims, 4..7: nu
+          const uint2v lo = lds_read_tr16(gt + toff[mt & 3][0] + st * 16 * 256);
+          const uint2v hi = lds_read_tr16(gt + toff[mt & 3][1] + st * 16 * 256);
+          const uint4v av = {lo[0], lo[1], hi[0], hi[1]};
+          num[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pa[st], num[mt], 0, 0, 0);
+        }
+    }
+  };
+  run_tiles(BoolTag<false>{});
+  {
+    // A weight or sum that overflowed the fixed reference (a tail logit more than ~2^127
+    // above it): redo the workgroup's tiles with the running maximum.
+    float chk = z_run * 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) chk = __builtin_fmaf(num[mt][idx], 0.f, chk);
+    const bool bad = __ballot(!(chk == 0.f)) != 0;
+    if (lane == 0) redo_s[w] = bad;
+    __syncthreads();                                      // also: every wave is past its last tile
+    if (redo_s[0] | redo_s[1]) run_tiles(BoolTag<true>{});
   }
 
   // ---- anchor results: mu_a, nu_a and log2 Z_a - log2(e) q-bar_a . mu_a / sqrt(d)

@@ -152,3 +152,19 @@ def test_maximum_sequence_length():
     the head in full, sampled output rows including the last block."""
     q, k, v = _qkv(1, 524288, 1, 2600)
     run_case(q, k, v, 1.28, sample=2, seed=7)
+
+
+def test_tail_logit_far_above_the_first_tiles():
+    """Key block 40 holds +-300 e_0 in alternate tokens: its block mean is zero, so it stays in
+    the tail, while its upper group (the keys along the mean query, e_0) scores about 380 log2
+    units above the tail groups of the first tiles for queries with q_0 = 10.  The tail pass's
+    fixed reference then overflows and the workgroup is redone with the running maximum; the
+    result still matches the oracle."""
+    B, N, H = 1, 4096, 1
+    q, k, v = _qkv(B, N, H, 3000)
+    q[..., 0] = 10.0
+    blk = 40
+    k[0, blk * 64:(blk + 1) * 64, 0, :] = 0.0
+    k[0, blk * 64:(blk + 1) * 64, 0, 0] = 300.0 * torch.tensor([1.0, -1.0]).repeat(32)
+    out, masks, _ = run_case(q, k, v, 1.0)
+    assert (~masks[0, 0, :, blk]).sum() >= 8, "block 40 is meant to stay in the tail"
