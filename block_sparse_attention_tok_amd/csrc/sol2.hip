@@ -371,10 +371,13 @@ hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStr
 
 // ---------------------------------------------------------------------------
 // Stage 2a: routing (draft, Method, Eq. (1) selection): s-hat_ij = Q-bar_i . K-bar_j /
-// sqrt(d) in fp32 from the dequantized block means, against tau_i, with the sink's
-// blocks forced exact.  One workgroup (four waves) per (b, h, 16 query blocks, 64-block
-// chunk c); wave w holds query blocks i0 + 4 w .. i0 + 4 w + 3 and lane l key block
-// 64 c + l, so each query block's routing word for the chunk is one ballot.
+// sqrt(d) from the dequantized block means, against tau_i, with the sink's blocks forced
+// exact.  One wave per (b, h, 32 query blocks from i0, 64-block chunk c): the 32 x 64
+// products on v_mfma_f32_32x32x2_f32 (fp32 operands and sums), A = the query-block means,
+// B = the key-block means, with the contraction order chosen so that lane (m, kh) reads
+// dims 64 kh .. 64 kh + 63 of its row contiguously (k-step s takes dim 64 kh + s).  The
+// accumulator of row i holds key blocks 32 t + n in lane n (+ 32 for rows i + 4), so one
+// ballot per row pair gives the routing bits of two query blocks.
 // ---------------------------------------------------------------------------
 struct Route2Args {
   int nb, nbp, nbw;
@@ -383,41 +386,47 @@ struct Route2Args {
   uint64_t* sel;
 };
 
-__global__ __launch_bounds__(256) void sol2_route_kernel(Route2Args a) {
-  __shared__ __attribute__((aligned(16))) float qb_s[16][kDim];
-  const int c = blockIdx.x, i0 = blockIdx.y * 16, bh = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int e = tid; e < 16 * 32; e += 256) {
-    const int r = e >> 5, c4 = e & 31;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i0 + r < a.nb) x = ((const float4*)(a.qbar + ((size_t)bh * a.nbp + i0 + r) * kDim))[c4];
-    ((float4*)qb_s[r])[c4] = x;
-  }
-  __syncthreads();
-  const int j = 64 * c + lane;
-  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp + j;   // dims 4 d4 .. 4 d4 + 3
-  float acc[4][2];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) acc[p][0] = acc[p][1] = 0.f;
-#pragma unroll
-  for (int half = 0; half < 2; ++half)
+__global__ __launch_bounds__(64) void sol2_route_kernel(Route2Args a) {
+  const int c = blockIdx.x, i0 = blockIdx.y * 32, bh = blockIdx.z;
+  const int lane = threadIdx.x, m = lane & 31, kh = lane >> 5;
+  // rows i0 + m < nbp and key blocks 64 c + 63 < nbp: padding rows / blocks are in memory
+  const float4* qa = (const float4*)(a.qbar + ((size_t)bh * a.nbp + i0 + m) * kDim) + 16 * kh;
+  const float4* kb = (const float4*)a.kbar_t + ((size_t)bh * 32 + 16 * kh) * a.nbp + 64 * c + m;
+  floatx16 acc[2] = {floatx16{}, floatx16{}};               // key blocks 64 c + 32 t + n
 #pragma unroll 4
-    for (int d4 = 16 * half; d4 < 16 * half + 16; ++d4) {
-      const float4 kk = kt[(size_t)d4 * a.nbp];
+  for (int cc = 0; cc < 16; ++cc) {
+    const float4 x = qa[cc];
+    const float4 y0 = kb[(size_t)cc * a.nbp];
+    const float4 y1 = kb[(size_t)cc * a.nbp + 32];
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y0.x, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y1.x, acc[1], 0, 0, 0);
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y0.y, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y1.y, acc[1], 0, 0, 0);
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y0.z, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y1.z, acc[1], 0, 0, 0);
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y0.w, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y1.w, acc[1], 0, 0, 0);
+  }
+  const bool sink[2] = {64 * c + m >= a.sink_b0 && 64 * c + m <= a.sink_b1,
+                        64 * c + 32 + m >= a.sink_b0 && 64 * c + 32 + m <= a.sink_b1};
+  const bool kvalid[2] = {64 * c + m < a.nb, 64 * c + 32 + m < a.nb};
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float4 qv = *(const float4*)(qb_s[4 * w + p] + 4 * d4);
-        acc[p][half] += qv.x * kk.x + qv.y * kk.y + qv.z * kk.z + qv.w * kk.w;
-      }
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + 8 * (r >> 2) + 4 * kh + (r & 3);     // this lane's query block in row r
+    const float tau = a.tau_i[(size_t)bh * a.nbp + i];
+    uint64_t bits[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float s_hat = acc[t][r] * kScale2;
+      bits[t] = __ballot(i < a.nb && kvalid[t] && (s_hat > tau || sink[t]));
     }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int i = i0 + 4 * w + p;
-    const float s_hat = (acc[p][0] + acc[p][1]) * kScale2;
-    const bool sel = i < a.nb && j < a.nb &&
-                     (s_hat > a.tau_i[(size_t)bh * a.nbp + min(i, a.nb - 1)] || (j >= a.sink_b0 && j <= a.sink_b1));
-    const uint64_t bits = __ballot(sel);
-    if (lane == 0 && i < a.nb) a.sel[((size_t)bh * a.nb + i) * a.nbw + c] = bits;
+    if (lane == 0) {
+      const int ilo = i0 + 8 * (r >> 2) + (r & 3);          // rows ilo (lanes 0..31) and ilo + 4
+      const uint64_t wlo = (bits[1] << 32) | (bits[0] & 0xffffffffull);
+      const uint64_t whi = (bits[1] & 0xffffffff00000000ull) | (bits[0] >> 32);
+      if (ilo < a.nb) a.sel[((size_t)bh * a.nb + ilo) * a.nbw + c] = wlo;
+      if (ilo + 4 < a.nb) a.sel[((size_t)bh * a.nb + ilo + 4) * a.nbw + c] = whi;
+    }
   }
 }
 
@@ -641,7 +650,7 @@ hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, 
   r.qbar = ws.qbar; r.kbar_t = ws.kbar_t; r.tau_i = ws.tau_i;
   r.sink_b0 = sink_b0; r.sink_b1 = sink_b1;
   r.sel = ws.sel;
-  hipLaunchKernelGGL(sol2_route_kernel, dim3(ws.nbp / 64, (ws.nb + 15) / 16, s.B * s.H), dim3(256), 0, stream, r);
+  hipLaunchKernelGGL(sol2_route_kernel, dim3(ws.nbp / 64, (ws.nb + 31) / 32, s.B * s.H), dim3(64), 0, stream, r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   Tail2Args a;
