@@ -38,7 +38,8 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov", "kpart",
         "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse",
-        "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale", "lse", "mrow", "mcol", "ld", "dkbar", "dvbar")]
+        "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale", "lse", "mrow", "mcol", "ld", "dkbar", "dvbar",
+        "kh", "vh")]
 
 
 class SolAttnError(RuntimeError):
@@ -362,8 +363,10 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
         nb=L.nb, nbp=nbp,
         qbar=view(L.qbar, torch.float32, (batch, heads, nbp, 128)),
         kbar_t=view(L.kbar_t, torch.float32, (batch, heads, 32, nbp, 4)),
-        kbar_h=view(L.kbar_h, torch.bfloat16, (batch, nbp, heads, 128)).transpose(1, 2),
-        vbar_h=view(L.vbar_h, torch.bfloat16, (batch, nbp, heads, 128)).transpose(1, 2),
+        kbar_h=view(L.kbar_h, torch.bfloat16, (batch, heads, nbp, 128)),
+        vbar_h=view(L.vbar_h, torch.bfloat16, (batch, heads, nbp, 128)),
+        kh=view(L.kh, torch.bfloat16, (batch, heads, tokens, 128)),
+        vh=view(L.vh, torch.bfloat16, (batch, heads, tokens, 128)),
         tau_i=view(L.tau_i, torch.float32, (batch, heads, nbp)),
         kstat=view(L.kstat, torch.float32, (batch, heads, 2, 128)),
         kcov=view(L.kcov, torch.float32, (batch, heads, 128, 128)),

@@ -81,6 +81,11 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   L->kstat = take(bh * 2 * kDim * 4);
   L->kcov = take(bh * kDim * kDim * 4);
   L->kpart = take(bh * 16 * 2 * kDim * 8);
+  // Sol-Attn: head-major copies of K and V written by stage 1, the tile source of stage 2
+  if (variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN) {
+    L->kh = take(bh * tokens * kDim * 2);
+    L->vh = take(bh * tokens * kDim * 2);
+  }
   if (variant == SOL_VARIANT_SOL2 || variant == SOL_VARIANT_SOL2_PV8) {
     const int64_t tp = nbp * kBlock;
     L->q8 = take(bh * tp * kDim);
@@ -133,6 +138,8 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.qbar = (float*)at(L.qbar);
   w.kbar_t = (float*)at(L.kbar_t);
   w.kbar_h = (uint16_t*)at(L.kbar_h);
+  w.kh = (uint16_t*)at(L.kh);
+  w.vh = (uint16_t*)at(L.vh);
   w.vbar_h = (uint16_t*)at(L.vbar_h);
   w.tau_i = (float*)at(L.tau_i);
   w.kstat = (float*)at(L.kstat);

@@ -47,7 +47,8 @@ struct BwdArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* out; const uint16_t* dout;
   uint16_t* dq; uint16_t* dk; uint16_t* dv;
   int B, N, H, nb, nbp, nbw, tp;
-  const uint16_t* kbar_h; const uint16_t* vbar_h;
+  const uint16_t* kbar_h; const uint16_t* vbar_h;   // [B][H][nbp][128]
+  const uint16_t* kh; const uint16_t* vh;           // head-major copies of k and v ([B][H][N][128])
   const float* lse;
   const uint64_t* mrow; uint64_t* mcol;
   float* ld;
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t rs = (size_t)a.H * kDim;
   const size_t head_off = (size_t)b * a.N * rs + (size_t)h * kDim;
-  const size_t pooled_head = ((size_t)b * a.nbp * a.H + h) * kDim;
+  const size_t pooled_head = (size_t)bh * a.nbp * kDim;
 
   // the lane's key column: token 64 jb + 32 w + l32, or pooled key 64 c + 32 w + l32
   const int key = (kPooled ? 64 * c : 64 * jb) + 32 * w + l32;
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
   const float bias = kPooled ? (key == a.nb - 1 ? __log2f((float)last_n) : 6.0f) : 0.f;
   bf16x8 kreg[8], vreg[8];
   if constexpr (kPooled) {
-    load_row_frags(a.kbar_h + pooled_head + (size_t)key * rs, kreg, kg);
-    load_row_frags(a.vbar_h + pooled_head + (size_t)key * rs, vreg, kg);
+    load_row_frags(a.kbar_h + pooled_head + (size_t)key * kDim, kreg, kg);
+    load_row_frags(a.vbar_h + pooled_head + (size_t)key * kDim, vreg, kg);
   } else {
     const int kr = key_ok ? key : a.N - 1;
     load_row_frags(a.k + head_off + (size_t)kr * rs, kreg, kg);
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t rs = (size_t)a.H * kDim;
   const size_t head_off = (size_t)b * a.N * rs + (size_t)h * kDim;
-  const size_t pooled_head = ((size_t)b * a.nbp * a.H + h) * kDim;
+  const size_t pooled_head = (size_t)bh * a.nbp * kDim;
 
   for (int cc = tid; cc < nchunks; cc += 128) {
     const uint64_t selm = a.mrow[((size_t)bh * a.nb + i) * a.nbw + cc];
@@ -429,9 +430,12 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
   const float dd = a.ld[((size_t)bh * a.tp + qrow) * 2 + 1];
   __syncthreads();
 
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
-  const uint32_t span_in = (uint32_t)((a.N - 1) * rs + kDim) * 2;
-  const uint32_t span_pool = (uint32_t)((a.nbp - 1) * rs + kDim) * 2;
+  // K / V tiles from the head-major copies and the pooled K-bar / V-bar: 256-byte rows,
+  // one head contiguous, rows past the end read as zeros
+  const uint32_t row_bytes = kDim * 2;
+  const uint32_t span_in = (uint32_t)a.N * row_bytes;
+  const uint32_t span_pool = (uint32_t)a.nbp * row_bytes;
+  const size_t kv_head = (size_t)bh * a.N * kDim;
   const DmaOffsetsD doff = dma_offsets_d(row_bytes, w, lane);
   auto issue = [&](int code, int buf) {
     if (code < 0) {
@@ -440,8 +444,8 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
       dma_tile_d(Vl[buf], make_rsrc(uniform_ptr(a.vbar_h + pooled_head), span_pool), toff, row_bytes, doff, w);
     } else {
       const uint32_t toff = (uint32_t)code * 64 * row_bytes;
-      dma_tile_d(Kl[buf], make_rsrc(uniform_ptr(a.k + head_off), span_in), toff, row_bytes, doff, w);
-      dma_tile_d(Vl[buf], make_rsrc(uniform_ptr(a.v + head_off), span_in), toff, row_bytes, doff, w);
+      dma_tile_d(Kl[buf], make_rsrc(uniform_ptr(a.kh + kv_head), span_in), toff, row_bytes, doff, w);
+      dma_tile_d(Vl[buf], make_rsrc(uniform_ptr(a.vh + kv_head), span_in), toff, row_bytes, doff, w);
     }
   };
   // tile order: per chunk, the pooled tile (code -(c + 1)) if the chunk has unselected
@@ -540,14 +544,15 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
 hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,
                            const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, Shape s,
                            const Workspace& ws, hipStream_t stream) {
-  if (!ws.lse || !ws.mrow || !ws.mcol || !ws.ld || !ws.dkbar || !ws.dvbar) return hipErrorInvalidValue;
+  if (!ws.lse || !ws.mrow || !ws.mcol || !ws.ld || !ws.dkbar || !ws.dvbar || !ws.kh || !ws.vh)
+    return hipErrorInvalidValue;
   const int nchunks = ws.nbp / 64;
   if (nchunks > kMaxChunksB) return hipErrorInvalidValue;
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = nchunks; a.tp = ws.nbp * kBlock;
-  a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h;
+  a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h; a.kh = ws.kh; a.vh = ws.vh;
   a.lse = ws.lse; a.mrow = ws.mrow; a.mcol = ws.mcol; a.ld = ws.ld;
   a.dkbar = ws.dkbar; a.dvbar = ws.dvbar;
   // pooled keys: enough (chunk, query range) workgroups to fill the chip twice over

@@ -53,6 +53,7 @@ struct FusedArgs {
   int S, cps;                   // key-range splits and routing chunks per split
   uint16_t* opart; float* olse; // split partials (S > 1)
   const float* qbar; const float* kbar_t; const uint16_t* kbar_h; const uint16_t* vbar_h;
+  const uint16_t* kh; const uint16_t* vh;   // head-major copies of k and v ([B][H][N][128])
   const float* tau_i;
   int sink_b0, sink_b1;
   uint64_t* mask_out;
@@ -128,13 +129,15 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // Buffer resources over this head's rows of k / v and of the pooled K-bar / V-bar
-  // (stored with the same row stride), so one set of lane offsets serves every
-  // tile; built at each use from kernel arguments so they stay in SGPRs.
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
-  const uint32_t span_in = (uint32_t)((a.N - 1) * rs + kDim) * 2;
-  const uint32_t span_pool = (uint32_t)((a.nbp - 1) * rs + kDim) * 2;
-  const size_t pooled_head = ((size_t)b * a.nbp * a.H + h) * kDim;
+  // Buffer resources over this head's rows of the head-major k / v copies and of the
+  // pooled K-bar / V-bar (both 256-byte rows, one head contiguous), so one set of lane
+  // offsets serves every tile; built at each use from kernel arguments so they stay in
+  // SGPRs.  Rows past the end of either read as zeros.
+  const uint32_t row_bytes = kDim * 2;
+  const uint32_t span_in = (uint32_t)a.N * row_bytes;
+  const uint32_t span_pool = (uint32_t)a.nbp * row_bytes;
+  const size_t pooled_head = (size_t)bh * a.nbp * kDim;
+  const size_t kv_head = (size_t)bh * a.N * kDim;
   const DmaOffsets doff = dma_offsets(row_bytes, w, lane);
   const int c_begin = split * a.cps;                        // this split's routing chunks
   const int c_end = min(a.nbp / 64, c_begin + a.cps);
@@ -232,8 +235,8 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
       return kBlock;
     }
     const uint32_t tile_off = (uint32_t)code * 64 * row_bytes;
-    if (is_v) dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.v + head_off), span_in), tile_off, row_bytes, doff, w);
-    else dma_tile<false>(Kl, make_rsrc(uniform_ptr(a.k + head_off), span_in), tile_off, row_bytes, doff, w);
+    if (is_v) dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.vh + kv_head), span_in), tile_off, row_bytes, doff, w);
+    else dma_tile<false>(Kl, make_rsrc(uniform_ptr(a.kh + kv_head), span_in), tile_off, row_bytes, doff, w);
     return min(kBlock, a.N - code * kBlock);
   };
 
@@ -458,12 +461,13 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const int nchunks = ws.nbp / 64;
   const int S = ws.kv_splits;
   const int cps = (nchunks + S - 1) / S;
-  if (cps > kMaxChunks || (S > 1 && (!ws.opart || !ws.olse))) return hipErrorInvalidValue;
+  if (cps > kMaxChunks || (S > 1 && (!ws.opart || !ws.olse)) || !ws.kh || !ws.vh) return hipErrorInvalidValue;
   FusedArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = (ws.nb + 63) / 64;
   a.S = S; a.cps = cps; a.opart = ws.opart; a.olse = ws.olse;
   a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h; a.tau_i = ws.tau_i;
+  a.kh = ws.kh; a.vh = ws.vh;
   a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
   a.lse = ws.lse; a.tp = ws.nbp * kBlock;
   const int total = s.B * s.H * S * ws.nb;

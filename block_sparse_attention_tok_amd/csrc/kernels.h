@@ -10,8 +10,10 @@ struct Workspace {
   int nb, nbp;
   float* qbar;      // [B][H][nbp][128]
   float* kbar_t;    // [B][H][32][nbp][4]
-  uint16_t* kbar_h; // [B][nbp][H][128] bf16 (row stride H * 128, like the inputs)
-  uint16_t* vbar_h; // [B][nbp][H][128] bf16
+  uint16_t* kbar_h; // [B][H][nbp][128] bf16
+  uint16_t* vbar_h; // [B][H][nbp][128] bf16
+  uint16_t* kh;     // [B][H][N][128] bf16 head-major copy of K (Sol-Attn)
+  uint16_t* vh;     // [B][H][N][128] bf16 head-major copy of V (Sol-Attn)
   float* tau_i;     // [B][H][nbp]
   float* kstat;     // [B][H][2][128]
   float* kcov;      // [B][H][128][128]

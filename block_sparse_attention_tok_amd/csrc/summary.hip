@@ -18,7 +18,8 @@ namespace solattn {
 __global__ __launch_bounds__(256) void summary_kernel(
     const uint4v* __restrict__ q, const uint4v* __restrict__ k, const uint4v* __restrict__ v,
     int N, int H, int nb, int nbp, float* __restrict__ qbar, float* __restrict__ kbar_t,
-    uint4v* __restrict__ kbar_h, uint4v* __restrict__ vbar_h) {
+    uint4v* __restrict__ kbar_h, uint4v* __restrict__ vbar_h, uint4v* __restrict__ kh_out,
+    uint4v* __restrict__ vh_out) {
   extern __shared__ float red[];
   const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int C = 16 * H;                                 // 16-byte chunks per token row
@@ -41,6 +42,11 @@ __global__ __launch_bounds__(256) void summary_kernel(
       for (int t = r; t < n; t += R) {
         const size_t off = base + (size_t)t * rowc + c;
         uint4v a = q[off], bb = k[off], cc = v[off];
+        if (kh_out != nullptr) {   // head-major copies: head c / 16, dims 8 (c % 16) ..
+          const size_t dst = (((size_t)b * H + c / 16) * N + t0 + t) * 16 + (c & 15);
+          kh_out[dst] = bb;
+          vh_out[dst] = cc;
+        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           qs[2 * m] += bf16_lo(a[m]);  qs[2 * m + 1] += bf16_hi(a[m]);
@@ -82,7 +88,7 @@ __global__ __launch_bounds__(256) void summary_kernel(
         kh[m] = pack_bf16x2(kb[2 * m], kb[2 * m + 1]);
         vh[m] = pack_bf16x2(vs[2 * m] * inv_n, vs[2 * m + 1] * inv_n);
       }
-      const size_t prow = ((size_t)b * nbp + j) * H + h;       // [B][nbp][H][128]
+      const size_t prow = bh * nbp + j;                       // [B][H][nbp][128]
       kbar_h[prow * 16 + d8] = kh;
       vbar_h[prow * 16 + d8] = vh;
     }
@@ -97,7 +103,7 @@ hipError_t launch_summary(const uint16_t* q, const uint16_t* k, const uint16_t* 
   dim3 grid(ws.nbp, s.B);
   hipLaunchKernelGGL(summary_kernel, grid, dim3(256), lds, stream, (const uint4v*)q, (const uint4v*)k,
                      (const uint4v*)v, s.N, s.H, ws.nb, ws.nbp, ws.qbar, ws.kbar_t, (uint4v*)ws.kbar_h,
-                     (uint4v*)ws.vbar_h);
+                     (uint4v*)ws.vbar_h, (uint4v*)ws.kh, (uint4v*)ws.vh);
   return hipGetLastError();
 }
 

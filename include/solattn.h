@@ -63,12 +63,14 @@ typedef enum {
  * [batch][head][...] unless shown otherwise.
  *   qbar     float [B][H][nbp][128]   Q block means (Sol-Attn2: of dequantized Q)
  *   kbar_t   float [B][H][32][nbp][4] K block means, 4-dim-interleaved
- *   kbar_h   bf16  [B][nbp][H][128]   K block means (MFMA operand; token-major like the inputs)
- *   vbar_h   bf16  [B][nbp][H][128]   V block means V-hat_j / n_j (MFMA operand)
+ *   kbar_h   bf16  [B][H][nbp][128]   K block means (MFMA operand)
+ *   vbar_h   bf16  [B][H][nbp][128]   V block means V-hat_j / n_j (MFMA operand)
  *   tau_i    float [B][H][nbp]        per-query-block threshold tau_i
  *   kstat    float [B][H][2][128]     mu_K and v_K
  *   kcov     float [B][H][128][128]   covariance of the K block means (EXACT only)
  *   kpart    double [B][H][16][2][128] partial sums of K block means and their squares
+ *   kh, vh   bf16  [B][H][N][128]     Sol-Attn: head-major copies of K and V (stage 1 writes
+ *                                      them; stage 2 and the backward stream tiles from them)
  *   q8, k8   uint8 [B][H][tp][128]    E4M3FN codes (Sol-Attn2)
  *   qscale, kscale float [B][H][nbp]  E4M3 block scales (Sol-Attn2)
  *   qhat     float [B][H][128]        mean-query direction (Sol-Attn2)
@@ -111,6 +113,7 @@ typedef struct {
     int64_t sel, tmu, tnu, tlz;
     int64_t v8t, vbmax, vscale;
     int64_t lse, mrow, mcol, ld, dkbar, dvbar;
+    int64_t kh, vh;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */

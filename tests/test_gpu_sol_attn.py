@@ -208,6 +208,20 @@ def test_kv_splits_match_oracle(N):
         assert d < 1e-2, f"kv_splits={kv} vs 1: {d:.3e}"
 
 
+def test_head_major_copies_are_the_inputs():
+    """Stage 1 writes head-major copies of K and V (the tile source of stage 2 and of the
+    backward); they are the inputs, bit for bit."""
+    B, N, H = 2, 333, 3
+    q, k, v = _qkv(B, N, H, 2700)
+    qg, kg, vg = to_gpu(q, k, v)
+    ws = bsa.alloc_workspace(1, qg)
+    bsa.prepare(1, qg, kg, vg, 1.0, ws)
+    torch.cuda.synchronize()
+    views = bsa.workspace_views(1, ws, B, N, H)
+    assert torch.equal(views["kh"], kg.permute(0, 2, 1, 3))
+    assert torch.equal(views["vh"], vg.permute(0, 2, 1, 3))
+
+
 # ---- degenerate inputs and the maximum length ---------------------------------------
 
 @pytest.mark.parametrize("N", [1, 2])
