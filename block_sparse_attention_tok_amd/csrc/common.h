@@ -66,7 +66,6 @@ namespace solattn {
 // s_waitcnt immediates for the gfx9 encoding (vmcnt in bits 3:0 and 15:14,
 // expcnt in 6:4, lgkmcnt in 11:8); the counters not named are left at max.
 constexpr int kWaitVm0 = 0x0F70;      // vmcnt(0)
-constexpr int kWaitVm8 = 0x0F78;      // vmcnt(8)
 constexpr int kWaitLgkm0 = 0xC07F;    // lgkmcnt(0)
 
 // Workgroup barrier for LDS hand-offs that must not wait for in-flight global
@@ -86,13 +85,6 @@ __device__ __forceinline__ void wait_vm0() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Wait until at most 8 of this wave's vector-memory operations are in flight
-// (they complete in issue order): all but the last 8 DMA instructions have landed.
-__device__ __forceinline__ void wait_vm8() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(kWaitVm8);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // Wait until at most N of this wave's vector-memory operations are in flight.
 template <int N>
@@ -104,20 +96,6 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l's
-// 16 bytes land at lds_base + 16 l; lds_base must be wave-uniform.
-typedef __attribute__((address_space(1))) const char global_char;
-
-__device__ __forceinline__ void dma16(const void* gsrc, unsigned char* lds_base) {
-  __builtin_amdgcn_global_load_lds((global_char*)gsrc, (lds_void*)lds_base, 16, 0, 0);
-}
-
-// Same, with the address split into a wave-uniform base and a 32-bit per-lane
-// byte offset (selects the SGPR-base + VGPR-offset addressing form).
-__device__ __forceinline__ void dma16_off(const void* uniform_base, uint32_t lane_off, unsigned char* lds_base) {
-  __builtin_amdgcn_global_load_lds((global_char*)uniform_base + lane_off, (lds_void*)lds_base, 16, 0, 0);
-}
 
 // Raw buffer resource over [base, base + bytes): loads past the end return zeros
 // instead of faulting (gfx9 word 3: default data format, no swizzle).
