@@ -85,6 +85,7 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   if (variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN) {
     L->kh = take(bh * tokens * kDim * 2);
     L->vh = take(bh * tokens * kDim * 2);
+    L->sel = take(bh * nb * (nbp / 64) * 8);
   }
   if (variant == SOL_VARIANT_SOL2 || variant == SOL_VARIANT_SOL2_PV8) {
     const int64_t tp = nbp * kBlock;
@@ -274,7 +275,10 @@ int sol_attn_prepare(const void* q, const void* k, const void* v, int64_t batch,
   hipStream_t hs = (hipStream_t)stream;
   st = hip_status(solattn::launch_summary((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s, w, hs));
   if (st != SOL_OK) return st;
-  return hip_status(solattn::launch_threshold(s, w, tau, thresh == SOL_THRESH_EXACT, hs));
+  st = hip_status(solattn::launch_threshold(s, w, tau, thresh == SOL_THRESH_EXACT, hs));
+  if (st != SOL_OK) return st;
+  // threshold routing words (the sink is forced in stage 2)
+  return hip_status(solattn::launch_route(s, w, 1, 0, w.sel, hs));
 }
 
 // Sol-Attn2 stage 2 parts: the routing + tail pass, the exact pass, or both in order.

@@ -56,7 +56,8 @@ struct FusedArgs {
   const uint16_t* kh; const uint16_t* vh;   // head-major copies of k and v ([B][H][N][128])
   const float* tau_i;
   int sink_b0, sink_b1;
-  uint64_t* mask_out;
+  const uint64_t* route;        // threshold routing words [B][H][nb][nbw] (stage 1, no sink)
+  uint64_t* mask_out;           // the words used, sink included (NULL = none)
   float* lse;                   // [B][H][tp] base-2 log-sum-exp per query row (NULL = none)
   int tp;
 };
@@ -96,8 +97,6 @@ enum TileMode { kExactFull = 0, kExactPartial = 1, kProxy = 2 };
 __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Kl[64 * 256];
   __shared__ __attribute__((aligned(1024))) unsigned char Vl[64 * 256];
-  __shared__ __attribute__((aligned(16))) float qb_s[kDim];
-  __shared__ float part[2][2][64];
   __shared__ uint64_t sel_s[kMaxChunks], prox_s[kMaxChunks];
   __shared__ int redo_s[2];
 
@@ -116,9 +115,6 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t rs = (size_t)a.H * kDim;                      // elements between tokens (BTHD)
   const size_t head_off = (size_t)b * a.N * rs + (size_t)h * kDim;
-
-  if (tid < 32) ((float4*)qb_s)[tid] = ((const float4*)(a.qbar + ((size_t)bh * a.nbp + i) * kDim))[tid];
-  const float tau_i = a.tau_i[(size_t)bh * a.nbp + i];
 
   const int qrow = i * kBlock + w * 32 + l32;
   bf16x8 qreg[8];
@@ -142,37 +138,24 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   const int c_begin = split * a.cps;                        // this split's routing chunks
   const int c_end = min(a.nbp / 64, c_begin + a.cps);
   const int nchunks = c_end - c_begin;
-  // The first tile is the pooled tile of the split's first chunk; its DMA is issued
-  // now and lands while the routing runs (the routing barriers do not wait for it).
+  // The routing words of this query block's chunks (threshold test of stage 1's routing
+  // pass) are loaded first, then the first tile's DMA (the pooled tile of the split's first
+  // chunk) is issued, so that the words do not wait for it.  The sink's blocks are forced
+  // exact here, since the sink is a stage-2 argument.
+  uint64_t selm = 0;
+  if (tid < nchunks) selm = a.route[((size_t)bh * a.nb + i) * a.nbw + c_begin + tid];
   auto pool = [&]() { return make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool); };
   dma_tile<false>(Kl, pool(), (uint32_t)c_begin * 64 * row_bytes, row_bytes, doff, w);
-
-  // ---- routing for every chunk (fp32); wave w sums dims 64 w .. 64 w + 63
-  const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
-  for (int c = c_begin; c < c_end; ++c) {
-    const int j = c * 64 + lane;
-    float4 kk[16];                                           // all 16 loads in flight at once
-#pragma unroll
-    for (int e = 0; e < 16; ++e) kk[e] = kt[(size_t)(16 * w + e) * a.nbp + j];
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int d4 = 16 * w + e;
-      acc += qb_s[4 * d4] * kk[e].x + qb_s[4 * d4 + 1] * kk[e].y + qb_s[4 * d4 + 2] * kk[e].z +
-             qb_s[4 * d4 + 3] * kk[e].w;
-    }
-    part[c & 1][w][lane] = acc;
-    lds_barrier();
-    const float s_hat = (part[c & 1][0][lane] + part[c & 1][1][lane]) * kScale;
-    const bool valid = j < a.nb;
-    const bool sel = valid && (s_hat > tau_i || (j >= a.sink_b0 && j <= a.sink_b1));
-    const uint64_t selm = __ballot(sel);
-    const uint64_t proxm = __ballot(valid) & ~selm;
-    if (tid == 0) {
-      sel_s[c - c_begin] = selm;
-      prox_s[c - c_begin] = proxm;
-      if (a.mask_out) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
-    }
+  if (tid < nchunks) {
+    const int c = c_begin + tid;
+    const int nvalid = a.nb - 64 * c;                       // valid blocks of the chunk (>= 1)
+    const uint64_t validm = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+    const int s0 = max(a.sink_b0, 64 * c), s1 = min(a.sink_b1, 64 * c + 63);
+    if (s0 <= s1) selm |= (~0ull >> (63 - (s1 - s0))) << (s0 - 64 * c);
+    selm &= validm;
+    sel_s[tid] = selm;
+    prox_s[tid] = validm & ~selm;
+    if (a.mask_out) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
   }
   lds_barrier();
 
@@ -461,7 +444,8 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const int nchunks = ws.nbp / 64;
   const int S = ws.kv_splits;
   const int cps = (nchunks + S - 1) / S;
-  if (cps > kMaxChunks || (S > 1 && (!ws.opart || !ws.olse)) || !ws.kh || !ws.vh) return hipErrorInvalidValue;
+  if (cps > kMaxChunks || (S > 1 && (!ws.opart || !ws.olse)) || !ws.kh || !ws.vh || !ws.sel)
+    return hipErrorInvalidValue;
   FusedArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = (ws.nb + 63) / 64;
@@ -469,6 +453,7 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h; a.tau_i = ws.tau_i;
   a.kh = ws.kh; a.vh = ws.vh;
   a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
+  a.route = ws.sel;
   a.lse = ws.lse; a.tp = ws.nbp * kBlock;
   const int total = s.B * s.H * S * ws.nb;
   hipLaunchKernelGGL(sol_fused_kernel, dim3(total), dim3(128), 0, stream, a);

@@ -644,14 +644,19 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   }
 }
 
-hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream) {
+hipError_t launch_route(Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* sel,
+                        hipStream_t stream) {
   Route2Args r;
   r.nb = ws.nb; r.nbp = ws.nbp; r.nbw = ws.nbp / 64;
   r.qbar = ws.qbar; r.kbar_t = ws.kbar_t; r.tau_i = ws.tau_i;
   r.sink_b0 = sink_b0; r.sink_b1 = sink_b1;
-  r.sel = ws.sel;
+  r.sel = sel;
   hipLaunchKernelGGL(sol2_route_kernel, dim3(ws.nbp / 64, (ws.nb + 31) / 32, s.B * s.H), dim3(64), 0, stream, r);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream) {
+  hipError_t e = launch_route(s, ws, sink_b0, sink_b1, ws.sel, stream);
   if (e != hipSuccess) return e;
   Tail2Args a;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = ws.nbp / 64;
