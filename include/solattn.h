@@ -81,7 +81,8 @@ typedef enum {
  *   opart    bf16  [S][B][N][H][128]   per-key-split normalized partial outputs (S = kv_splits > 1)
  *   olse     float [S][B][N][H]        per-key-split log2-sum-exp of the partial rows
  *   sel      uint64 [B][H][nb][nbp/64] routing bits, bit j % 64 of word j / 64 set iff block j
- *                                      is exact for query block i (Sol-Attn2)
+ *                                      is exact for query block i (Sol-Attn: threshold bits of
+ *                                      stage 1, the sink added by stage 2; Sol-Attn2: with the sink)
  *   tmu, tnu float [B][H][nbp][2][128] per-anchor tail key / value means mu_a, nu_a (Sol-Attn2)
  *   tlz      float [B][H][nbp][2]     log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d); -inf if the
  *                                      anchor's tail is empty (Sol-Attn2)
