@@ -169,18 +169,21 @@ int sol_attn(const void* q, const void* k, const void* v, void* out,
              float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 1 of sol_attn: block summaries (Q/K means, V sums as means) and the
+/* Stage 1 of sol_attn: block summaries (Q/K means, V sums as means), the
  * per-query-block threshold tau_i (paper §3.1 Eqs. (4)-(5); the paper keeps
- * only this threshold computation outside the attention kernel, §4.5).
- * Writes the workspace arrays qbar..kcov.  Same arguments as sol_attn minus
- * out and the sink. */
+ * only this threshold computation outside the attention kernel, §4.5), the
+ * routing bits s-hat_ij > tau_i of every (query block, key block) pair (Eq. (6),
+ * without the sink, which stage 2 adds), and the head-major K / V copies.
+ * Writes the workspace arrays qbar..kcov, kh, vh and sel.  Same arguments as
+ * sol_attn minus out and the sink. */
 int sol_attn_prepare(const void* q, const void* k, const void* v,
                      int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                      float tau, int thresh, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 2 of sol_attn: the fused routing + proxy-reuse + exact online-softmax
- * kernel (paper §3.2 "Hardware-Aligned Implementation").  Reads the workspace
- * written by sol_attn_prepare for the same q, k, v and shape. */
+/* Stage 2 of sol_attn: the fused proxy-reuse + exact online-softmax kernel
+ * (paper §3.2 "Hardware-Aligned Implementation") over stage 1's routing bits with
+ * the sink's blocks forced exact.  Reads the workspace written by
+ * sol_attn_prepare for the same q, k, v and shape. */
 int sol_attn_fused(const void* q, const void* k, const void* v, void* out,
                    int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                    int64_t sink_start, int64_t sink_tokens,
