@@ -1,20 +1,20 @@
 // Fused Sol-Attn forward kernel for gfx950 (Sol-Attn stage 2).
 //
 // Sol-Attn paper (arXiv 2607.24027) §3.2, Figure 4 and "Hardware-Aligned
-// Implementation": each program keeps one query block and its threshold
-// tau_i on chip and one online-softmax state in registers; it streams the
-// pooled keys / values in chunks, compares each block's proxy score
-// s_ij = Q-bar_i . K-bar_j / sqrt(d) with tau_i (Eq. (4), Eq. (6)), folds every
-// unselected block in through its proxy (token-to-block tile Q_i K-bar^T with
-// weight n_j and the V sum V-hat_j) and runs exact attention on the original
-// K/V blocks of the selected indices.  No proxy or routing map is written to
-// memory (only the optional test export).
+// Implementation": each program keeps one query block on chip and one
+// online-softmax state in registers; it streams the pooled keys / values in
+// chunks, folds every unselected block in through its proxy (token-to-block tile
+// Q_i K-bar^T with weight n_j and the V sum V-hat_j) and runs exact attention on
+// the original K/V blocks of the selected indices.  The selection itself (each
+// block's proxy score s_ij = Q-bar_i . K-bar_j / sqrt(d) against tau_i, Eq. (4),
+// Eq. (6)) comes from the routing pass of stage 1 as one bit per block pair; the
+// kernel adds the sink's blocks.  No proxy is written to memory.
 //
 // gfx950 mapping: one workgroup = one (batch, head, 64-row query block, key
 // split), two wave64s of 32 query rows; __launch_bounds__(128, 2) keeps two
 // waves per SIMD; workgroups are ordered so that each XCD walks its own heads.
-//   * Routing runs first, in fp32 from the fp32 block means (VALU), for every
-//     chunk of 64 pooled keys; the per-chunk selection words stay in LDS.
+//   * The routing words of the split's chunks are loaded first; the per-chunk
+//     selection and proxy masks stay in LDS.
 //   * The tile stream is the pooled tile of every chunk (K-bar / V-bar = V-hat/n
 //     rows with logit bias log2 n_j; selected and padding columns masked), then
 //     the selected exact blocks chunk by chunk.
