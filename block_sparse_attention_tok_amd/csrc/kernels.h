@@ -68,7 +68,8 @@ hipError_t launch_quant_summary(const uint16_t* q, const uint16_t* k, const uint
 hipError_t launch_qhat(Shape s, const Workspace& ws, hipStream_t stream);
 hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream);
 // Routing bits of every (query block, key block) pair from the fp32 block means and tau_i,
-// with the sink's blocks forced, into sel [B][H][nb][nbp / 64] (Sol-Attn and Sol-Attn2).
+// with the blocks [sink_b0, sink_b1] forced, into sel [B][H][nb][nbp / 64] (Sol-Attn stage 1
+// with an empty sink range, Sol-Attn2 stage 2 with the sink).
 hipError_t launch_route(Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* sel,
                         hipStream_t stream);
 // Sol-Attn2 stage 2: routing and the complementary tail per anchor (writes sel, tmu, tnu, tlz),

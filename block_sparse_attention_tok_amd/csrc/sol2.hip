@@ -370,68 +370,7 @@ hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStr
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2a: routing (draft, Method, Eq. (1) selection): s-hat_ij = Q-bar_i . K-bar_j /
-// sqrt(d) from the dequantized block means, against tau_i, with the sink's blocks forced
-// exact.  One wave per (b, h, 32 query blocks from i0, 64-block chunk c): the 32 x 64
-// products on v_mfma_f32_32x32x2_f32 (fp32 operands and sums), A = the query-block means,
-// B = the key-block means, with the contraction order chosen so that lane (m, kh) reads
-// dims 64 kh .. 64 kh + 63 of its row contiguously (k-step s takes dim 64 kh + s).  The
-// accumulator of row i holds key blocks 32 t + n in lane n (+ 32 for rows i + 4), so one
-// ballot per row pair gives the routing bits of two query blocks.
-// ---------------------------------------------------------------------------
-struct Route2Args {
-  int nb, nbp, nbw;
-  const float* qbar; const float* kbar_t; const float* tau_i;
-  int sink_b0, sink_b1;
-  uint64_t* sel;
-};
-
-__global__ __launch_bounds__(64) void sol2_route_kernel(Route2Args a) {
-  const int c = blockIdx.x, i0 = blockIdx.y * 32, bh = blockIdx.z;
-  const int lane = threadIdx.x, m = lane & 31, kh = lane >> 5;
-  // rows i0 + m < nbp and key blocks 64 c + 63 < nbp: padding rows / blocks are in memory
-  const float4* qa = (const float4*)(a.qbar + ((size_t)bh * a.nbp + i0 + m) * kDim) + 16 * kh;
-  const float4* kb = (const float4*)a.kbar_t + ((size_t)bh * 32 + 16 * kh) * a.nbp + 64 * c + m;
-  floatx16 acc[2] = {floatx16{}, floatx16{}};               // key blocks 64 c + 32 t + n
-#pragma unroll 4
-  for (int cc = 0; cc < 16; ++cc) {
-    const float4 x = qa[cc];
-    const float4 y0 = kb[(size_t)cc * a.nbp];
-    const float4 y1 = kb[(size_t)cc * a.nbp + 32];
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y0.x, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y1.x, acc[1], 0, 0, 0);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y0.y, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y1.y, acc[1], 0, 0, 0);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y0.z, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y1.z, acc[1], 0, 0, 0);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y0.w, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y1.w, acc[1], 0, 0, 0);
-  }
-  const bool sink[2] = {64 * c + m >= a.sink_b0 && 64 * c + m <= a.sink_b1,
-                        64 * c + 32 + m >= a.sink_b0 && 64 * c + 32 + m <= a.sink_b1};
-  const bool kvalid[2] = {64 * c + m < a.nb, 64 * c + 32 + m < a.nb};
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = i0 + 8 * (r >> 2) + 4 * kh + (r & 3);     // this lane's query block in row r
-    const float tau = a.tau_i[(size_t)bh * a.nbp + i];
-    uint64_t bits[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float s_hat = acc[t][r] * kScale2;
-      bits[t] = __ballot(i < a.nb && kvalid[t] && (s_hat > tau || sink[t]));
-    }
-    if (lane == 0) {
-      const int ilo = i0 + 8 * (r >> 2) + (r & 3);          // rows ilo (lanes 0..31) and ilo + 4
-      const uint64_t wlo = (bits[1] << 32) | (bits[0] & 0xffffffffull);
-      const uint64_t whi = (bits[1] & 0xffffffff00000000ull) | (bits[0] >> 32);
-      if (ilo < a.nb) a.sel[((size_t)bh * a.nb + ilo) * a.nbw + c] = wlo;
-      if (ilo + 4 < a.nb) a.sel[((size_t)bh * a.nb + ilo + 4) * a.nbw + c] = whi;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Stage 2b: the complementary tail of every anchor (draft, Method, Eq. (1)).  One
+// Stage 2a: the complementary tail of every anchor (draft, Method, Eq. (1)).  One
 // workgroup (two waves) per (b, h, 32 consecutive query blocks); wave w's lane column
 // n = lane % 32 is anchor n of query blocks i0 + 16 w .. i0 + 16 w + 15 (query block
 // i0 + 16 w + n / 2, half n % 2).  Tiles of 16 key blocks (32 groups) stream through
@@ -644,17 +583,6 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   }
 }
 
-hipError_t launch_route(Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* sel,
-                        hipStream_t stream) {
-  Route2Args r;
-  r.nb = ws.nb; r.nbp = ws.nbp; r.nbw = ws.nbp / 64;
-  r.qbar = ws.qbar; r.kbar_t = ws.kbar_t; r.tau_i = ws.tau_i;
-  r.sink_b0 = sink_b0; r.sink_b1 = sink_b1;
-  r.sel = sel;
-  hipLaunchKernelGGL(sol2_route_kernel, dim3(ws.nbp / 64, (ws.nb + 31) / 32, s.B * s.H), dim3(64), 0, stream, r);
-  return hipGetLastError();
-}
-
 hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream) {
   hipError_t e = launch_route(s, ws, sink_b0, sink_b1, ws.sel, stream);
   if (e != hipSuccess) return e;
@@ -668,7 +596,7 @@ hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, 
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2c: exact FP8 attention over the selected blocks, combined with the tail.
+// Stage 2b: exact FP8 attention over the selected blocks, combined with the tail.
 // One workgroup per (b, h, query block i), two wave64s; wave w owns query rows
 // 32 w .. 32 w + 31, which are exactly anchor a = (i, w).
 //   * The selected blocks (the routing bits of stage 2a) stream through LDS: the
