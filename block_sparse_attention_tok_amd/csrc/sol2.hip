@@ -639,6 +639,7 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   __shared__ uint64_t sel_s[kMaxChunks2];
   __shared__ __attribute__((aligned(16))) float mu_s[2][kDim];
   __shared__ __attribute__((aligned(16))) float nu_s[2][kDim];
+  __shared__ int redo2_s[2];
 
   const int total = a.B * a.H * a.nb;
   const int item = xcd_remap(blockIdx.x, total);
@@ -734,11 +735,16 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   float m_run = kNegInf, l_run = 0.f;
   const float qs = sq * kScale2 * kLog2e;
   const int last_partial = a.N % kBlock ? a.nb - 1 : -1;   // the only block with masked rows
-  // One selected block: scores, running max, P (bf16 or ExpCast bytes), PV.  kPartial masks
+  // One selected block: scores, reference, P (bf16 or ExpCast bytes), PV.  kPartial masks
   // the rows past the end of the sequence (only the last block, which comes last in the
-  // ascending order); full blocks take the logits straight from the raw scores.
-  auto tile = [&](auto partial_tag, int cur, int nxt) {
+  // ascending order); full blocks take the logits straight from the raw scores.  The
+  // ExpCast bytes are defined against the running maximum, so the FP8 PV path always keeps
+  // it (kSafe); the bf16 path takes its reference from the first exact block of the row
+  // (kSafe = false: no rescaling of O and l) and is redone with the running maximum if a sum
+  // overflows.
+  auto tile = [&](auto partial_tag, auto safe_tag, int cur, int nxt) {
     constexpr bool kPartial = decltype(partial_tag)::value;
+    constexpr bool kSafe = kPv8 || decltype(safe_tag)::value;
     floatx16 s0 = {}, s1 = {};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -766,17 +772,23 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
 #pragma unroll
     for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, fmaxf(s0[idx], s1[idx]));
     mx = max_with_partner(mx) * f;
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    // Unconditional rescale (skipping it behind a wave-uniform branch made results
-    // timing-dependent with two waves per SIMD).
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    l_run *= alpha;
+    float m_use, alpha = 1.f;
+    if constexpr (kSafe) {
+      const float m_new = fmaxf(m_run, mx);
+      m_use = m_new == kNegInf ? 0.f : m_new;
+      // Unconditional rescale (skipping it behind a wave-uniform branch made results
+      // timing-dependent with two waves per SIMD).
+      alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) o[mt][idx] *= alpha;
-    m_run = m_new;
+        for (int idx = 0; idx < 16; ++idx) o[mt][idx] *= alpha;
+      m_run = m_new;
+    } else {
+      m_run = m_run == kNegInf ? mx : m_run;               // the row's first exact block
+      m_use = m_run == kNegInf ? 0.f : m_run;
+    }
     if constexpr (kPv8) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) ol[idx] *= alpha;
@@ -822,16 +834,40 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
       pv_tile(o, Vl, voff, pa);
     }
   };
-  int cur = next_sel();
-  if (cur >= 0) issue_k(cur);
-  while (cur >= 0) {
-    const int nxt = next_sel();
-    wait_vm0();
-    lds_barrier();                                         // K8(cur) landed; V buffer free
-    issue_v(cur);
-    if (cur == last_partial) tile(BoolTag<true>{}, cur, nxt);
-    else tile(BoolTag<false>{}, cur, nxt);
-    cur = nxt;
+  auto run_tiles = [&](auto safe_tag) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) o[mt] = floatx16{};
+    m_run = kNegInf;
+    l_run = 0.f;
+    c_it = 0;
+    bits = 0;
+    int cur = next_sel();
+    if (cur >= 0) issue_k(cur);
+    while (cur >= 0) {
+      const int nxt = next_sel();
+      wait_vm0();
+      lds_barrier();                                       // K8(cur) landed; V buffer free
+      issue_v(cur);
+      if (cur == last_partial) tile(BoolTag<true>{}, safe_tag, cur, nxt);
+      else tile(BoolTag<false>{}, safe_tag, cur, nxt);
+      cur = nxt;
+    }
+  };
+  if constexpr (kPv8) {
+    run_tiles(BoolTag<true>{});
+  } else {
+    run_tiles(BoolTag<false>{});
+    // A sum that overflowed the row's reference (a logit more than ~2^127 above it): redo
+    // the workgroup's blocks with the running maximum.
+    float chk = l_run * 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) chk = __builtin_fmaf(o[mt][idx], 0.f, chk);
+    const bool bad = __ballot(!(chk == 0.f)) != 0;
+    if (lane == 0) redo2_s[w] = bad;
+    __syncthreads();                                       // also: both waves are past their last block
+    if (redo2_s[0] | redo2_s[1]) run_tiles(BoolTag<true>{});
   }
 
   // ---- epilogue: tail logit lambda_t = log2 Z_a + log2(e) q'_t . mu_a / sqrt(d) (the

@@ -168,3 +168,18 @@ def test_tail_logit_far_above_the_first_tiles():
     k[0, blk * 64:(blk + 1) * 64, 0, 0] = 300.0 * torch.tensor([1.0, -1.0]).repeat(32)
     out, masks, _ = run_case(q, k, v, 1.0)
     assert (~masks[0, 0, :, blk]).sum() >= 8, "block 40 is meant to stay in the tail"
+
+
+def test_exact_logit_far_above_the_first_exact_block():
+    """The bf16-V exact pass takes each row's reference from its first exact block (here the
+    sink's block 0); key block 40, along the queries' dominant direction at 300 e_0, is
+    selected and scores about 380 log2 units higher, so the sums overflow that reference and
+    the workgroup is redone with the running maximum.  The result still matches the oracle."""
+    B, N, H = 1, 4096, 1
+    q, k, v = _qkv(B, N, H, 3100)
+    q[..., 0] = 10.0
+    blk = 40
+    k[0, blk * 64:(blk + 1) * 64, 0, :] = 0.0
+    k[0, blk * 64:(blk + 1) * 64, 0, 0] = 300.0
+    out, masks, _ = run_case(q, k, v, 1.0, sink_start=0, sink_tokens=64)
+    assert masks[0, 0, :, blk].all() and masks[0, 0, :, 0].all()
