@@ -48,13 +48,12 @@ constexpr int kMaxChunks = 128;                         // nbp / 64 <= 128 (toke
 constexpr int kEnd = -0x7fffffff;
 
 struct FusedArgs {
-  const uint16_t* q; const uint16_t* k; const uint16_t* v; uint16_t* out;
+  const uint16_t* q; uint16_t* out;
   int B, N, H, nb, nbp, nbw;
   int S, cps;                   // key-range splits and routing chunks per split
   uint16_t* opart; float* olse; // split partials (S > 1)
-  const float* qbar; const float* kbar_t; const uint16_t* kbar_h; const uint16_t* vbar_h;
+  const uint16_t* kbar_h; const uint16_t* vbar_h;
   const uint16_t* kh; const uint16_t* vh;   // head-major copies of k and v ([B][H][N][128])
-  const float* tau_i;
   int sink_b0, sink_b1;
   const uint64_t* route;        // threshold routing words [B][H][nb][nbw] (stage 1, no sink)
   uint64_t* mask_out;           // the words used, sink included (NULL = none)
@@ -447,10 +446,10 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (cps > kMaxChunks || (S > 1 && (!ws.opart || !ws.olse)) || !ws.kh || !ws.vh || !ws.sel)
     return hipErrorInvalidValue;
   FusedArgs a;
-  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.q = q; a.out = out;   // k and v are read through stage 1's head-major copies
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = (ws.nb + 63) / 64;
   a.S = S; a.cps = cps; a.opart = ws.opart; a.olse = ws.olse;
-  a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h; a.tau_i = ws.tau_i;
+  a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h;
   a.kh = ws.kh; a.vh = ws.vh;
   a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
   a.route = ws.sel;
