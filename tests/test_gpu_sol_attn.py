@@ -255,3 +255,19 @@ def test_maximum_sequence_length():
     assert bsa.validate(1, N, 1, 128, 1.28, None, 0) == 0
     assert bsa.validate(1, N + 1, 1, 128, 1.28, None, 0) != 0
     run_case(q, k, v, 1.28, sample=3, seed=5)
+
+
+def test_exact_logit_far_above_the_pooled_reference():
+    """Key block 40 holds +-300 e_0 in alternate tokens and is the sink, so it is exact while its
+    pooled logit (the block mean, zero) stays near the first pooled tile's maximum.  For queries
+    with q_0 = 10 its exact logits sit about 380 log2 units above that fixed reference, the sums
+    overflow, and the workgroup is redone with the running maximum; the result still matches the
+    oracle."""
+    B, N, H = 1, 4096, 1
+    q, k, v = _qkv(B, N, H, 3200)
+    q[..., 0] = 10.0
+    blk = 40
+    k[0, blk * 64:(blk + 1) * 64, 0, :] = 0.0
+    k[0, blk * 64:(blk + 1) * 64, 0, 0] = 300.0 * torch.tensor([1.0, -1.0]).repeat(32)
+    out, masks, _ = run_case(q, k, v, 1.0, sink_start=blk * 64, sink_tokens=64)
+    assert masks[0, 0, :, blk].all()
