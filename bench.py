@@ -50,8 +50,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); multi-GPU runs are not part of "
-              "this build (the path shards by head with no communication).", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); there is no multi-GPU run: "
+              "the path shards by (batch, head) with no communication.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -14,7 +14,6 @@ typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 64;     // KV / query block size (Sol-Attn paper §4.1: fixed 64x64 physical blocks)
 constexpr int kDim = 128;      // head dimension fixed by the README's tensor contract
-constexpr int kAnchor = 32;    // Sol-Attn2 query anchor size (draft, Method)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
