@@ -271,3 +271,36 @@ def test_exact_logit_far_above_the_pooled_reference():
     k[0, blk * 64:(blk + 1) * 64, 0, 0] = 300.0 * torch.tensor([1.0, -1.0]).repeat(32)
     out, masks, _ = run_case(q, k, v, 1.0, sink_start=blk * 64, sink_tokens=64)
     assert masks[0, 0, :, blk].all()
+
+
+def test_kv_splits_with_batch_sink_and_ragged_tail():
+    """Key splits 1, 2 and 4 over a shape that exercises every edge at once: two batches, three
+    heads, 12317 tokens (193 blocks, so the last routing chunk holds one block of 29 tokens) and a
+    200-token sink in the middle of the sequence.  Every output row matches the oracle under the
+    kernel's own masks, and the splits agree with each other."""
+    B, N, H = 2, 12317, 3
+    q, k, v = _qkv(B, N, H, 3300)
+    tau, s0, st = 0.5, 5000, 200
+    qg, kg, vg = to_gpu(q, k, v)
+    _, masks, _ = bsa.debug_routing(1, qg, kg, vg, tau, "diag", s0, st)
+    gsel = masks.numpy()
+    ref = sa.routing_only(q, k, tau, s0, st, "diag")
+    nb = (N + 63) // 64
+    forced = np.zeros((B, H, nb, nb), dtype=bool)
+    forced[..., sa.sink_block_mask(N, s0, st)] = True
+    mask_check(gsel, ref["sel"], ref["s_hat"], ref["tau_i"], forced)
+    want = np.concatenate([oracle_rows(q, k, v, b, h, i, gsel[b, h, i])
+                           for b in range(B) for h in range(H) for i in range(nb)])
+    outs = {}
+    for kv in (1, 2, 4):
+        out = bsa.sol_attn(qg, kg, vg, tau, "diag", s0, st, kv_splits=kv)
+        torch.cuda.synchronize()
+        oc = out.float().cpu().numpy()
+        got = np.concatenate([oc[b, i * 64:min(N, i * 64 + 64), h, :]
+                              for b in range(B) for h in range(H) for i in range(nb)])
+        err, mx = compare_out(got, want, what=f"kv_splits={kv}")
+        say(f"   kv_splits {kv} (effective {bsa.kv_splits_for(B, N, H, kv)}): rel L2 {err:.2e} max abs {mx:.2e}")
+        outs[kv] = out.float()
+    for kv in (2, 4):
+        d = (outs[kv] - outs[1]).norm() / outs[1].norm()
+        assert d < 1e-2, f"kv_splits={kv} vs 1: {d:.3e}"
