@@ -50,7 +50,7 @@ int effective_splits(int64_t tokens, int requested) {
   const int64_t nb = (tokens + kBlock - 1) / kBlock;
   const int nchunks = (int)((nb + 63) / 64);
   int want = requested;
-  if (want <= 0) want = (nchunks + 3) / 4;                 // automatic: one split per four chunks
+  if (want <= 0) want = (nchunks + 5) / 6;                 // automatic: one split per six chunks
   if (want > kMaxSplits) want = kMaxSplits;
   if (want > nchunks) want = nchunks;
   if (want < 1) want = 1;

@@ -141,7 +141,7 @@ int sol_attn_workspace_layout(int variant, int64_t batch, int64_t tokens, int64_
  * separate workgroups and merged afterwards (partial outputs in bf16 with an fp32
  * log-sum-exp); on MI355X this keeps the K/V working set of the workgroups that
  * run together on one XCD inside its L2.  kv_splits = 0 means automatic: one
- * split per 256 key blocks (four 64-block routing chunks), at most 16.  Splits
+ * split per 384 key blocks (six 64-block routing chunks, rounded up), at most 16.  Splits
  * cover whole routing chunks: a request r becomes ceil(C / ceil(C / r)) for C
  * chunks (never above C).
  * Host-only; returns the effective split count (>= 1), or 0 on a shape error. */
