@@ -42,163 +42,150 @@ def parse():
     p.add_argument("--cpu-sample-heads", type=int, default=16, help="heads the CPU oracle is timed on")
     p.add_argument("--cpu-sample-blocks", type=int, default=256, help="query blocks per sampled head")
     p.add_argument("--kv-splits", type=int, default=0, help="key-range splits of the fused pass (0 = automatic)")
+    p.add_argument("--no-range", action="store_true",
+                   help="skip the extra range entries (80%%/85%% at 32K, 512+131072 at 90%%)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (scales FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); there is no multi-GPU run: "
-              "the path shards by (batch, head) with no communication.", file=sys.stderr)
-        sys.exit(2)
+def cpu_model() -> str:
+    """The host CPU's model name (what lscpu prints as "Model name"), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def make_inputs(video_tokens: int, text_sink: int, heads: int):
+    from workloads import block_offset_tensor, text_prefix_tensor
+    B, D = 1, 128
+    if text_sink:
+        return [text_prefix_tensor(B, text_sink, video_tokens, heads, D, 3000 + i) for i in range(3)]
+    return [block_offset_tensor(B, video_tokens, heads, D, 3000 + i) for i in range(3)]
+
+
+def measure(variant: int, qc, kc, vc, text_sink: int, target: float, tau_fixed, steps: int, warmup: int,
+            kv_splits: int, dense_baselines: bool):
+    """Time one workload: tau bisected on the kernel's own selected-pair counter to the target
+    token-pair sparsity, then `warmup` untimed and `steps` timed full calls (prepare + fused),
+    then the dominant kernel alone with HIP events on the launch stream."""
     import numpy as np
     import torch
 
     import block_sparse_attention_tok_amd as bsa
-    from workloads import block_offset_tensor, text_prefix_tensor
-
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
-        return
-    B, H, D = 1, args.heads, 128
-    N = args.tokens + args.text_sink
-    if args.variant == "sol1train":
-        return bench_train(args)
-    variant = {"sol1": 1, "sol2": 2, "sol2pv8": 3}[args.variant]
-    sink_start, sink_tokens = (0, args.text_sink) if args.text_sink else (None, 0)
-    log(f"[bench] generating B={B} N={N} H={H} d={D} ({args.variant})")
-    t0 = time.time()
-    if args.text_sink:
-        q, k, v = (text_prefix_tensor(B, args.text_sink, args.tokens, H, D, 3000 + i) for i in range(3))
-    else:
-        q, k, v = (block_offset_tensor(B, N, H, D, 3000 + i) for i in range(3))
-    qc, kc, vc = q, k, v
-    q, k, v = (t.to(dev) for t in (q, k, v))
+    B, N, H, D = qc.shape
+    q, k, v = (t.to(dev) for t in (qc, kc, vc))
     out = torch.empty_like(q)
-    ws = bsa.alloc_workspace(variant, q, args.kv_splits if variant == 1 else 0)
-    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; workspace {ws.numel() / 2**20:.1f} MiB")
-
+    sink_start, sink_tokens = (0, text_sink) if text_sink else (None, 0)
+    ws = bsa.alloc_workspace(variant, q, kv_splits if variant == 1 else 0)
+    log(f"[bench] N={N} H={H}: workspace {ws.numel() / 2**20:.1f} MiB")
     nb = (N + 63) // 64
     counts = np.full(nb, 64.0)
     counts[-1] = N - 64 * (nb - 1)
-    pair_w = np.outer(counts, counts)
+    all_pairs = B * H * float(N) ** 2
 
-    def routing(tau):
+    def routing(tau, masks=False):
         # (the FP8-PV workspace extends the Sol-Attn2 one and routes the same way)
-        _, m, _ = bsa.debug_routing(min(variant, 2), q, k, v, tau, "diag", sink_start, sink_tokens, out=None,
-                                    workspace=ws, kv_splits=args.kv_splits if variant == 1 else 0)
-        return m.numpy()
+        _, m, _, pairs = bsa.debug_routing(min(variant, 2), q, k, v, tau, "diag", sink_start, sink_tokens, out=None,
+                                           workspace=ws, kv_splits=kv_splits if variant == 1 else 0,
+                                           return_pairs=True)
+        return (m.numpy() if masks else None), pairs
 
-    def sparsity(m):
-        return 1.0 - float((m * pair_w).sum()) / (B * H * float(N) ** 2)
-
-    if args.tau is None:
+    if tau_fixed is None:
         lo, hi = -1.0, 4.0
         tau = 1.28
         for it in range(30):
-            s = sparsity(routing(tau))
-            if abs(s - args.sparsity) <= 0.0025:
+            s = 1.0 - routing(tau)[1] / all_pairs
+            if abs(s - target) <= 0.0025:
                 break
-            if s < args.sparsity:
+            if s < target:
                 lo = tau
             else:
                 hi = tau
             tau = 0.5 * (lo + hi)
         log(f"[bench] tau={tau:.4f} after {it + 1} routing passes")
     else:
-        tau = args.tau
-    masks = routing(tau)
-    real_sp = sparsity(masks)
-    exact_pairs = float((masks * pair_w).sum())
+        tau = tau_fixed
+    masks, exact_pairs = routing(tau, masks=True)
+    real_sp = 1.0 - exact_pairs / all_pairs
     proxy_units = float(((~masks) * counts[:, None]).sum())       # (query token, unselected block)
     flops_exact = 4.0 * D * exact_pairs
     flops_proxy = 4.0 * D * proxy_units if variant == 1 else 0.0   # Sol-Attn2 has a tail pass instead
     dense_flops = 4.0 * B * H * float(N) ** 2 * D
     log(f"[bench] realised sparsity {real_sp:.4f}; exact {flops_exact / 1e12:.3f} TFLOP"
         + (f", proxy {flops_proxy / 1e12:.3f} TFLOP" if variant == 1 else ""))
-
     stream = torch.cuda.current_stream(dev)
-
-    def step():
+    for _ in range(warmup):
         bsa.prepare(variant, q, k, v, tau, ws)
-        bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens, args.kv_splits)
-
-    for _ in range(args.warmup):
-        step()
+        bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens, kv_splits)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
+    for s_ in range(steps):
+        ev[s_][0].record(stream)
         bsa.prepare(variant, q, k, v, tau, ws)
-        ev[s][1].record(stream)
-        bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens, args.kv_splits)
-        ev[s][2].record(stream)
+        ev[s_][1].record(stream)
+        bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens, kv_splits)
+        ev[s_][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
     fused_ms = [e[1].elapsed_time(e[2]) for e in ev]
     step_ms = [e[0].elapsed_time(e[2]) for e in ev]
-    ms_per_step = wall * 1e3 / args.steps
-    med_step = float(np.median(step_ms))
-    fused_avg = float(np.mean(fused_ms))
-    value = dense_flops / (ms_per_step * 1e-3) / 1e12
+    ms_per_step = wall * 1e3 / steps
 
-    # Roofline of the dominant kernel, timed alone with events on its own stream: the
-    # fused Sol-Attn kernel (called without an output: no split merge, no final store),
-    # or the exact Sol-Attn2 kernel (after the tail pass of the last step).
+    # The dominant kernel timed alone with events on its own stream: the fused Sol-Attn kernel
+    # (called without an output: no split merge, no final store), or the exact Sol-Attn2
+    # kernel (after the tail pass of the last step).
     if variant == 1:
         kernel = "sol_fused_kernel"
-        run_kernel = lambda: bsa.fused(1, q, k, v, None, ws, sink_start, sink_tokens, args.kv_splits)  # noqa: E731
-        kernel_flops = flops_exact + flops_proxy
+        run_kernel = lambda: bsa.fused(1, q, k, v, None, ws, sink_start, sink_tokens, kv_splits)  # noqa: E731
         peak = 2500.0                                          # dense bf16 MFMA
     elif variant == 2:
         kernel = "sol2_fused_kernel"
         run_kernel = lambda: bsa.exact2(q, k, v, out, ws)    # noqa: E731
-        kernel_flops = flops_exact
         # QK^T on FP8 (5.0 PF) and PV on bf16 (2.5 PF), half the exact FLOPs each
-        peak = kernel_flops / (0.5 * kernel_flops / 5000.0 + 0.5 * kernel_flops / 2500.0)
+        peak = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
     else:
         kernel = "sol2_fused_kernel"
         run_kernel = lambda: bsa.exact2(q, k, v, out, ws, pv8=True)  # noqa: E731
-        kernel_flops = flops_exact
         peak = 5000.0                                          # QK^T and PV both on FP8
     for _ in range(2):
         run_kernel()
-    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for s in range(args.steps):
-        kev[s][0].record(stream)
+    for s_ in range(steps):
+        kev[s_][0].record(stream)
         run_kernel()
-        kev[s][1].record(stream)
+        kev[s_][1].record(stream)
     torch.cuda.synchronize()
     kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
-    achieved = kernel_flops / (kernel_ms * 1e-3) / 1e12
-    log(f"[bench] step {ms_per_step:.3f} ms (median event {med_step:.3f}); prepare {np.mean(prep_ms):.3f} ms, "
-        f"stage 2 {fused_avg:.3f} ms; {kernel} alone {kernel_ms:.3f} ms -> {achieved:.1f} TFLOP/s algorithmic")
-    from block_sparse_attention_tok_amd.profsum import read_traffic
-    tag = (("op_bench" if not args.text_sink else "long_sink") + f"_{N // 1024}k_{round(100 * args.sparsity)}pct"
-           + ("_pv8" if variant == 3 else ""))
-    traffic_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{kernel}_{tag}_traffic.md")
-    traffic = read_traffic(traffic_file, kernel)
+    kernel_flops = flops_exact + flops_proxy
+    res = dict(B=B, N=N, H=H, D=D, tau=tau, realised_sparsity=real_sp, exact_pairs=exact_pairs,
+               flops_exact=flops_exact, flops_proxy=flops_proxy, dense_flops=dense_flops,
+               ms_per_step=ms_per_step, median_event_ms=float(np.median(step_ms)),
+               prepare_ms=float(np.mean(prep_ms)), stage2_ms=float(np.mean(fused_ms)), kernel_ms=kernel_ms,
+               kernel=kernel, peak=peak, achieved=kernel_flops / (kernel_ms * 1e-3) / 1e12,
+               exact_frac=flops_exact / (kernel_ms * 1e-3) / (peak * 1e12),
+               kv_splits=bsa.kv_splits_for(B, N, H, kv_splits) if variant == 1 else 1,
+               workspace_mib=ws.numel() / 2**20)
+    log(f"[bench] step {ms_per_step:.3f} ms (median event {res['median_event_ms']:.3f}); prepare "
+        f"{res['prepare_ms']:.3f} ms, stage 2 {res['stage2_ms']:.3f} ms; {kernel} alone {kernel_ms:.3f} ms -> "
+        f"{res['achieved']:.1f} TFLOP/s algorithmic, exact-only fraction {res['exact_frac']:.4f}")
 
     baselines = {}
-    if not args.no_dense_baselines and variant == 1:
+    if dense_baselines and variant == 1:
         # (i) this library with every block exact (a sink over [0, N))
         def dense_own():
             bsa.prepare(1, q, k, v, tau, ws)
-            bsa.fused(1, q, k, v, out, ws, 0, N, args.kv_splits)
+            bsa.fused(1, q, k, v, out, ws, 0, N, kv_splits)
         # (ii) torch SDPA on ROCm, for comparison only
         qt, kt, vt = (t.transpose(1, 2) for t in (q, k, v))
 
@@ -219,19 +206,89 @@ def main():
                 baselines[name] = f"unavailable: {type(exc).__name__}"
         fastest = min([x for x in baselines.values() if isinstance(x, float)], default=None)
         if fastest:
-            baselines["speedup_vs_fastest_dense"] = fastest / med_step
+            baselines["speedup_vs_fastest_dense"] = fastest / res["median_event_ms"]
         log(f"[bench] dense baselines {baselines}")
+    res["dense_baselines"] = baselines
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); there is no multi-GPU run: "
+              "the path shards by (batch, head) with no communication.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.variant == "sol1train":
+        return bench_train(args)
+    variant = {"sol1": 1, "sol2": 2, "sol2pv8": 3}[args.variant]
+    H = args.heads
+    N = args.tokens + args.text_sink
+    log(f"[bench] generating B=1 N={N} H={H} d=128 ({args.variant})")
+    t0 = time.time()
+    qc, kc, vc = make_inputs(args.tokens, args.text_sink, H)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+    r = measure(variant, qc, kc, vc, args.text_sink, args.sparsity, args.tau, args.steps, args.warmup,
+                args.kv_splits, not args.no_dense_baselines)
+    value = r["dense_flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+
+    from block_sparse_attention_tok_amd.profsum import read_traffic
+    kernel = r["kernel"]
+    tag = (("op_bench" if not args.text_sink else "long_sink") + f"_{N // 1024}k_{round(100 * args.sparsity)}pct"
+           + ("_pv8" if variant == 3 else ""))
+    traffic_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{kernel}_{tag}_traffic.md")
+    traffic = read_traffic(traffic_file, kernel)
+
+    # The rest of the metric's range (Sol-Attn2 draft, "FP8 Kernel Performance": 32K-128K
+    # tokens; the Sources page's benchmark scope: 80/85/90% sparsity), measured in the same
+    # run on the same box: the operator shape at 80% and 85%, and 512 text-sink + 131072
+    # video tokens at 90%.  Each is a separate workload timed like the headline one.
+    rng_entries = []
+    if variant == 1 and not args.no_range and args.tau is None and not args.text_sink and args.tokens == 32768:
+        for video, sink, target in ((32768, 0, 0.80), (32768, 0, 0.85), (131072, 512, 0.90)):
+            if sink == args.text_sink and video == args.tokens and abs(target - args.sparsity) < 1e-9:
+                continue
+            log(f"[bench] range entry: {sink}+{video} tokens at {100 * target:.0f}%")
+            qr, kr, vr = (qc, kc, vc) if (video, sink) == (args.tokens, args.text_sink) else make_inputs(video, sink, H)
+            e = measure(variant, qr, kr, vr, sink, target, None, max(3, args.steps // 4 if video > 65536 else
+                                                                   args.steps // 2), 2, 0, False)
+            rng_entries.append({
+                "tokens": e["N"], "text_sink": sink, "target_sparsity": target,
+                "realised_sparsity": round(e["realised_sparsity"], 5), "tau": round(e["tau"], 5),
+                "ms_per_step": round(e["ms_per_step"], 4), "median_event_ms": round(e["median_event_ms"], 4),
+                "dense_eq_tflops": round(e["dense_flops"] / (e["ms_per_step"] * 1e-3) / 1e12, 2),
+                "kernel_ms": round(e["kernel_ms"], 4), "kv_splits": e["kv_splits"],
+                "exact_work_mfma_frac": round(e["exact_frac"], 4),
+                "exact_plus_proxy_mfma_frac": round(e["achieved"] / e["peak"], 4)})
+            del qr, kr, vr
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(qc, kc, vc, tau, sink_start, sink_tokens, variant, args.cpu_sample_heads,
-                           args.cpu_sample_blocks, dense_flops)
+        sink_start, sink_tokens = (0, args.text_sink) if args.text_sink else (None, 0)
+        cpu = cpu_baseline(qc, kc, vc, r["tau"], sink_start, sink_tokens, variant, args.cpu_sample_heads,
+                           args.cpu_sample_blocks, r["dense_flops"])
         log(f"[bench] cpu oracle {cpu}")
 
+    B, D = 1, 128
     workload = (f"{ {1: 'Sol-Attn', 2: 'Sol-Attn2 (FP8 Q/K)', 3: 'Sol-Attn2 (FP8 Q/K, ExpCast FP8 PV)'}[variant] } "
                 f"forward, B={B} H={H} d={D} "
                 f"N={N}{' (512 text sink + ' + str(args.tokens) + ' video)' if args.text_sink else ''}, "
                 f"block-offset synthetic data, {100 * args.sparsity:.0f}% target token-pair sparsity")
+    frac = r["achieved"] / r["peak"]
     rec = {
         "metric": "dense-equiv attn TFLOP/s + MFMA util, H32 d128 N=32K-128K @80-90% sparsity",
         "value": round(value, 2),
@@ -239,25 +296,29 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {1: "bf16", 2: "fp8(e4m3 QK)+bf16(PV)", 3: "fp8(e4m3 QK, ExpCast P, e4m3 V)"}[variant],
         "data": "synthetic (seeded block-offset Gaussian Q/K/V, bf16)",
         "config": {"workload": workload, "batch": B, "heads": H, "head_dim": D, "tokens": N,
-                   "tau": round(tau, 5), "realised_sparsity": round(real_sp, 5),
-                   "sink": [sink_start, sink_tokens], "median_event_ms": round(med_step, 4),
-                   "kv_splits": bsa.kv_splits_for(B, N, H, args.kv_splits) if variant == 1 else 1,
-                   "prepare_ms": round(float(np.mean(prep_ms)), 4), "stage2_ms": round(fused_avg, 4),
-                   "kernel_ms": round(kernel_ms, 4),
-                   "exact_work_mfma_frac": round(flops_exact / (kernel_ms * 1e-3) / (peak * 1e12), 4),
-                   "dense_baselines": baselines},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4),
+                   "tau": round(r["tau"], 5), "realised_sparsity": round(r["realised_sparsity"], 5),
+                   "selected_token_pairs": int(r["exact_pairs"]),
+                   "sink": [0 if args.text_sink else None, args.text_sink],
+                   "median_event_ms": round(r["median_event_ms"], 4),
+                   "kv_splits": r["kv_splits"], "workspace_mib": round(r["workspace_mib"], 1),
+                   "prepare_ms": round(r["prepare_ms"], 4), "stage2_ms": round(r["stage2_ms"], 4),
+                   "kernel_ms": round(r["kernel_ms"], 4),
+                   "exact_work_mfma_frac": round(r["exact_frac"], 4),
+                   "exact_plus_proxy_mfma_frac": round(frac, 4),
+                   "dense_baselines": r["dense_baselines"],
+                   "range": rng_entries},
+        "roofline": {"bound": "mfma", "achieved": round(r["achieved"], 2), "peak": round(r["peak"], 1),
+                     "unit": "TFLOP/s", "frac": round(frac, 4), "exact_only_frac": round(r["exact_frac"], 4),
                      "traffic": None if traffic is None else round(traffic),
                      "kernel": kernel,
-                     "work_per_launch": {"exact_flop": flops_exact, "proxy_flop": flops_proxy},
+                     "work_per_launch": {"exact_flop": r["flops_exact"], "proxy_flop": r["flops_proxy"]},
                      "traffic_source": os.path.relpath(traffic_file, os.path.dirname(os.path.abspath(__file__)))
                      if traffic is not None else None},
         "cpu_baseline": cpu,
@@ -395,7 +456,7 @@ def cpu_baseline(q, k, v, tau, sink_start, sink_tokens, variant, sample_heads, s
         n_blocks += len(blocks)
     t_full = B * H * (t_route / len(heads) + t_blocks / n_blocks * nb)
     return {"value": round(dense_flops / t_full / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",
-            "cores": int(cores), "kind": "oracle",
+            "cores": int(cores), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": (f"batch 0, {len(heads)} of {H} heads: full routing/summaries ({t_route:.1f} s) + "
                        f"{n_blocks // len(heads)} of {nb} query blocks each ({t_blocks:.1f} s), extrapolated to "
                        f"{B * H} heads x {nb} blocks = {t_full:.1f} s per call (float64 numpy)")}

@@ -93,7 +93,7 @@ def lib() -> ctypes.CDLL:
     for name in ("sol_attn_fused", "sol_attn2_fused"):
         getattr(L, name).argtypes = fused
         getattr(L, name).restype = i32
-    dbg = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, i32, vp, sz, vp, vp]
+    dbg = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, i32, vp, sz, vp, vp, vp]
     for name in ("sol_attn_debug_routing", "sol_attn2_debug_routing"):
         getattr(L, name).argtypes = dbg
         getattr(L, name).restype = i32
@@ -132,6 +132,25 @@ def _check_tensors(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
             raise ValueError(f"{name} must be a GPU tensor")
     if k.shape != q.shape or v.shape != q.shape or k.device != q.device or v.device != q.device:
         raise ValueError("k and v must have the same shape and device as q")
+
+
+def _check_like(t: Optional[torch.Tensor], q: torch.Tensor, name: str):
+    """A caller-supplied output must be a contiguous bf16 tensor of q's shape on q's device
+    (the kernels write it in full through a raw pointer)."""
+    if t is None:
+        return
+    if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_contiguous()
+            or t.shape != q.shape or t.device != q.device):
+        raise ValueError(f"{name} must be a contiguous bfloat16 tensor of q's shape {tuple(q.shape)} "
+                         f"on {q.device}")
+
+
+def _check_workspace(ws: torch.Tensor, q: torch.Tensor):
+    """The workspace is device memory on q's device; its size is passed in bytes."""
+    if not isinstance(ws, torch.Tensor) or ws.device != q.device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
+    if ws.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor (as alloc_workspace returns)")
 
 
 def kv_splits_for(batch: int, tokens: int, heads: int, kv_splits: int = 0) -> int:
@@ -177,10 +196,12 @@ def _full_call(fn_name: str, variant: int, q, k, v, tau, sink_start, sink_tokens
     if not math.isfinite(float(tau)):
         raise ValueError("tau must be finite")
     B, N, H, D = q.shape
+    _check_like(out, q, "out")
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
         workspace = alloc_workspace(variant, q)
+    _check_workspace(workspace, q)
     st = getattr(lib(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, float(tau),
                                  _sink_start(sink_start), int(sink_tokens), THRESH[thresh], _ptr(workspace),
                                  workspace.numel(), _stream(q.device))
@@ -201,6 +222,7 @@ def sol_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0
         return _full_call("sol_attn", SOL_VARIANT_SOL1, q, k, v, tau, sink_start, sink_tokens, thresh, out,
                           workspace)
     _check_tensors(q, k, v)
+    _check_like(out, q, "out")
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
@@ -246,6 +268,9 @@ def backward(q, k, v, out, dout, workspace: torch.Tensor, dq: Optional[torch.Ten
         if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.shape != q.shape or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous bfloat16 tensor of q's shape on q's device")
     B, N, H, D = q.shape
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_like(t, q, name)
+    _check_workspace(workspace, q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
@@ -281,6 +306,7 @@ def sol_attn_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float
 def prepare(variant: int, q, k, v, tau: float, workspace: torch.Tensor, thresh: str = "diag"):
     """Stage 1 (summaries + threshold [+ Sol-Attn2 quantization and groups]) into `workspace`."""
     _check_tensors(q, k, v)
+    _check_workspace(workspace, q)
     B, N, H, D = q.shape
     name = {SOL_VARIANT_SOL1: "sol_attn_prepare", SOL_VARIANT_SOL2: "sol_attn2_prepare",
             SOL_VARIANT_SOL2_PV8: "sol_attn2_pv8_prepare"}[variant]
@@ -291,6 +317,9 @@ def prepare(variant: int, q, k, v, tau: float, workspace: torch.Tensor, thresh: 
 def fused(variant: int, q, k, v, out, workspace: torch.Tensor, sink_start: Optional[int] = None,
           sink_tokens: int = 0, kv_splits: int = 0):
     """Stage 2 (the fused kernel [+ split merge]) reading a workspace prepared for the same inputs."""
+    _check_tensors(q, k, v)
+    _check_like(out, q, "out")
+    _check_workspace(workspace, q)
     B, N, H, D = q.shape
     if variant == SOL_VARIANT_SOL1:
         _check(lib().sol_attn_fused_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
@@ -308,6 +337,8 @@ def fused(variant: int, q, k, v, out, workspace: torch.Tensor, sink_start: Optio
 
 def tail2(q, k, v, workspace: torch.Tensor, sink_start: Optional[int] = None, sink_tokens: int = 0):
     """Sol-Attn2 stage 2a: routing bits and the per-anchor tail, into the workspace."""
+    _check_tensors(q, k, v)
+    _check_workspace(workspace, q)
     B, N, H, D = q.shape
     _check(lib().sol_attn2_tail(_ptr(q), _ptr(k), _ptr(v), B, N, H, D, _sink_start(sink_start), int(sink_tokens),
                                 _ptr(workspace), workspace.numel(), _stream(q.device)), "sol_attn2_tail")
@@ -315,6 +346,11 @@ def tail2(q, k, v, workspace: torch.Tensor, sink_start: Optional[int] = None, si
 
 def exact2(q, k, v, out, workspace: torch.Tensor, pv8: bool = False):
     """Sol-Attn2 stage 2b: the exact FP8 pass (FP8 PV with pv8) combined with the tail of stage 2a."""
+    _check_tensors(q, k, v)
+    _check_like(out, q, "out")
+    if out is None:
+        raise ValueError("out is required")
+    _check_workspace(workspace, q)
     B, N, H, D = q.shape
     name = "sol_attn2_pv8_exact" if pv8 else "sol_attn2_exact"
     _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _ptr(workspace),
@@ -323,24 +359,31 @@ def exact2(q, k, v, out, workspace: torch.Tensor, pv8: bool = False):
 
 def debug_routing(variant: int, q, k, v, tau: float = 1.0, thresh: str = "diag", sink_start: Optional[int] = None,
                   sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, kv_splits: int = 0):
-    """Run the full call and return (out, masks [B, H, nb, nb] bool on the CPU, workspace).
+                  workspace: Optional[torch.Tensor] = None, kv_splits: int = 0, return_pairs: bool = False):
+    """Run the full call and return (out, masks [B, H, nb, nb] bool on the CPU, workspace), plus,
+    with return_pairs, the kernel's count of selected token pairs sum n_i n_j (a Python int).
 
-    The masks are the decisions the fused kernel itself made (test export)."""
+    The masks and the count are what the fused kernel itself decided (test export)."""
     _check_tensors(q, k, v)
+    _check_like(out, q, "out")
     B, N, H, D = q.shape
     nb = (N + 63) // 64
     nbw = (nb + 63) // 64
     if workspace is None:
         workspace = alloc_workspace(variant, q, kv_splits)
+    _check_workspace(workspace, q)
     words = torch.zeros(B * H * nb * nbw, dtype=torch.int64, device=q.device)
+    pairs = torch.zeros(1, dtype=torch.int64, device=q.device)
     name = "sol_attn_debug_routing" if variant == SOL_VARIANT_SOL1 else "sol_attn2_debug_routing"
     _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, float(tau),
                                 _sink_start(sink_start), int(sink_tokens), THRESH[thresh], int(kv_splits),
-                                _ptr(workspace), workspace.numel(), _ptr(words), _stream(q.device)), name)
+                                _ptr(workspace), workspace.numel(), _ptr(words), _ptr(pairs), _stream(q.device)),
+           name)
     w = words.view(B, H, nb, nbw).cpu()
     bits = torch.arange(64, dtype=torch.int64)
     m = ((w.unsqueeze(-1) >> bits) & 1).bool().reshape(B, H, nb, nbw * 64)[..., :nb]
+    if return_pairs:
+        return out, m, workspace, int(pairs.item())
     return out, m, workspace
 
 

@@ -85,7 +85,6 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   if (variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN) {
     L->kh = take(bh * tokens * kDim * 2);
     L->vh = take(bh * tokens * kDim * 2);
-    L->sel = take(bh * nb * (nbp / 64) * 8);
   }
   if (variant == SOL_VARIANT_SOL2 || variant == SOL_VARIANT_SOL2_PV8) {
     const int64_t tp = nbp * kBlock;
@@ -275,10 +274,8 @@ int sol_attn_prepare(const void* q, const void* k, const void* v, int64_t batch,
   hipStream_t hs = (hipStream_t)stream;
   st = hip_status(solattn::launch_summary((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s, w, hs));
   if (st != SOL_OK) return st;
-  st = hip_status(solattn::launch_threshold(s, w, tau, thresh == SOL_THRESH_EXACT, hs));
-  if (st != SOL_OK) return st;
-  // threshold routing words (the sink is forced in stage 2)
-  return hip_status(solattn::launch_route(s, w, 1, 0, w.sel, hs));
+  // the routing itself happens inside the fused kernel of stage 2
+  return hip_status(solattn::launch_threshold(s, w, tau, thresh == SOL_THRESH_EXACT, hs));
 }
 
 // Sol-Attn2 stage 2 parts: the routing + tail pass, the exact pass, or both in order.
@@ -287,7 +284,8 @@ enum { kStage2Tail = 1, kStage2Exact = 2, kStage2Both = 3 };
 static int fused_common(int variant, const void* q, const void* k, const void* v, void* out, int64_t batch,
                         int64_t tokens, int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens,
                         void* workspace, size_t workspace_bytes, uint64_t* mask_bits, void* stream,
-                        bool out_required, int kv_splits = 0, int stage2 = kStage2Both) {
+                        bool out_required, int kv_splits = 0, int stage2 = kStage2Both,
+                        uint64_t* selected_pairs = nullptr) {
   sol_ws_layout L;
   if (check_kv(kv_splits) != SOL_OK) return SOL_ERR_ARG;
   int st = prologue(variant, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L, kv_splits);
@@ -301,7 +299,7 @@ static int fused_common(int variant, const void* q, const void* k, const void* v
   if (variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN)
     return hip_status(solattn::launch_fused((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                             (uint16_t*)out, s, w, b0, b1, mask_bits ? mask_bits : w.mrow,
-                                            (hipStream_t)stream));
+                                            (unsigned long long*)selected_pairs, (hipStream_t)stream));
   hipStream_t hs = (hipStream_t)stream;
   if (stage2 & kStage2Tail) {
     if ((st = hip_status(solattn::launch_tail2(s, w, b0, b1, hs))) != SOL_OK) return st;
@@ -313,7 +311,7 @@ static int fused_common(int variant, const void* q, const void* k, const void* v
   }
   if (!(stage2 & kStage2Exact)) return SOL_OK;
   return hip_status(solattn::launch_fused2((const uint16_t*)v, (uint16_t*)out, s, w,
-                                           variant == SOL_VARIANT_SOL2_PV8, hs));
+                                           variant == SOL_VARIANT_SOL2_PV8, (unsigned long long*)selected_pairs, hs));
 }
 
 int sol_attn_fused(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
@@ -375,7 +373,7 @@ int sol_attn_backward(const void* q, const void* k, const void* v, const void* o
 int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
                            int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens,
                            int thresh, int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
-                           void* stream) {
+                           uint64_t* selected_pairs, void* stream) {
   if (!mask_bits) return SOL_ERR_NULL;
   int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
   if (st != SOL_OK) return st;
@@ -383,7 +381,7 @@ int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* ou
   st = sol_attn_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);
   if (st != SOL_OK) return st;
   return fused_common(SOL_VARIANT_SOL1, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
-                      workspace, workspace_bytes, mask_bits, stream, false, kv_splits);
+                      workspace, workspace_bytes, mask_bits, stream, false, kv_splits, kStage2Both, selected_pairs);
 }
 
 static int prepare2(int variant, const void* q, const void* k, const void* v, int64_t batch, int64_t tokens,
@@ -476,7 +474,7 @@ int sol_attn2(const void* q, const void* k, const void* v, void* out, int64_t ba
 int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
                             int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens,
                             int thresh, int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
-                            void* stream) {
+                            uint64_t* selected_pairs, void* stream) {
   if (!mask_bits) return SOL_ERR_NULL;
   if (kv_splits != 0 && kv_splits != 1) return SOL_ERR_ARG;
   int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
@@ -484,7 +482,7 @@ int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* o
   st = sol_attn2_prepare(q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace, workspace_bytes, stream);
   if (st != SOL_OK) return st;
   return fused_common(SOL_VARIANT_SOL2, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
-                      workspace, workspace_bytes, mask_bits, stream, false);
+                      workspace, workspace_bytes, mask_bits, stream, false, 0, kStage2Both, selected_pairs);
 }
 
 }  // extern "C"

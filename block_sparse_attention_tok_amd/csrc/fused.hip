@@ -5,16 +5,21 @@
 // online-softmax state in registers; it streams the pooled keys / values in
 // chunks, folds every unselected block in through its proxy (token-to-block tile
 // Q_i K-bar^T with weight n_j and the V sum V-hat_j) and runs exact attention on
-// the original K/V blocks of the selected indices.  The selection itself (each
-// block's proxy score s_ij = Q-bar_i . K-bar_j / sqrt(d) against tau_i, Eq. (4),
-// Eq. (6)) comes from the routing pass of stage 1 as one bit per block pair; the
-// kernel adds the sink's blocks.  No proxy is written to memory.
+// the original K/V blocks of the selected indices.  The selection is made here,
+// chunk by chunk (§3.1 Eq. (4), §3.2 Eq. (6)): each block's proxy score
+// s_ij = Q-bar_i . K-bar_j / sqrt(d), from the fp32 block means of stage 1,
+// against the query block's threshold tau_i, with the sink's blocks forced exact.
+// The decisions live in LDS only; no proxy score or routing map is written to
+// memory (the test export may copy the words out).
 //
 // gfx950 mapping: one workgroup = one (batch, head, 64-row query block, key
 // split), two wave64s of 32 query rows; __launch_bounds__(128, 2) keeps two
 // waves per SIMD; workgroups are ordered so that each XCD walks its own heads.
-//   * The routing words of the split's chunks are loaded first; the per-chunk
-//     selection and proxy masks stay in LDS.
+//   * Routing: lane l of a wave scores key block 64 c + l of chunk c (128 fp32
+//     FMAs over the block means, Q-bar_i broadcast from LDS), and one ballot
+//     against tau_i gives the chunk's 64-bit selection word; the two waves take
+//     alternate chunks of the split while the first pooled tile's DMA is in
+//     flight.  The per-chunk selection and proxy masks stay in LDS.
 //   * The tile stream is the pooled tile of every chunk (K-bar / V-bar = V-hat/n
 //     rows with logit bias log2 n_j; selected and padding columns masked), then
 //     the selected exact blocks chunk by chunk.
@@ -54,9 +59,12 @@ struct FusedArgs {
   uint16_t* opart; float* olse; // split partials (S > 1)
   const uint16_t* kbar_h; const uint16_t* vbar_h;
   const uint16_t* kh; const uint16_t* vh;   // head-major copies of k and v ([B][H][N][128])
+  const float* qbar;            // [B][H][nbp][128] fp32 query-block means
+  const float* kbar_t;          // [B][H][32][nbp][4] fp32 key-block means, 4-dim interleaved
+  const float* tau_i;           // [B][H][nbp] thresholds
   int sink_b0, sink_b1;
-  const uint64_t* route;        // threshold routing words [B][H][nb][nbw] (stage 1, no sink)
-  uint64_t* mask_out;           // the words used, sink included (NULL = none)
+  uint64_t* mask_out;           // the selection words used, sink included (NULL = none)
+  unsigned long long* pairs;    // += selected token pairs n_i n_j of this work item (NULL = none)
   float* lse;                   // [B][H][tp] base-2 log-sum-exp per query row (NULL = none)
   int tp;
 };
@@ -97,6 +105,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Kl[64 * 256];
   __shared__ __attribute__((aligned(1024))) unsigned char Vl[64 * 256];
   __shared__ uint64_t sel_s[kMaxChunks], prox_s[kMaxChunks];
+  __shared__ float4 qbar_s[kDim / 4];                        // Q-bar_i (fp32), read by every lane
   __shared__ int redo_s[2];
 
   // Work item order: query block fastest, then key split, then (batch, head), so the
@@ -122,6 +131,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, src[2 * ks + kg]);
   }
+  if (tid < kDim / 4) qbar_s[tid] = ((const float4*)(a.qbar + ((size_t)bh * a.nbp + i) * kDim))[tid];
   __syncthreads();
 
   // Buffer resources over this head's rows of the head-major k / v copies and of the
@@ -137,26 +147,53 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   const int c_begin = split * a.cps;                        // this split's routing chunks
   const int c_end = min(a.nbp / 64, c_begin + a.cps);
   const int nchunks = c_end - c_begin;
-  // The routing words of this query block's chunks (threshold test of stage 1's routing
-  // pass) are loaded first, then the first tile's DMA (the pooled tile of the split's first
-  // chunk) is issued, so that the words do not wait for it.  The sink's blocks are forced
-  // exact here, since the sink is a stage-2 argument.
-  uint64_t selm = 0;
-  if (tid < nchunks) selm = a.route[((size_t)bh * a.nb + i) * a.nbw + c_begin + tid];
+  // Routing of the split's chunks (Sol-Attn paper §3.1 Eq. (4), §3.2 Eq. (6)).  The first
+  // pooled tile's DMA does not depend on it and is issued first.  Wave w scores chunks
+  // c_begin + w, c_begin + w + 2, ...: lane l takes key block j = 64 c + l (j < nbp, so the
+  // padded fp32 means are in memory) and sums Q-bar_i . K-bar_j over the 128 dims in
+  // ascending order with fp32 FMAs; s_ij > tau_i is one ballot.  The sink's blocks are
+  // forced exact and the chunk's padding blocks cleared.
   auto pool = [&]() { return make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool); };
   dma_tile<false>(Kl, pool(), (uint32_t)c_begin * 64 * row_bytes, row_bytes, doff, w);
-  if (tid < nchunks) {
-    const int c = c_begin + tid;
-    const int nvalid = a.nb - 64 * c;                       // valid blocks of the chunk (>= 1)
-    const uint64_t validm = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
-    const int s0 = max(a.sink_b0, 64 * c), s1 = min(a.sink_b1, 64 * c + 63);
-    if (s0 <= s1) selm |= (~0ull >> (63 - (s1 - s0))) << (s0 - 64 * c);
-    selm &= validm;
-    sel_s[tid] = selm;
-    prox_s[tid] = validm & ~selm;
-    if (a.mask_out) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
+  {
+    const float tau = a.tau_i[(size_t)bh * a.nbp + i];
+    const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
+    for (int cc = w; cc < nchunks; cc += 2) {
+      const int c = c_begin + cc;
+      const int j = 64 * c + lane;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int g = 0; g < 32; ++g) {
+        const float4 kv = kt[(size_t)g * a.nbp + j];
+        const float4 qv = qbar_s[g];
+        acc = __builtin_fmaf(qv.x, kv.x, acc);
+        acc = __builtin_fmaf(qv.y, kv.y, acc);
+        acc = __builtin_fmaf(qv.z, kv.z, acc);
+        acc = __builtin_fmaf(qv.w, kv.w, acc);
+      }
+      uint64_t selm = __ballot(acc * kScale > tau);
+      const int nvalid = a.nb - 64 * c;                      // valid blocks of the chunk (>= 1)
+      const uint64_t validm = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+      const int s0 = max(a.sink_b0, 64 * c), s1 = min(a.sink_b1, 64 * c + 63);
+      if (s0 <= s1) selm |= (~0ull >> (63 - (s1 - s0))) << (s0 - 64 * c);
+      selm &= validm;
+      if (lane == 0) {
+        sel_s[cc] = selm;
+        prox_s[cc] = validm & ~selm;
+        if (a.mask_out) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = selm;
+      }
+    }
   }
   lds_barrier();
+  if (a.pairs != nullptr && tid == 0) {
+    // selected token pairs of this work item: n_i times the valid tokens of its exact blocks
+    unsigned long long cols = 0;
+    for (int cc = 0; cc < nchunks; ++cc) cols += 64ull * (unsigned)__builtin_popcountll(sel_s[cc]);
+    const int last = a.nb - 1, last_n = a.N - last * kBlock;
+    if (last >= 64 * c_begin && last < 64 * c_end && ((sel_s[last / 64 - c_begin] >> (last & 63)) & 1))
+      cols -= (unsigned long long)(kBlock - last_n);
+    atomicAdd(a.pairs, cols * (unsigned long long)min(kBlock, a.N - i * kBlock));
+  }
 
   // ---- per-lane LDS offsets
   // S^T A operand: key row 32 mt + l32, k-step ks reads logical chunk 2 ks + kg, physical slot
@@ -437,13 +474,18 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const uint4v* __restr
   out[t] = r;
 }
 
+// Clears the selected-pair counter on the stream (a kernel rather than a memset, so the
+// call can also sit in a captured graph).
+__global__ void zero_counter_kernel(unsigned long long* p) { *p = 0ull; }
+
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                         Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* mask_out,
-                        hipStream_t stream) {
+                        unsigned long long* pairs, hipStream_t stream) {
   const int nchunks = ws.nbp / 64;
   const int S = ws.kv_splits;
   const int cps = (nchunks + S - 1) / S;
-  if (cps > kMaxChunks || (S > 1 && (!ws.opart || !ws.olse)) || !ws.kh || !ws.vh || !ws.sel)
+  if (cps > kMaxChunks || (S > 1 && (!ws.opart || !ws.olse)) || !ws.kh || !ws.vh || !ws.qbar || !ws.kbar_t ||
+      !ws.tau_i)
     return hipErrorInvalidValue;
   FusedArgs a;
   a.q = q; a.out = out;   // k and v are read through stage 1's head-major copies
@@ -451,9 +493,15 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   a.S = S; a.cps = cps; a.opart = ws.opart; a.olse = ws.olse;
   a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h;
   a.kh = ws.kh; a.vh = ws.vh;
+  a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.tau_i = ws.tau_i;
   a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
-  a.route = ws.sel;
+  a.pairs = pairs;
   a.lse = ws.lse; a.tp = ws.nbp * kBlock;
+  if (pairs != nullptr) {
+    hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(1), 0, stream, pairs);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   const int total = s.B * s.H * S * ws.nb;
   hipLaunchKernelGGL(sol_fused_kernel, dim3(total), dim3(128), 0, stream, a);
   hipError_t e = hipGetLastError();

@@ -31,7 +31,7 @@ struct Workspace {
   int kv_splits;    // key-range splits of the fused Sol-Attn pass (1 = none)
   uint16_t* opart;  // [S][B][N][H][128] bf16 normalized partial outputs
   float* olse;      // [S][B][N][H] log2-sum-exp of the partial rows
-  uint64_t* sel;    // [B][H][nb][nbp / 64] Sol-Attn2 routing bits
+  uint64_t* sel;    // [B][H][nb][nbp / 64] Sol-Attn2 routing bits (the tail and exact passes)
   float* tmu;       // [B][H][nbp][2][128] Sol-Attn2 tail key means per anchor
   float* tnu;       // [B][H][nbp][2][128] Sol-Attn2 tail value means per anchor
   float* tlz;       // [B][H][nbp][2] log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d)
@@ -56,10 +56,12 @@ hipError_t launch_summary(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           const Workspace& ws, hipStream_t stream);
 // Key statistics and per-query-block thresholds (diag or exact).
 hipError_t launch_threshold(Shape s, const Workspace& ws, float tau, int exact, hipStream_t stream);
-// Sol-Attn stage 2: fused routing + proxy reuse + exact attention.
+// Sol-Attn stage 2: fused routing + proxy reuse + exact attention.  mask_out (optional)
+// receives the selection words the kernel used; pairs (optional) is cleared and then
+// receives the number of selected token pairs sum n_i n_j.
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                         Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* mask_out,
-                        hipStream_t stream);
+                        unsigned long long* pairs, hipStream_t stream);
 
 // Sol-Attn2 stage 1: FP8 quantization of Q/K with block means of the dequantized values
 // and V block means; then the mean-query direction and key groups.
@@ -68,15 +70,15 @@ hipError_t launch_quant_summary(const uint16_t* q, const uint16_t* k, const uint
 hipError_t launch_qhat(Shape s, const Workspace& ws, hipStream_t stream);
 hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream);
 // Routing bits of every (query block, key block) pair from the fp32 block means and tau_i,
-// with the blocks [sink_b0, sink_b1] forced, into sel [B][H][nb][nbp / 64] (Sol-Attn stage 1
-// with an empty sink range, Sol-Attn2 stage 2 with the sink).
+// with the blocks [sink_b0, sink_b1] forced, into sel [B][H][nb][nbp / 64] (Sol-Attn2 stage 2:
+// the tail pass and the exact pass both read them, so they agree on every exact set).
 hipError_t launch_route(Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* sel,
                         hipStream_t stream);
 // Sol-Attn2 stage 2: routing and the complementary tail per anchor (writes sel, tmu, tnu, tlz),
 // then the exact FP8 pass combined with the tail.
 hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream);
 hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, bool pv8,
-                         hipStream_t stream);
+                         unsigned long long* pairs, hipStream_t stream);
 // Sol-Attn backward with the forward's routing fixed: D and the transposed masks, the
 // pooled-key gradients, dK / dV per key block, then dQ per query block.
 hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,

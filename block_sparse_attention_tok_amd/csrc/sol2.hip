@@ -621,6 +621,7 @@ struct Fused2Args {
   const uint8_t* q8; const uint8_t* k8; const float* qscale; const float* kscale;
   const uint64_t* sel; const float* tmu; const float* tnu; const float* tlz;
   const uint8_t* v8t; const float* vscale;   // FP8 PV only
+  unsigned long long* pairs;                 // += selected token pairs n_i n_j (NULL = none)
 };
 
 // 16-byte slot swizzle of the 128 x 64-byte FP8 V^T tile (rows = dims): 16 consecutive
@@ -669,6 +670,14 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
     qf[1] = src[2 + kg];      // dims 64 + 32 kg .. + 31
   }
   __syncthreads();
+  if (a.pairs != nullptr && tid == 0) {
+    // selected token pairs of this query block: n_i times the valid tokens of its exact blocks
+    unsigned long long cols = 0;
+    for (int c = 0; c < a.nbw; ++c) cols += 64ull * (unsigned)__builtin_popcountll(sel_s[c]);
+    const int last = a.nb - 1;
+    if ((sel_s[last / 64] >> (last & 63)) & 1) cols -= (unsigned long long)(kBlock - (a.N - last * kBlock));
+    atomicAdd(a.pairs, cols * (unsigned long long)min(kBlock, a.N - i * kBlock));
+  }
 
   // K8 operand reads: row 32 mt + l32, logical chunks 4 ks + 2 kg (+1); swz8 depends on l32 only.
   const int sz = swz8(l32);
@@ -912,8 +921,10 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   }
 }
 
+__global__ void zero_counter2_kernel(unsigned long long* p) { *p = 0ull; }
+
 hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, bool pv8,
-                         hipStream_t stream) {
+                         unsigned long long* pairs, hipStream_t stream) {
   if (ws.nbp / 64 > kMaxChunks2 || (pv8 && (!ws.v8t || !ws.vscale))) return hipErrorInvalidValue;
   Fused2Args a;
   a.v = v; a.out = out;
@@ -921,6 +932,12 @@ hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Worksp
   a.q8 = ws.q8; a.k8 = ws.k8; a.qscale = ws.qscale; a.kscale = ws.kscale;
   a.sel = ws.sel; a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
   a.v8t = ws.v8t; a.vscale = ws.vscale;
+  a.pairs = pairs;
+  if (pairs != nullptr) {   // the counter is cleared on the stream by a kernel (graph-safe)
+    hipLaunchKernelGGL(zero_counter2_kernel, dim3(1), dim3(1), 0, stream, pairs);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   const int total = s.B * s.H * ws.nb;
   if (pv8) hipLaunchKernelGGL(sol2_fused_kernel<true>, dim3(total), dim3(128), 0, stream, a);
   else hipLaunchKernelGGL(sol2_fused_kernel<false>, dim3(total), dim3(128), 0, stream, a);

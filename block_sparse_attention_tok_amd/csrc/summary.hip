@@ -118,9 +118,13 @@ hipError_t launch_summary(const uint16_t* q, const uint16_t* k, const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Routing (Sol-Attn paper §3.1, Eq. (6); Sol-Attn2 draft, Method, Eq. (1) selection):
-// s-hat_ij = Q-bar_i . K-bar_j / sqrt(d) from the fp32 block means (for Sol-Attn2 of the
-// dequantized values), against tau_i, with the blocks of a sink range forced exact.  One wave per (b, h, 32 query blocks from i0, 64-block chunk c): the 32 x 64
+// Sol-Attn2 routing (Sol-Attn2 draft, Method, Eq. (1) selection, with the Sol-Attn rule of
+// §3.1 Eq. (4)): s-hat_ij = Q-bar_i . K-bar_j / sqrt(d) from the fp32 means of the
+// dequantized blocks, against tau_i, with the blocks of a sink range forced exact.  Its
+// two consumers, the tail pass (32 query blocks per workgroup) and the exact pass (one
+// query block per workgroup), must agree on every exact set, so the bits are decided once
+// here.  (Sol-Attn routes inside its fused kernel and has no such pass.)  One wave per
+// (b, h, 32 query blocks from i0, 64-block chunk c): the 32 x 64
 // products on v_mfma_f32_32x32x2_f32 (fp32 operands and sums), A = the query-block means,
 // B = the key-block means, with the contraction order chosen so that lane (m, kh) reads
 // dims 64 kh .. 64 kh + 63 of its row contiguously (k-step s takes dim 64 kh + s).  The

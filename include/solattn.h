@@ -80,9 +80,11 @@ typedef enum {
  *   qanc     float [B][H][nbp][2][128] 32-token anchor means of dequantized Q (Sol-Attn2)
  *   opart    bf16  [S][B][N][H][128]   per-key-split normalized partial outputs (S = kv_splits > 1)
  *   olse     float [S][B][N][H]        per-key-split log2-sum-exp of the partial rows
- *   sel      uint64 [B][H][nb][nbp/64] routing bits, bit j % 64 of word j / 64 set iff block j
- *                                      is exact for query block i (Sol-Attn: threshold bits of
- *                                      stage 1, the sink added by stage 2; Sol-Attn2: with the sink)
+ *   sel      uint64 [B][H][nb][nbp/64] Sol-Attn2 routing bits (sink included), bit j % 64 of word
+ *                                      j / 64 set iff block j is exact for query block i; written
+ *                                      by stage 2a, read by the tail and exact passes, which must
+ *                                      agree on every exact set.  Sol-Attn has no routing array:
+ *                                      its fused kernel decides each chunk on chip
  *   tmu, tnu float [B][H][nbp][2][128] per-anchor tail key / value means mu_a, nu_a (Sol-Attn2)
  *   tlz      float [B][H][nbp][2]     log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d); -inf if the
  *                                      anchor's tail is empty (Sol-Attn2)
@@ -171,19 +173,19 @@ int sol_attn(const void* q, const void* k, const void* v, void* out,
 
 /* Stage 1 of sol_attn: block summaries (Q/K means, V sums as means), the
  * per-query-block threshold tau_i (paper §3.1 Eqs. (4)-(5); the paper keeps
- * only this threshold computation outside the attention kernel, §4.5), the
- * routing bits s-hat_ij > tau_i of every (query block, key block) pair (Eq. (6),
- * without the sink, which stage 2 adds), and the head-major K / V copies.
- * Writes the workspace arrays qbar..kcov, kh, vh and sel.  Same arguments as
- * sol_attn minus out and the sink. */
+ * only this threshold computation outside the attention kernel, §4.5), and the
+ * head-major K / V copies.  Writes the workspace arrays qbar..kpart, kh and vh.
+ * Same arguments as sol_attn minus out and the sink. */
 int sol_attn_prepare(const void* q, const void* k, const void* v,
                      int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                      float tau, int thresh, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 2 of sol_attn: the fused proxy-reuse + exact online-softmax kernel
- * (paper §3.2 "Hardware-Aligned Implementation") over stage 1's routing bits with
- * the sink's blocks forced exact.  Reads the workspace written by
- * sol_attn_prepare for the same q, k, v and shape. */
+/* Stage 2 of sol_attn: the fused routing + proxy-reuse + exact online-softmax
+ * kernel (paper §3.2 "Hardware-Aligned Implementation", Eq. (6)): each query
+ * block's proxy scores s_ij = Q-bar_i . K-bar_j / sqrt(d) are compared with tau_i
+ * chunk by chunk inside the kernel (the sink's blocks forced exact) and the
+ * decisions stay on chip.  Reads the workspace written by sol_attn_prepare for
+ * the same q, k, v and shape. */
 int sol_attn_fused(const void* q, const void* k, const void* v, void* out,
                    int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                    int64_t sink_start, int64_t sink_tokens,
@@ -234,12 +236,18 @@ int sol_attn_backward(const void* q, const void* k, const void* v, const void* o
  * fused kernel also writes the routing decision it made, as bit masks
  * mask_bits[b][h][i][w] (device, uint64, nbw = ceil(nb/64) words per query
  * block; bit (j % 64) of word j / 64 set iff KV block j was exact for query
- * block i).  `out` may be NULL to skip the output store. */
+ * block i).  selected_pairs (device, one uint64, may be NULL) receives the
+ * number of selected token pairs, sum over exact (i, j) of n_i n_j with n the
+ * valid tokens of a block, counted by the fused kernel from the words it used
+ * (the realised token-pair sparsity is 1 - selected_pairs / (B H N^2); Sol-Attn2
+ * draft, "FP8 Kernel Performance", reports sparsity over token pairs); the call
+ * clears it first.  `out` may be NULL to skip the output store.  Errors as
+ * sol_attn; SOL_ERR_NULL if mask_bits is NULL. */
 int sol_attn_debug_routing(const void* q, const void* k, const void* v, void* out,
                            int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                            float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
                            int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
-                           void* stream);
+                           uint64_t* selected_pairs, void* stream);
 
 /*
  * Sol-Attn2 forward with the complementary tail (Sol-Attn2 draft, Method,
@@ -313,12 +321,12 @@ int sol_attn2_pv8_exact(const void* q, const void* k, const void* v, void* out,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sol-Attn2 routing export, as sol_attn_debug_routing (kv_splits must be 0 or 1:
- * the Sol-Attn2 pass is not split). */
+ * the Sol-Attn2 pass is not split); selected_pairs is counted by the exact pass. */
 int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* out,
                             int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                             float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
                             int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
-                            void* stream);
+                            uint64_t* selected_pairs, void* stream);
 
 #ifdef __cplusplus
 }

@@ -225,13 +225,20 @@ def sol_attn_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float = 1.0,
     return HeadResult(out, sel, s_hat, tau_i, mu_i, sigma_i, counts)
 
 
+def selected_pairs(sel: np.ndarray, n_tokens: int, block: int = BLOCK) -> int:
+    """Exact token pairs sum_{exact (i, j)} n_i n_j over [..., nb, nb] masks, as an integer
+    (the token-pair count behind the realised sparsity; Sol-Attn2 draft, "FP8 Kernel
+    Performance", states sparsity over token pairs)."""
+    c = block_counts(n_tokens, block).astype(np.int64)
+    sel = np.asarray(sel, dtype=bool)
+    return int((sel.astype(np.int64) * np.outer(c, c)).sum())
+
+
 def realised_sparsity(sel: np.ndarray, n_tokens: int, block: int = BLOCK) -> float:
     """Token-pair sparsity 1 - sum_{exact (i,j)} n_i n_j / N^2 over [..., nb, nb] masks."""
-    c = block_counts(n_tokens, block)
-    pairs = np.outer(c, c)
     sel = np.asarray(sel, dtype=bool)
     lead = int(np.prod(sel.shape[:-2])) if sel.ndim > 2 else 1
-    return 1.0 - float((sel * pairs).sum()) / (lead * float(n_tokens) ** 2)
+    return 1.0 - selected_pairs(sel, n_tokens, block) / (lead * float(n_tokens) ** 2)
 
 
 def _head(x, b: int, h: int) -> np.ndarray:

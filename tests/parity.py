@@ -32,6 +32,28 @@ def mask_check(gpu_sel: np.ndarray, ref_sel: np.ndarray, s_hat: np.ndarray, tau_
     return int(diff.sum())
 
 
+def pair_check(gpu_pairs: int, gpu_sel: np.ndarray, ref_sel: np.ndarray, n_tokens: int):
+    """The kernel's selected-token-pair counter equals the oracle's count of its own masks
+    (integer, exact), and the oracle's masks' count wherever the two mask sets agree."""
+    want = sa.selected_pairs(gpu_sel, n_tokens)
+    assert gpu_pairs == want, f"selected pairs {gpu_pairs} != {want} counted from the kernel's masks"
+    if np.array_equal(gpu_sel, ref_sel):
+        assert gpu_pairs == sa.selected_pairs(ref_sel, n_tokens)
+
+
+def anchor_errors(got: np.ndarray, want: np.ndarray, anchor: int = 32) -> list:
+    """Relative L2 error of each 32-row anchor of one query block's rows (rows [0, 32) and
+    [32, n)); an anchor whose reference is zero is skipped."""
+    errs = []
+    for a0 in range(0, want.shape[0], anchor):
+        w = np.asarray(want[a0:a0 + anchor], dtype=np.float64)
+        g = np.asarray(got[a0:a0 + anchor], dtype=np.float64)
+        nw = np.linalg.norm(w)
+        if nw > 0:
+            errs.append(float(np.linalg.norm(g - w) / nw))
+    return errs
+
+
 def oracle_rows(q, k, v, b, h, i, sel_row):
     """Oracle output rows of query block i for (b, h) under a given selection row."""
     qh = q[b, :, h, :].to(torch.float64).numpy()

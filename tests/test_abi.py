@@ -80,8 +80,11 @@ def test_workspace_sizes_and_layout(L):
                           for o in [getattr(lay, name)] if o >= 0)
             assert all(o % 256 == 0 for o in offs)
             assert offs[-1] < n
-            if variant == 1:
-                assert lay.q8 == -1 and lay.gk == -1
+            if variant in (1, 4):
+                # Sol-Attn routes inside its fused kernel: no routing array in its workspace
+                assert lay.q8 == -1 and lay.gk == -1 and lay.sel == -1
+            else:
+                assert lay.sel >= 0
     assert L.sol_attn_workspace_bytes(1, 1, 1024, 2, 64) == 0
     assert L.sol_attn_workspace_bytes(5, 1, 1024, 2, 128) == 0
 
@@ -165,9 +168,16 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
     assert L.sol_attn(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 0, vp(0x1010), 1 << 30, None) == 8
     # unknown threshold type
     assert L.sol_attn(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 9, fake, 1 << 30, None) == 8
-    # missing mask buffer for the debug export
+    # missing mask buffer for the debug export (the selected-pair counter is optional: a NULL
+    # counter is not an error, so the non-finite tau is what gets reported)
     assert L.sol_attn_debug_routing(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, 0, fake, 1 << 30,
-                                    None, None) == 1
+                                    None, fake, None) == 1
+    assert L.sol_attn_debug_routing(fake, fake, fake, None, 1, 1024, 2, 128, float("nan"), -1, 0, 0, 0, fake,
+                                    1 << 30, fake, None, None) == 4
+    assert L.sol_attn2_debug_routing(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, 0, fake, 1 << 30,
+                                     None, None, None) == 1
+    assert L.sol_attn2_debug_routing(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, 2, fake, 1 << 30,
+                                     fake, None, None) == 8
     # kv_splits out of range
     assert L.sol_attn_fused_kv(fake, fake, fake, fake, 1, 1024, 2, 128, -1, 0, 17, fake, 1 << 30, None) == 8
     # Sol-Attn2 stage 2 parts: sink out of range, missing output, workspace too small
@@ -196,3 +206,27 @@ def test_python_validate_wrapper():
     assert _lib.validate(1, 1024, 2, 128, 1.0, None, 0) == 0
     assert _lib.validate(1, 1024, 2, 128, 1.0, None, 2000) == 5
     assert _lib.validate(1, 1024, 2, 128, 1.0, None, 0, "bogus") == 8
+
+
+def test_binding_rejects_bad_outputs_and_workspaces():
+    """The binding checks caller-supplied outputs and workspaces before any pointer reaches the
+    library: wrong dtype, shape, layout or device for out / dq / dk / dv, a workspace of the
+    wrong type or device (host-side checks; no GPU needed)."""
+    import torch
+    from block_sparse_attention_tok_amd import _lib
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16)
+    _lib._check_like(None, q, "out")
+    _lib._check_like(torch.empty_like(q), q, "out")
+    for bad in (q.float(), q[:, :32].contiguous(), q.transpose(1, 2), torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16),
+                torch.empty(64 * 2 * 128, dtype=torch.bfloat16)):
+        with pytest.raises(ValueError):
+            _lib._check_like(bad, q, "out")
+    with pytest.raises(ValueError):
+        _lib._check_like(torch.empty(1, 64, 2, 128, dtype=torch.bfloat16, device="meta"), q, "dq")
+    _lib._check_workspace(torch.empty(4096, dtype=torch.uint8), q)
+    with pytest.raises(ValueError):
+        _lib._check_workspace(torch.empty(1024, dtype=torch.float32), q)
+    with pytest.raises(ValueError):
+        _lib._check_workspace(torch.empty(4096, dtype=torch.uint8, device="meta"), q)
+    with pytest.raises(ValueError):
+        _lib._check_workspace(torch.empty(2, 4096, dtype=torch.uint8)[:, :100], q)

@@ -14,7 +14,7 @@ import torch
 
 import block_sparse_attention_tok_amd as bsa
 from oracle import sol_attn as sa
-from parity import compare_out, mask_check, oracle_rows, say, to_gpu
+from parity import compare_out, mask_check, oracle_rows, pair_check, say, to_gpu
 from workloads import block_offset_tensor, long_sink, operator_bench, wan_dit
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +29,8 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, thresh="diag", sample
     say(f"[sol_attn] B={B} N={N} H={H} tau={tau} sink=({sink_start},{sink_tokens}) thresh={thresh}")
     qg, kg, vg = to_gpu(q, k, v)
     out = torch.empty_like(qg)
-    _, masks, ws = bsa.debug_routing(1, qg, kg, vg, tau, thresh, sink_start, sink_tokens, out=out)
+    _, masks, ws, pairs = bsa.debug_routing(1, qg, kg, vg, tau, thresh, sink_start, sink_tokens, out=out,
+                                            return_pairs=True)
     out2 = bsa.sol_attn(qg, kg, vg, tau, thresh, sink_start, sink_tokens)
     torch.cuda.synchronize()
     assert torch.equal(out, out2), (f"export and product calls disagree: max diff "
@@ -41,6 +42,7 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, thresh="diag", sample
     forced[..., sa.sink_block_mask(N, sink_start, sink_tokens)] = True
     gsel = masks.numpy()
     flips = mask_check(gsel, ref["sel"], ref["s_hat"], ref["tau_i"], forced)
+    pair_check(pairs, gsel, ref["sel"], N)
     out_c = out.float().cpu().numpy()
     rng = np.random.default_rng(seed)
     got, want = [], []

@@ -6,7 +6,9 @@ membership wherever a key's projection is more than a small margin from its
 block's mean projection (the decision is taken in fp32 on the GPU, fp64 in the
 oracle).  Masks are bit-exact outside the 1e-3 proxy margin.  Outputs: relative
 L2 <= 3e-2 against the float64 oracle run on the same dequantized Q/K, with the
-kernel's own selection.
+kernel's own selection, both over all sampled rows and for every 32-row anchor
+on its own (so one anchor with a wrong tail cannot hide in the aggregate).  The
+kernel's selected-token-pair counter equals the count of its masks.
 """
 import math
 
@@ -17,7 +19,7 @@ import torch
 import block_sparse_attention_tok_amd as bsa
 from oracle import sol_attn as sa
 from oracle import sol_attn2 as s2
-from parity import mask_check, say, to_gpu
+from parity import anchor_errors, mask_check, pair_check, say, to_gpu
 from workloads import block_offset_tensor, sol2_bench, wan_dit
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +39,8 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, sample=No
     say(f"[sol_attn2] B={B} N={N} H={H} tau={tau} sink=({sink_start},{sink_tokens})")
     qg, kg, vg = to_gpu(q, k, v)
     out = torch.empty_like(qg)
-    _, masks, ws = bsa.debug_routing(2, qg, kg, vg, tau, "diag", sink_start, sink_tokens, out=out)
+    _, masks, ws, pairs = bsa.debug_routing(2, qg, kg, vg, tau, "diag", sink_start, sink_tokens, out=out,
+                                            return_pairs=True)
     out2 = bsa.sol_attn2(qg, kg, vg, tau, "diag", sink_start, sink_tokens)
     torch.cuda.synchronize()
     assert torch.equal(out, out2), "export and product calls disagree"
@@ -45,8 +48,10 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, sample=No
     nb = (N + 63) // 64
     out_c = out.float().cpu().numpy()
     gsel = masks.numpy()
+    assert pairs == sa.selected_pairs(gsel, N), "selected-pair counter differs from the kernel's masks"
     rng = np.random.default_rng(seed)
     got, want, want_unq = [], [], []
+    worst_anchor = 0.0
     flips = 0
     scale = 1 / math.sqrt(128)
     for b in range(B):
@@ -83,6 +88,7 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, sample=No
                 s, e = i * 64, min(i * 64 + 64, N)
                 want.append(s2.attend_query_block2(r.q_deq, r.k_deq, vh, i, gsel[b, h, i], r.groups, scale))
                 got.append(out_c[b, s:e, h, :])
+                worst_anchor = max([worst_anchor] + anchor_errors(got[-1], want[-1]))
                 want_unq.append(s2.attend_query_block2(qh, kh, vh, i, gsel[b, h, i],
                                                        s2.all_key_groups(kh, vh, qh.mean(axis=0)), scale))
     got, want, want_unq = (np.concatenate(x) for x in (got, want, want_unq))
@@ -90,8 +96,9 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, sample=No
     err = np.linalg.norm(got - want) / np.linalg.norm(want)
     err_unq = np.linalg.norm(got - want_unq) / np.linalg.norm(want_unq)
     say(f"   ok: rel L2 {err:.2e} (vs unquantized oracle {err_unq:.2e}), max abs {np.abs(got - want).max():.2e}, "
-        f"mask flips {flips}, density {gsel.mean():.3f}")
+        f"worst anchor rel L2 {worst_anchor:.2e}, mask flips {flips}, density {gsel.mean():.3f}")
     assert err <= REL_L2_FP8, f"rel L2 {err:.3e} > {REL_L2_FP8}"
+    assert worst_anchor <= REL_L2_FP8, f"an anchor's rel L2 {worst_anchor:.3e} > {REL_L2_FP8}"
     return out, masks, views
 
 

@@ -3,9 +3,11 @@
 Bit for bit: the per-head V scale and the E4M3 V codes (fp32 division and RNE on
 both sides), read back from the workspace in the kernel's operand order.  Outputs:
 relative L2 <= 3e-2 against the float64 oracle with pv="expcast" on the same
-dequantized Q/K and the kernel's own routing.  The oracle's ExpCast pivot is the
-row's final maximum while the kernel's is its running maximum, so individual
-bytes may differ by one step; the output bar covers that.
+dequantized Q/K and the kernel's own routing, over all sampled rows and for every
+32-row anchor on its own.  Both sides take the ExpCast pivot online, one selected
+64-token block at a time in ascending order (each block's bytes against the
+running row maximum including that block); the bytes can still differ by one
+step where fp32 and fp64 round a score differently, which the output bar covers.
 """
 import math
 
@@ -15,7 +17,7 @@ import torch
 
 import block_sparse_attention_tok_amd as bsa
 from oracle import sol_attn2 as s2
-from parity import say, to_gpu
+from parity import anchor_errors, say, to_gpu
 from workloads import block_offset_tensor, sol2_bench
 
 pytestmark = pytest.mark.gpu
@@ -64,6 +66,7 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, sample=No
     rng = np.random.default_rng(seed)
     scale = 1 / math.sqrt(128)
     got, want, want_bf16 = [], [], []
+    worst_anchor = 0.0
     tp = views["v8t"].shape[-1]
     for b in range(B):
         for h in (range(H) if heads is None else heads):
@@ -80,13 +83,15 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, sample=No
                                                    pv="expcast", v_exact=vd))
                 want_bf16.append(s2.attend_query_block2(r.q_deq, r.k_deq, vh, i, gsel[b, h, i], r.groups, scale))
                 got.append(out_c[b, s:e, h, :])
+                worst_anchor = max([worst_anchor] + anchor_errors(got[-1], want[-1]))
     got, want, want_bf16 = (np.concatenate(x) for x in (got, want, want_bf16))
     assert np.isfinite(got).all()
     err = np.linalg.norm(got - want) / np.linalg.norm(want)
     err_bf = np.linalg.norm(got - want_bf16) / np.linalg.norm(want_bf16)
     say(f"   ok: rel L2 {err:.2e} (vs bf16-PV oracle {err_bf:.2e}), max abs {np.abs(got - want).max():.2e}, "
-        f"density {gsel.mean():.3f}")
+        f"worst anchor rel L2 {worst_anchor:.2e}, density {gsel.mean():.3f}")
     assert err <= REL_L2_FP8, f"rel L2 {err:.3e} > {REL_L2_FP8}"
+    assert worst_anchor <= REL_L2_FP8, f"an anchor's rel L2 {worst_anchor:.3e} > {REL_L2_FP8}"
     return out
 
 
