@@ -30,8 +30,10 @@ EXPORTED = [
     "sol_attn", "sol_attn_prepare", "sol_attn_fused", "sol_attn_fused_kv", "sol_attn_debug_routing",
     "sol_attn2", "sol_attn2_prepare", "sol_attn2_fused", "sol_attn2_tail", "sol_attn2_exact",
     "sol_attn2_debug_routing", "sol_attn2_pv8", "sol_attn2_pv8_prepare", "sol_attn2_pv8_exact",
-    "sol_attn_forward_train", "sol_attn_backward",
+    "sol_attn_forward_train", "sol_attn_backward", "sol_attn_noalloc",
 ]
+SOL_ERR_SCRATCH = 9
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class WsLayout(ctypes.Structure):
@@ -99,6 +101,8 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).restype = i32
     L.sol_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
     L.sol_attn_backward.restype = i32
+    L.sol_attn_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp]
+    L.sol_attn_noalloc.restype = i32
     _LIB = L
     return L
 
@@ -229,6 +233,28 @@ def sol_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0
         workspace = alloc_workspace(SOL_VARIANT_SOL1, q, kv_splits)
     prepare(SOL_VARIANT_SOL1, q, k, v, tau, workspace, thresh)
     fused(SOL_VARIANT_SOL1, q, k, v, out, workspace, sink_start, sink_tokens, kv_splits)
+    return out
+
+
+def sol_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, tau: float = 1.0,
+                     thresh: str = "diag", sink_start: Optional[int] = None, sink_tokens: int = 0) -> torch.Tensor:
+    """Sol-Attn on the library's static per-device scratch: the C call allocates nothing.
+
+    The caller passes `out` (a contiguous bf16 tensor of q's shape); shapes whose workspace
+    exceeds NOALLOC_SCRATCH_BYTES raise SolAttnError (status SOL_ERR_SCRATCH).  Calls that
+    overlap on one device race on the shared scratch."""
+    _check_tensors(q, k, v)
+    if out is None:
+        raise ValueError("out is required (the no-allocation call writes into the caller's tensor)")
+    _check_like(out, q, "out")
+    if thresh not in THRESH:
+        raise ValueError("thresh must be 'diag' or 'exact'")
+    if not math.isfinite(float(tau)):
+        raise ValueError("tau must be finite")
+    B, N, H, D = q.shape
+    _check(lib().sol_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, float(tau),
+                                  _sink_start(sink_start), int(sink_tokens), THRESH[thresh], _stream(q.device)),
+           "sol_attn_noalloc")
     return out
 
 

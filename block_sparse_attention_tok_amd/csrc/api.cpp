@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -213,6 +214,9 @@ const char* sol_status_string(int status) {
     case SOL_ERR_WORKSPACE: return "workspace smaller than sol_attn_workspace_bytes()";
     case SOL_ERR_HIP: return "HIP runtime or kernel launch error";
     case SOL_ERR_ARG: return "invalid argument (threshold type, variant or pointer alignment)";
+    case SOL_ERR_SCRATCH:
+      return "the shape needs more workspace than sol_attn_noalloc's static scratch holds "
+             "(SOL_NOALLOC_SCRATCH_BYTES); use sol_attn with a caller workspace";
     default: return "unknown status";
   }
 }
@@ -483,6 +487,57 @@ int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* o
   if (st != SOL_OK) return st;
   return fused_common(SOL_VARIANT_SOL2, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
                       workspace, workspace_bytes, mask_bits, stream, false, 0, kStage2Both, selected_pairs);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// sol_attn_noalloc: sol_attn on a workspace held in a static device array, for callers
+// that cannot allocate.  Each device that runs it holds its own copy of `scratch` until
+// the process ends.  The array's name is only a host-side stand-in: its device address
+// comes from hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever passed to the kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SOL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];            // device address of `scratch` per device, once set up
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SOL_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SOL_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SOL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sol_attn_noalloc(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                     int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+                     void* stream) {
+  if (!q || !k || !v || !out) return SOL_ERR_NULL;
+  int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
+  if (st != SOL_OK) return st;
+  const size_t need = sol_attn_workspace_bytes(SOL_VARIANT_SOL1, batch, tokens, heads, head_dim);
+  if (need == 0) return SOL_ERR_SHAPE;
+  if (need > (size_t)SOL_NOALLOC_SCRATCH_BYTES) return SOL_ERR_SCRATCH;
+  // Every array of the workspace is written by the call before it is read, so the
+  // previous call's contents need no clearing.
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != SOL_OK) return st;
+  return sol_attn(q, k, v, out, batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh, ws,
+                  (size_t)SOL_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -41,8 +41,12 @@ typedef enum {
     SOL_ERR_SINK = 5,        /* sink_tokens < 0, or the sink range leaves [0, tokens) */
     SOL_ERR_WORKSPACE = 6,   /* workspace smaller than sol_attn_workspace_bytes() */
     SOL_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
-    SOL_ERR_ARG = 8          /* unknown threshold type or variant, bad alignment */
+    SOL_ERR_ARG = 8,         /* unknown threshold type or variant, bad alignment */
+    SOL_ERR_SCRATCH = 9      /* sol_attn_noalloc: the shape's workspace exceeds its static scratch */
 } sol_status;
+
+/* Size of the static device scratch behind sol_attn_noalloc (128 MiB per device). */
+#define SOL_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 /* Threshold estimator (Sol-Attn paper §3.1 Eq. (5) and its appendix
  * "Diagonal threshold estimator").  DIAG is the default hot path. */
@@ -327,6 +331,25 @@ int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* o
                             float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
                             int kv_splits, void* workspace, size_t workspace_bytes, uint64_t* mask_bits,
                             uint64_t* selected_pairs, void* stream);
+
+/*
+ * sol_attn without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, output and errors as sol_attn minus the workspace: the workspace is a
+ * static device array of SOL_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per
+ * device (its address is looked up once per device, on the first call with that device
+ * current); nothing is allocated or freed, here or later.  The current device must be the
+ * one `stream` belongs to.  Shapes whose Sol-Attn workspace (sol_attn_workspace_bytes with
+ * SOL_VARIANT_SOL1) exceeds the scratch are rejected with SOL_ERR_SCRATCH before any
+ * launch (e.g. B=1, H=12, 14040 tokens needs 88 MiB and fits; B=1, H=32, 32768 tokens
+ * needs 1059 MiB and does not).  Every call on a device shares that device's scratch: calls
+ * that overlap on one device (other streams, other host threads) race and must be
+ * serialized by the caller.  The scratch keeps the last call's contents; the call writes
+ * every array it reads, so nothing needs clearing between calls.
+ */
+int sol_attn_noalloc(const void* q, const void* k, const void* v, void* out,
+                     int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                     float tau, int64_t sink_start, int64_t sink_tokens, int thresh, void* stream);
 
 #ifdef __cplusplus
 }

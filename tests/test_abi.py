@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(0, 9):
+    for s in range(0, 10):
         assert L.sol_status_string(s)
     assert L.sol_status_string(123) == b"unknown status"
 
@@ -230,3 +230,25 @@ def test_binding_rejects_bad_outputs_and_workspaces():
         _lib._check_workspace(torch.empty(4096, dtype=torch.uint8, device="meta"), q)
     with pytest.raises(ValueError):
         _lib._check_workspace(torch.empty(2, 4096, dtype=torch.uint8)[:, :100], q)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_launch(L):
+    """sol_attn_noalloc checks the shape's workspace against its static scratch on the host:
+    a shape that does not fit returns SOL_ERR_SCRATCH (no device is touched), argument errors
+    come first, and the scratch size in the header is the one the binding states."""
+    from block_sparse_attention_tok_amd import _lib
+    fake = ctypes.c_void_p(0x1000)
+    text = open(HEADER).read()
+    assert re.search(r"#define SOL_NOALLOC_SCRATCH_BYTES \(128u << 20\)", text)
+    assert _lib.NOALLOC_SCRATCH_BYTES == 128 << 20
+    # 1 x 32768 x 32 needs ~1059 MiB of workspace: rejected
+    assert L.sol_attn_workspace_bytes(1, 1, 32768, 32, 128) > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.sol_attn_noalloc(fake, fake, fake, fake, 1, 32768, 32, 128, 1.0, -1, 0, 0, None) == 9
+    assert b"scratch" in L.sol_status_string(9)
+    # argument errors are reported before the size check
+    assert L.sol_attn_noalloc(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, None) == 1
+    assert L.sol_attn_noalloc(fake, fake, fake, fake, 1, 1024, 2, 128, float("nan"), -1, 0, 0, None) == 4
+    assert L.sol_attn_noalloc(fake, fake, fake, fake, 1, 1024, 2, 64, 1.0, -1, 0, 0, None) == 3
+    assert L.sol_attn_noalloc(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, 1000, 100, 0, None) == 5
+    # the Wan-2.1-shaped call (B=1, H=12, 14040 tokens) fits
+    assert L.sol_attn_workspace_bytes(1, 1, 14040, 12, 128) <= _lib.NOALLOC_SCRATCH_BYTES
