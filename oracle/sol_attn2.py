@@ -18,11 +18,12 @@ Steps, per (batch, head):
    Each key block j splits into G_hi = {u : k'_u . q-hat >= mean_u k'_u . q-hat}
    and G_lo = the rest; an empty group is dropped.  Group sizes n_g, mean
    keys k-bar_g (of k') and mean values v-bar_g.
-   -- parity unpinned: the draft names "the mean-query direction" and
-   "two content groups by its key projections" without defining the
-   direction's averaging set or the split point; this reading (per-(b,h)
-   mean query, split at the block's mean projection, ties to G_hi) has no
-   worked example on the pages to pin it.
+   The draft names the mean-query direction and a split of each block into
+   two content groups by key projection without defining the direction's
+   averaging set or the split point; this is a reading (per-(b,h) mean query,
+   split at the block's mean projection of the dequantized keys, ties to
+   G_hi).  It is pinned by a hand-worked example whose inputs separate it
+   from the other plausible readings (tests/golden/sol2_groups.txt).
 3. Anchors are the two 32-token halves of each 64-token query block (clipped
    to N); q-bar_a = mean of q' over the anchor.
 4. Tail T_a = the groups of every key block j that is not exact for the
@@ -45,7 +46,7 @@ online pivot m: the selected key blocks are taken in ascending order, m is
 raised to each block's largest logit before that block's bytes are formed, and
 the sums so far are rescaled by e^{m_old - m} (the pages give the pivot as
 online; the reading takes the order and granularity of the tiled pass, one
-64-token block at a time).  The same p-hat weights form the exact numerator
+64-token block at a time; `pivot_block` sets another granularity).  The same p-hat weights form the exact numerator
 (with the dequantized V) and the exact part of the denominator.  The tail keeps
 the bf16 group means of V.
 """
@@ -160,13 +161,16 @@ def tail_stats(qbar_a: np.ndarray, groups: list, scale: float):
 
 def attend_query_block2(q: np.ndarray, k: np.ndarray, v: np.ndarray, i: int, sel_row: np.ndarray,
                         groups: list, scale: float, anchor: int = ANCHOR, block: int = BLOCK,
-                        return_parts: bool = False, pv: str = "bf16", v_exact: Optional[np.ndarray] = None):
+                        return_parts: bool = False, pv: str = "bf16", v_exact: Optional[np.ndarray] = None,
+                        pivot_block: int = BLOCK):
     """Output rows of query block i: exact blocks plus the first-order-corrected tail.
 
     return_parts also returns, per anchor, (range, ln Z_a, mu_a, nu_a) and
     per-token alpha_t = Z_E / (Z_E + Z-hat) (output table, Sol-Attn2 row).
     pv="expcast" uses ExpCast weights for the exact tokens and v_exact (the
     per-head FP8-dequantized V) as their values; the tail still uses `groups`.
+    pivot_block: how many consecutive exact keys share one step of the online
+    ExpCast pivot (the reading: one 64-token block; the pages fix no granularity).
     """
     n, d = q.shape
     s, e = i * block, min(i * block + block, n)
@@ -194,8 +198,9 @@ def attend_query_block2(q: np.ndarray, k: np.ndarray, v: np.ndarray, i: int, sel
             wnum = np.zeros((a1 - a0, d))
             wden = np.zeros(a1 - a0)
             col = 0
-            for j in np.flatnonzero(sel_row):
-                bs, be = ranges[j]
+            steps = [(s0, min(s0 + pivot_block, be)) for j in np.flatnonzero(sel_row)
+                     for bs, be in [ranges[j]] for s0 in range(bs, be, pivot_block)]
+            for bs, be in steps:
                 zj = z[:, col:col + (be - bs)]
                 col += be - bs
                 p_new = np.maximum(p, zj.max(axis=1))

@@ -84,13 +84,13 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, sample=No
             assert not bad.any(), f"{int(bad.sum())} mask bits differ outside the margin"
             flips += int((gsel[b, h] != ref_sel).sum())
             blocks = range(nb) if sample is None else sorted(set(rng.choice(nb, size=min(sample, nb), replace=False)) | {nb - 1})
+            groups_unq = s2.all_key_groups(kh, vh, qh.mean(axis=0))
             for i in blocks:
                 s, e = i * 64, min(i * 64 + 64, N)
                 want.append(s2.attend_query_block2(r.q_deq, r.k_deq, vh, i, gsel[b, h, i], r.groups, scale))
                 got.append(out_c[b, s:e, h, :])
                 worst_anchor = max([worst_anchor] + anchor_errors(got[-1], want[-1]))
-                want_unq.append(s2.attend_query_block2(qh, kh, vh, i, gsel[b, h, i],
-                                                       s2.all_key_groups(kh, vh, qh.mean(axis=0)), scale))
+                want_unq.append(s2.attend_query_block2(qh, kh, vh, i, gsel[b, h, i], groups_unq, scale))
     got, want, want_unq = (np.concatenate(x) for x in (got, want, want_unq))
     assert np.isfinite(got).all()
     err = np.linalg.norm(got - want) / np.linalg.norm(want)
@@ -142,9 +142,11 @@ def test_wan21_dit_shape():
 
 
 def test_sol2_bench_shape():
-    """B=1, H=32, N=32768, tau near 90% sparsity: 3 heads checked in full routing, sampled outputs."""
+    """B=1, H=32, N=32768, tau near 90% sparsity: E4M3 codes and scales, the mean-query
+    direction, the group split bits and the routing of all 32 heads; 3 sampled query blocks
+    per head (the last included) for the outputs."""
     q, k, v = sol2_bench().qkv()
-    run_case(q, k, v, 1.28, heads=[0, 13, 31], sample=3, seed=6)
+    run_case(q, k, v, 1.28, heads=None, sample=3, seed=6)
 
 
 def test_single_token():
@@ -190,3 +192,52 @@ def test_exact_logit_far_above_the_first_exact_block():
     k[0, blk * 64:(blk + 1) * 64, 0, 0] = 300.0
     out, masks, _ = run_case(q, k, v, 1.0, sink_start=0, sink_tokens=64)
     assert masks[0, 0, :, blk].all() and masks[0, 0, :, 0].all()
+
+
+@pytest.mark.parametrize("case", ["tail", "sink"])
+def test_hand_worked_group_fixture(case):
+    """The hand-worked head of tests/golden/sol2_groups.txt (d = 4 values embedded in d = 128,
+    dims 4.. zero): the kernels' mean-query direction, split bits (the tie included) and group
+    counts are exactly the fixture's, and every output row matches its closed form (tau = 100:
+    no exact block; with the sink [64, 96): block 1 exact, delta_t nonzero in the last anchor)."""
+    from sol2_fixture import inputs, load
+    fx = load(128)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).view(1, 96, 1, 128) for x in inputs(128))
+    sink = (64, 32) if case == "sink" else (None, 0)
+    say(f"[sol_attn2 fixture] case {case}")
+    qg, kg, vg = to_gpu(q, k, v)
+    out = torch.empty_like(qg)
+    _, masks, ws, pairs = bsa.debug_routing(2, qg, kg, vg, 100.0, "diag", sink[0], sink[1], out=out,
+                                            return_pairs=True)
+    torch.cuda.synchronize()
+    want_sel = np.array([[False, True], [False, True]]) if case == "sink" else np.zeros((2, 2), dtype=bool)
+    assert np.array_equal(masks[0, 0].numpy(), want_sel)
+    assert pairs == (96 * 32 if case == "sink" else 0)
+    views = bsa.workspace_views(2, ws, 1, 96, 1)
+    qhat = views["qhat"][0, 0].cpu().double().numpy()
+    assert np.array_equal(qhat[:4], fx["qhat"]) and not qhat[4:].any()
+    ghi = views["ghi"][0, 0, :2].cpu().numpy().view(np.uint64)
+    want_hi0 = sum(1 << u for u in range(64) if u % 8 in fx["hi_residues"].astype(int).tolist())
+    assert int(ghi[0]) == want_hi0, f"block 0 split {int(ghi[0]):#018x} != {want_hi0:#018x}"
+    assert int(ghi[1]) == (1 << 32) - 1, "the all-equal partial block must be one group"
+    glogn = views["glogn"][0, 0, :2].cpu().double().numpy()
+    np.testing.assert_allclose(glogn[0], np.log([fx["n_hi"][0], fx["n_lo"][0]]), rtol=1e-6)
+    assert glogn[1, 0] == pytest.approx(math.log(fx["n_b1"][0]), rel=1e-6) and glogn[1, 1] == -np.inf
+    gk = views["gk"][0, 0, :2].cpu().double().numpy()
+    np.testing.assert_allclose(gk[0, 0, :4], fx["kbar_hi"], atol=4e-3)
+    np.testing.assert_allclose(gk[0, 1, :4], fx["kbar_lo"], atol=4e-3)
+    np.testing.assert_allclose(gk[1, 0, :4], fx["kbar_b1"], atol=4e-3)
+    got = out[0, :, 0, :].float().cpu().double().numpy()
+    assert not got[:, 4:].any()
+    if case == "tail":
+        rows = [("out_tail_a0", 0, 32), ("out_tail_a1", 32, 64), ("out_tail_a2", 64, 96)]
+    else:
+        rows = [("out_sink_a0", 0, 32), ("out_sink_a1", 32, 64), ("out_sink_a2_hi", 64, 80),
+                ("out_sink_a2_lo", 80, 96)]
+    want = np.zeros((96, 4))
+    for name, t0, t1 in rows:
+        want[t0:t1] = fx[name]
+    err = np.linalg.norm(got[:, :4] - want) / np.linalg.norm(want)
+    mx = np.abs(got[:, :4] - want).max()
+    say(f"   ok: rel L2 {err:.2e}, max abs {mx:.2e}")
+    assert err <= REL_L2_FP8 and mx <= 3e-2

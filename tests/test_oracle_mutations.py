@@ -90,13 +90,60 @@ def _tail_mutation(kind):
     return tail
 
 
+def _split_rule(kind):
+    orig = s2.key_groups
+
+    def groups(k_blk, v_blk, qhat, grouping="split2"):
+        if grouping != "split2":
+            return orig(k_blk, v_blk, qhat, grouping)
+        p = k_blk @ qhat
+        hi = p >= np.median(p) if kind == "median" else p > p.mean()
+        out = []
+        for m in (hi, ~hi):
+            if m.any():
+                out.append((m, float(m.sum()), k_blk[m].mean(axis=0), v_blk[m].mean(axis=0)))
+        return out
+    return groups
+
+
+def _per_query_block_direction(mp):
+    orig_attend, orig_groups = s2.attend_query_block2, s2.all_key_groups
+
+    def attend(q, k, v, i, sel_row, groups, scale, *args, **kw):
+        s, e = i * 64, min(i * 64 + 64, q.shape[0])
+        return orig_attend(q, k, v, i, sel_row, orig_groups(k, v, q[s:e].mean(axis=0)), scale, *args, **kw)
+    mp.setattr(s2, "attend_query_block2", attend)
+
+
+def _split_on_unquantized_keys(mp):
+    orig_head, orig_groups = s2.sol_attn2_head, s2.all_key_groups
+
+    def head(q, k, v, *args, **kw):
+        raw = np.asarray(k, dtype=np.float64)
+        mp.setattr(s2, "all_key_groups", lambda kd, vv, qh, grouping="split2", block=64:
+                   orig_groups(raw, vv, qh, grouping, block))
+        try:
+            return orig_head(q, k, v, *args, **kw)
+        finally:
+            mp.setattr(s2, "all_key_groups", orig_groups)
+    mp.setattr(s2, "sol_attn2_head", head)
+
+
 MUTATIONS_SOL2 = {
     "no_group_count": lambda mp: mp.setattr(s2, "tail_stats", _tail_mutation("no_group_count")),
     "delta_sign": lambda mp: mp.setattr(s2, "tail_stats", _tail_mutation("mu_sign")),
     "swap_mu_nu": lambda mp: mp.setattr(s2, "tail_stats", _tail_mutation("swap_mu_nu")),
+    # the group readings pinned by the hand-worked fixture (tests/golden/sol2_groups.txt)
+    "median_split": lambda mp: mp.setattr(s2, "key_groups", _split_rule("median")),
+    "ties_to_g_lo": lambda mp: mp.setattr(s2, "key_groups", _split_rule("ties_lo")),
+    "per_query_block_direction": _per_query_block_direction,
+    "split_on_unquantized_keys": _split_on_unquantized_keys,
 }
 
+import test_oracle_sol2_groups as p2g  # noqa: E402
+
 PINS_SOL2 = [
+    (p2g.test_group_readings_match_the_hand_worked_fixture, ()),
     (p2.test_singleton_groups_and_constant_anchor_queries_are_dense, ()),
     (p2.test_anchor_one_whole_block_groups_reduce_to_sol_attn, (1.0, (None, 0))),
     (p2.test_extra_biased_key_form, (False,)),
