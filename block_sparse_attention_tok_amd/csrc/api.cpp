@@ -45,13 +45,21 @@ int sink_range(int64_t tokens, int64_t sink_start, int64_t sink_tokens, int* b0,
 }
 
 constexpr int kMaxSplits = 16;
+// Automatic split counts stay at or below this: each split keeps an fp32 partial row per
+// (token, head) (512 bytes), so 4 splits hold at most twice the bytes of q, k, v and out.
+constexpr int kMaxAutoSplits = 4;
 
 // Effective split count: splits cover whole 64-block routing chunks.
 int effective_splits(int64_t tokens, int requested) {
   const int64_t nb = (tokens + kBlock - 1) / kBlock;
   const int nchunks = (int)((nb + 63) / 64);
   int want = requested;
-  if (want <= 0) want = (nchunks + 5) / 6;                 // automatic: one split per six chunks
+  if (want <= 0) {
+    // automatic: none up to 8 chunks (the split merge costs more than it saves there), then
+    // one split per six chunks, at most kMaxAutoSplits
+    want = nchunks <= 8 ? 1 : (nchunks + 5) / 6;
+    if (want > kMaxAutoSplits) want = kMaxAutoSplits;
+  }
   if (want > kMaxSplits) want = kMaxSplits;
   if (want > nchunks) want = nchunks;
   if (want < 1) want = 1;
@@ -113,7 +121,7 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   const bool sol1 = variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN;
   L->kv_splits = sol1 ? effective_splits(tokens, kv_splits) : 1;
   if (L->kv_splits > 1) {
-    L->opart = take(L->kv_splits * bh * tokens * kDim * 2);
+    L->opart = take(L->kv_splits * bh * tokens * kDim * 4);
     L->olse = take(L->kv_splits * bh * tokens * 4);
   }
   // forward state for the backward, and backward scratch (Sol-Attn training)
@@ -157,7 +165,7 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.ghi = (uint64_t*)at(L.ghi);
   w.qanc = (float*)at(L.qanc);
   w.kv_splits = (int)L.kv_splits;
-  w.opart = (uint16_t*)at(L.opart);
+  w.opart = (float*)at(L.opart);
   w.olse = (float*)at(L.olse);
   w.sel = (uint64_t*)at(L.sel);
   w.tmu = (float*)at(L.tmu);

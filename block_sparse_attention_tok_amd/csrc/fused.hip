@@ -56,7 +56,7 @@ struct FusedArgs {
   const uint16_t* q; uint16_t* out;
   int B, N, H, nb, nbp, nbw;
   int S, cps;                   // key-range splits and routing chunks per split
-  uint16_t* opart; float* olse; // split partials (S > 1)
+  float* opart; float* olse;    // split partials (S > 1): fp32 normalized rows, log2-sum-exp
   const uint16_t* kbar_h; const uint16_t* vbar_h;
   const uint16_t* kh; const uint16_t* vh;   // head-major copies of k and v ([B][H][N][128])
   const float* qbar;            // [B][H][nbp][128] fp32 query-block means
@@ -417,31 +417,41 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     }
   }
 
-  // ---- epilogue: O / l, bf16 RNE, BTHD store (or this split's partial row and its
-  // log2-sum-exp m + log2 l for the merge)
+  // ---- epilogue: O / l, bf16 RNE, BTHD store; with key splits, this split's normalized
+  // row in fp32 and its log2-sum-exp m + log2 l instead (the merge rounds to bf16 once)
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  uint16_t* dst_base = a.S > 1 ? a.opart + (size_t)split * a.B * a.N * rs : a.out;
-  if (qrow < a.N && dst_base != nullptr) {
-    uint16_t* dst = dst_base + head_off + (size_t)qrow * rs;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2v pk;
-        pk[0] = pack_bf16x2(o[mt][4 * g] * inv, o[mt][4 * g + 1] * inv);
-        pk[1] = pack_bf16x2(o[mt][4 * g + 2] * inv, o[mt][4 * g + 3] * inv);
-        *(uint2v*)(dst + 32 * mt + 8 * g + 4 * kg) = pk;
-      }
+  if (qrow < a.N) {
     const float lse2 = l_tot > 0.f ? m_fin + __log2f(l_tot) : kNegInf;
-    if (a.S > 1 && kg == 0) a.olse[((size_t)split * a.B * a.N + (size_t)b * a.N + qrow) * a.H + h] = lse2;
-    if (a.S == 1 && a.lse != nullptr && kg == 0) a.lse[(size_t)bh * a.tp + qrow] = lse2;
+    if (a.S > 1) {
+      float* dst = a.opart + ((size_t)split * a.B * a.N * rs) + head_off + (size_t)qrow * rs;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(float4*)(dst + 32 * mt + 8 * g + 4 * kg) = make_float4(o[mt][4 * g] * inv, o[mt][4 * g + 1] * inv,
+                                                                    o[mt][4 * g + 2] * inv, o[mt][4 * g + 3] * inv);
+      if (kg == 0) a.olse[((size_t)split * a.B * a.N + (size_t)b * a.N + qrow) * a.H + h] = lse2;
+    } else if (a.out != nullptr) {
+      uint16_t* dst = a.out + head_off + (size_t)qrow * rs;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2v pk;
+          pk[0] = pack_bf16x2(o[mt][4 * g] * inv, o[mt][4 * g + 1] * inv);
+          pk[1] = pack_bf16x2(o[mt][4 * g + 2] * inv, o[mt][4 * g + 3] * inv);
+          *(uint2v*)(dst + 32 * mt + 8 * g + 4 * kg) = pk;
+        }
+      if (a.lse != nullptr && kg == 0) a.lse[(size_t)bh * a.tp + qrow] = lse2;
+    }
   }
 }
 
-// Merge of the key-range splits: o = sum_s 2^(lse_s - lse) o_s with lse = log2 sum_s 2^lse_s.
-// One thread per (row, 8 dims); partials are BTHD like the output.  With `lse` set, the
-// first thread of each row also stores the merged log2-sum-exp at [b][h][n] (row stride tp).
-__global__ __launch_bounds__(256) void merge_splits_kernel(const uint4v* __restrict__ opart,
+// Merge of the key-range splits: o = sum_s 2^(lse_s - lse) o_s / sum_s 2^(lse_s - lse), the
+// fp32 partial rows o_s weighted by their softmax masses, rounded to bf16 once.  One thread
+// per (row, 8 dims); partials are BTHD like the output.  With `lse` set, the first thread
+// of each row also stores the merged log2-sum-exp at [b][h][n] (row stride tp).
+__global__ __launch_bounds__(256) void merge_splits_kernel(const float4* __restrict__ opart,
                                                            const float* __restrict__ olse, int S,
                                                            size_t rows, uint4v* __restrict__ out,
                                                            float* __restrict__ lse, int N, int H, int tp) {
@@ -455,13 +465,11 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const uint4v* __restr
   for (int sp = 0; sp < S; ++sp) {
     const float ls = olse[sp * rows + row];
     const float wt = ls == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ls - m);
-    const uint4v x = opart[sp * rows * 16 + t];
+    const float4 x0 = opart[(sp * rows * 16 + t) * 2];
+    const float4 x1 = opart[(sp * rows * 16 + t) * 2 + 1];
     wsum += wt;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += wt * bf16_lo(x[e]);
-      acc[2 * e + 1] += wt * bf16_hi(x[e]);
-    }
+    acc[0] += wt * x0.x; acc[1] += wt * x0.y; acc[2] += wt * x0.z; acc[3] += wt * x0.w;
+    acc[4] += wt * x1.x; acc[5] += wt * x1.y; acc[6] += wt * x1.z; acc[7] += wt * x1.w;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   if (lse != nullptr && (t & 15) == 0) {
@@ -508,7 +516,7 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (e != hipSuccess || S == 1 || out == nullptr) return e;
   const size_t rows = (size_t)s.B * s.N * s.H;
   hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
-                     (const uint4v*)ws.opart, ws.olse, S, rows, (uint4v*)out, ws.lse, s.N, s.H, ws.nbp * kBlock);
+                     (const float4*)ws.opart, ws.olse, S, rows, (uint4v*)out, ws.lse, s.N, s.H, ws.nbp * kBlock);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ struct Workspace {
   uint64_t* ghi;    // [B][H][nbp]
   float* qanc;      // [B][H][nbp][2][128]
   int kv_splits;    // key-range splits of the fused Sol-Attn pass (1 = none)
-  uint16_t* opart;  // [S][B][N][H][128] bf16 normalized partial outputs
+  float* opart;     // [S][B][N][H][128] fp32 normalized partial outputs
   float* olse;      // [S][B][N][H] log2-sum-exp of the partial rows
   uint64_t* sel;    // [B][H][nb][nbp / 64] Sol-Attn2 routing bits (the tail and exact passes)
   float* tmu;       // [B][H][nbp][2][128] Sol-Attn2 tail key means per anchor

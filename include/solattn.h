@@ -82,7 +82,8 @@ typedef enum {
  *   glogn    float [B][H][nbp][2]     ln n_g, -inf for an empty group (Sol-Attn2)
  *   ghi      uint64 [B][H][nbp]       bit u set iff token u of the block is in G_hi (Sol-Attn2)
  *   qanc     float [B][H][nbp][2][128] 32-token anchor means of dequantized Q (Sol-Attn2)
- *   opart    bf16  [S][B][N][H][128]   per-key-split normalized partial outputs (S = kv_splits > 1)
+ *   opart    float [S][B][N][H][128]   per-key-split normalized partial outputs (S = kv_splits > 1),
+ *                                      fp32 so that the merge rounds each output to bf16 once
  *   olse     float [S][B][N][H]        per-key-split log2-sum-exp of the partial rows
  *   sel      uint64 [B][H][nb][nbp/64] Sol-Attn2 routing bits (sink included), bit j % 64 of word
  *                                      j / 64 set iff block j is exact for query block i; written
@@ -144,12 +145,14 @@ int sol_attn_workspace_layout(int variant, int64_t batch, int64_t tokens, int64_
 
 /* Split-KV (Sol-Attn README, "Long-sequence tuning on H100": kv_splits).  The
  * fused Sol-Attn pass can split each query block's key range into S parts run by
- * separate workgroups and merged afterwards (partial outputs in bf16 with an fp32
- * log-sum-exp); on MI355X this keeps the K/V working set of the workgroups that
- * run together on one XCD inside its L2.  kv_splits = 0 means automatic: one
- * split per 384 key blocks (six 64-block routing chunks, rounded up), at most 16.  Splits
- * cover whole routing chunks: a request r becomes ceil(C / ceil(C / r)) for C
- * chunks (never above C).
+ * separate workgroups and merged afterwards (fp32 partial rows with their
+ * log-sum-exp, rounded to bf16 once by the merge); on MI355X this keeps the K/V
+ * working set of the workgroups that run together on one XCD inside its L2.
+ * kv_splits = 0 means automatic: no split up to 512 key blocks (8 routing chunks
+ * of 64 blocks), then one split per six chunks rounded up, at most 4 (the fp32
+ * partials then take at most twice the bytes of q, k, v and out).  Splits cover
+ * whole routing chunks: a request r becomes ceil(C / ceil(C / r)) for C chunks
+ * (never above C); explicit requests may ask for up to 16.
  * Host-only; returns the effective split count (>= 1), or 0 on a shape error. */
 int sol_attn_kv_splits(int64_t batch, int64_t tokens, int64_t heads, int kv_splits);
 

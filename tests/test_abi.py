@@ -128,12 +128,14 @@ def test_training_layout_extends_the_sol_attn_layout(L, B, N, H):
 
 
 @pytest.mark.parametrize("tokens,req,expect", [
-    (1024, 0, 1), (8192, 0, 1), (8193, 0, 1), (14040, 0, 1), (16385, 0, 1), (24577, 0, 2), (32768, 0, 2),
-    (49152, 0, 2), (65536, 0, 3), (66048, 0, 3), (131072, 0, 6), (131584, 0, 6),
+    (1024, 0, 1), (8192, 0, 1), (8193, 0, 1), (14040, 0, 1), (16385, 0, 1), (24577, 0, 1), (32768, 0, 1),
+    (32769, 0, 2), (49152, 0, 2), (65536, 0, 3), (66048, 0, 3), (98304, 0, 4), (131072, 0, 4), (131584, 0, 4),
+    (524288, 0, 4),
     (32768, 1, 1), (32768, 2, 2), (32768, 3, 3), (32768, 8, 8), (32768, 16, 8), (1024, 4, 1), (131584, 16, 11),
 ])
 def test_kv_split_rule(L, tokens, req, expect):
-    """Splits cover whole 64-block routing chunks; automatic = one split per six chunks (rounded up)."""
+    """Splits cover whole 64-block routing chunks; automatic = none up to 8 chunks, then one
+    split per six chunks (rounded up), at most 4."""
     assert L.sol_attn_kv_splits(1, tokens, 32, req) == expect
     lay = __import__("block_sparse_attention_tok_amd")._lib.workspace_layout(1, 1, tokens, 32, kv_splits=req)
     assert lay.kv_splits == expect
