@@ -218,3 +218,30 @@ PINS_BACKWARD = [
 def test_backward_mutation_is_caught(name, monkeypatch):
     MUTATIONS_BACKWARD[name](monkeypatch)
     assert any(_fails(fn, *args) for fn, args in PINS_BACKWARD), f"mutation {name} not caught"
+
+
+import test_oracle_backward2 as p5  # noqa: E402
+from oracle import sol_attn2_bwd as b2  # noqa: E402
+
+MUTATIONS_BACKWARD2 = {
+    # the group softmax backward forgets mu's dependence on the group logits
+    "no_dmu_in_group_grad": lambda mp: mp.setattr(
+        b2, "_group_logit_grad", lambda pi, dlnz, kb, mu, dmu, vb, nu, dnu: pi * (dlnz + (vb - nu) @ dnu)),
+    # the group softmax backward forgets nu's dependence on the group logits
+    "no_dnu_in_group_grad": lambda mp: mp.setattr(
+        b2, "_group_logit_grad", lambda pi, dlnz, kb, mu, dmu, vb, nu, dnu: pi * (dlnz + (kb - mu) @ dmu)),
+    # the means' chain rule (anchor queries, group keys / values) passes the whole gradient
+    "mean_chain_rule_dropped": lambda mp: mp.setattr(b2, "_mean_grad", lambda g, count: g),
+}
+
+PINS_BACKWARD2 = [
+    (p5.test_directional_derivatives_match_central_differences, (200, 8, 0.5, (None, 0))),
+    (p5.test_single_coordinates_through_the_tail, ()),
+    (p5.test_singleton_groups_with_constant_anchor_queries_give_the_dense_gradient, ()),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_BACKWARD2))
+def test_backward2_mutation_is_caught(name, monkeypatch):
+    MUTATIONS_BACKWARD2[name](monkeypatch)
+    assert any(_fails(fn, *args) for fn, args in PINS_BACKWARD2), f"mutation {name} not caught"
