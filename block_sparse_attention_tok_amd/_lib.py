@@ -22,6 +22,7 @@ SOL_VARIANT_SOL1 = 1
 SOL_VARIANT_SOL2 = 2
 SOL_VARIANT_SOL2_PV8 = 3
 SOL_VARIANT_SOL1_TRAIN = 4
+SOL_VARIANT_SOL2_TRAIN = 5
 THRESH = {"diag": 0, "exact": 1}
 
 EXPORTED = [
@@ -30,7 +31,8 @@ EXPORTED = [
     "sol_attn", "sol_attn_prepare", "sol_attn_fused", "sol_attn_fused_kv", "sol_attn_debug_routing",
     "sol_attn2", "sol_attn2_prepare", "sol_attn2_fused", "sol_attn2_tail", "sol_attn2_exact",
     "sol_attn2_debug_routing", "sol_attn2_pv8", "sol_attn2_pv8_prepare", "sol_attn2_pv8_exact",
-    "sol_attn_forward_train", "sol_attn_backward", "sol_attn_noalloc",
+    "sol_attn_forward_train", "sol_attn_backward", "sol_attn_noalloc", "sol_attn2_forward_train",
+    "sol_attn2_backward",
 ]
 SOL_ERR_SCRATCH = 9
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -41,7 +43,7 @@ class WsLayout(ctypes.Structure):
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov", "kpart",
         "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse",
         "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale", "lse", "mrow", "mcol", "ld", "dkbar", "dvbar",
-        "kh", "vh")]
+        "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz", "aextra", "gdk", "gdv", "ofp")]
 
 
 class SolAttnError(RuntimeError):
@@ -84,7 +86,7 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         getattr(L, name).restype = i32
     full = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp]
-    for name in ("sol_attn", "sol_attn2", "sol_attn2_pv8", "sol_attn_forward_train"):
+    for name in ("sol_attn", "sol_attn2", "sol_attn2_pv8", "sol_attn_forward_train", "sol_attn2_forward_train"):
         getattr(L, name).argtypes = full
         getattr(L, name).restype = i32
     prep = [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp, sz, vp]
@@ -99,8 +101,9 @@ def lib() -> ctypes.CDLL:
     for name in ("sol_attn_debug_routing", "sol_attn2_debug_routing"):
         getattr(L, name).argtypes = dbg
         getattr(L, name).restype = i32
-    L.sol_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
-    L.sol_attn_backward.restype = i32
+    for name in ("sol_attn_backward", "sol_attn2_backward"):
+        getattr(L, name).argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        getattr(L, name).restype = i32
     L.sol_attn_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp]
     L.sol_attn_noalloc.restype = i32
     _LIB = L
@@ -285,10 +288,19 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float 
     return out, workspace
 
 
-def backward(q, k, v, out, dout, workspace: torch.Tensor, dq: Optional[torch.Tensor] = None,
-             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None):
-    """Gradients (dq, dk, dv) of sum(dout * out) with the routing of the `forward_train` call
-    that filled `workspace` held fixed."""
+def forward_train2(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
+                   sink_start: Optional[int] = None, sink_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """Sol-Attn2 forward that keeps its routing, groups, anchor tails and row log-sum-exp for
+    `backward2`; returns (out, workspace)."""
+    if workspace is None:
+        workspace = alloc_workspace(SOL_VARIANT_SOL2_TRAIN, q)
+    out = _full_call("sol_attn2_forward_train", SOL_VARIANT_SOL2_TRAIN, q, k, v, tau, sink_start, sink_tokens,
+                     thresh, out, workspace)
+    return out, workspace
+
+
+def _backward_call(fn_name: str, q, k, v, out, dout, workspace, dq, dk, dv):
     _check_tensors(q, k, v)
     for name, t in (("out", out), ("dout", dout)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.shape != q.shape or t.device != q.device:
@@ -300,10 +312,23 @@ def backward(q, k, v, out, dout, workspace: torch.Tensor, dq: Optional[torch.Ten
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    _check(lib().sol_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                                   B, N, H, D, _ptr(workspace), workspace.numel(), _stream(q.device)),
-           "sol_attn_backward")
+    _check(getattr(lib(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   B, N, H, D, _ptr(workspace), workspace.numel(), _stream(q.device)), fn_name)
     return dq, dk, dv
+
+
+def backward2(q, k, v, out, dout, workspace: torch.Tensor, dq: Optional[torch.Tensor] = None,
+              dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(dout * out) with the routing and groups of the
+    `forward_train2` call that filled `workspace` held fixed."""
+    return _backward_call("sol_attn2_backward", q, k, v, out, dout, workspace, dq, dk, dv)
+
+
+def backward(q, k, v, out, dout, workspace: torch.Tensor, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(dout * out) with the routing of the `forward_train` call
+    that filled `workspace` held fixed."""
+    return _backward_call("sol_attn_backward", q, k, v, out, dout, workspace, dq, dk, dv)
 
 
 class SolAttnFunction(torch.autograd.Function):
@@ -327,6 +352,30 @@ def sol_attn_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float
                    sink_start: Optional[int] = None, sink_tokens: int = 0) -> torch.Tensor:
     """Differentiable Sol-Attn (autograd): gradients flow through q, k, v with the forward's routing fixed."""
     return SolAttnFunction.apply(q, k, v, tau, thresh, sink_start, sink_tokens)
+
+
+class SolAttn2Function(torch.autograd.Function):
+    """Sol-Attn2 as a differentiable op: forward_train2, then backward2 with routing and groups fixed."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, tau, thresh, sink_start, sink_tokens):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        out, ws = forward_train2(q, k, v, tau, thresh, sink_start, sink_tokens)
+        ctx.save_for_backward(q, k, v, out, ws)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, ws = ctx.saved_tensors
+        dq, dk, dv = backward2(q, k, v, out, dout.contiguous(), ws)
+        return dq, dk, dv, None, None, None, None
+
+
+def sol_attn2_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float = 1.0, thresh: str = "diag",
+                    sink_start: Optional[int] = None, sink_tokens: int = 0) -> torch.Tensor:
+    """Differentiable Sol-Attn2 (autograd): gradients flow through q, k, v (the E4M3 quantizer
+    passed straight through) with the forward's routing and key groups fixed."""
+    return SolAttn2Function.apply(q, k, v, tau, thresh, sink_start, sink_tokens)
 
 
 def prepare(variant: int, q, k, v, tau: float, workspace: torch.Tensor, thresh: str = "diag"):
@@ -440,7 +489,7 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
         kstat=view(L.kstat, torch.float32, (batch, heads, 2, 128)),
         kcov=view(L.kcov, torch.float32, (batch, heads, 128, 128)),
     )
-    if variant in (SOL_VARIANT_SOL2, SOL_VARIANT_SOL2_PV8):
+    if variant in (SOL_VARIANT_SOL2, SOL_VARIANT_SOL2_PV8, SOL_VARIANT_SOL2_TRAIN):
         tp = nbp * 64
         d.update(
             q8=view(L.q8, torch.uint8, (batch, heads, tp, 128)),
@@ -467,6 +516,24 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
             ld=view(L.ld, torch.float32, (batch, heads, tp, 2)),
             dkbar=view(L.dkbar, torch.float32, (batch, heads, nbp, 128)),
             dvbar=view(L.dvbar, torch.float32, (batch, heads, nbp, 128)),
+        )
+    if variant == SOL_VARIANT_SOL2_TRAIN:
+        tp = nbp * 64
+        d.update(
+            lse=view(L.lse, torch.float32, (batch, heads, tp)),
+            ofp=view(L.ofp, torch.float32, (batch, heads, tp, 128)),
+            mcol=view(L.mcol, torch.int64, (batch, heads, L.nb, nbp // 64)),
+            ld=view(L.ld, torch.float32, (batch, heads, tp, 2)),
+            qd=view(L.qd, torch.bfloat16, (batch, tokens, heads, 128)),
+            kd=view(L.kd, torch.bfloat16, (batch, tokens, heads, 128)),
+            dlam=view(L.dlam, torch.float32, (batch, heads, tp)),
+            qab=view(L.qab, torch.bfloat16, (batch, heads, nbp, 2, 128)),
+            dmub=view(L.dmub, torch.bfloat16, (batch, heads, nbp, 2, 128)),
+            dnub=view(L.dnub, torch.bfloat16, (batch, heads, nbp, 2, 128)),
+            alz=view(L.alz, torch.float32, (batch, heads, nbp, 2, 2)),
+            aextra=view(L.aextra, torch.float32, (batch, heads, nbp, 2, 128)),
+            gdk=view(L.gdk, torch.float32, (batch, heads, nbp, 2, 128)),
+            gdv=view(L.gdv, torch.float32, (batch, heads, nbp, 2, 128)),
         )
     if variant == SOL_VARIANT_SOL2_PV8:
         tp = nbp * 64

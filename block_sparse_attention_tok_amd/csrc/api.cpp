@@ -72,7 +72,7 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   int st = check_shape(batch, tokens, heads, head_dim);
   if (st != SOL_OK) return st;
   if (variant != SOL_VARIANT_SOL1 && variant != SOL_VARIANT_SOL2 && variant != SOL_VARIANT_SOL2_PV8 &&
-      variant != SOL_VARIANT_SOL1_TRAIN)
+      variant != SOL_VARIANT_SOL1_TRAIN && variant != SOL_VARIANT_SOL2_TRAIN)
     return SOL_ERR_ARG;
   std::memset(L, 0xff, sizeof(*L));          // every offset -1
   const int64_t nb = (tokens + kBlock - 1) / kBlock;
@@ -95,7 +95,8 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->kh = take(bh * tokens * kDim * 2);
     L->vh = take(bh * tokens * kDim * 2);
   }
-  if (variant == SOL_VARIANT_SOL2 || variant == SOL_VARIANT_SOL2_PV8) {
+  const bool sol2 = variant == SOL_VARIANT_SOL2 || variant == SOL_VARIANT_SOL2_PV8 || variant == SOL_VARIANT_SOL2_TRAIN;
+  if (sol2) {
     const int64_t tp = nbp * kBlock;
     L->q8 = take(bh * tp * kDim);
     L->k8 = take(bh * tp * kDim);
@@ -123,6 +124,26 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   if (L->kv_splits > 1) {
     L->opart = take(L->kv_splits * bh * tokens * kDim * 4);
     L->olse = take(L->kv_splits * bh * tokens * 4);
+  }
+  // forward state for the backward, and backward scratch (Sol-Attn2 training)
+  if (variant == SOL_VARIANT_SOL2_TRAIN) {
+    const int64_t tp = nbp * kBlock;
+    L->lse = take(bh * tp * 4);
+    L->ofp = take(bh * tp * kDim * 4);
+    L->mcol = take(bh * nb * (nbp / 64) * 8);
+    L->ld = take(bh * tp * 2 * 4);
+    L->kh = take(bh * tokens * kDim * 2);
+    L->vh = take(bh * tokens * kDim * 2);
+    L->qd = take(bh * tokens * kDim * 2);
+    L->kd = take(bh * tokens * kDim * 2);
+    L->dlam = take(bh * tp * 4);
+    L->qab = take(bh * 2 * nbp * kDim * 2);
+    L->dmub = take(bh * 2 * nbp * kDim * 2);
+    L->dnub = take(bh * 2 * nbp * kDim * 2);
+    L->alz = take(bh * 2 * nbp * 2 * 4);
+    L->aextra = take(bh * 2 * nbp * kDim * 4);
+    L->gdk = take(bh * nbp * 2 * kDim * 4);
+    L->gdv = take(bh * nbp * 2 * kDim * 4);
   }
   // forward state for the backward, and backward scratch (Sol-Attn training)
   if (variant == SOL_VARIANT_SOL1_TRAIN) {
@@ -180,6 +201,17 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.ld = (float*)at(L.ld);
   w.dkbar = (float*)at(L.dkbar);
   w.dvbar = (float*)at(L.dvbar);
+  w.qd = (uint16_t*)at(L.qd);
+  w.kd = (uint16_t*)at(L.kd);
+  w.dlam = (float*)at(L.dlam);
+  w.qab = (uint16_t*)at(L.qab);
+  w.dmub = (uint16_t*)at(L.dmub);
+  w.dnub = (uint16_t*)at(L.dnub);
+  w.alz = (float*)at(L.alz);
+  w.aextra = (float*)at(L.aextra);
+  w.gdk = (float*)at(L.gdk);
+  w.gdv = (float*)at(L.gdv);
+  w.ofp = (float*)at(L.ofp);
   return w;
 }
 
@@ -481,6 +513,34 @@ int sol_attn2(const void* q, const void* k, const void* v, void* out, int64_t ba
   if (st != SOL_OK) return st;
   return sol_attn2_fused(q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens, workspace,
                          workspace_bytes, stream);
+}
+
+int sol_attn2_forward_train(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
+                            int64_t heads, int64_t head_dim, float tau, int64_t sink_start, int64_t sink_tokens,
+                            int thresh, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return SOL_ERR_NULL;
+  int st = sol_attn_validate(batch, tokens, heads, head_dim, tau, sink_start, sink_tokens, thresh);
+  if (st != SOL_OK) return st;
+  st = prepare2(SOL_VARIANT_SOL2_TRAIN, q, k, v, batch, tokens, heads, head_dim, tau, thresh, workspace,
+                workspace_bytes, stream);
+  if (st != SOL_OK) return st;
+  return fused_common(SOL_VARIANT_SOL2_TRAIN, q, k, v, out, batch, tokens, heads, head_dim, sink_start,
+                      sink_tokens, workspace, workspace_bytes, nullptr, stream, true);
+}
+
+int sol_attn2_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, void* dq,
+                       void* dk, void* dv, int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out || !dout || !dq || !dk || !dv) return SOL_ERR_NULL;
+  sol_ws_layout L;
+  int st = prologue(SOL_VARIANT_SOL2_TRAIN, q, k, v, batch, tokens, heads, head_dim, workspace, workspace_bytes, &L);
+  if (st != SOL_OK) return st;
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return SOL_ERR_ARG;
+  solattn::Workspace w = resolve(L, workspace);
+  return hip_status(solattn::launch_backward2((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                              (const uint16_t*)out, (const uint16_t*)dout, (uint16_t*)dq,
+                                              (uint16_t*)dk, (uint16_t*)dv, shape_of(batch, tokens, heads), w,
+                                              (hipStream_t)stream));
 }
 
 int sol_attn2_debug_routing(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,

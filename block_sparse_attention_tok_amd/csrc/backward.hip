@@ -54,6 +54,12 @@ struct BwdArgs {
   float* ld;
   float* dkbar; float* dvbar;
   int nrange, bpr;            // pooled-key kernel: query ranges per chunk, query blocks per range
+  // Sol-Attn2 (sol2 = 1): no pooled tiles; the exact keys' epilogue adds their group's
+  // gradient (ghi: group bits per key block, gdk / gdv: [B][H][nbp][2][128]) and the dQ
+  // epilogue the tail terms (dlam [B][H][tp], tmu and aextra [B][H][2 nbp][128]).
+  int sol2;
+  const uint64_t* ghi; const float* gdk; const float* gdv;
+  const float* dlam; const float* tmu; const float* aextra;
 };
 
 // Slot swizzle of a 64 x 256-byte tile that is read both by rows (16 consecutive rows,
@@ -367,9 +373,23 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
         }
     }
   } else if (key_ok) {
-    const float inv_n = 1.0f / (float)(jb == a.nb - 1 ? last_n : kBlock);
-    const float* gk = a.dkbar + ((size_t)bh * a.nbp + jb) * kDim;
-    const float* gv = a.dvbar + ((size_t)bh * a.nbp + jb) * kDim;
+    const int n_blk = jb == a.nb - 1 ? last_n : kBlock;
+    float inv_n;
+    const float* gk;
+    const float* gv;
+    if (a.sol2) {
+      // Sol-Attn2: the key's group (G_hi if its bit is set) passes 1/n_g of its gradient
+      const uint64_t hi = a.ghi[(size_t)bh * a.nbp + jb];
+      const int grp = ((hi >> (32 * w + l32)) & 1ull) ? 0 : 1;
+      const int nh = __popcll(hi);
+      inv_n = 1.0f / (float)(grp == 0 ? nh : n_blk - nh);
+      gk = a.gdk + (((size_t)bh * a.nbp + jb) * 2 + grp) * kDim;
+      gv = a.gdv + (((size_t)bh * a.nbp + jb) * 2 + grp) * kDim;
+    } else {
+      inv_n = 1.0f / (float)n_blk;
+      gk = a.dkbar + ((size_t)bh * a.nbp + jb) * kDim;
+      gv = a.dvbar + ((size_t)bh * a.nbp + jb) * kDim;
+    }
     uint16_t* dkr = a.dk + head_off + (size_t)key * rs;
     uint16_t* dvr = a.dv + head_off + (size_t)key * rs;
 #pragma unroll
@@ -419,7 +439,7 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
     const int nvalid = min(64, a.nb - 64 * cc);
     const uint64_t validm = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
     sel_s[cc] = selm & validm;
-    prox_s[cc] = validm & ~selm;
+    prox_s[cc] = a.sol2 ? 0ull : validm & ~selm;            // Sol-Attn2: the tail has its own kernels
   }
   const int qrow = i * kBlock + w * 32 + l32;
   const int qr = qrow < a.N ? qrow : a.N - 1;
@@ -527,16 +547,455 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
 
   if (qrow < a.N) {
     uint16_t* dst = a.dq + head_off + (size_t)qrow * rs;
+    if (a.sol2) {
+      // Sol-Attn2 tail terms of row t in anchor a = (i, w): s dlambda_t mu_a (through
+      // lambda_t) plus the anchor's share of dq-bar_a
+      const size_t arow = ((size_t)bh * a.nbp + i) * 2 + w;
+      const float sdl = a.dlam[(size_t)bh * a.tp + qrow] * kScaleB;
+      const float* mu = a.tmu + arow * kDim;
+      const float* ax = a.aextra + arow * kDim;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * mt + 8 * g + 4 * kg;
+          const floatx4 m4 = *(const floatx4*)(mu + d0);
+          const floatx4 x4 = *(const floatx4*)(ax + d0);
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(dqT[mt][4 * g + e], kScaleB, __builtin_fmaf(sdl, m4[e], x4[e]));
+          uint2v pk;
+          pk[0] = pack_bf16x2(r[0], r[1]);
+          pk[1] = pack_bf16x2(r[2], r[3]);
+          *(uint2v*)(dst + d0) = pk;
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2v pk;
+          pk[0] = pack_bf16x2(dqT[mt][4 * g] * kScaleB, dqT[mt][4 * g + 1] * kScaleB);
+          pk[1] = pack_bf16x2(dqT[mt][4 * g + 2] * kScaleB, dqT[mt][4 * g + 3] * kScaleB);
+          *(uint2v*)(dst + 32 * mt + 8 * g + 4 * kg) = pk;
+        }
+    }
+  }
+}
+
+// ===========================================================================
+// Sol-Attn2 backward (draft, Method, Stage A1 passage: routing and groups fixed).  With the
+// tail of anchor a written as a softmax over groups g with logits l_g = ln n_g + s q-bar_a .
+// k-bar_g, probabilities pi_g, mu_a = sum pi_g k-bar_g, nu_a = sum pi_g v-bar_g, and each
+// row's tail logit lambda_t = ln Z_a + s (q'_t - q-bar_a) . mu_a, the gradient splits into
+//   rows:     dlambda_t = P_t,tail (dO_t . nu_a - D_t),  dq_t += s dlambda_t mu_a;
+//   anchors:  dlnZ_a = sum_t dlambda_t,  dmu_a = s sum_t dlambda_t (q'_t - q-bar_a),
+//             dnu_a = sum_t P_t,tail dO_t;
+//   groups:   dl_g = pi_g (dmu_a . k-bar_g + dnu_a . v-bar_g + c_a) with
+//             c_a = dlnZ_a - dmu_a . mu_a - dnu_a . nu_a -- the backward of an attention of
+//             anchors over groups with "output gradient" [dmu_a | dnu_a], "values"
+//             [k-bar_g | v-bar_g] and D = -c_a -- giving dq-bar_a = s sum_g dl_g k-bar_g -
+//             s dlnZ_a mu_a, dk-bar_g = s sum_a dl_g q-bar_a + sum_a pi_g dmu_a and
+//             dv-bar_g = sum_a pi_g dnu_a;
+//   means:    every row of anchor a gets dq-bar_a / n_a, every token of group g gets
+//             dk-bar_g / n_g and dv-bar_g / n_g (added by the exact-key kernel's epilogue).
+// The E4M3 quantizer of Q and K is passed straight through: the exact products run on the
+// dequantized q', k' rounded to bf16.
+// ===========================================================================
+struct Bwd2Args {
+  int B, N, H, nb, nbp, nbw, tp;
+  const uint16_t* v; const uint16_t* dout;                          // BTHD
+  const float* ofp;                                                 // [B][H][tp][128] fp32 output rows
+  const uint8_t* q8; const uint8_t* k8; const float* qscale; const float* kscale;
+  const float* qanc; const float* tmu; const float* tnu; const float* tlz; const float* lse;
+  const uint16_t* gk; const uint16_t* gv; const float* glogn;       // group rows [B][H][2 nbp]
+  const uint64_t* sel; const uint64_t* mcol;
+  uint16_t* qd; uint16_t* kd; uint16_t* kh; uint16_t* vh;
+  float* ld; float* dlam;
+  uint16_t* qab; uint16_t* dmub; uint16_t* dnub; float* alz; float* aextra;
+  float* gdk; float* gdv;
+};
+
+// bf16 copies of q' = s_q E4M3(q / s_q) and k' (BTHD, and k' head-major) and a head-major
+// copy of v; 16 threads per (b, n, h) row, 8 dims each.
+__global__ __launch_bounds__(256) void bwd2_prep_kernel(Bwd2Args a) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = t >> 4;
+  if (row >= (size_t)a.B * a.N * a.H) return;
+  const int c = (int)(t & 15);
+  const int h = (int)(row % a.H);
+  const size_t n = (row / a.H) % a.N, b = row / ((size_t)a.H * a.N);
+  const size_t bh = b * a.H + h;
+  const size_t src8 = (bh * a.tp + n) * kDim + 8 * c;
+  const size_t blk = bh * a.nbp + n / kBlock;
+  const float sq = a.qscale[blk], sk = a.kscale[blk];
+  const uint2v cq = *(const uint2v*)(a.q8 + src8);
+  const uint2v ck = *(const uint2v*)(a.k8 + src8);
+  uint4v oq, ok;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    auto q01 = __builtin_amdgcn_cvt_pk_f32_fp8(cq[m], false), q23 = __builtin_amdgcn_cvt_pk_f32_fp8(cq[m], true);
+    auto k01 = __builtin_amdgcn_cvt_pk_f32_fp8(ck[m], false), k23 = __builtin_amdgcn_cvt_pk_f32_fp8(ck[m], true);
+    oq[2 * m] = pack_bf16x2(q01[0] * sq, q01[1] * sq);
+    oq[2 * m + 1] = pack_bf16x2(q23[0] * sq, q23[1] * sq);
+    ok[2 * m] = pack_bf16x2(k01[0] * sk, k01[1] * sk);
+    ok[2 * m + 1] = pack_bf16x2(k23[0] * sk, k23[1] * sk);
+  }
+  const size_t dst = row * kDim + 8 * c;
+  const size_t dsth = (bh * a.N + n) * kDim + 8 * c;
+  *(uint4v*)(a.qd + dst) = oq;
+  *(uint4v*)(a.kd + dst) = ok;
+  *(uint4v*)(a.kh + dsth) = ok;
+  *(uint4v*)(a.vh + dsth) = *(const uint4v*)(a.v + dst);
+}
+
+// Per query block i (< nbp; blocks past the sequence give empty anchors): each row's
+// (lse, D) pair for the exact kernels and dlambda_t; each anchor's bf16 q-bar_a, dmu_a,
+// dnu_a, its (log2 Z_a, -c_a) pair (log2 Z_a = +inf for an anchor without rows or tail,
+// which zeroes its group probabilities) and the first part of dq-bar_a / n_a.
+// Threads: phase 1 row tid / 4, dims 32 (tid % 4) ..; phase 2 anchor tid / 128, dim tid % 128.
+__global__ __launch_bounds__(256) void bwd2_anchor_kernel(Bwd2Args a) {
+  __shared__ float mu_s[2][kDim], nu_s[2][kDim];
+  __shared__ float dl_s[64], pt_s[64];
+  __shared__ float red_s[4][2];
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int b = bh / a.H, h = bh % a.H;
+  const int n_i = i < a.nb ? min(kBlock, a.N - i * kBlock) : 0;
+  const size_t blk = (size_t)bh * a.nbp + i;
+  const float sq = i < a.nb ? a.qscale[blk] : 1.f;
+  for (int e = tid; e < 2 * kDim; e += 256) {
+    const int w = e >> 7, d = e & (kDim - 1);
+    const bool live = n_i > 32 * w;
+    mu_s[w][d] = live ? a.tmu[(blk * 2 + w) * kDim + d] : 0.f;
+    nu_s[w][d] = live ? a.tnu[(blk * 2 + w) * kDim + d] : 0.f;
+  }
+  __syncthreads();
+
+  // phase 1: D_t = dO_t . O_t (O_t the forward's fp32 row: with bf16 rows the rounding of
+  // O would swamp dlambda_t where the tail carries nearly all of a row's weight, and
+  // dlambda_t is then a small difference), dO_t . nu_a and q'_t . mu_a over the row's
+  // four quarters
+  {
+    const int r = tid >> 2, c = tid & 3, wa = r >> 5;
+    const int t = i * kBlock + r;
+    const bool valid = r < n_i;
+    float od = 0.f, nd = 0.f, qm = 0.f;
+    if (valid) {
+      const size_t g0 = (((size_t)b * a.N + t) * a.H + h) * kDim + 32 * c;
+      const floatx4* op = (const floatx4*)(a.ofp + ((size_t)bh * a.tp + t) * kDim + 32 * c);
+      const uint4v* gp = (const uint4v*)(a.dout + g0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint4v g = gp[m];
+        const floatx4 x0 = op[2 * m], x1 = op[2 * m + 1];
+        const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = 32 * c + 8 * m + 2 * e;
+          const float g0v = bf16_lo(g[e]), g1v = bf16_hi(g[e]);
+          od += g0v * xs[2 * e] + g1v * xs[2 * e + 1];
+          nd += g0v * nu_s[wa][d] + g1v * nu_s[wa][d + 1];
+        }
+      }
+      const uint4v* qp = (const uint4v*)(a.q8 + ((size_t)bh * a.tp + t) * kDim + 32 * c);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint4v cw = qp[m];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(cw[e], false), f23 = __builtin_amdgcn_cvt_pk_f32_fp8(cw[e], true);
+          const float* mu = mu_s[wa] + 32 * c + 16 * m + 4 * e;
+          qm += f01[0] * mu[0] + f01[1] * mu[1] + f23[0] * mu[2] + f23[1] * mu[3];
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o <= 2; o <<= 1) {
+      od += __shfl_xor(od, o);
+      nd += __shfl_xor(nd, o);
+      qm += __shfl_xor(qm, o);
+    }
+    const float tl = n_i > 32 * wa ? a.tlz[blk * 2 + wa] : kNegInf;
+    const float lse2 = valid ? a.lse[(size_t)bh * a.tp + t] : __builtin_inff();
+    float dl = 0.f, pt = 0.f;
+    if (valid && tl != kNegInf) {
+      pt = __builtin_amdgcn_exp2f(tl + qm * sq * kScaleLog2B - lse2);
+      dl = pt * (nd - od);
+    }
+    if (c == 0) {
+      const size_t rr = (size_t)bh * a.tp + t;
+      a.ld[2 * rr] = lse2;
+      a.ld[2 * rr + 1] = valid ? od : 0.f;
+      a.dlam[rr] = dl;
+      dl_s[r] = dl;
+      pt_s[r] = pt;
+    }
+  }
+  __syncthreads();
+
+  // phase 2: the anchor sums
+  const int w2 = tid >> 7, d = tid & (kDim - 1);
+  const size_t arow = blk * 2 + w2;
+  const int n_a = w2 == 0 ? min(n_i, 32) : max(n_i - 32, 0);
+  float sdq = 0.f, snu = 0.f, dlnz = 0.f;
+  for (int rr = 0; rr < n_a; ++rr) {
+    const int t = i * kBlock + 32 * w2 + rr;
+    const float dlv = dl_s[32 * w2 + rr], ptv = pt_s[32 * w2 + rr];
+    dlnz += dlv;
+    const uint32_t code = a.q8[((size_t)bh * a.tp + t) * kDim + d];
+    const float qv = __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0] * sq;
+    const float gv = bf16_bits_to_f32(a.dout[(((size_t)b * a.N + t) * a.H + h) * kDim + d]);
+    sdq = __builtin_fmaf(dlv, qv, sdq);
+    snu = __builtin_fmaf(ptv, gv, snu);
+  }
+  const float qa = n_a > 0 ? a.qanc[arow * kDim + d] : 0.f;
+  const float mu = mu_s[w2][d], nu = nu_s[w2][d];
+  const float dmu = kScaleB * (sdq - dlnz * qa);
+  const __bf16 dmu_b = (__bf16)dmu, dnu_b = (__bf16)snu, qa_b = (__bf16)qa;
+  a.qab[arow * kDim + d] = __builtin_bit_cast(uint16_t, qa_b);
+  a.dmub[arow * kDim + d] = __builtin_bit_cast(uint16_t, dmu_b);
+  a.dnub[arow * kDim + d] = __builtin_bit_cast(uint16_t, dnu_b);
+  a.aextra[arow * kDim + d] = n_a > 0 ? -kScaleB * dlnz * mu / (float)n_a : 0.f;
+  // c_a uses the bf16 dmu_a, dnu_a that the group products see
+  float pc = (float)dmu_b * mu + (float)dnu_b * nu;
+  float pq = qa * mu;
+  pc = wave_sum(pc);
+  pq = wave_sum(pq);
+  if ((tid & 63) == 0) {
+    red_s[tid >> 6][0] = pc;
+    red_s[tid >> 6][1] = pq;
+  }
+  __syncthreads();
+  if (d == 0) {
+    const float ct = red_s[2 * w2][0] + red_s[2 * w2 + 1][0];
+    const float qt = red_s[2 * w2][1] + red_s[2 * w2 + 1][1];
+    const float tl = n_a > 0 ? a.tlz[arow] : kNegInf;
+    const bool live = tl != kNegInf;
+    a.alz[arow * 2] = live ? tl + qt * kScaleLog2B : __builtin_inff();
+    a.alz[arow * 2 + 1] = live ? ct - dlnz : 0.f;
+  }
+}
+
+// dP accumulation (no zeroing): s0 / s1 += rows 0..31 / 32..63 of the tile at L times breg.
+__device__ __forceinline__ void row_product_acc(const unsigned char* L, const int (&roff)[8], const bf16x8 (&breg)[8],
+                                                floatx16& s0, floatx16& s1) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x8 a0 = *(const bf16x8*)(L + roff[ks]);
+    const bf16x8 a1 = *(const bf16x8*)(L + 32 * 256 + roff[ks]);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, breg[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, breg[ks], s1, 0, 0, 0);
+  }
+}
+
+// dq-bar_a: one workgroup per (b, h, 64 anchors = 32 query blocks), two waves of 32 anchors
+// (one per lane column), over the tiles of 64 groups (32 key blocks) whose blocks lie in
+// the sequence: S^T = K-bar Q-bar^T, dP^T = K-bar dmu^T + V-bar dnu^T (rows = groups),
+// dS^T = P^T (dP^T - D), dq-bar^T += K-bar^T dS^T.  Adds s dq-bar_a / n_a to aextra.
+__global__ __launch_bounds__(128, 1) void bwd2_tail_dq_kernel(Bwd2Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char Kl[2][16384];
+  __shared__ __attribute__((aligned(16))) unsigned char Vl[2][16384];
+  __shared__ __attribute__((aligned(16))) float Bl[2][256];     // ln n_g of the tile's groups + copies
+  const int nt = (a.nb + 31) / 32;
+  const int item = xcd_remap(blockIdx.x, a.B * a.H * nt);
+  const int at = __builtin_amdgcn_readfirstlane(item % nt);
+  const int bh = __builtin_amdgcn_readfirstlane(item / nt);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int al = 32 * w + l32;
+  const size_t rows_bh = (size_t)bh * 2 * a.nbp;
+  const size_t arow = rows_bh + 64 * at + al;
+  const int ia = 32 * at + (al >> 1);
+  const bool a_ok = ia < a.nb;
+  bf16x8 qreg[8], mreg[8], nreg[8];
+  load_row_frags(a.qab + arow * kDim, qreg, kg);
+  load_row_frags(a.dmub + arow * kDim, mreg, kg);
+  load_row_frags(a.dnub + arow * kDim, nreg, kg);
+  const float lz = a.alz[arow * 2], dd = a.alz[arow * 2 + 1];
+  const uint64_t* selrow = a.sel + ((size_t)bh * a.nb + (a_ok ? ia : 0)) * a.nbw;
+
+  const uint32_t row_bytes = kDim * 2;
+  const uint32_t span = (uint32_t)(2 * a.nbp) * row_bytes;
+  const DmaOffsetsD doff = dma_offsets_d(row_bytes, w, lane);
+  auto issue = [&](int gt, int buf) {
+    const uint32_t toff = (uint32_t)gt * 64 * row_bytes;
+    dma_tile_d(Kl[buf], make_rsrc(uniform_ptr(a.gk + rows_bh * kDim), span), toff, row_bytes, doff, w);
+    dma_tile_d(Vl[buf], make_rsrc(uniform_ptr(a.gv + rows_bh * kDim), span), toff, row_bytes, doff, w);
+    if (w == 0)   // 64 floats = 256 bytes; lanes 16..63 repeat lanes 0..15 into the copies
+      dma16_buf(make_rsrc(uniform_ptr(a.glogn + rows_bh), (uint32_t)(2 * a.nbp) * 4),
+                (uint32_t)gt * 256 + (lane & 15) * 16, 0, (unsigned char*)Bl[buf]);
+  };
+  int roff[8];
+  row_offsets(lane, roff);
+  int toff[4][2];
+  tr_offsets(lane, toff);
+
+  floatx16 dqT[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) dqT[mt] = floatx16{};
+  issue(0, 0);
+  int buf = 0;
+  for (int gt = 0; gt < nt; ++gt) {
+    wait_vm0();
+    lds_barrier();                                           // tile gt landed; other buffer free
+    if (gt + 1 < nt) issue(gt + 1, buf ^ 1);
+    const unsigned char* K = Kl[buf];
+    const unsigned char* V = Vl[buf];
+    floatx16 s0, s1, d0, d1;
+    row_product(K, roff, qreg, s0, s1);                      // S^T (rows = groups)
+    row_product(K, roff, mreg, d0, d1);                      // dP^T = K-bar dmu^T ...
+    row_product_acc(V, roff, nreg, d0, d1);                  // ... + V-bar dnu^T
+    // groups of blocks the anchor's query block selected are exact tokens, not tail
+    const uint32_t exact = a_ok ? (uint32_t)(selrow[gt >> 1] >> (32 * (gt & 1))) : 0xffffffffu;
+    bf16x8 pd[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const floatx4 b0 = *(const floatx4*)(Bl[buf] + 8 * q4 + 4 * kg);
+      const floatx4 b1 = *(const floatx4*)(Bl[buf] + 32 + 8 * q4 + 4 * kg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * q4 + e;
+        const int r0 = 8 * q4 + 4 * kg + e;
+        const bool ok0 = !((exact >> (r0 >> 1)) & 1u) && b0[e] != kNegInf;
+        const bool ok1 = !((exact >> ((r0 + 32) >> 1)) & 1u) && b1[e] != kNegInf;
+        const float p0 = ok0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], kScaleLog2B, b0[e] * kLog2e - lz)) : 0.f;
+        const float p1 = ok1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], kScaleLog2B, b1[e] * kLog2e - lz)) : 0.f;
+        pd[idx >> 3][idx & 7] = (__bf16)(p0 * (d0[idx] - dd));
+        pd[2 + (idx >> 3)][idx & 7] = (__bf16)(p1 * (d1[idx] - dd));
+      }
+    }
+    tr_product(dqT, K, toff, pd);                            // dq-bar^T += K-bar^T dS^T
+    buf ^= 1;
+  }
+
+  const int n_i = a_ok ? min(kBlock, a.N - ia * kBlock) : 0;
+  const int n_a = (al & 1) ? max(n_i - 32, 0) : min(n_i, 32);
+  if (n_a > 0) {
+    const float f = kScaleB / (float)n_a;
+    float* dst = a.aextra + arow * kDim;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        uint2v pk;
-        pk[0] = pack_bf16x2(dqT[mt][4 * g] * kScaleB, dqT[mt][4 * g + 1] * kScaleB);
-        pk[1] = pack_bf16x2(dqT[mt][4 * g + 2] * kScaleB, dqT[mt][4 * g + 3] * kScaleB);
-        *(uint2v*)(dst + 32 * mt + 8 * g + 4 * kg) = pk;
+        const int d0 = 32 * mt + 8 * g + 4 * kg;
+        floatx4 x = *(floatx4*)(dst + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(dqT[mt][4 * g + e], f, x[e]);
+        *(floatx4*)(dst + d0) = x;
       }
   }
+}
+
+// dk-bar_g, dv-bar_g: one workgroup per (b, h, 64 groups = 32 key blocks), two waves of 32
+// groups (one per lane column), over the tiles of 64 anchors whose blocks lie in the
+// sequence: S = Q-bar K-bar^T, dP = dmu K-bar^T + dnu V-bar^T (rows = anchors),
+// dS' = s P (dP - D), dv-bar^T += dnu^T P, dk-bar^T += Q-bar^T dS' + dmu^T P.
+__global__ __launch_bounds__(128, 1) void bwd2_group_grad_kernel(Bwd2Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char Ql[2][16384];
+  __shared__ __attribute__((aligned(16))) unsigned char Ml[2][16384];
+  __shared__ __attribute__((aligned(16))) unsigned char Nl[2][16384];
+  __shared__ __attribute__((aligned(16))) float St[2][256];     // (log2 Z_a, D) of 64 anchors + copy
+  const int nt = (a.nb + 31) / 32;
+  const int item = xcd_remap(blockIdx.x, a.B * a.H * nt);
+  const int gt = __builtin_amdgcn_readfirstlane(item % nt);
+  const int bh = __builtin_amdgcn_readfirstlane(item / nt);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gl = 32 * w + l32;
+  const size_t rows_bh = (size_t)bh * 2 * a.nbp;
+  const size_t grow = rows_bh + 64 * gt + gl;
+  const int jg = 32 * gt + (gl >> 1);
+  bf16x8 kreg[8], vreg[8];
+  load_row_frags(a.gk + grow * kDim, kreg, kg);
+  load_row_frags(a.gv + grow * kDim, vreg, kg);
+  const float lnb = a.glogn[grow];
+  const bool g_ok = jg < a.nb && lnb != kNegInf;
+  const float bias = g_ok ? lnb * kLog2e : 0.f;
+  const uint64_t* mc = a.mcol + ((size_t)bh * a.nb + (jg < a.nb ? jg : 0)) * a.nbw;
+
+  const uint32_t row_bytes = kDim * 2;
+  const uint32_t span = (uint32_t)(2 * a.nbp) * row_bytes;
+  const DmaOffsetsD doff = dma_offsets_d(row_bytes, w, lane);
+  auto issue = [&](int at, int buf) {
+    const uint32_t toff = (uint32_t)at * 64 * row_bytes;
+    dma_tile_d(Ql[buf], make_rsrc(uniform_ptr(a.qab + rows_bh * kDim), span), toff, row_bytes, doff, w);
+    dma_tile_d(Ml[buf], make_rsrc(uniform_ptr(a.dmub + rows_bh * kDim), span), toff, row_bytes, doff, w);
+    dma_tile_d(Nl[buf], make_rsrc(uniform_ptr(a.dnub + rows_bh * kDim), span), toff, row_bytes, doff, w);
+    if (w == 0)   // 64 (log2 Z, D) pairs = 512 bytes; lanes 32..63 repeat lanes 0..31 into the copy
+      dma16_buf(make_rsrc(uniform_ptr(a.alz + rows_bh * 2), (uint32_t)(2 * a.nbp) * 8),
+                (uint32_t)at * 512 + (lane & 31) * 16, 0, (unsigned char*)St[buf]);
+  };
+  int roff[8];
+  row_offsets(lane, roff);
+  int toff[4][2];
+  tr_offsets(lane, toff);
+
+  floatx16 dkT[4], dvT[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    dkT[mt] = floatx16{};
+    dvT[mt] = floatx16{};
+  }
+  issue(0, 0);
+  int buf = 0;
+  for (int at = 0; at < nt; ++at) {
+    wait_vm0();
+    lds_barrier();                                           // tile at landed; other buffer free
+    if (at + 1 < nt) issue(at + 1, buf ^ 1);
+    const unsigned char* Q = Ql[buf];
+    const unsigned char* M = Ml[buf];
+    const unsigned char* Nn = Nl[buf];
+    floatx16 s0, s1, d0, d1;
+    row_product(Q, roff, kreg, s0, s1);                      // S (rows = anchors)
+    row_product(M, roff, kreg, d0, d1);                      // dP = dmu K-bar^T ...
+    row_product_acc(Nn, roff, vreg, d0, d1);                 // ... + dnu V-bar^T
+    // anchors whose query block selected the group's block see its tokens exactly
+    const uint32_t exact = g_ok ? (uint32_t)(mc[at >> 1] >> (32 * (at & 1))) : 0xffffffffu;
+    bf16x8 pp[4], pd[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float* st = St[buf] + 2 * (32 * half + 8 * q4 + 4 * kg);
+        const floatx4 ld0 = *(const floatx4*)st;
+        const floatx4 ld1 = *(const floatx4*)(st + 4);
+        const float lz4[4] = {ld0[0], ld0[2], ld1[0], ld1[2]};
+        const float dd4[4] = {ld0[1], ld0[3], ld1[1], ld1[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = 4 * q4 + e;
+          const int r = 32 * half + 8 * q4 + 4 * kg + e;       // anchor row of the tile
+          const bool ok = !((exact >> (r >> 1)) & 1u) && 32 * at + (r >> 1) < a.nb;
+          const float sv = half ? s1[idx] : s0[idx];
+          const float dv = half ? d1[idx] : d0[idx];
+          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, kScaleLog2B, bias - lz4[e])) : 0.f;
+          pp[2 * half + (idx >> 3)][idx & 7] = (__bf16)p;
+          pd[2 * half + (idx >> 3)][idx & 7] = (__bf16)(p * (dv - dd4[e]) * kScaleB);
+        }
+      }
+    }
+    tr_product(dvT, Nn, toff, pp);                           // dv-bar^T += dnu^T P
+    tr_product(dkT, M, toff, pp);                            // dk-bar^T += dmu^T P
+    tr_product(dkT, Q, toff, pd);                            //          + Q-bar^T dS'
+    buf ^= 1;
+  }
+
+  float* gk = a.gdk + grow * kDim;
+  float* gv = a.gdv + grow * kDim;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * mt + 8 * g + 4 * kg;
+      floatx4 k4, v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k4[e] = dkT[mt][4 * g + e];
+        v4[e] = dvT[mt][4 * g + e];
+      }
+      *(floatx4*)(gk + d0) = k4;
+      *(floatx4*)(gv + d0) = v4;
+    }
 }
 
 }  // namespace
@@ -555,6 +1014,8 @@ hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.kbar_h = ws.kbar_h; a.vbar_h = ws.vbar_h; a.kh = ws.kh; a.vh = ws.vh;
   a.lse = ws.lse; a.mrow = ws.mrow; a.mcol = ws.mcol; a.ld = ws.ld;
   a.dkbar = ws.dkbar; a.dvbar = ws.dvbar;
+  a.sol2 = 0;
+  a.ghi = nullptr; a.gdk = nullptr; a.gdv = nullptr; a.dlam = nullptr; a.tmu = nullptr; a.aextra = nullptr;
   // pooled keys: enough (chunk, query range) workgroups to fill the chip twice over
   const int bhc = s.B * s.H * nchunks;
   int nrange = (2048 + bhc - 1) / bhc;
@@ -578,6 +1039,62 @@ hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t*
   hipLaunchKernelGGL(bwd_kv_kernel<false>, dim3(s.B * s.H * ws.nb), dim3(128), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(s.B * s.H * ws.nb), dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward2(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,
+                            const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, Shape s,
+                            const Workspace& ws, hipStream_t stream) {
+  (void)q;
+  (void)k;   // the backward reads the forward's E4M3 codes and scales from the workspace
+  if (!ws.lse || !ws.sel || !ws.mcol || !ws.ld || !ws.kh || !ws.vh || !ws.qd || !ws.kd || !ws.dlam || !ws.qab ||
+      !ws.dmub || !ws.dnub || !ws.alz || !ws.aextra || !ws.gdk || !ws.gdv || !ws.q8 || !ws.k8 || !ws.qscale ||
+      !ws.kscale || !ws.qanc || !ws.tmu || !ws.tnu || !ws.tlz || !ws.gk || !ws.gv || !ws.glogn || !ws.ghi ||
+      !ws.ofp)
+    return hipErrorInvalidValue;
+  const int nchunks = ws.nbp / 64;
+  if (nchunks > kMaxChunksB) return hipErrorInvalidValue;
+  Bwd2Args t;
+  t.B = s.B; t.N = s.N; t.H = s.H; t.nb = ws.nb; t.nbp = ws.nbp; t.nbw = nchunks; t.tp = ws.nbp * kBlock;
+  t.v = v; t.dout = dout; t.ofp = ws.ofp;
+  t.q8 = ws.q8; t.k8 = ws.k8; t.qscale = ws.qscale; t.kscale = ws.kscale;
+  t.qanc = ws.qanc; t.tmu = ws.tmu; t.tnu = ws.tnu; t.tlz = ws.tlz; t.lse = ws.lse;
+  t.gk = ws.gk; t.gv = ws.gv; t.glogn = ws.glogn;
+  t.sel = ws.sel; t.mcol = ws.mcol;
+  t.qd = ws.qd; t.kd = ws.kd; t.kh = ws.kh; t.vh = ws.vh;
+  t.ld = ws.ld; t.dlam = ws.dlam;
+  t.qab = ws.qab; t.dmub = ws.dmub; t.dnub = ws.dnub; t.alz = ws.alz; t.aextra = ws.aextra;
+  t.gdk = ws.gdk; t.gdv = ws.gdv;
+
+  BwdArgs a;
+  a.q = ws.qd; a.k = ws.kd; a.v = v; a.out = out; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = nchunks; a.tp = ws.nbp * kBlock;
+  a.kbar_h = nullptr; a.vbar_h = nullptr; a.kh = ws.kh; a.vh = ws.vh;
+  a.lse = ws.lse; a.mrow = ws.sel; a.mcol = ws.mcol; a.ld = ws.ld;
+  a.dkbar = nullptr; a.dvbar = nullptr;
+  a.nrange = 1; a.bpr = ws.nb;
+  a.sol2 = 1;
+  a.ghi = ws.ghi; a.gdk = ws.gdk; a.gdv = ws.gdv; a.dlam = ws.dlam; a.tmu = ws.tmu; a.aextra = ws.aextra;
+
+  const size_t rows16 = (size_t)s.B * s.N * s.H * 16;
+  const int nt = (ws.nb + 31) / 32;
+  const int bhn = s.B * s.H;
+  hipLaunchKernelGGL(bwd2_prep_kernel, dim3((unsigned)((rows16 + 255) / 256)), dim3(256), 0, stream, t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t ntr = (size_t)bhn * ws.nb * nchunks;
+  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)((ntr + 255) / 256)), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd2_anchor_kernel, dim3(ws.nbp, bhn), dim3(256), 0, stream, t);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd2_tail_dq_kernel, dim3(bhn * nt), dim3(128), 0, stream, t);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd2_group_grad_kernel, dim3(bhn * nt), dim3(128), 0, stream, t);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_kv_kernel<false>, dim3(bhn * ws.nb), dim3(128), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(bhn * ws.nb), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

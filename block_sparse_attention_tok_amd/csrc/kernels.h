@@ -45,6 +45,18 @@ struct Workspace {
   float* ld;        // [B][H][tp][2] (lse, D = dO . O) per query row
   float* dkbar;     // [B][H][nbp][128] gradient w.r.t. the pooled keys K-bar_j (times 1/sqrt(d))
   float* dvbar;     // [B][H][nbp][128] gradient w.r.t. the pooled values V-bar_j
+  // Sol-Attn2 training layout (the forward's lse, mcol and ld above are shared): backward scratch
+  uint16_t* qd;     // [B][N][H][128] bf16 dequantized q' (BTHD)
+  uint16_t* kd;     // [B][N][H][128] bf16 dequantized k' (BTHD); kh / vh hold k' and v head-major
+  float* dlam;      // [B][H][tp] gradient w.r.t. each row's tail logit lambda_t
+  uint16_t* qab;    // [B][H][2 nbp][128] bf16 anchor means q-bar_a
+  uint16_t* dmub;   // [B][H][2 nbp][128] bf16 gradient w.r.t. mu_a
+  uint16_t* dnub;   // [B][H][2 nbp][128] bf16 gradient w.r.t. nu_a
+  float* alz;       // [B][H][2 nbp][2] (log2 Z_a, -c_a) per anchor
+  float* aextra;    // [B][H][2 nbp][128] per-anchor share of dq through q-bar_a (added to each row)
+  float* gdk;       // [B][H][nbp][2][128] gradient w.r.t. the group mean keys (with 1/sqrt(d))
+  float* gdv;       // [B][H][nbp][2][128] gradient w.r.t. the group mean values
+  float* ofp;       // [B][H][tp][128] the Sol-Attn2 training forward's output rows in fp32
 };
 
 struct Shape {
@@ -84,6 +96,11 @@ hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Worksp
 hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,
                            const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, Shape s,
                            const Workspace& ws, hipStream_t stream);
+// Sol-Attn2 backward with the forward's routing and groups fixed: dequantized copies, the
+// per-anchor tail gradients, the group gradients, then the exact dK / dV and dQ passes.
+hipError_t launch_backward2(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,
+                            const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, Shape s,
+                            const Workspace& ws, hipStream_t stream);
 // FP8 PV variant, stage 1 addition: per-head V scale and the E4M3 V codes (v8t).
 hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream);
 

@@ -622,6 +622,8 @@ struct Fused2Args {
   const uint64_t* sel; const float* tmu; const float* tnu; const float* tlz;
   const uint8_t* v8t; const float* vscale;   // FP8 PV only
   unsigned long long* pairs;                 // += selected token pairs n_i n_j (NULL = none)
+  float* lse;                                // [B][H][tp] base-2 log of each row's denominator (NULL = none)
+  float* ofp;                                // [B][H][tp][128] fp32 output rows (training; NULL = none)
 };
 
 // 16-byte slot swizzle of the 128 x 64-byte FP8 V^T tile (rows = dims): 16 consecutive
@@ -903,6 +905,8 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   const float vs = kPv8 ? a.vscale[bh] : 1.f;
   const float l_tot = l_ex * alpha + wt;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (a.lse != nullptr && kg == 0 && qrow < a.N)     // training forward: the row's log2-sum-exp
+    a.lse[(size_t)bh * a.tp + qrow] = l_tot > 0.f ? m_use + __log2f(l_tot) : kNegInf;
   if (qrow < a.N && a.out != nullptr) {
     uint16_t* dst = a.out + head_off + (size_t)qrow * rs;
 #pragma unroll
@@ -913,6 +917,7 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
         float r4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) r4[e] = (o[mt][4 * g + e] * (alpha * vs) + wt * nu_s[w][d0 + e]) * inv;
+        if (a.ofp != nullptr) *(floatx4*)(a.ofp + ((size_t)bh * a.tp + qrow) * kDim + d0) = floatx4{r4[0], r4[1], r4[2], r4[3]};
         uint2v pk;
         pk[0] = pack_bf16x2(r4[0], r4[1]);
         pk[1] = pack_bf16x2(r4[2], r4[3]);
@@ -933,6 +938,8 @@ hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Worksp
   a.sel = ws.sel; a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
   a.v8t = ws.v8t; a.vscale = ws.vscale;
   a.pairs = pairs;
+  a.lse = pv8 ? nullptr : ws.lse;            // set for the Sol-Attn2 training layout only
+  a.ofp = pv8 ? nullptr : ws.ofp;
   if (pairs != nullptr) {   // the counter is cleared on the stream by a kernel (graph-safe)
     hipLaunchKernelGGL(zero_counter2_kernel, dim3(1), dim3(1), 0, stream, pairs);
     hipError_t e0 = hipGetLastError();

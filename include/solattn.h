@@ -57,7 +57,8 @@ typedef enum {
     SOL_VARIANT_SOL1 = 1,      /* Sol-Attn */
     SOL_VARIANT_SOL2 = 2,      /* Sol-Attn2: FP8 Q/K, bf16 V */
     SOL_VARIANT_SOL2_PV8 = 3,  /* Sol-Attn2 with ExpCast P and per-head FP8 V (FP8 PV) */
-    SOL_VARIANT_SOL1_TRAIN = 4 /* Sol-Attn forward that keeps its state for sol_attn_backward */
+    SOL_VARIANT_SOL1_TRAIN = 4, /* Sol-Attn forward that keeps its state for sol_attn_backward */
+    SOL_VARIANT_SOL2_TRAIN = 5  /* Sol-Attn2 forward that keeps its state for sol_attn2_backward */
 } sol_variant;
 
 /* Byte offsets into the workspace of the intermediate arrays (for tests and
@@ -107,10 +108,21 @@ typedef enum {
  *   ld       float [B][H][tp][2]      (lse, dO . O) per query row (backward scratch)
  *   dkbar, dvbar float [B][H][nbp][128] gradients w.r.t. the pooled keys (times 1/sqrt(d))
  *                                      and pooled values (backward scratch)
+ * SOL_VARIANT_SOL2_TRAIN (the Sol-Attn2 arrays above, then): lse and ld as for Sol-Attn
+ * training (lse written by sol_attn2_forward_train), ofp float [B][H][tp][128] (the
+ * forward's output rows before rounding to bf16, so that the backward's D_t = dO_t . O_t
+ * does not inherit the output's rounding), mcol (sel by key block), kh / vh (dequantized
+ * k' and v head-major), and the backward scratch
+ *   qd, kd   bf16  [B][N][H][128]     dequantized q', k' (BTHD)
+ *   dlam     float [B][H][tp]         gradient w.r.t. each row's tail logit
+ *   qab, dmub, dnub bf16 [B][H][2 nbp][128] anchor means and the gradients w.r.t. mu_a, nu_a
+ *   alz      float [B][H][2 nbp][2]   (log2 Z_a, -c_a) per anchor
+ *   aextra   float [B][H][2 nbp][128] per-anchor share of dq through the anchor mean
+ *   gdk, gdv float [B][H][nbp][2][128] gradients w.r.t. the group mean keys / values
  * The SOL_VARIANT_SOL2_PV8 layout is the SOL_VARIANT_SOL2 layout with v8t, vbmax and
  * vscale appended, so the Sol-Attn2 stage calls accept either workspace; likewise the
  * SOL_VARIANT_SOL1_TRAIN layout is the SOL_VARIANT_SOL1 one with the training arrays
- * appended.
+ * appended, and the SOL_VARIANT_SOL2_TRAIN layout the SOL_VARIANT_SOL2 one.
  */
 typedef struct {
     int64_t total_bytes;
@@ -122,6 +134,8 @@ typedef struct {
     int64_t v8t, vbmax, vscale;
     int64_t lse, mrow, mcol, ld, dkbar, dvbar;
     int64_t kh, vh;
+    int64_t qd, kd, dlam, qab, dmub, dnub, alz, aextra, gdk, gdv;
+    int64_t ofp;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */
@@ -237,6 +251,34 @@ int sol_attn_forward_train(const void* q, const void* k, const void* v, void* ou
 int sol_attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                       void* dq, void* dk, void* dv, int64_t batch, int64_t tokens, int64_t heads,
                       int64_t head_dim, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sol-Attn2 training forward (draft, Method, Stage A1 passage: block selection and the
+ * key groups stay fixed in the backward).  Same arguments, output and errors as
+ * sol_attn2, on a workspace of at least sol_attn_workspace_bytes(SOL_VARIANT_SOL2_TRAIN,
+ * ...) bytes; the call also leaves in the workspace everything sol_attn2_backward reads:
+ * the E4M3 codes and scales, the routing bits (sel), the group bits, sizes and means,
+ * each anchor's tail (mu_a, nu_a, Z_a) and each row's log-sum-exp (lse).  The workspace
+ * must then be left untouched until the backward call. */
+int sol_attn2_forward_train(const void* q, const void* k, const void* v, void* out,
+                            int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                            float tau, int64_t sink_start, int64_t sink_tokens, int thresh,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of sol_attn2_forward_train with its routing and groups fixed: the gradients of
+ * sum(dout * out) w.r.t. q, k and v (draft, Method, Eqs. (1)-(3), differentiated with the
+ * selection and the memberships constant).  Gradients reach every exact token directly;
+ * every anchor's queries through its tail logit and, as 1/n_a shares, through its mean
+ * q-bar_a; every token of an unselected block, as 1/n_g of its group's mean-key and
+ * mean-value gradients.  The E4M3 quantizer of q and k is passed straight through (the
+ * gradient w.r.t. the dequantized value is the gradient returned), and the exact products
+ * use the dequantized q', k' rounded to bf16.  q, k, v, out: the tensors of the forward
+ * call (device, bf16 BTHD, unchanged since); dout: device bf16 BTHD; dq, dk, dv: device
+ * bf16 BTHD outputs, fully written.  workspace: the forward's (SOL_VARIANT_SOL2_TRAIN
+ * layout), also used as scratch; the shape must be the forward's.  Errors as
+ * sol_attn_backward.  No atomics: results are deterministic. */
+int sol_attn2_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                       void* dq, void* dk, void* dv, int64_t batch, int64_t tokens, int64_t heads,
+                       int64_t head_dim, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Test and tooling export, not part of the hot path: like sol_attn (with an
  * explicit kv_splits, 0 = automatic, and a workspace sized for it), and the

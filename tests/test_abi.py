@@ -68,7 +68,7 @@ def test_validate(L, args, status):
 
 def test_workspace_sizes_and_layout(L):
     from block_sparse_attention_tok_amd import _lib
-    for variant in (1, 2, 4):
+    for variant in (1, 2, 4, 5):
         for (B, N, H) in ((1, 1024, 2), (1, 14040, 12), (2, 333, 3), (1, 32768, 32)):
             n = L.sol_attn_workspace_bytes(variant, B, N, H, 128)
             lay = _lib.workspace_layout(variant, B, N, H)
@@ -86,7 +86,7 @@ def test_workspace_sizes_and_layout(L):
             else:
                 assert lay.sel >= 0
     assert L.sol_attn_workspace_bytes(1, 1, 1024, 2, 64) == 0
-    assert L.sol_attn_workspace_bytes(5, 1, 1024, 2, 128) == 0
+    assert L.sol_attn_workspace_bytes(6, 1, 1024, 2, 128) == 0
 
 
 @pytest.mark.parametrize("B,N,H", [(1, 1024, 2), (1, 14040, 12), (2, 333, 3)])
@@ -125,6 +125,35 @@ def test_training_layout_extends_the_sol_attn_layout(L, B, N, H):
     assert l4.mrow - l4.lse >= B * H * tp * 4
     assert l4.mcol - l4.mrow >= B * H * l4.nb * nbw * 8
     assert l4.dvbar - l4.dkbar >= B * H * l4.nbp * 128 * 4
+
+
+@pytest.mark.parametrize("B,N,H", [(1, 1024, 2), (1, 14040, 12), (2, 333, 3), (1, 32768, 32)])
+def test_sol2_training_layout_extends_the_sol2_layout(L, B, N, H):
+    """The Sol-Attn2 training workspace is the Sol-Attn2 one with the forward's row
+    log-sum-exp and the backward scratch appended (so every Sol-Attn2 stage call runs on it
+    unchanged), each array large enough for its documented shape."""
+    from block_sparse_attention_tok_amd import _lib
+    l2 = _lib.workspace_layout(2, B, N, H)
+    l5 = _lib.workspace_layout(5, B, N, H)
+    extra = ("lse", "ofp", "mcol", "ld", "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz", "aextra",
+             "gdk", "gdv")
+    for name, _ in _lib.WsLayout._fields_:
+        if name in ("total_bytes",) + extra:
+            continue
+        assert getattr(l2, name) == getattr(l5, name), name
+    assert all(getattr(l2, n) == -1 for n in extra)
+    assert l5.mrow == l5.dkbar == l5.dvbar == l5.v8t == -1
+    assert all(getattr(l1, n) == -1 for l1 in (_lib.workspace_layout(1, B, N, H),) for n in ("ofp", "qd", "gdk"))
+    offs = [getattr(l5, n) for n in extra] + [l5.total_bytes]
+    assert offs == sorted(offs) and offs[0] >= l2.total_bytes
+    bh, nbp, nb = B * H, l5.nbp, l5.nb
+    tp = nbp * 64
+    need = dict(lse=bh * tp * 4, ofp=bh * tp * 512, mcol=bh * nb * (nbp // 64) * 8, ld=bh * tp * 8, kh=bh * N * 256, vh=bh * N * 256,
+                qd=bh * N * 256, kd=bh * N * 256, dlam=bh * tp * 4, qab=bh * 2 * nbp * 256,
+                dmub=bh * 2 * nbp * 256, dnub=bh * 2 * nbp * 256, alz=bh * 2 * nbp * 8, aextra=bh * 2 * nbp * 512,
+                gdk=bh * 2 * nbp * 512, gdv=bh * 2 * nbp * 512)
+    for a, b in zip(extra, offs[1:]):
+        assert b - getattr(l5, a) >= need[a], a
 
 
 @pytest.mark.parametrize("tokens,req,expect", [
