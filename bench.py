@@ -29,7 +29,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--variant", choices=["sol1", "sol2", "sol2pv8", "sol1train"], default="sol1",
+    p.add_argument("--variant", choices=["sol1", "sol2", "sol2pv8", "sol1train", "sol2train"], default="sol1",
                    help="sol1: Sol-Attn; sol2: Sol-Attn2 (FP8 Q/K); sol2pv8: Sol-Attn2 with ExpCast FP8 PV; "
                         "sol1train: Sol-Attn training step (forward that keeps its routing + backward)")
     p.add_argument("--tokens", type=int, default=32768, help="video tokens (32768 = operator benchmark shape)")
@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--cpu-sample-heads", type=int, default=16, help="heads the CPU oracle is timed on")
     p.add_argument("--cpu-sample-blocks", type=int, default=256, help="query blocks per sampled head")
     p.add_argument("--kv-splits", type=int, default=0, help="key-range splits of the fused pass (0 = automatic)")
+    p.add_argument("--thresh", choices=["diag", "exact"], default="diag",
+                   help="threshold estimator: diagonal (default) or full covariance (paper §3.1 Eq. (5))")
     p.add_argument("--no-range", action="store_true",
                    help="skip the extra range entries (80%%/85%% at 32K, 512+131072 at 90%%)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -70,7 +72,7 @@ def make_inputs(video_tokens: int, text_sink: int, heads: int):
 
 
 def measure(variant: int, qc, kc, vc, text_sink: int, target: float, tau_fixed, steps: int, warmup: int,
-            kv_splits: int, dense_baselines: bool):
+            kv_splits: int, dense_baselines: bool, thresh: str = "diag"):
     """Time one workload: tau bisected on the kernel's own selected-pair counter to the target
     token-pair sparsity, then `warmup` untimed and `steps` timed full calls (prepare + fused),
     then the dominant kernel alone with HIP events on the launch stream."""
@@ -92,7 +94,7 @@ def measure(variant: int, qc, kc, vc, text_sink: int, target: float, tau_fixed, 
 
     def routing(tau, masks=False):
         # (the FP8-PV workspace extends the Sol-Attn2 one and routes the same way)
-        _, m, _, pairs = bsa.debug_routing(min(variant, 2), q, k, v, tau, "diag", sink_start, sink_tokens, out=None,
+        _, m, _, pairs = bsa.debug_routing(min(variant, 2), q, k, v, tau, thresh, sink_start, sink_tokens, out=None,
                                            workspace=ws, kv_splits=kv_splits if variant == 1 else 0,
                                            return_pairs=True)
         return (m.numpy() if masks else None), pairs
@@ -122,7 +124,7 @@ def measure(variant: int, qc, kc, vc, text_sink: int, target: float, tau_fixed, 
         + (f", proxy {flops_proxy / 1e12:.3f} TFLOP" if variant == 1 else ""))
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
-        bsa.prepare(variant, q, k, v, tau, ws)
+        bsa.prepare(variant, q, k, v, tau, ws, thresh)
         bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens, kv_splits)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -130,7 +132,7 @@ def measure(variant: int, qc, kc, vc, text_sink: int, target: float, tau_fixed, 
     t_start = time.perf_counter()
     for s_ in range(steps):
         ev[s_][0].record(stream)
-        bsa.prepare(variant, q, k, v, tau, ws)
+        bsa.prepare(variant, q, k, v, tau, ws, thresh)
         ev[s_][1].record(stream)
         bsa.fused(variant, q, k, v, out, ws, sink_start, sink_tokens, kv_splits)
         ev[s_][2].record(stream)
@@ -233,7 +235,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
         return
-    if args.variant == "sol1train":
+    if args.variant in ("sol1train", "sol2train"):
         return bench_train(args)
     variant = {"sol1": 1, "sol2": 2, "sol2pv8": 3}[args.variant]
     H = args.heads
@@ -243,7 +245,7 @@ def main():
     qc, kc, vc = make_inputs(args.tokens, args.text_sink, H)
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
     r = measure(variant, qc, kc, vc, args.text_sink, args.sparsity, args.tau, args.steps, args.warmup,
-                args.kv_splits, not args.no_dense_baselines)
+                args.kv_splits, not args.no_dense_baselines, args.thresh)
     value = r["dense_flops"] / (r["ms_per_step"] * 1e-3) / 1e12
 
     from block_sparse_attention_tok_amd.profsum import read_traffic
@@ -258,7 +260,8 @@ def main():
     # run on the same box: the operator shape at 80% and 85%, and 512 text-sink + 131072
     # video tokens at 90%.  Each is a separate workload timed like the headline one.
     rng_entries = []
-    if variant == 1 and not args.no_range and args.tau is None and not args.text_sink and args.tokens == 32768:
+    if (variant == 1 and not args.no_range and args.tau is None and not args.text_sink and args.tokens == 32768
+            and args.thresh == "diag"):
         for video, sink, target in ((32768, 0, 0.80), (32768, 0, 0.85), (131072, 512, 0.90)):
             if sink == args.text_sink and video == args.tokens and abs(target - args.sparsity) < 1e-9:
                 continue
@@ -287,7 +290,8 @@ def main():
     workload = (f"{ {1: 'Sol-Attn', 2: 'Sol-Attn2 (FP8 Q/K)', 3: 'Sol-Attn2 (FP8 Q/K, ExpCast FP8 PV)'}[variant] } "
                 f"forward, B={B} H={H} d={D} "
                 f"N={N}{' (512 text sink + ' + str(args.tokens) + ' video)' if args.text_sink else ''}, "
-                f"block-offset synthetic data, {100 * args.sparsity:.0f}% target token-pair sparsity")
+                f"block-offset synthetic data, {100 * args.sparsity:.0f}% target token-pair sparsity"
+                + (", full-covariance threshold" if args.thresh == "exact" else ""))
     frac = r["achieved"] / r["peak"]
     rec = {
         "metric": "dense-equiv attn TFLOP/s + MFMA util, H32 d128 N=32K-128K @80-90% sparsity",
@@ -303,7 +307,8 @@ def main():
         "dtype": {1: "bf16", 2: "fp8(e4m3 QK)+bf16(PV)", 3: "fp8(e4m3 QK, ExpCast P, e4m3 V)"}[variant],
         "data": "synthetic (seeded block-offset Gaussian Q/K/V, bf16)",
         "config": {"workload": workload, "batch": B, "heads": H, "head_dim": D, "tokens": N,
-                   "tau": round(r["tau"], 5), "realised_sparsity": round(r["realised_sparsity"], 5),
+                   "tau": round(r["tau"], 5), "thresh": args.thresh,
+                   "realised_sparsity": round(r["realised_sparsity"], 5),
                    "selected_token_pairs": int(r["exact_pairs"]),
                    "sink": [0 if args.text_sink else None, args.text_sink],
                    "median_event_ms": round(r["median_event_ms"], 4),
@@ -327,21 +332,27 @@ def main():
 
 
 def bench_train(args):
-    """Training step: sol_attn_forward_train + sol_attn_backward (routing fixed), timed as one
-    step.  value = dense-equivalent training TFLOP/s, 14 B H N^2 d per step (forward 4, backward
-    10: S recomputed, dP, dV, dK, dQ).  The roofline covers the backward call: algorithmic FLOP
-    are 14 d per selected token pair and per (query token, unselected block), 8 d in the dK / dV
-    kernels and 6 d in the dQ kernel."""
+    """Training step: the training forward + the backward with routing (and Sol-Attn2's key
+    groups) fixed, timed as one step.  value = dense-equivalent training TFLOP/s,
+    14 B H N^2 d per step (forward 4, backward 10: S recomputed, dP, dV, dK, dQ).  The
+    roofline covers the backward call.  Algorithmic FLOP: 14 d per selected token pair (8 d in
+    the dK / dV kernel, 6 d in the dQ kernel); Sol-Attn adds 14 d per (query token,
+    unselected block) for the pooled keys; Sol-Attn2 adds 20 d per (anchor, tail group) pair
+    (8 d for dq-bar: S, dP over [k-bar | v-bar], dq-bar; 12 d for the group gradients: S, dP,
+    dv-bar, and dk-bar's two products)."""
     import numpy as np
     import torch
 
     import block_sparse_attention_tok_amd as bsa
     from workloads import block_offset_tensor, text_prefix_tensor
+    sol2 = args.variant == "sol2train"
+    variant = bsa.SOL_VARIANT_SOL2_TRAIN if sol2 else bsa.SOL_VARIANT_SOL1_TRAIN
+    fwd_call, bwd_call = (bsa.forward_train2, bsa.backward2) if sol2 else (bsa.forward_train, bsa.backward)
     dev = torch.device("cuda:0")
     B, H, D = 1, args.heads, 128
     N = args.tokens + args.text_sink
     sink_start, sink_tokens = (0, args.text_sink) if args.text_sink else (None, 0)
-    log(f"[bench] generating B={B} N={N} H={H} d={D} (training step)")
+    log(f"[bench] generating B={B} N={N} H={H} d={D} ({args.variant} training step)")
     if args.text_sink:
         q, k, v = (text_prefix_tensor(B, args.text_sink, args.tokens, H, D, 3000 + i) for i in range(3))
     else:
@@ -349,32 +360,42 @@ def bench_train(args):
     g = torch.Generator().manual_seed(3999)
     dout = torch.randn(*q.shape, generator=g).to(torch.bfloat16)
     q, k, v, dout = (t.to(dev) for t in (q, k, v, dout))
-    ws = bsa.alloc_workspace(bsa.SOL_VARIANT_SOL1_TRAIN, q)
+    ws = bsa.alloc_workspace(variant, q)
+    log(f"[bench] workspace {ws.numel() / 2**20:.1f} MiB")
     out = torch.empty_like(q)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     tau = 1.28 if args.tau is None else args.tau
-    bsa.forward_train(q, k, v, tau, "diag", sink_start, sink_tokens, out=out, workspace=ws)
+    fwd_call(q, k, v, tau, args.thresh, sink_start, sink_tokens, out=out, workspace=ws)
     torch.cuda.synchronize()
-    views = bsa.workspace_views(bsa.SOL_VARIANT_SOL1_TRAIN, ws, B, N, H)
+    views = bsa.workspace_views(variant, ws, B, N, H)
     nb = views["nb"]
-    w = views["mrow"].cpu()
+    w = views["sel" if sol2 else "mrow"].cpu()
     bits = torch.arange(64, dtype=torch.int64)
     masks = ((w.unsqueeze(-1) >> bits) & 1).bool().reshape(B, H, nb, -1)[..., :nb].numpy()
     counts = np.full(nb, 64.0)
     counts[-1] = N - 64 * (nb - 1)
     exact_pairs = float((masks * np.outer(counts, counts)).sum())
-    proxy_units = float(((~masks) * counts[:, None]).sum())
     real_sp = 1.0 - exact_pairs / (B * H * float(N) ** 2)
-    bwd_flops = 14.0 * D * (exact_pairs + proxy_units)
-    fwd_flops = 4.0 * D * (exact_pairs + proxy_units)
+    if sol2:
+        groups = np.isfinite(views["glogn"][..., :nb, :].cpu().numpy()).sum(-1).astype(np.float64)   # [B, H, nb]
+        anchors = np.where(counts > 32, 2.0, 1.0)
+        tail_pairs = float(np.einsum("bhij,bhj,i->", (~masks).astype(np.float64), groups, anchors))
+        bwd_flops = 14.0 * D * exact_pairs + 20.0 * D * tail_pairs
+        fwd_flops = 4.0 * D * exact_pairs + 6.0 * D * tail_pairs
+        extra = {"tail_anchor_group_pairs": tail_pairs}
+    else:
+        proxy_units = float(((~masks) * counts[:, None]).sum())
+        bwd_flops = 14.0 * D * (exact_pairs + proxy_units)
+        fwd_flops = 4.0 * D * (exact_pairs + proxy_units)
+        extra = {"proxy_units": proxy_units}
     dense_flops = 14.0 * B * H * float(N) ** 2 * D
     stream = torch.cuda.current_stream(dev)
 
     def fwd():
-        bsa.forward_train(q, k, v, tau, "diag", sink_start, sink_tokens, out=out, workspace=ws)
+        fwd_call(q, k, v, tau, args.thresh, sink_start, sink_tokens, out=out, workspace=ws)
 
     def bwd():
-        bsa.backward(q, k, v, out, dout, ws, dq, dk, dv)
+        bwd_call(q, k, v, out, dout, ws, dq, dk, dv)
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -394,20 +415,24 @@ def bench_train(args):
     achieved = bwd_flops / (bwd_ms * 1e-3) / 1e12
     log(f"[bench] training step {ms_per_step:.3f} ms: forward {fwd_ms:.3f} ms, backward {bwd_ms:.3f} ms "
         f"-> backward {achieved:.1f} TFLOP/s algorithmic; realised sparsity {real_sp:.4f}")
+    name = "Sol-Attn2 (FP8 Q/K)" if sol2 else "Sol-Attn"
     rec = {
         "metric": "dense-equiv attn TFLOP/s + MFMA util, H32 d128 N=32K-128K @80-90% sparsity",
         "value": round(dense_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s (dense-equivalent training step, 14*B*H*N^2*d / t_step)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8(e4m3 QK forward)+bf16" if sol2 else "bf16",
         "data": "synthetic (seeded block-offset Gaussian Q/K/V and dO, bf16)",
-        "config": {"workload": f"Sol-Attn training step (forward + backward, routing fixed), B={B} H={H} d={D} "
+        "config": {"workload": f"{name} training step (forward + backward, routing fixed), B={B} H={H} d={D} "
                                f"N={N}, block-offset synthetic data, tau {tau}",
-                   "tau": tau, "realised_sparsity": round(real_sp, 5), "forward_ms": round(fwd_ms, 4),
-                   "backward_ms": round(bwd_ms, 4), "forward_algorithmic_tflop": fwd_flops / 1e12,
-                   "backward_algorithmic_tflop": bwd_flops / 1e12},
+                   "tau": tau, "thresh": args.thresh, "realised_sparsity": round(real_sp, 5),
+                   "forward_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
+                   "forward_algorithmic_tflop": fwd_flops / 1e12, "backward_algorithmic_tflop": bwd_flops / 1e12,
+                   "workspace_mib": round(ws.numel() / 2**20, 1), **extra},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": round(achieved / 2500.0, 4), "traffic": None, "kernel": "sol_attn_backward (all kernels)",
+                     "frac": round(achieved / 2500.0, 4), "traffic": None,
+                     "kernel": ("sol_attn2_backward" if sol2 else "sol_attn_backward") + " (all kernels)",
                      "work_per_launch": {"backward_flop": bwd_flops}},
         "cpu_baseline": None,
     }

@@ -43,7 +43,7 @@ class WsLayout(ctypes.Structure):
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov", "kpart",
         "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse",
         "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale", "lse", "mrow", "mcol", "ld", "dkbar", "dvbar",
-        "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz", "aextra", "gdk", "gdv", "ofp")]
+        "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz", "aextra", "gdk", "gdv", "ofp", "kcovp")]
 
 
 class SolAttnError(RuntimeError):

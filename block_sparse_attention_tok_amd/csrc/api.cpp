@@ -90,6 +90,7 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   L->kstat = take(bh * 2 * kDim * 4);
   L->kcov = take(bh * kDim * kDim * 4);
   L->kpart = take(bh * 16 * 2 * kDim * 8);
+  L->kcovp = take(bh * 8 * kDim * kDim * 4);
   // Sol-Attn: head-major copies of K and V written by stage 1, the tile source of stage 2
   if (variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN) {
     L->kh = take(bh * tokens * kDim * 2);
@@ -212,6 +213,7 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.gdk = (float*)at(L.gdk);
   w.gdv = (float*)at(L.gdv);
   w.ofp = (float*)at(L.ofp);
+  w.kcovp = (float*)at(L.kcovp);
   return w;
 }
 

@@ -39,8 +39,9 @@
 //   * O^T += V^T P^T: A = V^T gathered from the row-major V tile with
 //     ds_read_b64_tr_b16, B = P straight from the S^T accumulator (the k order
 //     inside each MFMA is permuted identically on both operands).
-//   * Several key splits write bf16 partial rows and their log2-sum-exp; a
-//     small merge kernel combines them.
+//   * Several key splits write fp32 normalized partial rows and their
+//     log2-sum-exp; a small merge kernel combines them and rounds each output
+//     to bf16 once.
 #include "common.h"
 #include "kernels.h"
 #include "pipe.h"

@@ -57,6 +57,7 @@ struct Workspace {
   float* gdk;       // [B][H][nbp][2][128] gradient w.r.t. the group mean keys (with 1/sqrt(d))
   float* gdv;       // [B][H][nbp][2][128] gradient w.r.t. the group mean values
   float* ofp;       // [B][H][tp][128] the Sol-Attn2 training forward's output rows in fp32
+  float* kcovp;     // [B][H][8][128][128] per-slice centred key-mean outer products (exact threshold)
 };
 
 struct Shape {

@@ -193,93 +193,6 @@ hipError_t launch_route(Shape s, const Workspace& ws, int sink_b0, int sink_b1, 
   return hipGetLastError();
 }
 
-// One workgroup per (batch, head).  mu_K and v_K are averages over the nb key
-// blocks with weight 1/nb; v_K is accumulated in the centred two-pass form
-// mean_j (K-bar_j - mu_K)^2, which equals the printed mean of squares minus the
-// squared mean.  tau_i = mu_i + tau sigma_i in scaled-logit units (1/sqrt d).
-// exact != 0 uses the full covariance (Eq. (5)): sigma_i^2 = Q-bar_i Cov Q-bar_i^T.
-__global__ __launch_bounds__(256) void threshold_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar_t, int nb, int nbp, float tau,
-    int exact, float* __restrict__ kstat, float* __restrict__ kcov, float* __restrict__ tau_i) {
-  __shared__ float s_mu[kDim], s_var[kDim], s_part[256];
-  __shared__ float s_chunk[32][kDim];                   // 32 centred key means, for the covariance
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int d = tid & 127, half = tid >> 7;
-  const float* kt = kbar_t + (size_t)bh * 32 * nbp * 4;
-  auto kval = [&](int jj, int dd) { return kt[((size_t)(dd >> 2) * nbp + jj) * 4 + (dd & 3)]; };
-
-  float acc = 0.f;
-  for (int jj = half; jj < nb; jj += 2) acc += kval(jj, d);
-  s_part[tid] = acc;
-  __syncthreads();
-  if (tid < kDim) s_mu[tid] = (s_part[tid] + s_part[tid + 128]) / (float)nb;
-  __syncthreads();
-  const float mu = s_mu[d];
-  acc = 0.f;
-  for (int jj = half; jj < nb; jj += 2) { float x = kval(jj, d) - mu; acc += x * x; }
-  s_part[tid] = acc;
-  __syncthreads();
-  if (tid < kDim) {
-    s_var[tid] = (s_part[tid] + s_part[tid + 128]) / (float)nb;
-    kstat[(size_t)bh * 256 + tid] = s_mu[tid];
-    kstat[(size_t)bh * 256 + 128 + tid] = s_var[tid];
-  }
-  __syncthreads();
-
-  float* cov = kcov + (size_t)bh * kDim * kDim;
-  if (exact) {
-    // thread owns row r = tid / 2 and 64 columns starting at 64 * (tid % 2)
-    const int r = tid >> 1, c0 = (tid & 1) * 64;
-    float cacc[64];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) cacc[e] = 0.f;
-    for (int j0 = 0; j0 < nb; j0 += 32) {
-      __syncthreads();
-      for (int idx = tid; idx < 32 * kDim; idx += 256) {
-        int jj = j0 + idx / kDim, dd = idx % kDim;
-        s_chunk[idx / kDim][dd] = jj < nb ? kval(jj, dd) - s_mu[dd] : 0.f;
-      }
-      __syncthreads();
-      for (int jj = 0; jj < 32; ++jj) {
-        const float xr = s_chunk[jj][r];
-#pragma unroll
-        for (int e = 0; e < 64; ++e) cacc[e] += xr * s_chunk[jj][c0 + e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 64; ++e) cov[(size_t)r * kDim + c0 + e] = cacc[e] / (float)nb;
-    __threadfence_block();
-    __syncthreads();
-  }
-
-  const float scale = 0.08838834764831845f;             // 1/sqrt(128)
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int i = wave; i < nb; i += 4) {
-    const float* qi = qbar + ((size_t)bh * nbp + i) * kDim;
-    const float q0 = qi[lane], q1 = qi[lane + 64];
-    float m = q0 * s_mu[lane] + q1 * s_mu[lane + 64];
-    float var;
-    if (exact) {
-      // (Cov q)[lane] and [lane + 64], then q . (Cov q)
-      float c0 = 0.f, c1 = 0.f;
-      for (int e = 0; e < kDim; ++e) {
-        const float qe = qi[e];
-        c0 += cov[(size_t)lane * kDim + e] * qe;
-        c1 += cov[(size_t)(lane + 64) * kDim + e] * qe;
-      }
-      var = q0 * c0 + q1 * c1;
-    } else {
-      var = q0 * q0 * s_var[lane] + q1 * q1 * s_var[lane + 64];
-    }
-    m = wave_sum(m);
-    var = wave_sum(var);
-    if (lane == 0) {
-      const float sigma = sqrtf(fmaxf(var, 0.f)) * scale;
-      tau_i[(size_t)bh * nbp + i] = m * scale + tau * sigma;
-    }
-  }
-}
-
 // Diagonal threshold in two wide passes (the single-workgroup-per-head kernel
 // above is latency-bound on long sequences).  Pass 1: per (b, h, slice of key
 // blocks) the sums of K-bar_j and K-bar_j (.) K-bar_j in fp64.  Pass 2: mu_K and
@@ -344,14 +257,127 @@ __global__ __launch_bounds__(256) void tau_diag_kernel(const double* __restrict_
   }
 }
 
-hipError_t launch_threshold(Shape s, const Workspace& ws, float tau, int exact, hipStream_t stream) {
-  if (exact) {
-    hipLaunchKernelGGL(threshold_kernel, dim3(s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t, ws.nb,
-                       ws.nbp, tau, exact, ws.kstat, ws.kcov, ws.tau_i);
-    return hipGetLastError();
+// Full-covariance threshold (§3.1 Eq. (5)): sigma_i^2 = Q-bar_i Cov Q-bar_i^T with
+// Cov = mean_j (K-bar_j - mu_K)(K-bar_j - mu_K)^T, the centred form of the printed
+// second moment minus the squared mean.  Three wide passes after the fp64 sums of pass 1:
+//   cov_partial_kernel  per (b, h, slice of key blocks): the slice's centred outer
+//                       products, one 8 x 8 tile of the 128 x 128 sum per thread;
+//   cov_reduce_kernel   per (b, h, 8 rows): the slices summed, / nb, into kcov (and kstat);
+//   tau_cov_kernel      per (b, h, 32 query blocks): Cov in LDS, y = Cov Q-bar_i^T with
+//                       lanes reading Cov's rows contiguously (Cov is symmetric), then
+//                       tau_i = mu_i + tau sigma_i.
+constexpr int kCovSlices = 8;
+
+// mu_K (fp32) of (b, h) from the fp64 slice sums of kstat_partial_kernel, for dim d.
+__device__ __forceinline__ float mean_from_part(const double* __restrict__ part, size_t bh, int d, int nb) {
+  double a = 0.0;
+  const double* p = part + bh * kStatSlices * 2 * kDim;
+  for (int sl = 0; sl < kStatSlices; ++sl) a += p[sl * 2 * kDim + d];
+  return (float)(a / nb);
+}
+
+__global__ __launch_bounds__(256) void cov_partial_kernel(const float* __restrict__ kbar_t, const double* __restrict__ part,
+                                                          int nb, int nbp, float* __restrict__ covp) {
+  __shared__ float s_mu[kDim];
+  __shared__ __attribute__((aligned(16))) float s_x[32][kDim + 4];
+  const int bh = blockIdx.x, sl = blockIdx.y, tid = threadIdx.x;
+  if (tid < kDim) s_mu[tid] = mean_from_part(part, bh, tid, nb);
+  const int per = (nb + kCovSlices - 1) / kCovSlices;
+  const int j0 = sl * per, j1 = min(nb, j0 + per);
+  const int ti = tid >> 4, tj = tid & 15;                // rows 8 ti .., columns 8 tj ..
+  const float* kt = kbar_t + (size_t)bh * 32 * nbp * 4;
+  float acc[8][8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
+  for (int c0 = j0; c0 < j1; c0 += 32) {
+    __syncthreads();                                     // s_mu written; previous chunk consumed
+    for (int e = tid; e < 32 * kDim; e += 256) {
+      const int r = e >> 7, d = e & (kDim - 1), j = c0 + r;
+      s_x[r][d] = j < j1 ? kt[((size_t)(d >> 2) * nbp + j) * 4 + (d & 3)] - s_mu[d] : 0.f;
+    }
+    __syncthreads();
+    const int rows = min(32, j1 - c0);
+    for (int r = 0; r < rows; ++r) {
+      const float4 a0 = *(const float4*)&s_x[r][8 * ti], a1 = *(const float4*)&s_x[r][8 * ti + 4];
+      const float4 b0 = *(const float4*)&s_x[r][8 * tj], b1 = *(const float4*)&s_x[r][8 * tj + 4];
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+#pragma unroll
+        for (int y = 0; y < 8; ++y) acc[x][y] = __builtin_fmaf(av[x], bv[y], acc[x][y]);
+    }
   }
+  float* dst = covp + ((size_t)bh * kCovSlices + sl) * kDim * kDim;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    float* row = dst + (size_t)(8 * ti + x) * kDim + 8 * tj;
+    *(float4*)row = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+    *(float4*)(row + 4) = make_float4(acc[x][4], acc[x][5], acc[x][6], acc[x][7]);
+  }
+}
+
+__global__ __launch_bounds__(256) void cov_reduce_kernel(const float* __restrict__ covp, const double* __restrict__ part,
+                                                         int nb, float* __restrict__ kcov, float* __restrict__ kstat) {
+  const int bh = blockIdx.x, rb = blockIdx.y, tid = threadIdx.x;
+  const size_t e = (size_t)rb * 8 * kDim + 4 * tid;      // 4 consecutive entries of rows 8 rb ..
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sl = 0; sl < kCovSlices; ++sl) {
+    const float4 x = *(const float4*)(covp + ((size_t)bh * kCovSlices + sl) * kDim * kDim + e);
+    s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+  }
+  const float inv = 1.0f / (float)nb;
+  s.x *= inv; s.y *= inv; s.z *= inv; s.w *= inv;
+  *(float4*)(kcov + (size_t)bh * kDim * kDim + e) = s;
+  // kstat: mu_K (first row block) and the diagonal of Cov
+  if (rb == 0 && tid < kDim) kstat[(size_t)bh * 256 + tid] = mean_from_part(part, bh, tid, nb);
+  const int r = (int)(e / kDim), c = (int)(e % kDim);
+  if (c <= r && r < c + 4) kstat[(size_t)bh * 256 + kDim + r] = r == c ? s.x : r == c + 1 ? s.y : r == c + 2 ? s.z : s.w;
+}
+
+__global__ __launch_bounds__(256) void tau_cov_kernel(const float* __restrict__ kcov, const float* __restrict__ kstat,
+                                                      const float* __restrict__ qbar, int nb, int nbp, float tau,
+                                                      float* __restrict__ tau_i) {
+  __shared__ __attribute__((aligned(16))) float s_c[kDim * kDim];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const float* cv = kcov + (size_t)bh * kDim * kDim;
+  for (int e = 4 * tid; e < kDim * kDim; e += 1024) *(float4*)&s_c[e] = *(const float4*)(cv + e);
+  __syncthreads();
+  const float scale = 0.08838834764831845f;             // 1/sqrt(128)
+  const int wave = tid >> 6, lane = tid & 63;
+  const float mu0 = kstat[(size_t)bh * 256 + lane], mu1 = kstat[(size_t)bh * 256 + lane + 64];
+  const int i0 = blockIdx.y * 32 + wave * 8;
+  for (int i = i0; i < min(nb, i0 + 8); ++i) {
+    const float* qi = qbar + ((size_t)bh * nbp + i) * kDim;
+    const float q0 = qi[lane], q1 = qi[lane + 64];
+    float y0 = 0.f, y1 = 0.f;                            // (Cov q)[lane], [lane + 64]
+#pragma unroll 8
+    for (int e = 0; e < kDim; ++e) {
+      const float qe = qi[e];                            // uniform: one scalar load per dim
+      y0 = __builtin_fmaf(s_c[e * kDim + lane], qe, y0);
+      y1 = __builtin_fmaf(s_c[e * kDim + lane + 64], qe, y1);
+    }
+    const float m = wave_sum(q0 * mu0 + q1 * mu1);
+    const float var = wave_sum(q0 * y0 + q1 * y1);
+    if (lane == 0) tau_i[(size_t)bh * nbp + i] = m * scale + tau * sqrtf(fmaxf(var, 0.f)) * scale;
+  }
+}
+
+hipError_t launch_threshold(Shape s, const Workspace& ws, float tau, int exact, hipStream_t stream) {
   hipLaunchKernelGGL(kstat_partial_kernel, dim3(s.B * s.H, kStatSlices), dim3(256), 0, stream, ws.kbar_t, ws.nb,
                      ws.nbp, ws.kpart);
+  if (exact) {
+    if (!ws.kcovp) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cov_partial_kernel, dim3(s.B * s.H, kCovSlices), dim3(256), 0, stream, ws.kbar_t, ws.kpart,
+                       ws.nb, ws.nbp, ws.kcovp);
+    hipLaunchKernelGGL(cov_reduce_kernel, dim3(s.B * s.H, kDim / 8), dim3(256), 0, stream, ws.kcovp, ws.kpart, ws.nb,
+                       ws.kcov, ws.kstat);
+    hipLaunchKernelGGL(tau_cov_kernel, dim3(s.B * s.H, (ws.nb + 31) / 32), dim3(256), 0, stream, ws.kcov, ws.kstat,
+                       ws.qbar, ws.nb, ws.nbp, tau, ws.tau_i);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(tau_diag_kernel, dim3(s.B * s.H, (ws.nb + 31) / 32), dim3(256), 0, stream, ws.kpart, ws.qbar,
                      ws.nb, ws.nbp, tau, ws.kstat, ws.tau_i);
   return hipGetLastError();

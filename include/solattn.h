@@ -74,6 +74,8 @@ typedef enum {
  *   kstat    float [B][H][2][128]     mu_K and v_K
  *   kcov     float [B][H][128][128]   covariance of the K block means (EXACT only)
  *   kpart    double [B][H][16][2][128] partial sums of K block means and their squares
+ *   kcovp    float  [B][H][8][128][128] per-slice sums of the centred outer products of the
+ *            K block means (thresh = SOL_THRESH_EXACT only)
  *   kh, vh   bf16  [B][H][N][128]     Sol-Attn: head-major copies of K and V (stage 1 writes
  *                                      them; stage 2 and the backward stream tiles from them)
  *   q8, k8   uint8 [B][H][tp][128]    E4M3FN codes (Sol-Attn2)
@@ -135,7 +137,7 @@ typedef struct {
     int64_t lse, mrow, mcol, ld, dkbar, dvbar;
     int64_t kh, vh;
     int64_t qd, kd, dlam, qab, dmub, dnub, alz, aextra, gdk, gdv;
-    int64_t ofp;
+    int64_t ofp, kcovp;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */

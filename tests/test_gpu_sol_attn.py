@@ -137,6 +137,30 @@ def test_summaries_and_threshold_match_oracle():
             np.testing.assert_allclose(views["tau_i"][0, h, :nb].cpu().double().numpy(), tau_ref, rtol=1e-4, atol=2e-5)
 
 
+@pytest.mark.parametrize("N,H", [(40, 2), (130, 1), (14040, 12), (131584, 2)])
+def test_exact_threshold_sizes(N, H):
+    """The full-covariance threshold (sliced outer products, reduction, wide tau pass) at one
+    block, a few blocks (most slices empty), the Wan-2.1 shape and the longest sequence:
+    covariance, mu_K and tau_i against the oracle's definitions (Eq. (5))."""
+    q, k, v = _qkv(1, N, H, 1750)
+    qg, kg, vg = to_gpu(q, k, v)
+    ws = bsa.alloc_workspace(1, qg)
+    bsa.prepare(1, qg, kg, vg, 1.3, ws, "exact")
+    torch.cuda.synchronize()
+    views = bsa.workspace_views(1, ws, 1, N, H)
+    nb = views["nb"]
+    for h in range(H):
+        qh, kh = (t[0, :, h, :].double().numpy() for t in (q, k))
+        qbar, kbar = sa.block_means(qh), sa.block_means(kh)
+        cov = np.cov(kbar.T, bias=True) if nb > 1 else np.zeros((128, 128))
+        np.testing.assert_allclose(views["kcov"][0, h].cpu().double().numpy(), cov, rtol=1e-4,
+                                   atol=1e-5 * max(1.0, np.abs(cov).max()))
+        np.testing.assert_allclose(views["kstat"][0, h, 0].cpu().double().numpy(), kbar.mean(axis=0), rtol=1e-5,
+                                   atol=1e-6)
+        tau_ref = sa.exact_threshold(qbar, kbar, 1.3, 1 / math.sqrt(128))[0]
+        np.testing.assert_allclose(views["tau_i"][0, h, :nb].cpu().double().numpy(), tau_ref, rtol=1e-4, atol=2e-5)
+
+
 def test_deterministic_and_stream_ordered():
     q, k, v = _qkv(1, 3000, 2, 1800)
     qg, kg, vg = to_gpu(q, k, v)
