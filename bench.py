@@ -152,12 +152,12 @@ def measure(variant: int, qc, kc, vc, text_sink: int, target: float, tau_fixed, 
         peak = 2500.0                                          # dense bf16 MFMA
     elif variant == 2:
         kernel = "sol2_fused_kernel"
-        run_kernel = lambda: bsa.exact2(q, k, v, out, ws)    # noqa: E731
+        run_kernel = lambda: bsa.exact2(q, k, v, out, ws, False, sink_start, sink_tokens)    # noqa: E731
         # QK^T on FP8 (5.0 PF) and PV on bf16 (2.5 PF), half the exact FLOPs each
         peak = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
     else:
         kernel = "sol2_fused_kernel"
-        run_kernel = lambda: bsa.exact2(q, k, v, out, ws, pv8=True)  # noqa: E731
+        run_kernel = lambda: bsa.exact2(q, k, v, out, ws, True, sink_start, sink_tokens)  # noqa: E731
         peak = 5000.0                                          # QK^T and PV both on FP8
     for _ in range(2):
         run_kernel()

@@ -83,7 +83,7 @@ def lib() -> ctypes.CDLL:
     L.sol_attn2_tail.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
     L.sol_attn2_tail.restype = i32
     for name in ("sol_attn2_exact", "sol_attn2_pv8_exact"):
-        getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
         getattr(L, name).restype = i32
     full = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i64, i64, i32, vp, sz, vp]
     for name in ("sol_attn", "sol_attn2", "sol_attn2_pv8", "sol_attn_forward_train", "sol_attn2_forward_train"):
@@ -403,7 +403,7 @@ def fused(variant: int, q, k, v, out, workspace: torch.Tensor, sink_start: Optio
         return
     if variant == SOL_VARIANT_SOL2_PV8:
         tail2(q, k, v, workspace, sink_start, sink_tokens)
-        exact2(q, k, v, out, workspace, pv8=True)
+        exact2(q, k, v, out, workspace, pv8=True, sink_start=sink_start, sink_tokens=sink_tokens)
         return
     _check(lib().sol_attn2_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
                                  int(sink_tokens), _ptr(workspace), workspace.numel(), _stream(q.device)),
@@ -411,7 +411,7 @@ def fused(variant: int, q, k, v, out, workspace: torch.Tensor, sink_start: Optio
 
 
 def tail2(q, k, v, workspace: torch.Tensor, sink_start: Optional[int] = None, sink_tokens: int = 0):
-    """Sol-Attn2 stage 2a: routing bits and the per-anchor tail, into the workspace."""
+    """Sol-Attn2 stage 2a: the per-anchor tail (routed on chip), into the workspace."""
     _check_tensors(q, k, v)
     _check_workspace(workspace, q)
     B, N, H, D = q.shape
@@ -419,8 +419,10 @@ def tail2(q, k, v, workspace: torch.Tensor, sink_start: Optional[int] = None, si
                                 _ptr(workspace), workspace.numel(), _stream(q.device)), "sol_attn2_tail")
 
 
-def exact2(q, k, v, out, workspace: torch.Tensor, pv8: bool = False):
-    """Sol-Attn2 stage 2b: the exact FP8 pass (FP8 PV with pv8) combined with the tail of stage 2a."""
+def exact2(q, k, v, out, workspace: torch.Tensor, pv8: bool = False, sink_start: Optional[int] = None,
+           sink_tokens: int = 0):
+    """Sol-Attn2 stage 2b: the exact FP8 pass (FP8 PV with pv8), routed on chip with the sink
+    given to stage 2a, combined with the tail of stage 2a."""
     _check_tensors(q, k, v)
     _check_like(out, q, "out")
     if out is None:
@@ -428,8 +430,8 @@ def exact2(q, k, v, out, workspace: torch.Tensor, pv8: bool = False):
     _check_workspace(workspace, q)
     B, N, H, D = q.shape
     name = "sol_attn2_pv8_exact" if pv8 else "sol_attn2_exact"
-    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _ptr(workspace),
-                                workspace.numel(), _stream(q.device)), name)
+    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, _sink_start(sink_start),
+                                sink_tokens, _ptr(workspace), workspace.numel(), _stream(q.device)), name)
 
 
 def debug_routing(variant: int, q, k, v, tau: float = 1.0, thresh: str = "diag", sink_start: Optional[int] = None,
@@ -502,7 +504,6 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
             glogn=view(L.glogn, torch.float32, (batch, heads, nbp, 2)),
             ghi=view(L.ghi, torch.int64, (batch, heads, nbp)),
             qanc=view(L.qanc, torch.float32, (batch, heads, nbp, 2, 128)),
-            sel=view(L.sel, torch.int64, (batch, heads, L.nb, nbp // 64)),
             tmu=view(L.tmu, torch.float32, (batch, heads, nbp, 2, 128)),
             tnu=view(L.tnu, torch.float32, (batch, heads, nbp, 2, 128)),
             tlz=view(L.tlz, torch.float32, (batch, heads, nbp, 2)),
@@ -520,6 +521,7 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
     if variant == SOL_VARIANT_SOL2_TRAIN:
         tp = nbp * 64
         d.update(
+            sel=view(L.sel, torch.int64, (batch, heads, L.nb, nbp // 64)),
             lse=view(L.lse, torch.float32, (batch, heads, tp)),
             ofp=view(L.ofp, torch.float32, (batch, heads, tp, 128)),
             mcol=view(L.mcol, torch.int64, (batch, heads, L.nb, nbp // 64)),

@@ -109,7 +109,6 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->glogn = take(bh * nbp * 2 * 4);
     L->ghi = take(bh * nbp * 8);
     L->qanc = take(bh * nbp * 2 * kDim * 4);
-    L->sel = take(bh * nb * (nbp / 64) * 8);
     L->tmu = take(bh * nbp * 2 * kDim * 4);
     L->tnu = take(bh * nbp * 2 * kDim * 4);
     L->tlz = take(bh * nbp * 2 * 4);
@@ -129,6 +128,7 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   // forward state for the backward, and backward scratch (Sol-Attn2 training)
   if (variant == SOL_VARIANT_SOL2_TRAIN) {
     const int64_t tp = nbp * kBlock;
+    L->sel = take(bh * nb * (nbp / 64) * 8);
     L->lse = take(bh * tp * 4);
     L->ofp = take(bh * tp * kDim * 4);
     L->mcol = take(bh * nb * (nbp / 64) * 8);
@@ -349,15 +349,13 @@ static int fused_common(int variant, const void* q, const void* k, const void* v
   hipStream_t hs = (hipStream_t)stream;
   if (stage2 & kStage2Tail) {
     if ((st = hip_status(solattn::launch_tail2(s, w, b0, b1, hs))) != SOL_OK) return st;
-    if (mask_bits) {
-      const size_t bytes = (size_t)batch * heads * w.nb * (w.nbp / 64) * sizeof(uint64_t);
-      if ((st = hip_status(hipMemcpyAsync(mask_bits, w.sel, bytes, hipMemcpyDeviceToDevice, hs))) != SOL_OK)
-        return st;
-    }
   }
   if (!(stage2 & kStage2Exact)) return SOL_OK;
+  // the exact pass exports its routing words for the test export and the training forward
+  uint64_t* words = mask_bits ? mask_bits : (variant == SOL_VARIANT_SOL2_TRAIN ? w.sel : nullptr);
   return hip_status(solattn::launch_fused2((const uint16_t*)v, (uint16_t*)out, s, w,
-                                           variant == SOL_VARIANT_SOL2_PV8, (unsigned long long*)selected_pairs, hs));
+                                           variant == SOL_VARIANT_SOL2_PV8, (unsigned long long*)selected_pairs,
+                                           b0, b1, words, hs));
 }
 
 int sol_attn_fused(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
@@ -467,9 +465,10 @@ int sol_attn2_pv8_prepare(const void* q, const void* k, const void* v, int64_t b
 }
 
 int sol_attn2_pv8_exact(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
-                        int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes, void* stream) {
-  return fused_common(SOL_VARIANT_SOL2_PV8, q, k, v, out, batch, tokens, heads, head_dim, -1, 0, workspace,
-                      workspace_bytes, nullptr, stream, true, 0, kStage2Exact);
+                        int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return fused_common(SOL_VARIANT_SOL2_PV8, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
+                      workspace, workspace_bytes, nullptr, stream, true, 0, kStage2Exact);
 }
 
 int sol_attn2_pv8(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
@@ -500,9 +499,10 @@ int sol_attn2_tail(const void* q, const void* k, const void* v, int64_t batch, i
 }
 
 int sol_attn2_exact(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens,
-                    int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes, void* stream) {
-  return fused_common(SOL_VARIANT_SOL2, q, k, v, out, batch, tokens, heads, head_dim, -1, 0, workspace,
-                      workspace_bytes, nullptr, stream, true, 0, kStage2Exact);
+                    int64_t heads, int64_t head_dim, int64_t sink_start, int64_t sink_tokens, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return fused_common(SOL_VARIANT_SOL2, q, k, v, out, batch, tokens, heads, head_dim, sink_start, sink_tokens,
+                      workspace, workspace_bytes, nullptr, stream, true, 0, kStage2Exact);
 }
 
 int sol_attn2(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t tokens, int64_t heads,

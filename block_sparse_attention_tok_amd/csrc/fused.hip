@@ -161,23 +161,10 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
     for (int cc = w; cc < nchunks; cc += 2) {
       const int c = c_begin + cc;
-      const int j = 64 * c + lane;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int g = 0; g < 32; ++g) {
-        const float4 kv = kt[(size_t)g * a.nbp + j];
-        const float4 qv = qbar_s[g];
-        acc = __builtin_fmaf(qv.x, kv.x, acc);
-        acc = __builtin_fmaf(qv.y, kv.y, acc);
-        acc = __builtin_fmaf(qv.z, kv.z, acc);
-        acc = __builtin_fmaf(qv.w, kv.w, acc);
-      }
-      uint64_t selm = __ballot(acc * kScale > tau);
+      const float acc = proxy_dot(qbar_s, kt, a.nbp, 64 * c + lane);
+      const uint64_t selm = exact_word(__ballot(acc * kScale > tau), c, a.nb, a.sink_b0, a.sink_b1);
       const int nvalid = a.nb - 64 * c;                      // valid blocks of the chunk (>= 1)
       const uint64_t validm = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
-      const int s0 = max(a.sink_b0, 64 * c), s1 = min(a.sink_b1, 64 * c + 63);
-      if (s0 <= s1) selm |= (~0ull >> (63 - (s1 - s0))) << (s0 - 64 * c);
-      selm &= validm;
       if (lane == 0) {
         sel_s[cc] = selm;
         prox_s[cc] = validm & ~selm;

@@ -31,7 +31,7 @@ struct Workspace {
   int kv_splits;    // key-range splits of the fused Sol-Attn pass (1 = none)
   float* opart;     // [S][B][N][H][128] fp32 normalized partial outputs
   float* olse;      // [S][B][N][H] log2-sum-exp of the partial rows
-  uint64_t* sel;    // [B][H][nb][nbp / 64] Sol-Attn2 routing bits (the tail and exact passes)
+  uint64_t* sel;    // [B][H][nb][nbp / 64] Sol-Attn2 training: the forward's routing bits
   float* tmu;       // [B][H][nbp][2][128] Sol-Attn2 tail key means per anchor
   float* tnu;       // [B][H][nbp][2][128] Sol-Attn2 tail value means per anchor
   float* tlz;       // [B][H][nbp][2] log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d)
@@ -82,16 +82,14 @@ hipError_t launch_quant_summary(const uint16_t* q, const uint16_t* k, const uint
                                 const Workspace& ws, hipStream_t stream);
 hipError_t launch_qhat(Shape s, const Workspace& ws, hipStream_t stream);
 hipError_t launch_groups(const uint16_t* v, Shape s, const Workspace& ws, hipStream_t stream);
-// Routing bits of every (query block, key block) pair from the fp32 block means and tau_i,
-// with the blocks [sink_b0, sink_b1] forced, into sel [B][H][nb][nbp / 64] (Sol-Attn2 stage 2:
-// the tail pass and the exact pass both read them, so they agree on every exact set).
-hipError_t launch_route(Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* sel,
-                        hipStream_t stream);
-// Sol-Attn2 stage 2: routing and the complementary tail per anchor (writes sel, tmu, tnu, tlz),
-// then the exact FP8 pass combined with the tail.
+// Sol-Attn2 stage 2: the complementary tail per anchor (writes tmu, tnu, tlz), then the exact
+// FP8 pass combined with the tail.  Both route on chip with the same fp32 arithmetic, the
+// blocks [sink_b0, sink_b1] forced; the exact pass writes its routing words to mask_out when
+// that is not NULL (training forward, test export).
 hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream);
 hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, bool pv8,
-                         unsigned long long* pairs, hipStream_t stream);
+                         unsigned long long* pairs, int sink_b0, int sink_b1, uint64_t* mask_out,
+                         hipStream_t stream);
 // Sol-Attn backward with the forward's routing fixed: D and the transposed masks, the
 // pooled-key gradients, dK / dV per key block, then dQ per query block.
 hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,

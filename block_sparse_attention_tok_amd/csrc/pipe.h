@@ -56,6 +56,36 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)uniform64((uint64_t)p);
 }
 
+// Routing numerator Q-bar_i . K-bar_j for key block j (the proxy score of Sol-Attn paper
+// §3.1 Eq. (4) before its 1/sqrt(d) scale): 128 fp32 FMAs over the dims in ascending order,
+// from Q-bar_i as 32 float4 (in LDS) and the head's 4-dim-interleaved fp32 key-block means
+// kt = [32][nbp] float4.  Every kernel that routes a pair uses this one FMA sequence, so
+// kernels that need the same pair's decision take it bit for bit alike.
+__device__ __forceinline__ float proxy_dot(const float4* qb, const float4* kt, int nbp, int j) {
+  float acc = 0.f;
+#pragma unroll 8
+  for (int g = 0; g < 32; ++g) {
+    const float4 kv = kt[(size_t)g * nbp + j];
+    const float4 qv = qb[g];
+    acc = __builtin_fmaf(qv.x, kv.x, acc);
+    acc = __builtin_fmaf(qv.y, kv.y, acc);
+    acc = __builtin_fmaf(qv.z, kv.z, acc);
+    acc = __builtin_fmaf(qv.w, kv.w, acc);
+  }
+  return acc;
+}
+
+// The exact-set word of 64-block chunk c (c < nbp / 64, so the chunk holds at least one
+// block below nb) from the ballot of s_ij > tau_i: the sink's blocks [sink_b0, sink_b1]
+// forced exact, the padding blocks cleared.
+__device__ __forceinline__ uint64_t exact_word(uint64_t ballot, int c, int nb, int sink_b0, int sink_b1) {
+  const int nvalid = nb - 64 * c;
+  const uint64_t validm = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+  const int s0 = max(sink_b0, 64 * c), s1 = min(sink_b1, 64 * c + 63);
+  if (s0 <= s1) ballot |= (~0ull >> (63 - (s1 - s0))) << (s0 - 64 * c);
+  return ballot & validm;
+}
+
 // Sum of the 8 bf16 values of a packed P fragment into acc (v_dot2c_f32_bf16 with ones).
 // The pairs are taken with shufflevector: extracting them from a bit_cast to
 // 4 x uint32 lowers, with the ROCm 7.2 compiler, to four reads of the first pair.

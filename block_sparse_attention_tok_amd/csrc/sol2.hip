@@ -375,7 +375,8 @@ hipError_t launch_vquant(const uint16_t* v, Shape s, const Workspace& ws, hipStr
 // n = lane % 32 is anchor n of query blocks i0 + 16 w .. i0 + 16 w + 15 (query block
 // i0 + 16 w + n / 2, half n % 2).  Tiles of 16 key blocks (32 groups) stream through
 // LDS two tiles ahead, each row a group's bf16 mean key then mean value, with ln n_g of
-// the tile's groups and the routing words of its chunk:
+// the tile's groups; the routing words of the workgroup's query blocks are decided on
+// chip first (below):
 //   scores   l_ga = ln n_g + q-bar_a . k-bar_g / sqrt(d) on v_mfma_f32_32x32x16_bf16
 //            (A = the group rows, B = the anchors), masked to groups of blocks the
 //            anchor's query block did not select; online log-sum-exp per anchor;
@@ -393,26 +394,27 @@ struct Tail2Args {
   int B, N, H, nb, nbp, nbw;
   const float* qanc;
   const uint16_t* gk; const uint16_t* gv; const float* glogn;
-  const uint64_t* sel;
+  const float* qbar; const float* kbar_t; const float* tau_i;   // routing inputs (fp32 block means)
+  int sink_b0, sink_b1;
   float* tmu; float* tnu; float* tlz;
 };
 
 constexpr int kTailBufs = 3;               // tiles in flight: the one computed and two more
-constexpr int kTailDmaPerTile = 10;        // buffer loads per wave per tile
+constexpr int kTailDmaPerTile = 9;         // buffer loads per wave per tile
 
 __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   // Per buffer, filled by buffer DMA: the 32 group mean keys and mean values (32 rows x
   // 256 B each, 16-byte slots swizzled by swz_g so that both the row reads of the scores
   // and the transposed reads of the means are conflict-free); ln n_g of the tile's groups
-  // (wave w brings groups 16 w .. 16 w + 15 into gl_s[.][w]); the routing words of the
-  // tile's 64-block chunk as 32-bit halves (wave w brings query blocks 16 w .. 16 w + 15
-  // into sw_s[.][w]).  Lanes past those ranges read outside the buffer and store zeros
-  // in the unused tail of each row.
+  // (wave w brings groups 16 w .. 16 w + 15 into gl_s[.][w]); lanes past that range read
+  // outside the buffer and store zeros in the unused tail of each row.  The routing words
+  // of the workgroup's 32 query blocks (every chunk) are decided in the prologue and kept
+  // in wsel (dynamic LDS, 32 x nbw words).
   __shared__ __attribute__((aligned(1024))) unsigned char Gk_s[kTailBufs][32 * 256];
   __shared__ __attribute__((aligned(1024))) unsigned char Gv_s[kTailBufs][32 * 256];
   __shared__ __attribute__((aligned(256))) float gl_s[kTailBufs][2][64];
-  __shared__ __attribute__((aligned(256))) uint32_t sw_s[kTailBufs][2][64];
   __shared__ int redo_s[2];
+  extern __shared__ uint64_t wsel[];
 
   const int bh = blockIdx.y, i0 = blockIdx.x * 32;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
@@ -448,25 +450,72 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) goff[ks] = l32 * 256 + 16 * ((2 * ks + kg) ^ swz_g(l32));
 
+  // Routing of the workgroup's 32 query blocks i0 .. i0 + 31 against every key block, on
+  // chip (Sol-Attn paper §3.1 Eq. (4) with the sink forced): the FMA sequence of
+  // proxy_dot, the one the exact pass uses for its own query block, so both passes take
+  // every decision alike.  Wave w takes chunks w, w + 2, w + 4, ... two at a time (c and
+  // c + 2), lane l key blocks 64 c + l and 64 (c + 2) + l, each with 32 accumulators; the
+  // Q-bar values are wave-uniform and come through scalar loads, each feeding 8 FMAs.
+  {
+    // the 32 Q-bar rows (rows i0 + q < nbp: in memory) are wave-uniform and read-only
+    // here: read them through the constant address space, i.e. with scalar loads
+    typedef const __attribute__((address_space(4))) float const_float;
+    const const_float* qs = (const const_float*)(a.qbar + ((size_t)bh * a.nbp + i0) * kDim);
+    const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
+    for (int c = w; c < a.nbw; c += 4) {                 // chunks c and c + 2 together
+      const bool two = c + 2 < a.nbw;                    // uniform
+      const int j0 = 64 * c + lane, j1 = two ? 64 * (c + 2) + lane : j0;
+      float acc0[32], acc1[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) acc0[q] = acc1[q] = 0.f;
+      for (int g = 0; g < 32; ++g) {
+        const float4 kv0 = kt[(size_t)g * a.nbp + j0];
+        const float4 kv1 = kt[(size_t)g * a.nbp + j1];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          const float4 qv = make_float4(qs[128 * q + 4 * g], qs[128 * q + 4 * g + 1], qs[128 * q + 4 * g + 2],
+                                        qs[128 * q + 4 * g + 3]);
+          acc0[q] = __builtin_fmaf(qv.x, kv0.x, acc0[q]);
+          acc0[q] = __builtin_fmaf(qv.y, kv0.y, acc0[q]);
+          acc0[q] = __builtin_fmaf(qv.z, kv0.z, acc0[q]);
+          acc0[q] = __builtin_fmaf(qv.w, kv0.w, acc0[q]);
+          acc1[q] = __builtin_fmaf(qv.x, kv1.x, acc1[q]);
+          acc1[q] = __builtin_fmaf(qv.y, kv1.y, acc1[q]);
+          acc1[q] = __builtin_fmaf(qv.z, kv1.z, acc1[q]);
+          acc1[q] = __builtin_fmaf(qv.w, kv1.w, acc1[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const int qi = i0 + q;
+        const float tau = a.tau_i[(size_t)bh * a.nbp + qi];
+        const uint64_t w0 = exact_word(__ballot(acc0[q] * kScale2 > tau), c, a.nb, a.sink_b0, a.sink_b1);
+        if (lane == 0) wsel[q * a.nbw + c] = qi < a.nb ? w0 : 0ull;
+        if (two) {
+          const uint64_t w1 = exact_word(__ballot(acc1[q] * kScale2 > tau), c + 2, a.nb, a.sink_b0, a.sink_b1);
+          if (lane == 0) wsel[q * a.nbw + c + 2] = qi < a.nb ? w1 : 0ull;
+        }
+      }
+    }
+    __syncthreads();                                      // words complete; staging buffer free
+  }
+
   // DMA of tile t (key blocks 16 t .. 16 t + 15) into buffer `buf`: wave w, instruction n
   // fills 1 KB segment 4 w + n of each group array (rows r = 16 w + 4 n + lane / 16; slot
   // lane % 16 holds logical chunk (lane % 16) ^ swz_g(r)), then one dword per lane of
-  // ln n_g and of the routing words.
+  // ln n_g.
   const uint32_t grow = (uint32_t)(16 * w + (lane >> 4));
   uint32_t gdma[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) gdma[n] = (grow + 4 * n) * 256 + 16 * ((lane & 15) ^ swz_g(grow + 4 * n));
   constexpr uint32_t kPastEnd = 0x80000000u;             // beyond every buffer's range: reads zero
   const uint32_t gldma = lane < 16 ? (uint32_t)(16 * w + lane) * 4 : kPastEnd;
-  const uint32_t swdma = lane < 32 ? ((uint32_t)(i0 + 16 * w + (lane >> 1)) * a.nbw * 8 + 4 * (lane & 1)) : kPastEnd;
   const int ntiles = a.nbp / 16;
   auto issue_tile = [&](int t, int buf) {
     const uint32_t gbytes = (uint32_t)a.nbp * 2 * 256;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(a.gk + (size_t)bh * a.nbp * 2 * kDim), gbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(a.gv + (size_t)bh * a.nbp * 2 * kDim), gbytes);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(uniform_ptr(a.glogn + (size_t)bh * a.nbp * 2), (uint32_t)a.nbp * 2 * 4);
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(uniform_ptr(a.sel + (size_t)bh * a.nb * a.nbw), (uint32_t)a.nb * a.nbw * 8);
     const uint32_t toff_g = (uint32_t)t * 32 * 256;          // 32 group rows per tile
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -474,7 +523,6 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
       dma16_buf(rv, toff_g + gdma[n], 0, Gv_s[buf] + 1024 * (4 * w + n));
     }
     dma4_buf(rl, lane < 16 ? (uint32_t)t * 32 * 4 + gldma : kPastEnd, 0, (unsigned char*)gl_s[buf][w]);
-    dma4_buf(rs, lane < 32 ? (uint32_t)(t >> 2) * 8 + swdma : kPastEnd, 0, (unsigned char*)sw_s[buf][w]);
   };
 
   floatx16 num[8];                                        // rows: dims (0..127 mu, 128..255 nu); cols: anchors
@@ -502,7 +550,7 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
       for (int ks = 0; ks < 8; ++ks)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(Gk_s[buf] + goff[ks]), qa[ks], s, 0, 0, 0);
       // routing bits of the anchor's query block for the tile's 16 key blocks
-      const uint32_t mine = (sw_s[buf][w][2 * (qr & 15) + ((t >> 1) & 1)] >> (16 * (t & 1))) & 0xffffu;
+      const uint32_t mine = (uint32_t)(wsel[qr * a.nbw + (t >> 2)] >> (16 * (t & 3))) & 0xffffu;
       float mx = kNegInf;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
@@ -584,14 +632,15 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
 }
 
 hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream) {
-  hipError_t e = launch_route(s, ws, sink_b0, sink_b1, ws.sel, stream);
-  if (e != hipSuccess) return e;
   Tail2Args a;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = ws.nbp / 64;
   a.qanc = ws.qanc;
   a.gk = ws.gk; a.gv = ws.gv; a.glogn = ws.glogn;
-  a.sel = ws.sel; a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
-  hipLaunchKernelGGL(sol2_tail_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(128), 0, stream, a);
+  a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.tau_i = ws.tau_i;
+  a.sink_b0 = sink_b0; a.sink_b1 = sink_b1;
+  a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
+  const size_t words_lds = (size_t)32 * a.nbw * sizeof(uint64_t);   // <= 32 KB (nbw <= 128)
+  hipLaunchKernelGGL(sol2_tail_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(128), words_lds, stream, a);
   return hipGetLastError();
 }
 
@@ -599,7 +648,8 @@ hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, 
 // Stage 2b: exact FP8 attention over the selected blocks, combined with the tail.
 // One workgroup per (b, h, query block i), two wave64s; wave w owns query rows
 // 32 w .. 32 w + 31, which are exactly anchor a = (i, w).
-//   * The selected blocks (the routing bits of stage 2a) stream through LDS: the
+//   * Routing on chip: the query block's words, decided with the tail pass's arithmetic.
+//   * The selected blocks stream through LDS: the
 //     FP8 K tile (64 x 128 B) and the bf16 V tile (64 x 256 B) by buffer DMA
 //     (buffer_load ... lds), V of tile t overlapping S_t, K of tile t + 1
 //     overlapping PV_t.
@@ -619,7 +669,10 @@ struct Fused2Args {
   const uint16_t* v; uint16_t* out;
   int B, N, H, nb, nbp, nbw, tp;
   const uint8_t* q8; const uint8_t* k8; const float* qscale; const float* kscale;
-  const uint64_t* sel; const float* tmu; const float* tnu; const float* tlz;
+  const float* qbar; const float* kbar_t; const float* tau_i;   // routing inputs (fp32 block means)
+  int sink_b0, sink_b1;
+  uint64_t* mask_out;                        // routing words out (training / test export; NULL = none)
+  const float* tmu; const float* tnu; const float* tlz;
   const uint8_t* v8t; const float* vscale;   // FP8 PV only
   unsigned long long* pairs;                 // += selected token pairs n_i n_j (NULL = none)
   float* lse;                                // [B][H][tp] base-2 log of each row's denominator (NULL = none)
@@ -640,6 +693,7 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   __shared__ __attribute__((aligned(1024))) unsigned char K8l[64 * 128];
   __shared__ __attribute__((aligned(1024))) unsigned char Vl[64 * 256];
   __shared__ uint64_t sel_s[kMaxChunks2];
+  __shared__ float4 qbar_s[kDim / 4];                        // Q-bar_i (fp32), read by every lane
   __shared__ __attribute__((aligned(16))) float mu_s[2][kDim];
   __shared__ __attribute__((aligned(16))) float nu_s[2][kDim];
   __shared__ int redo2_s[2];
@@ -655,7 +709,7 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
   const size_t head_off = (size_t)b * a.N * rs + (size_t)h * kDim;
   const size_t qrow_blk = (size_t)bh * a.nbp + i;
 
-  for (int c = tid; c < a.nbw; c += 128) sel_s[c] = a.sel[((size_t)bh * a.nb + i) * a.nbw + c];
+  if (tid < kDim / 4) qbar_s[tid] = ((const float4*)(a.qbar + qrow_blk * kDim))[tid];
   const size_t arow = qrow_blk * 2 + w;
   if (lane < 32) {
     ((float4*)mu_s[w])[lane] = ((const float4*)(a.tmu + arow * kDim))[lane];
@@ -670,6 +724,22 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
     const intx8* src = (const intx8*)(a.q8 + ((size_t)bh * a.tp + qrow) * kDim);
     qf[0] = src[kg];          // dims 32 kg .. 32 kg + 31
     qf[1] = src[2 + kg];      // dims 64 + 32 kg .. + 31
+  }
+  __syncthreads();
+  // Routing on chip (Sol-Attn paper §3.1 Eq. (4), sink forced): wave w scores chunks w,
+  // w + 2, ..., lane l key block 64 c + l, with proxy_dot -- the FMA sequence the tail pass
+  // uses for the same pairs -- and one ballot per chunk; the words stay in LDS.
+  {
+    const float tau = a.tau_i[qrow_blk];
+    const float4* kt = (const float4*)a.kbar_t + (size_t)bh * 32 * a.nbp;
+    for (int c = w; c < a.nbw; c += 2) {
+      const float acc = proxy_dot(qbar_s, kt, a.nbp, 64 * c + lane);
+      const uint64_t word = exact_word(__ballot(acc * kScale2 > tau), c, a.nb, a.sink_b0, a.sink_b1);
+      if (lane == 0) {
+        sel_s[c] = word;
+        if (a.mask_out != nullptr) a.mask_out[((size_t)bh * a.nb + i) * a.nbw + c] = word;
+      }
+    }
   }
   __syncthreads();
   if (a.pairs != nullptr && tid == 0) {
@@ -929,13 +999,16 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
 __global__ void zero_counter2_kernel(unsigned long long* p) { *p = 0ull; }
 
 hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Workspace& ws, bool pv8,
-                         unsigned long long* pairs, hipStream_t stream) {
+                         unsigned long long* pairs, int sink_b0, int sink_b1, uint64_t* mask_out,
+                         hipStream_t stream) {
   if (ws.nbp / 64 > kMaxChunks2 || (pv8 && (!ws.v8t || !ws.vscale))) return hipErrorInvalidValue;
   Fused2Args a;
   a.v = v; a.out = out;
   a.B = s.B; a.N = s.N; a.H = s.H; a.nb = ws.nb; a.nbp = ws.nbp; a.nbw = ws.nbp / 64; a.tp = ws.nbp * kBlock;
   a.q8 = ws.q8; a.k8 = ws.k8; a.qscale = ws.qscale; a.kscale = ws.kscale;
-  a.sel = ws.sel; a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
+  a.qbar = ws.qbar; a.kbar_t = ws.kbar_t; a.tau_i = ws.tau_i;
+  a.sink_b0 = sink_b0; a.sink_b1 = sink_b1; a.mask_out = mask_out;
+  a.tmu = ws.tmu; a.tnu = ws.tnu; a.tlz = ws.tlz;
   a.v8t = ws.v8t; a.vscale = ws.vscale;
   a.pairs = pairs;
   a.lse = pv8 ? nullptr : ws.lse;            // set for the Sol-Attn2 training layout only

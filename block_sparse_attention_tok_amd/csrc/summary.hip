@@ -15,7 +15,6 @@ namespace solattn {
 // workgroups in flight than one per block (measured 4 / 8 / 16 / 32: 291 / 297 / 307 / 305 us
 // for prepare at 32768 tokens x 32 heads).
 constexpr int kSummaryHeads = 4;
-constexpr float kScaleR = 0.08838834764831845f;       // 1/sqrt(128)
 
 // One workgroup per (64-token block j < nbp, batch b, group of hpw heads).  In
 // BTHD the group's part of each token row is one contiguous span of hpw * 256
@@ -114,82 +113,6 @@ hipError_t launch_summary(const uint16_t* q, const uint16_t* k, const uint16_t* 
   hipLaunchKernelGGL(summary_kernel, grid, dim3(256), lds, stream, (const uint4v*)q, (const uint4v*)k,
                      (const uint4v*)v, s.N, s.H, ws.nb, ws.nbp, ws.qbar, ws.kbar_t, (uint4v*)ws.kbar_h,
                      (uint4v*)ws.vbar_h, (uint4v*)ws.kh, (uint4v*)ws.vh, hpw);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Sol-Attn2 routing (Sol-Attn2 draft, Method, Eq. (1) selection, with the Sol-Attn rule of
-// §3.1 Eq. (4)): s-hat_ij = Q-bar_i . K-bar_j / sqrt(d) from the fp32 means of the
-// dequantized blocks, against tau_i, with the blocks of a sink range forced exact.  Its
-// two consumers, the tail pass (32 query blocks per workgroup) and the exact pass (one
-// query block per workgroup), must agree on every exact set, so the bits are decided once
-// here.  (Sol-Attn routes inside its fused kernel and has no such pass.)  One wave per
-// (b, h, 32 query blocks from i0, 64-block chunk c): the 32 x 64
-// products on v_mfma_f32_32x32x2_f32 (fp32 operands and sums), A = the query-block means,
-// B = the key-block means, with the contraction order chosen so that lane (m, kh) reads
-// dims 64 kh .. 64 kh + 63 of its row contiguously (k-step s takes dim 64 kh + s).  The
-// accumulator of row i holds key blocks 32 t + n in lane n (+ 32 for rows i + 4), so one
-// ballot per row pair gives the routing bits of two query blocks.
-// ---------------------------------------------------------------------------
-struct RouteArgs {
-  int nb, nbp, nbw;
-  const float* qbar; const float* kbar_t; const float* tau_i;
-  int sink_b0, sink_b1;
-  uint64_t* sel;
-};
-
-__global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
-  const int c = blockIdx.x, i0 = blockIdx.y * 32, bh = blockIdx.z;
-  const int lane = threadIdx.x, m = lane & 31, kh = lane >> 5;
-  // rows i0 + m < nbp and key blocks 64 c + 63 < nbp: padding rows / blocks are in memory
-  const float4* qa = (const float4*)(a.qbar + ((size_t)bh * a.nbp + i0 + m) * kDim) + 16 * kh;
-  const float4* kb = (const float4*)a.kbar_t + ((size_t)bh * 32 + 16 * kh) * a.nbp + 64 * c + m;
-  floatx16 acc[2] = {floatx16{}, floatx16{}};               // key blocks 64 c + 32 t + n
-#pragma unroll 4
-  for (int cc = 0; cc < 16; ++cc) {
-    const float4 x = qa[cc];
-    const float4 y0 = kb[(size_t)cc * a.nbp];
-    const float4 y1 = kb[(size_t)cc * a.nbp + 32];
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y0.x, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y1.x, acc[1], 0, 0, 0);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y0.y, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y1.y, acc[1], 0, 0, 0);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y0.z, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y1.z, acc[1], 0, 0, 0);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y0.w, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y1.w, acc[1], 0, 0, 0);
-  }
-  const bool sink[2] = {64 * c + m >= a.sink_b0 && 64 * c + m <= a.sink_b1,
-                        64 * c + 32 + m >= a.sink_b0 && 64 * c + 32 + m <= a.sink_b1};
-  const bool kvalid[2] = {64 * c + m < a.nb, 64 * c + 32 + m < a.nb};
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = i0 + 8 * (r >> 2) + 4 * kh + (r & 3);     // this lane's query block in row r
-    const float tau = a.tau_i[(size_t)bh * a.nbp + i];
-    uint64_t bits[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float s_hat = acc[t][r] * kScaleR;
-      bits[t] = __ballot(i < a.nb && kvalid[t] && (s_hat > tau || sink[t]));
-    }
-    if (lane == 0) {
-      const int ilo = i0 + 8 * (r >> 2) + (r & 3);          // rows ilo (lanes 0..31) and ilo + 4
-      const uint64_t wlo = (bits[1] << 32) | (bits[0] & 0xffffffffull);
-      const uint64_t whi = (bits[1] & 0xffffffff00000000ull) | (bits[0] >> 32);
-      if (ilo < a.nb) a.sel[((size_t)bh * a.nb + ilo) * a.nbw + c] = wlo;
-      if (ilo + 4 < a.nb) a.sel[((size_t)bh * a.nb + ilo + 4) * a.nbw + c] = whi;
-    }
-  }
-}
-
-hipError_t launch_route(Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* sel,
-                        hipStream_t stream) {
-  RouteArgs r;
-  r.nb = ws.nb; r.nbp = ws.nbp; r.nbw = ws.nbp / 64;
-  r.qbar = ws.qbar; r.kbar_t = ws.kbar_t; r.tau_i = ws.tau_i;
-  r.sink_b0 = sink_b0; r.sink_b1 = sink_b1;
-  r.sel = sel;
-  hipLaunchKernelGGL(route_kernel, dim3(ws.nbp / 64, (ws.nb + 31) / 32, s.B * s.H), dim3(64), 0, stream, r);
   return hipGetLastError();
 }
 

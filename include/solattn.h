@@ -88,11 +88,8 @@ typedef enum {
  *   opart    float [S][B][N][H][128]   per-key-split normalized partial outputs (S = kv_splits > 1),
  *                                      fp32 so that the merge rounds each output to bf16 once
  *   olse     float [S][B][N][H]        per-key-split log2-sum-exp of the partial rows
- *   sel      uint64 [B][H][nb][nbp/64] Sol-Attn2 routing bits (sink included), bit j % 64 of word
- *                                      j / 64 set iff block j is exact for query block i; written
- *                                      by stage 2a, read by the tail and exact passes, which must
- *                                      agree on every exact set.  Sol-Attn has no routing array:
- *                                      its fused kernel decides each chunk on chip
+ *   (No layout has a routing array for the forward: each fused kernel decides its blocks
+ *   on chip.  The Sol-Attn2 training layout keeps the forward's words in sel, below.)
  *   tmu, tnu float [B][H][nbp][2][128] per-anchor tail key / value means mu_a, nu_a (Sol-Attn2)
  *   tlz      float [B][H][nbp][2]     log2 Z_a - log2(e) qbar_a . mu_a / sqrt(d); -inf if the
  *                                      anchor's tail is empty (Sol-Attn2)
@@ -110,7 +107,9 @@ typedef enum {
  *   ld       float [B][H][tp][2]      (lse, dO . O) per query row (backward scratch)
  *   dkbar, dvbar float [B][H][nbp][128] gradients w.r.t. the pooled keys (times 1/sqrt(d))
  *                                      and pooled values (backward scratch)
- * SOL_VARIANT_SOL2_TRAIN (the Sol-Attn2 arrays above, then): lse and ld as for Sol-Attn
+ * SOL_VARIANT_SOL2_TRAIN (the Sol-Attn2 arrays above, then): sel uint64 [B][H][nb][nbp/64]
+ * (the routing words the forward's exact pass decided, bit j % 64 of word j / 64 set iff
+ * block j is exact for query block i, sink included), lse and ld as for Sol-Attn
  * training (lse written by sol_attn2_forward_train), ofp float [B][H][tp][128] (the
  * forward's output rows before rounding to bf16, so that the backward's D_t = dO_t . O_t
  * does not inherit the output's rounding), mcol (sel by key block), kh / vh (dequantized
@@ -328,22 +327,27 @@ int sol_attn2_fused(const void* q, const void* k, const void* v, void* out,
                     int64_t sink_start, int64_t sink_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 2a (Sol-Attn2 draft, Method, Eq. (1)): routing of every (query block, key
- * block) pair on the dequantized block means (bits into the workspace array sel),
- * and per 32-token anchor the tail over the groups of the unselected blocks:
- * log2 Z_a, mu_a, nu_a (workspace arrays tmu, tnu, tlz).  Needs stage 1 on this
- * workspace.  q, k, v are only validated (the pass reads the workspace). */
+/* Stage 2a (Sol-Attn2 draft, Method, Eq. (1)): per 32-token anchor the tail over the
+ * groups of the unselected blocks: log2 Z_a, mu_a, nu_a (workspace arrays tmu, tnu,
+ * tlz).  The pass routes its 32 query blocks per workgroup on chip (proxy scores of
+ * the dequantized fp32 block means against tau_i, the sink forced) with the same fp32
+ * arithmetic as stage 2b, so both stages take the same decisions; no routing map is
+ * written.  Needs stage 1 on this workspace.  q, k, v are only validated (the pass
+ * reads the workspace). */
 int sol_attn2_tail(const void* q, const void* k, const void* v,
                    int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                    int64_t sink_start, int64_t sink_tokens,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 2b (Sol-Attn2 draft, Eqs. (2), (3); "FP8 quantization and ExpCast"): exact
- * attention over the selected blocks with FP8 Q K^T and bf16 P V, combined with
- * the anchor tail through delta_t and one shared denominator; writes out (device,
- * bf16 BTHD, non-NULL).  Needs stage 2a on this workspace. */
+/* Stage 2b (Sol-Attn2 draft, Eqs. (2), (3); "FP8 quantization and ExpCast"): routes
+ * its query block on chip (as stage 2a: sink_start / sink_tokens must be the ones
+ * stage 2a was given), then exact attention over the selected blocks with FP8 Q K^T
+ * and bf16 P V, combined with the anchor tail through delta_t and one shared
+ * denominator; writes out (device, bf16 BTHD, non-NULL).  Needs stage 2a on this
+ * workspace. */
 int sol_attn2_exact(const void* q, const void* k, const void* v, void* out,
                     int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                    int64_t sink_start, int64_t sink_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -365,10 +369,12 @@ int sol_attn2_pv8_prepare(const void* q, const void* k, const void* v,
                           int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
                           float tau, int thresh, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 2b of sol_attn2_pv8 (after sol_attn2_tail on the same workspace): exact
- * attention with FP8 Q K^T and FP8 P V (ExpCast P), combined with the tail. */
+/* Stage 2b of sol_attn2_pv8 (after sol_attn2_tail on the same workspace, with the
+ * same sink): exact attention with FP8 Q K^T and FP8 P V (ExpCast P), combined with
+ * the tail. */
 int sol_attn2_pv8_exact(const void* q, const void* k, const void* v, void* out,
                         int64_t batch, int64_t tokens, int64_t heads, int64_t head_dim,
+                        int64_t sink_start, int64_t sink_tokens,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sol-Attn2 routing export, as sol_attn_debug_routing (kv_splits must be 0 or 1:

@@ -24,8 +24,8 @@ What is computed, per (batch, head), with blocks of 64 tokens:
    to 0.
 4. Block j is exact for query block i iff s_ij > tau_i (strict, Eq. (4)), or
    j overlaps the exact KV sink (README "Exact KV sink"), or, optionally,
-   |i - j| <= adjacent (GGML docs: "Adjacent blocks remain exact"; off by
-   default).
+   |i - j| <= adjacent (GGML docs, implementation notes: an option that keeps
+   neighbouring blocks exact; off by default, and not in the kernels).
 5. For token t of block i (paper §3.2 "Proxy-Score Reuse as Approximate
    Correction", Figure 4): exact logits z_tu = q_t.k_u*scale over the tokens
    of the exact blocks, pooled logits zt_tj = q_t.K-bar_j*scale over the

@@ -80,11 +80,11 @@ def test_workspace_sizes_and_layout(L):
                           for o in [getattr(lay, name)] if o >= 0)
             assert all(o % 256 == 0 for o in offs)
             assert offs[-1] < n
+            # every fused kernel routes on chip: only the Sol-Attn2 training layout keeps the
+            # forward's routing words (for its backward)
+            assert (lay.sel >= 0) == (variant == 5)
             if variant in (1, 4):
-                # Sol-Attn routes inside its fused kernel: no routing array in its workspace
-                assert lay.q8 == -1 and lay.gk == -1 and lay.sel == -1
-            else:
-                assert lay.sel >= 0
+                assert lay.q8 == -1 and lay.gk == -1
     assert L.sol_attn_workspace_bytes(1, 1, 1024, 2, 64) == 0
     assert L.sol_attn_workspace_bytes(6, 1, 1024, 2, 128) == 0
 
@@ -135,8 +135,8 @@ def test_sol2_training_layout_extends_the_sol2_layout(L, B, N, H):
     from block_sparse_attention_tok_amd import _lib
     l2 = _lib.workspace_layout(2, B, N, H)
     l5 = _lib.workspace_layout(5, B, N, H)
-    extra = ("lse", "ofp", "mcol", "ld", "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz", "aextra",
-             "gdk", "gdv")
+    extra = ("sel", "lse", "ofp", "mcol", "ld", "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz",
+             "aextra", "gdk", "gdv")
     for name, _ in _lib.WsLayout._fields_:
         if name in ("total_bytes",) + extra:
             continue
@@ -148,7 +148,7 @@ def test_sol2_training_layout_extends_the_sol2_layout(L, B, N, H):
     assert offs == sorted(offs) and offs[0] >= l2.total_bytes
     bh, nbp, nb = B * H, l5.nbp, l5.nb
     tp = nbp * 64
-    need = dict(lse=bh * tp * 4, ofp=bh * tp * 512, mcol=bh * nb * (nbp // 64) * 8, ld=bh * tp * 8, kh=bh * N * 256, vh=bh * N * 256,
+    need = dict(sel=bh * nb * (nbp // 64) * 8, lse=bh * tp * 4, ofp=bh * tp * 512, mcol=bh * nb * (nbp // 64) * 8, ld=bh * tp * 8, kh=bh * N * 256, vh=bh * N * 256,
                 qd=bh * N * 256, kd=bh * N * 256, dlam=bh * tp * 4, qab=bh * 2 * nbp * 256,
                 dmub=bh * 2 * nbp * 256, dnub=bh * 2 * nbp * 256, alz=bh * 2 * nbp * 8, aextra=bh * 2 * nbp * 512,
                 gdk=bh * 2 * nbp * 512, gdv=bh * 2 * nbp * 512)
@@ -213,8 +213,10 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
     assert L.sol_attn_fused_kv(fake, fake, fake, fake, 1, 1024, 2, 128, -1, 0, 17, fake, 1 << 30, None) == 8
     # Sol-Attn2 stage 2 parts: sink out of range, missing output, workspace too small
     assert L.sol_attn2_tail(fake, fake, fake, 1, 1024, 2, 128, 1000, 100, fake, 1 << 30, None) == 5
-    assert L.sol_attn2_exact(fake, fake, fake, None, 1, 1024, 2, 128, fake, 1 << 30, None) == 1
-    assert L.sol_attn2_exact(fake, fake, fake, fake, 1, 1024, 2, 128, fake, 16, None) == 6
+    assert L.sol_attn2_exact(fake, fake, fake, None, 1, 1024, 2, 128, -1, 0, fake, 1 << 30, None) == 1
+    assert L.sol_attn2_exact(fake, fake, fake, fake, 1, 1024, 2, 128, -1, 0, fake, 16, None) == 6
+    assert L.sol_attn2_exact(fake, fake, fake, fake, 1, 1024, 2, 128, 1000, 100, fake, 1 << 30, None) == 5
+    assert L.sol_attn2_pv8_exact(fake, fake, fake, fake, 1, 1024, 2, 128, 0, -3, fake, 1 << 30, None) == 5
     # training forward / backward: missing output or gradient, workspace sized for the plain forward,
     # misaligned gradient
     assert L.sol_attn_forward_train(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, 1 << 30, None) == 1
@@ -228,6 +230,20 @@ def test_entry_points_reject_bad_arguments_before_any_launch(L):
                                1 << 30, None) == 8
     assert L.sol_attn_backward(fake, fake, fake, fake, fake, fake, fake, fake, 1, 1024, 2, 64, fake, 1 << 30,
                                None) == 3
+    # Sol-Attn2 training: a workspace sized for the plain Sol-Attn2 forward is too small
+    small2 = L.sol_attn_workspace_bytes(2, 1, 1024, 2, 128)
+    assert L.sol_attn2_forward_train(fake, fake, fake, None, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, 1 << 30,
+                                     None) == 1
+    assert L.sol_attn2_forward_train(fake, fake, fake, fake, 1, 1024, 2, 128, 1.0, -1, 0, 0, fake, small2,
+                                     None) == 6
+    assert L.sol_attn2_forward_train(fake, fake, fake, fake, 1, 1024, 2, 128, float("inf"), -1, 0, 0, fake,
+                                     1 << 30, None) == 4
+    assert L.sol_attn2_backward(fake, fake, fake, fake, fake, fake, None, fake, 1, 1024, 2, 128, fake, 1 << 30,
+                                None) == 1
+    assert L.sol_attn2_backward(fake, fake, fake, fake, fake, fake, fake, fake, 1, 1024, 2, 128, fake, small2,
+                                None) == 6
+    assert L.sol_attn2_backward(fake, fake, fake, fake, fake, fake, fake, vp(0x1004), 1, 1024, 2, 128, fake,
+                                1 << 30, None) == 8
 
 
 def test_python_validate_wrapper():

@@ -223,7 +223,7 @@ def test_operator_bench_shape_at_80_and_85_percent(target, tau):
 
 def test_long_sequence_131k_with_text_sink():
     """B=1, H=32, 512 text tokens (exact sink) + 131072 video tokens at ~90% sparsity (the
-    automatic six key splits): full routing of every head against the oracle and 4 sampled
+    automatic four key splits): full routing of every head against the oracle and 4 sampled
     query blocks per head, the last one always among them."""
     w = long_sink(131072)
     q, k, v = w.qkv()
