@@ -3,7 +3,7 @@ that ties a counter summary to the kernel it was taken on.
 
     python -m block_sparse_attention_tok_amd.profsum stats  KERNEL_STATS_CSV --title T --command C --out FILE
     python -m block_sparse_attention_tok_amd.profsum traffic --kernel K --fetch CSV --write CSV \
-        --copy-fetch CSV --copy-write CSV --copy-bytes N --title T --cmds C1 C2 C3 C4 --out FILE
+        --copy-fetch CSV --copy-write CSV --copy-bytes N --title T --cmds CMD1 CMD2 CMD3 CMD4 --out FILE
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same
 counters read for a plain device copy of known size, and records the source hash
