@@ -1,4 +1,6 @@
-// Sol-Attn backward pass with the forward's routing held fixed, for gfx950.
+// Sol-Attn and Sol-Attn2 backward passes with the forward's routing (and Sol-Attn2's key
+// groups) held fixed, for gfx950.  The Sol-Attn2 part (its tail, anchors and group means) is
+// the second half of this file; its exact tokens reuse the Sol-Attn kernels below.
 //
 // What is differentiated: the Sol-Attn output (paper arXiv 2607.24027, §3.2
 // "Proxy-Score Reuse as Approximate Correction") with the block masks treated
