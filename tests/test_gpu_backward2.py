@@ -25,7 +25,7 @@ from oracle import sol_attn as sa
 from oracle import sol_attn2 as s2
 from oracle import sol_attn2_bwd as sb2
 from parity import say, to_gpu
-from workloads import block_offset_tensor, operator_bench, wan_dit
+from workloads import block_offset_tensor, long_sink, operator_bench, wan_dit
 
 pytestmark = pytest.mark.gpu
 
@@ -73,14 +73,14 @@ def _state(ws, B, N, H):
     return sel, masks, views
 
 
-def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, seed=0):
+def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, seed=0, thresh="diag"):
     B, N, H, _ = q.shape
     say(f"[backward2] B={B} N={N} H={H} tau={tau} sink=({sink_start},{sink_tokens})")
     do = _dout(q.shape, 8000 + seed)
     qg, kg, vg, dog = to_gpu(q, k, v, do)
-    out, ws = bsa.forward_train2(qg, kg, vg, tau, "diag", sink_start, sink_tokens)
+    out, ws = bsa.forward_train2(qg, kg, vg, tau, thresh, sink_start, sink_tokens)
     dq, dk, dv = bsa.backward2(qg, kg, vg, out, dog, ws)
-    plain = bsa.sol_attn2(qg, kg, vg, tau, "diag", sink_start, sink_tokens)
+    plain = bsa.sol_attn2(qg, kg, vg, tau, thresh, sink_start, sink_tokens)
     torch.cuda.synchronize()
     assert torch.equal(out, plain), "the training forward changed the output"
     gsel, gmasks, views = _state(ws, B, N, H)
@@ -120,6 +120,10 @@ def test_exact_sink(sink):
 
 def test_batch_and_odd_heads():
     run_case(*_qkv(2, 700, 3, 2300), 0.5)
+
+
+def test_exact_covariance_threshold():
+    run_case(*_qkv(1, 2000, 2, 2350), 1.0, thresh="exact")
 
 
 def test_everything_exact_is_the_dense_gradient():
@@ -166,3 +170,9 @@ def test_operator_bench_shape():
     """The 32K x 32-head shape: two heads compared in full."""
     q, k, v = operator_bench().qkv()
     run_case(q, k, v, 1.28, heads=[0, 31])
+
+
+def test_long_sequence_with_text_sink():
+    """512 text tokens (exact sink) + 65536 video tokens, 32 heads: one head compared in full."""
+    q, k, v = long_sink(video_tokens=65536).qkv()
+    run_case(q, k, v, 1.3, 0, 512, heads=[7])
