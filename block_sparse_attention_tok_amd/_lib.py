@@ -43,7 +43,8 @@ class WsLayout(ctypes.Structure):
         "total_bytes", "nb", "nbp", "qbar", "kbar_t", "kbar_h", "vbar_h", "tau_i", "kstat", "kcov", "kpart",
         "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse",
         "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale", "lse", "mrow", "mcol", "ld", "dkbar", "dvbar",
-        "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz", "aextra", "gdk", "gdv", "ofp", "kcovp")]
+        "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz", "aextra", "gdk", "gdv", "ofp", "kcovp",
+        "wcnt", "qcount", "order")]
 
 
 class SolAttnError(RuntimeError):
@@ -490,6 +491,9 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
         tau_i=view(L.tau_i, torch.float32, (batch, heads, nbp)),
         kstat=view(L.kstat, torch.float32, (batch, heads, 2, 128)),
         kcov=view(L.kcov, torch.float32, (batch, heads, 128, 128)),
+        wcnt=view(L.wcnt, torch.uint8, (batch, heads, nbp // 64, nbp)),
+        qcount=view(L.qcount, torch.int32, (batch, heads, nbp)),
+        order=view(L.order, torch.int32, (batch, heads, nbp)),
     )
     if variant in (SOL_VARIANT_SOL2, SOL_VARIANT_SOL2_PV8, SOL_VARIANT_SOL2_TRAIN):
         tp = nbp * 64

@@ -95,6 +95,11 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
   if (variant == SOL_VARIANT_SOL1 || variant == SOL_VARIANT_SOL1_TRAIN) {
     L->kh = take(bh * tokens * kDim * 2);
     L->vh = take(bh * tokens * kDim * 2);
+    // stage 2's work order: exact-block counts per routing chunk and query block, their
+    // sums, and each head's query blocks by descending count
+    L->wcnt = take(bh * (nbp / 64) * nbp);
+    L->qcount = take(bh * nbp * 4);
+    L->order = take(bh * nbp * 4);
   }
   const bool sol2 = variant == SOL_VARIANT_SOL2 || variant == SOL_VARIANT_SOL2_PV8 || variant == SOL_VARIANT_SOL2_TRAIN;
   if (sol2) {
@@ -214,6 +219,9 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.gdv = (float*)at(L.gdv);
   w.ofp = (float*)at(L.ofp);
   w.kcovp = (float*)at(L.kcovp);
+  w.wcnt = (uint8_t*)at(L.wcnt);
+  w.qcount = (int*)at(L.qcount);
+  w.order = (int*)at(L.order);
   return w;
 }
 

@@ -68,6 +68,7 @@ struct FusedArgs {
   unsigned long long* pairs;    // += selected token pairs n_i n_j of this work item (NULL = none)
   float* lse;                   // [B][H][tp] base-2 log-sum-exp per query row (NULL = none)
   int tp;
+  const int* order;             // [B][H][nbp] query blocks by descending exact-block count (NULL = block order)
 };
 
 // Tile order: first the pooled tile of every chunk c (code -(c + 1)), then the selected
@@ -110,15 +111,19 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   __shared__ int redo_s[2];
 
   // Work item order: query block fastest, then key split, then (batch, head), so the
-  // workgroups that run together on one XCD share a head and a key range.
+  // workgroups that run together on one XCD share a head and a key range.  Within a head
+  // the query blocks come by descending exact-block count (the order array): the longest
+  // items start first, and the workgroups that share an XCD's L2 at a time stream their
+  // selected tiles at similar rates.
   const int total = a.B * a.H * a.S * a.nb;
   const int item = xcd_remap(blockIdx.x, total);
   // The divisions run on the VALU; readfirstlane keeps the (uniform) indices in
   // SGPRs so addresses and buffer resources derived from them stay scalar.
-  const int i = __builtin_amdgcn_readfirstlane(item % a.nb);
+  const int i0 = __builtin_amdgcn_readfirstlane(item % a.nb);
   const int rest = __builtin_amdgcn_readfirstlane(item / a.nb);
   const int split = __builtin_amdgcn_readfirstlane(rest % a.S);
   const int bh = __builtin_amdgcn_readfirstlane(rest / a.S);
+  const int i = a.order ? __builtin_amdgcn_readfirstlane(a.order[(size_t)bh * a.nbp + i0]) : i0;
   const int h = __builtin_amdgcn_readfirstlane(bh % a.H), b = __builtin_amdgcn_readfirstlane(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -435,6 +440,72 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   }
 }
 
+// Stage 2's work order, first pass: the number of exact blocks of each query block within
+// each 64-block routing chunk, decided exactly as the fused pass decides them (the same FMA
+// sequence as proxy_dot, the same threshold test and sink rule), so that the counts are
+// the fused pass's own.  A workgroup takes 32 query blocks (their fp32 means read as
+// wave-uniform scalars), each wave every fourth chunk; lane l scores key block 64 c + l.
+__global__ __launch_bounds__(256) void count_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar_t,
+                                                    const float* __restrict__ tau_i, int nb, int nbp, int sink_b0,
+                                                    int sink_b1, uint8_t* __restrict__ wcnt) {
+  const int bh = blockIdx.y, i0 = blockIdx.x * 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nchunks = nbp / 64;
+  typedef const __attribute__((address_space(4))) float const_float;
+  const const_float* qs = (const const_float*)(qbar + ((size_t)bh * nbp + i0) * kDim);   // rows < nbp
+  const float4* kt = (const float4*)kbar_t + (size_t)bh * 32 * nbp;
+  for (int c = w; c < nchunks; c += 4) {
+    const int j = 64 * c + lane;
+    float acc[32];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) acc[q] = 0.f;
+    for (int g = 0; g < 32; ++g) {
+      const float4 kv = kt[(size_t)g * nbp + j];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        acc[q] = __builtin_fmaf(qs[128 * q + 4 * g], kv.x, acc[q]);
+        acc[q] = __builtin_fmaf(qs[128 * q + 4 * g + 1], kv.y, acc[q]);
+        acc[q] = __builtin_fmaf(qs[128 * q + 4 * g + 2], kv.z, acc[q]);
+        acc[q] = __builtin_fmaf(qs[128 * q + 4 * g + 3], kv.w, acc[q]);
+      }
+    }
+    int mine = 0;                                        // lane q keeps query block i0 + q's count
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const float tau = tau_i[(size_t)bh * nbp + i0 + q];
+      const uint64_t word = exact_word(__ballot(acc[q] * kScale > tau), c, nb, sink_b0, sink_b1);
+      if (lane == q) mine = __builtin_popcountll(word);
+    }
+    if (lane < 32 && i0 + lane < nb) wcnt[((size_t)bh * nchunks + c) * nbp + i0 + lane] = (uint8_t)mine;
+  }
+}
+
+// Second pass, one workgroup per (batch, head): each query block's total count, and its rank
+// by descending count (equal counts in block order), so that order[rank] = block.  The
+// ranks are a strict order, so the result is a permutation of 0 .. nb - 1.
+__global__ __launch_bounds__(256) void order_kernel(const uint8_t* __restrict__ wcnt, int nb, int nbp,
+                                                    int* __restrict__ qcount, int* __restrict__ order) {
+  extern __shared__ int qc[];                            // [nb]
+  const int bh = blockIdx.x, nchunks = nbp / 64;
+  const uint8_t* wc = wcnt + (size_t)bh * nchunks * nbp;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+    int c = 0;
+    for (int ch = 0; ch < nchunks; ++ch) c += wc[(size_t)ch * nbp + i];
+    qc[i] = c;
+    qcount[(size_t)bh * nbp + i] = c;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+    const int ci = qc[i];
+    int r = 0;
+    for (int i2 = 0; i2 < nb; ++i2) {
+      const int c2 = qc[i2];
+      r += (c2 > ci) | ((c2 == ci) & (i2 < i));
+    }
+    order[(size_t)bh * nbp + r] = i;
+  }
+}
+
 // Merge of the key-range splits: o = sum_s 2^(lse_s - lse) o_s / sum_s 2^(lse_s - lse), the
 // fp32 partial rows o_s weighted by their softmax masses, rounded to bf16 once.  One thread
 // per (row, 8 dims); partials are BTHD like the output.  With `lse` set, the first thread
@@ -497,6 +568,16 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(1), 0, stream, pairs);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
+  }
+  a.order = nullptr;
+  if (ws.wcnt != nullptr && ws.qcount != nullptr && ws.order != nullptr) {
+    hipLaunchKernelGGL(count_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t,
+                       ws.tau_i, ws.nb, ws.nbp, sink_b0, sink_b1, ws.wcnt);
+    hipLaunchKernelGGL(order_kernel, dim3(s.B * s.H), dim3(256), ws.nb * sizeof(int), stream, ws.wcnt, ws.nb, ws.nbp,
+                       ws.qcount, ws.order);
+    hipError_t e1 = hipGetLastError();
+    if (e1 != hipSuccess) return e1;
+    a.order = ws.order;
   }
   const int total = s.B * s.H * S * ws.nb;
   hipLaunchKernelGGL(sol_fused_kernel, dim3(total), dim3(128), 0, stream, a);

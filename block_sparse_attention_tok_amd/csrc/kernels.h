@@ -58,6 +58,9 @@ struct Workspace {
   float* gdv;       // [B][H][nbp][2][128] gradient w.r.t. the group mean values
   float* ofp;       // [B][H][tp][128] the Sol-Attn2 training forward's output rows in fp32
   float* kcovp;     // [B][H][8][128][128] per-slice centred key-mean outer products (exact threshold)
+  uint8_t* wcnt;    // [B][H][nbp / 64][nbp] Sol-Attn: exact blocks per (routing chunk, query block)
+  int* qcount;      // [B][H][nbp] Sol-Attn: exact blocks per query block
+  int* order;       // [B][H][nbp] Sol-Attn: the head's query blocks by descending qcount (stage 2's work order)
 };
 
 struct Shape {

@@ -78,6 +78,14 @@ typedef enum {
  *            K block means (thresh = SOL_THRESH_EXACT only)
  *   kh, vh   bf16  [B][H][N][128]     Sol-Attn: head-major copies of K and V (stage 1 writes
  *                                      them; stage 2 and the backward stream tiles from them)
+ *   wcnt     uint8 [B][H][nbp/64][nbp] Sol-Attn: exact blocks of each query block within each
+ *                                      64-block routing chunk (sink included), written by stage 2
+ *                                      before its fused pass
+ *   qcount   int32 [B][H][nbp]        Sol-Attn: exact blocks of each query block (their sum)
+ *   order    int32 [B][H][nbp]        Sol-Attn: the head's nb query blocks by descending qcount
+ *                                      (equal counts in block order), the order in which the
+ *                                      fused pass takes its work items; not a routing map: the
+ *                                      fused pass still decides every block on chip
  *   q8, k8   uint8 [B][H][tp][128]    E4M3FN codes (Sol-Attn2)
  *   qscale, kscale float [B][H][nbp]  E4M3 block scales (Sol-Attn2)
  *   qhat     float [B][H][128]        mean-query direction (Sol-Attn2)
@@ -137,6 +145,7 @@ typedef struct {
     int64_t kh, vh;
     int64_t qd, kd, dlam, qab, dmub, dnub, alz, aextra, gdk, gdv;
     int64_t ofp, kcovp;
+    int64_t wcnt, qcount, order;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */

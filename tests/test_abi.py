@@ -128,6 +128,22 @@ def test_training_layout_extends_the_sol_attn_layout(L, B, N, H):
 
 
 @pytest.mark.parametrize("B,N,H", [(1, 1024, 2), (1, 14040, 12), (2, 333, 3), (1, 32768, 32)])
+def test_work_order_arrays(L, B, N, H):
+    """Sol-Attn's stage-2 work order (per-chunk counts, per-block counts, the order itself) has
+    its documented sizes in both Sol-Attn layouts and exists in no Sol-Attn2 layout."""
+    from block_sparse_attention_tok_amd import _lib
+    for variant in (1, 4):
+        l = _lib.workspace_layout(variant, B, N, H)
+        bh, nbp = B * H, l.nbp
+        assert l.wcnt >= 0 and l.qcount - l.wcnt >= bh * (nbp // 64) * nbp
+        assert l.order - l.qcount >= bh * nbp * 4 and l.total_bytes - l.order >= bh * nbp * 4
+        assert l.wcnt % 256 == 0 and l.qcount % 256 == 0 and l.order % 256 == 0
+    for variant in (2, 3, 5):
+        l = _lib.workspace_layout(variant, B, N, H)
+        assert l.wcnt == l.qcount == l.order == -1
+
+
+@pytest.mark.parametrize("B,N,H", [(1, 1024, 2), (1, 14040, 12), (2, 333, 3), (1, 32768, 32)])
 def test_sol2_training_layout_extends_the_sol2_layout(L, B, N, H):
     """The Sol-Attn2 training workspace is the Sol-Attn2 one with the forward's row
     log-sum-exp and the backward scratch appended (so every Sol-Attn2 stage call runs on it
