@@ -545,6 +545,15 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float4* __restr
 // call can also sit in a captured graph).
 __global__ void zero_counter_kernel(unsigned long long* p) { *p = 0ull; }
 
+hipError_t launch_order(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream) {
+  if (ws.wcnt == nullptr || ws.qcount == nullptr || ws.order == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(count_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t,
+                     ws.tau_i, ws.nb, ws.nbp, sink_b0, sink_b1, ws.wcnt);
+  hipLaunchKernelGGL(order_kernel, dim3(s.B * s.H), dim3(256), ws.nb * sizeof(int), stream, ws.wcnt, ws.nb, ws.nbp,
+                     ws.qcount, ws.order);
+  return hipGetLastError();
+}
+
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                         Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* mask_out,
                         unsigned long long* pairs, hipStream_t stream) {
@@ -569,16 +578,9 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
-  a.order = nullptr;
-  if (ws.wcnt != nullptr && ws.qcount != nullptr && ws.order != nullptr) {
-    hipLaunchKernelGGL(count_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t,
-                       ws.tau_i, ws.nb, ws.nbp, sink_b0, sink_b1, ws.wcnt);
-    hipLaunchKernelGGL(order_kernel, dim3(s.B * s.H), dim3(256), ws.nb * sizeof(int), stream, ws.wcnt, ws.nb, ws.nbp,
-                       ws.qcount, ws.order);
-    hipError_t e1 = hipGetLastError();
-    if (e1 != hipSuccess) return e1;
-    a.order = ws.order;
-  }
+  hipError_t e1 = launch_order(s, ws, sink_b0, sink_b1, stream);
+  if (e1 != hipSuccess) return e1;
+  a.order = ws.order;
   const int total = s.B * s.H * S * ws.nb;
   hipLaunchKernelGGL(sol_fused_kernel, dim3(total), dim3(128), 0, stream, a);
   hipError_t e = hipGetLastError();

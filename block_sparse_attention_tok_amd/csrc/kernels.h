@@ -75,6 +75,10 @@ hipError_t launch_threshold(Shape s, const Workspace& ws, float tau, int exact, 
 // Sol-Attn stage 2: fused routing + proxy reuse + exact attention.  mask_out (optional)
 // receives the selection words the kernel used; pairs (optional) is cleared and then
 // receives the number of selected token pairs sum n_i n_j.
+// Stage 2's work order: per-chunk and per-block exact-block counts and each head's query
+// blocks by descending count (ws.wcnt, ws.qcount, ws.order); returns hipSuccess without
+// launching if the workspace has no such arrays.
+hipError_t launch_order(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream);
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                         Shape s, const Workspace& ws, int sink_b0, int sink_b1, uint64_t* mask_out,
                         unsigned long long* pairs, hipStream_t stream);

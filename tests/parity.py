@@ -73,3 +73,20 @@ def compare_out(gpu: np.ndarray, ref: np.ndarray, rel=REL_L2_BF16, max_abs=MAX_A
     assert err <= rel, f"{what}: rel L2 {err:.3e} > {rel}"
     assert mx <= max_abs, f"{what}: max abs {mx:.3e} > {max_abs}"
     return err, mx
+
+
+def order_check(variant, ws, gsel, B, N, H):
+    """Sol-Attn stage 2's work order: qcount is each query block's number of exact blocks,
+    counted by the same decision procedure as the fused pass, so it equals the row sums of
+    the masks that pass exported, exactly; order lists each head's blocks by descending
+    count, equal counts in block order: a permutation, so every block is computed once."""
+    import block_sparse_attention_tok_amd as bsa
+    views = bsa.workspace_views(variant, ws, B, N, H)
+    nb = views["nb"]
+    qcount = views["qcount"].cpu().numpy()[..., :nb]
+    order = views["order"].cpu().numpy()[..., :nb]
+    np.testing.assert_array_equal(qcount, gsel.sum(-1))
+    for b in range(B):
+        for h in range(H):
+            want = sorted(range(nb), key=lambda i: (-qcount[b, h, i], i))
+            np.testing.assert_array_equal(order[b, h], want)
