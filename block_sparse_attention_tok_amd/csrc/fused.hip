@@ -444,7 +444,8 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 // each 64-block routing chunk, decided exactly as the fused pass decides them (the same FMA
 // sequence as proxy_dot, the same threshold test and sink rule), so that the counts are
 // the fused pass's own.  A workgroup takes 32 query blocks (their fp32 means read as
-// wave-uniform scalars), each wave every fourth chunk; lane l scores key block 64 c + l.
+// wave-uniform scalars), each wave chunks w, w + 4, ..., two at a time so that each scalar
+// mean feeds both; lane l scores key block 64 c + l.
 __global__ __launch_bounds__(256) void count_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar_t,
                                                     const float* __restrict__ tau_i, int nb, int nbp, int sink_b0,
                                                     int sink_b1, uint8_t* __restrict__ wcnt) {
@@ -454,56 +455,89 @@ __global__ __launch_bounds__(256) void count_kernel(const float* __restrict__ qb
   typedef const __attribute__((address_space(4))) float const_float;
   const const_float* qs = (const const_float*)(qbar + ((size_t)bh * nbp + i0) * kDim);   // rows < nbp
   const float4* kt = (const float4*)kbar_t + (size_t)bh * 32 * nbp;
-  for (int c = w; c < nchunks; c += 4) {
-    const int j = 64 * c + lane;
-    float acc[32];
+  for (int c = w; c < nchunks; c += 8) {                  // chunks c and c + 4 together
+    const bool two = c + 4 < nchunks;                     // uniform
+    const int j0 = 64 * c + lane, j1 = two ? j0 + 256 : j0;
+    float acc0[32], acc1[32];
 #pragma unroll
-    for (int q = 0; q < 32; ++q) acc[q] = 0.f;
+    for (int q = 0; q < 32; ++q) acc0[q] = acc1[q] = 0.f;
     for (int g = 0; g < 32; ++g) {
-      const float4 kv = kt[(size_t)g * nbp + j];
+      const float4 kv0 = kt[(size_t)g * nbp + j0];
+      const float4 kv1 = kt[(size_t)g * nbp + j1];
 #pragma unroll
       for (int q = 0; q < 32; ++q) {
-        acc[q] = __builtin_fmaf(qs[128 * q + 4 * g], kv.x, acc[q]);
-        acc[q] = __builtin_fmaf(qs[128 * q + 4 * g + 1], kv.y, acc[q]);
-        acc[q] = __builtin_fmaf(qs[128 * q + 4 * g + 2], kv.z, acc[q]);
-        acc[q] = __builtin_fmaf(qs[128 * q + 4 * g + 3], kv.w, acc[q]);
+        const float4 qv = make_float4(qs[128 * q + 4 * g], qs[128 * q + 4 * g + 1], qs[128 * q + 4 * g + 2],
+                                      qs[128 * q + 4 * g + 3]);
+        acc0[q] = __builtin_fmaf(qv.x, kv0.x, acc0[q]);
+        acc0[q] = __builtin_fmaf(qv.y, kv0.y, acc0[q]);
+        acc0[q] = __builtin_fmaf(qv.z, kv0.z, acc0[q]);
+        acc0[q] = __builtin_fmaf(qv.w, kv0.w, acc0[q]);
+        acc1[q] = __builtin_fmaf(qv.x, kv1.x, acc1[q]);
+        acc1[q] = __builtin_fmaf(qv.y, kv1.y, acc1[q]);
+        acc1[q] = __builtin_fmaf(qv.z, kv1.z, acc1[q]);
+        acc1[q] = __builtin_fmaf(qv.w, kv1.w, acc1[q]);
       }
     }
-    int mine = 0;                                        // lane q keeps query block i0 + q's count
+    int mine0 = 0, mine1 = 0;                            // lane q keeps query block i0 + q's counts
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
       const float tau = tau_i[(size_t)bh * nbp + i0 + q];
-      const uint64_t word = exact_word(__ballot(acc[q] * kScale > tau), c, nb, sink_b0, sink_b1);
-      if (lane == q) mine = __builtin_popcountll(word);
+      const uint64_t w0 = exact_word(__ballot(acc0[q] * kScale > tau), c, nb, sink_b0, sink_b1);
+      const uint64_t w1 = exact_word(__ballot(acc1[q] * kScale > tau), two ? c + 4 : c, nb, sink_b0, sink_b1);
+      if (lane == q) {
+        mine0 = __builtin_popcountll(w0);
+        mine1 = __builtin_popcountll(w1);
+      }
     }
-    if (lane < 32 && i0 + lane < nb) wcnt[((size_t)bh * nchunks + c) * nbp + i0 + lane] = (uint8_t)mine;
+    if (lane < 32 && i0 + lane < nb) {
+      wcnt[((size_t)bh * nchunks + c) * nbp + i0 + lane] = (uint8_t)mine0;
+      if (two) wcnt[((size_t)bh * nchunks + c + 4) * nbp + i0 + lane] = (uint8_t)mine1;
+    }
   }
 }
 
-// Second pass, one workgroup per (batch, head): each query block's total count, and its rank
-// by descending count (equal counts in block order), so that order[rank] = block.  The
-// ranks are a strict order, so the result is a permutation of 0 .. nb - 1.
+// Second pass, one workgroup per (batch, head): each query block's total count and a
+// counting sort by descending count: a histogram of the counts, its scan from the largest
+// count down, and one slot per block taken with an LDS atomic, so that order[] is a
+// permutation of 0 .. nb - 1 sorted by descending count (blocks with equal counts in any
+// order: the order only schedules work, every block's result is the same).
 __global__ __launch_bounds__(256) void order_kernel(const uint8_t* __restrict__ wcnt, int nb, int nbp,
                                                     int* __restrict__ qcount, int* __restrict__ order) {
-  extern __shared__ int qc[];                            // [nb]
-  const int bh = blockIdx.x, nchunks = nbp / 64;
+  extern __shared__ int sm[];
+  int* slot = sm;                                        // [nb + 1] histogram, then next free slot per count
+  unsigned short* qc = (unsigned short*)(sm + nb + 1);   // [nb] counts (<= nb <= 8192)
+  __shared__ int part[256];
+  const int bh = blockIdx.x, nchunks = nbp / 64, tid = threadIdx.x;
   const uint8_t* wc = wcnt + (size_t)bh * nchunks * nbp;
-  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+  for (int v = tid; v <= nb; v += 256) slot[v] = 0;
+  __syncthreads();
+  for (int i = tid; i < nb; i += 256) {
     int c = 0;
     for (int ch = 0; ch < nchunks; ++ch) c += wc[(size_t)ch * nbp + i];
     qc[i] = c;
     qcount[(size_t)bh * nbp + i] = c;
+    atomicAdd(&slot[c], 1);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-    const int ci = qc[i];
-    int r = 0;
-    for (int i2 = 0; i2 < nb; ++i2) {
-      const int c2 = qc[i2];
-      r += (c2 > ci) | ((c2 == ci) & (i2 < i));
-    }
-    order[(size_t)bh * nbp + r] = i;
+  // exclusive scan from count nb down to 0: thread t owns the bins v with nb - v in [t per, (t + 1) per)
+  const int per = (nb + 1 + 255) / 256;
+  int local = 0;
+  for (int u = tid * per; u < min(nb + 1, (tid + 1) * per); ++u) local += slot[nb - u];
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int t = 0; t < 256; ++t) { const int x = part[t]; part[t] = acc; acc += x; }
   }
+  __syncthreads();
+  int acc = part[tid];
+  for (int u = tid * per; u < min(nb + 1, (tid + 1) * per); ++u) {
+    const int x = slot[nb - u];
+    slot[nb - u] = acc;
+    acc += x;
+  }
+  __syncthreads();
+  for (int i = tid; i < nb; i += 256) order[(size_t)bh * nbp + atomicAdd(&slot[qc[i]], 1)] = i;
 }
 
 // Merge of the key-range splits: o = sum_s 2^(lse_s - lse) o_s / sum_s 2^(lse_s - lse), the
@@ -549,7 +583,7 @@ hipError_t launch_order(Shape s, const Workspace& ws, int sink_b0, int sink_b1, 
   if (ws.wcnt == nullptr || ws.qcount == nullptr || ws.order == nullptr) return hipSuccess;
   hipLaunchKernelGGL(count_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t,
                      ws.tau_i, ws.nb, ws.nbp, sink_b0, sink_b1, ws.wcnt);
-  hipLaunchKernelGGL(order_kernel, dim3(s.B * s.H), dim3(256), ws.nb * sizeof(int), stream, ws.wcnt, ws.nb, ws.nbp,
+  hipLaunchKernelGGL(order_kernel, dim3(s.B * s.H), dim3(256), (ws.nb + 1) * sizeof(int) + ws.nb * sizeof(unsigned short), stream, ws.wcnt, ws.nb, ws.nbp,
                      ws.qcount, ws.order);
   return hipGetLastError();
 }

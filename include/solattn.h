@@ -83,7 +83,7 @@ typedef enum {
  *                                      before its fused pass
  *   qcount   int32 [B][H][nbp]        Sol-Attn: exact blocks of each query block (their sum)
  *   order    int32 [B][H][nbp]        Sol-Attn: the head's nb query blocks by descending qcount
- *                                      (equal counts in block order), the order in which the
+ *                                      (equal counts in any order), the order in which the
  *                                      fused pass takes its work items; not a routing map: the
  *                                      fused pass still decides every block on chip
  *   q8, k8   uint8 [B][H][tp][128]    E4M3FN codes (Sol-Attn2)
