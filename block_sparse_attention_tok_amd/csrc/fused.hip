@@ -443,31 +443,32 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 // Stage 2's work order, first pass: the number of exact blocks of each query block within
 // each 64-block routing chunk, decided exactly as the fused pass decides them (the same FMA
 // sequence as proxy_dot, the same threshold test and sink rule), so that the counts are
-// the fused pass's own.  A workgroup takes 32 query blocks (their fp32 means read as
-// wave-uniform scalars), each wave chunks w, w + 4, ..., two at a time so that each scalar
-// mean feeds both; lane l scores key block 64 c + l.
+// the fused pass's own.  A workgroup takes 16 query blocks, their fp32 means staged in LDS
+// and read as broadcasts; each wave takes chunks w, w + 4, ..., two at a time so that each
+// mean read feeds both; lane l scores key block 64 c + l.
 __global__ __launch_bounds__(256) void count_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar_t,
                                                     const float* __restrict__ tau_i, int nb, int nbp, int sink_b0,
                                                     int sink_b1, uint8_t* __restrict__ wcnt) {
-  const int bh = blockIdx.y, i0 = blockIdx.x * 32;
+  __shared__ float4 qs[16][kDim / 4];
+  const int bh = blockIdx.y, i0 = blockIdx.x * 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nchunks = nbp / 64;
-  typedef const __attribute__((address_space(4))) float const_float;
-  const const_float* qs = (const const_float*)(qbar + ((size_t)bh * nbp + i0) * kDim);   // rows < nbp
+  for (int t = threadIdx.x; t < 16 * kDim / 4; t += 256)     // rows i0 .. i0 + 15 < nbp
+    qs[t >> 5][t & 31] = ((const float4*)(qbar + ((size_t)bh * nbp + i0) * kDim))[t];
+  __syncthreads();
   const float4* kt = (const float4*)kbar_t + (size_t)bh * 32 * nbp;
   for (int c = w; c < nchunks; c += 8) {                  // chunks c and c + 4 together
     const bool two = c + 4 < nchunks;                     // uniform
     const int j0 = 64 * c + lane, j1 = two ? j0 + 256 : j0;
-    float acc0[32], acc1[32];
+    float acc0[16], acc1[16];
 #pragma unroll
-    for (int q = 0; q < 32; ++q) acc0[q] = acc1[q] = 0.f;
+    for (int q = 0; q < 16; ++q) acc0[q] = acc1[q] = 0.f;
     for (int g = 0; g < 32; ++g) {
       const float4 kv0 = kt[(size_t)g * nbp + j0];
       const float4 kv1 = kt[(size_t)g * nbp + j1];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        const float4 qv = make_float4(qs[128 * q + 4 * g], qs[128 * q + 4 * g + 1], qs[128 * q + 4 * g + 2],
-                                      qs[128 * q + 4 * g + 3]);
+      for (int q = 0; q < 16; ++q) {
+        const float4 qv = qs[q][g];
         acc0[q] = __builtin_fmaf(qv.x, kv0.x, acc0[q]);
         acc0[q] = __builtin_fmaf(qv.y, kv0.y, acc0[q]);
         acc0[q] = __builtin_fmaf(qv.z, kv0.z, acc0[q]);
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(256) void count_kernel(const float* __restrict__ qb
     }
     int mine0 = 0, mine1 = 0;                            // lane q keeps query block i0 + q's counts
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const float tau = tau_i[(size_t)bh * nbp + i0 + q];
       const uint64_t w0 = exact_word(__ballot(acc0[q] * kScale > tau), c, nb, sink_b0, sink_b1);
       const uint64_t w1 = exact_word(__ballot(acc1[q] * kScale > tau), two ? c + 4 : c, nb, sink_b0, sink_b1);
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(256) void count_kernel(const float* __restrict__ qb
         mine1 = __builtin_popcountll(w1);
       }
     }
-    if (lane < 32 && i0 + lane < nb) {
+    if (lane < 16 && i0 + lane < nb) {
       wcnt[((size_t)bh * nchunks + c) * nbp + i0 + lane] = (uint8_t)mine0;
       if (two) wcnt[((size_t)bh * nchunks + c + 4) * nbp + i0 + lane] = (uint8_t)mine1;
     }
@@ -581,7 +582,7 @@ __global__ void zero_counter_kernel(unsigned long long* p) { *p = 0ull; }
 
 hipError_t launch_order(Shape s, const Workspace& ws, int sink_b0, int sink_b1, hipStream_t stream) {
   if (ws.wcnt == nullptr || ws.qcount == nullptr || ws.order == nullptr) return hipSuccess;
-  hipLaunchKernelGGL(count_kernel, dim3((ws.nb + 31) / 32, s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t,
+  hipLaunchKernelGGL(count_kernel, dim3((ws.nb + 15) / 16, s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t,
                      ws.tau_i, ws.nb, ws.nbp, sink_b0, sink_b1, ws.wcnt);
   hipLaunchKernelGGL(order_kernel, dim3(s.B * s.H), dim3(256), (ws.nb + 1) * sizeof(int) + ws.nb * sizeof(unsigned short), stream, ws.wcnt, ws.nb, ws.nbp,
                      ws.qcount, ws.order);
