@@ -492,8 +492,8 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
         kstat=view(L.kstat, torch.float32, (batch, heads, 2, 128)),
         kcov=view(L.kcov, torch.float32, (batch, heads, 128, 128)),
         wcnt=view(L.wcnt, torch.uint8, (batch, heads, nbp // 64, nbp)),
-        qcount=view(L.qcount, torch.int32, (batch, heads, nbp)),
-        order=view(L.order, torch.int32, (batch, heads, nbp)),
+        qcount=view(L.qcount, torch.int32, (batch, heads, max(1, L.kv_splits), nbp)),
+        order=view(L.order, torch.int32, (batch, heads, max(1, L.kv_splits), nbp)),
     )
     if variant in (SOL_VARIANT_SOL2, SOL_VARIANT_SOL2_PV8, SOL_VARIANT_SOL2_TRAIN):
         tp = nbp * 64

@@ -96,10 +96,12 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->kh = take(bh * tokens * kDim * 2);
     L->vh = take(bh * tokens * kDim * 2);
     // stage 2's work order: exact-block counts per routing chunk and query block, their
-    // sums, and each head's query blocks by descending count
+    // sums over each key split's chunks, and each (head, split)'s query blocks by descending
+    // count
+    const int64_t splits = effective_splits(tokens, kv_splits);
     L->wcnt = take(bh * (nbp / 64) * nbp);
-    L->qcount = take(bh * nbp * 4);
-    L->order = take(bh * nbp * 4);
+    L->qcount = take(bh * splits * nbp * 4);
+    L->order = take(bh * splits * nbp * 4);
   }
   const bool sol2 = variant == SOL_VARIANT_SOL2 || variant == SOL_VARIANT_SOL2_PV8 || variant == SOL_VARIANT_SOL2_TRAIN;
   if (sol2) {

@@ -111,10 +111,10 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   __shared__ int redo_s[2];
 
   // Work item order: query block fastest, then key split, then (batch, head), so the
-  // workgroups that run together on one XCD share a head and a key range.  Within a head
-  // the query blocks come by descending exact-block count (the order array): the longest
-  // items start first, and the workgroups that share an XCD's L2 at a time stream their
-  // selected tiles at similar rates.
+  // workgroups that run together on one XCD share a head and a key range.  Within a (head,
+  // split) the query blocks come by descending exact-block count over the split's key range
+  // (the order array): the longest items start first, and the workgroups that share an
+  // XCD's L2 at a time stream their selected tiles at similar rates.
   const int total = a.B * a.H * a.S * a.nb;
   const int item = xcd_remap(blockIdx.x, total);
   // The divisions run on the VALU; readfirstlane keeps the (uniform) indices in
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   const int rest = __builtin_amdgcn_readfirstlane(item / a.nb);
   const int split = __builtin_amdgcn_readfirstlane(rest % a.S);
   const int bh = __builtin_amdgcn_readfirstlane(rest / a.S);
-  const int i = a.order ? __builtin_amdgcn_readfirstlane(a.order[(size_t)bh * a.nbp + i0]) : i0;
+  const int i = a.order ? __builtin_amdgcn_readfirstlane(a.order[((size_t)bh * a.S + split) * a.nbp + i0]) : i0;
   const int h = __builtin_amdgcn_readfirstlane(bh % a.H), b = __builtin_amdgcn_readfirstlane(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -497,26 +497,29 @@ __global__ __launch_bounds__(256) void count_kernel(const float* __restrict__ qb
   }
 }
 
-// Second pass, one workgroup per (batch, head): each query block's total count and a
-// counting sort by descending count: a histogram of the counts, its scan from the largest
-// count down, and one slot per block taken with an LDS atomic, so that order[] is a
-// permutation of 0 .. nb - 1 sorted by descending count (blocks with equal counts in any
-// order: the order only schedules work, every block's result is the same).
-__global__ __launch_bounds__(256) void order_kernel(const uint8_t* __restrict__ wcnt, int nb, int nbp,
+// Second pass, one workgroup per (batch, head, key split): each query block's count over the
+// split's routing chunks and a counting sort by descending count: a histogram of the counts,
+// its scan from the largest count down, and one slot per block taken with an LDS atomic, so
+// that the split's order[] is a permutation of 0 .. nb - 1 sorted by descending count
+// (blocks with equal counts in any order: the order only schedules work, every block's
+// result is the same).
+__global__ __launch_bounds__(256) void order_kernel(const uint8_t* __restrict__ wcnt, int nb, int nbp, int cps,
                                                     int* __restrict__ qcount, int* __restrict__ order) {
   extern __shared__ int sm[];
   int* slot = sm;                                        // [nb + 1] histogram, then next free slot per count
   unsigned short* qc = (unsigned short*)(sm + nb + 1);   // [nb] counts (<= nb <= 8192)
   __shared__ int part[256];
-  const int bh = blockIdx.x, nchunks = nbp / 64, tid = threadIdx.x;
+  const int sp = blockIdx.x, S = gridDim.x, bh = blockIdx.y, nchunks = nbp / 64, tid = threadIdx.x;
+  const int c0 = sp * cps, c1 = min(nchunks, c0 + cps);
   const uint8_t* wc = wcnt + (size_t)bh * nchunks * nbp;
+  const size_t row = ((size_t)bh * S + sp) * nbp;
   for (int v = tid; v <= nb; v += 256) slot[v] = 0;
   __syncthreads();
   for (int i = tid; i < nb; i += 256) {
     int c = 0;
-    for (int ch = 0; ch < nchunks; ++ch) c += wc[(size_t)ch * nbp + i];
+    for (int ch = c0; ch < c1; ++ch) c += wc[(size_t)ch * nbp + i];
     qc[i] = c;
-    qcount[(size_t)bh * nbp + i] = c;
+    qcount[row + i] = c;
     atomicAdd(&slot[c], 1);
   }
   __syncthreads();
@@ -538,7 +541,7 @@ __global__ __launch_bounds__(256) void order_kernel(const uint8_t* __restrict__ 
     acc += x;
   }
   __syncthreads();
-  for (int i = tid; i < nb; i += 256) order[(size_t)bh * nbp + atomicAdd(&slot[qc[i]], 1)] = i;
+  for (int i = tid; i < nb; i += 256) order[row + atomicAdd(&slot[qc[i]], 1)] = i;
 }
 
 // Merge of the key-range splits: o = sum_s 2^(lse_s - lse) o_s / sum_s 2^(lse_s - lse), the
@@ -584,7 +587,9 @@ hipError_t launch_order(Shape s, const Workspace& ws, int sink_b0, int sink_b1, 
   if (ws.wcnt == nullptr || ws.qcount == nullptr || ws.order == nullptr) return hipSuccess;
   hipLaunchKernelGGL(count_kernel, dim3((ws.nb + 15) / 16, s.B * s.H), dim3(256), 0, stream, ws.qbar, ws.kbar_t,
                      ws.tau_i, ws.nb, ws.nbp, sink_b0, sink_b1, ws.wcnt);
-  hipLaunchKernelGGL(order_kernel, dim3(s.B * s.H), dim3(256), (ws.nb + 1) * sizeof(int) + ws.nb * sizeof(unsigned short), stream, ws.wcnt, ws.nb, ws.nbp,
+  const int nchunks = ws.nbp / 64, S = ws.kv_splits, cps = (nchunks + S - 1) / S;
+  hipLaunchKernelGGL(order_kernel, dim3(S, s.B * s.H), dim3(256),
+                     (ws.nb + 1) * sizeof(int) + ws.nb * sizeof(unsigned short), stream, ws.wcnt, ws.nb, ws.nbp, cps,
                      ws.qcount, ws.order);
   return hipGetLastError();
 }

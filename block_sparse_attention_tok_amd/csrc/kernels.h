@@ -59,8 +59,8 @@ struct Workspace {
   float* ofp;       // [B][H][tp][128] the Sol-Attn2 training forward's output rows in fp32
   float* kcovp;     // [B][H][8][128][128] per-slice centred key-mean outer products (exact threshold)
   uint8_t* wcnt;    // [B][H][nbp / 64][nbp] Sol-Attn: exact blocks per (routing chunk, query block)
-  int* qcount;      // [B][H][nbp] Sol-Attn: exact blocks per query block
-  int* order;       // [B][H][nbp] Sol-Attn: the head's query blocks by descending qcount (stage 2's work order)
+  int* qcount;      // [B][H][S][nbp] Sol-Attn: exact blocks per query block within each key split
+  int* order;       // [B][H][S][nbp] Sol-Attn: query blocks by descending qcount per (head, split) (stage 2's work order)
 };
 
 struct Shape {

@@ -81,11 +81,12 @@ typedef enum {
  *   wcnt     uint8 [B][H][nbp/64][nbp] Sol-Attn: exact blocks of each query block within each
  *                                      64-block routing chunk (sink included), written by stage 2
  *                                      before its fused pass
- *   qcount   int32 [B][H][nbp]        Sol-Attn: exact blocks of each query block (their sum)
- *   order    int32 [B][H][nbp]        Sol-Attn: the head's nb query blocks by descending qcount
- *                                      (equal counts in any order), the order in which the
- *                                      fused pass takes its work items; not a routing map: the
- *                                      fused pass still decides every block on chip
+ *   qcount   int32 [B][H][S][nbp]     Sol-Attn: exact blocks of each query block among the
+ *                                      routing chunks of key split s (S = kv_splits)
+ *   order    int32 [B][H][S][nbp]     Sol-Attn: the nb query blocks by descending qcount per
+ *                                      (head, split) (equal counts in any order), the order in
+ *                                      which the fused pass takes its work items; not a routing
+ *                                      map: the fused pass still decides every block on chip
  *   q8, k8   uint8 [B][H][tp][128]    E4M3FN codes (Sol-Attn2)
  *   qscale, kscale float [B][H][nbp]  E4M3 block scales (Sol-Attn2)
  *   qhat     float [B][H][128]        mean-query direction (Sol-Attn2)

@@ -75,20 +75,29 @@ def compare_out(gpu: np.ndarray, ref: np.ndarray, rel=REL_L2_BF16, max_abs=MAX_A
     return err, mx
 
 
-def order_check(variant, ws, gsel, B, N, H):
-    """Sol-Attn stage 2's work order: qcount is each query block's number of exact blocks,
-    counted by the same decision procedure as the fused pass, so it equals the row sums of
-    the masks that pass exported, exactly; order lists each head's blocks by descending
-    count (equal counts in any order) and is a permutation, so every block is computed
-    once."""
+def order_check(variant, ws, gsel, B, N, H, kv_splits=0):
+    """Sol-Attn stage 2's work order: qcount is each query block's number of exact blocks
+    within each key split, counted by the same decision procedure as the fused pass, so over
+    the splits it sums to the row sums of the masks that pass exported, exactly; each (head,
+    split)'s order lists the blocks by descending count (equal counts in any order) and is a
+    permutation, so every block is computed once per split."""
     import block_sparse_attention_tok_amd as bsa
-    views = bsa.workspace_views(variant, ws, B, N, H)
-    nb = views["nb"]
-    qcount = views["qcount"].cpu().numpy()[..., :nb]
-    order = views["order"].cpu().numpy()[..., :nb]
-    np.testing.assert_array_equal(qcount, gsel.sum(-1))
+    from block_sparse_attention_tok_amd import _lib
+    L = _lib.workspace_layout(variant, B, N, H, kv_splits=kv_splits) if kv_splits else None
+    views = bsa.workspace_views(variant, ws, B, N, H) if L is None else None
+    if views is None:
+        nbp, S = L.nbp, L.kv_splits
+        qc_t = ws[L.qcount:L.qcount + B * H * S * nbp * 4].view(torch.int32).view(B, H, S, nbp)
+        or_t = ws[L.order:L.order + B * H * S * nbp * 4].view(torch.int32).view(B, H, S, nbp)
+        nb = L.nb
+    else:
+        qc_t, or_t, nb = views["qcount"], views["order"], views["nb"]
+    qcount = qc_t.cpu().numpy()[..., :nb]
+    order = or_t.cpu().numpy()[..., :nb]
+    np.testing.assert_array_equal(qcount.sum(2), gsel.sum(-1))
     for b in range(B):
         for h in range(H):
-            np.testing.assert_array_equal(np.sort(order[b, h]), np.arange(nb))
-            c = qcount[b, h][order[b, h]]
-            assert (np.diff(c) <= 0).all(), "order is not by descending count"
+            for sp in range(qcount.shape[2]):
+                np.testing.assert_array_equal(np.sort(order[b, h, sp]), np.arange(nb))
+                c = qcount[b, h, sp][order[b, h, sp]]
+                assert (np.diff(c) <= 0).all(), "order is not by descending count"

@@ -134,9 +134,9 @@ def test_work_order_arrays(L, B, N, H):
     from block_sparse_attention_tok_amd import _lib
     for variant in (1, 4):
         l = _lib.workspace_layout(variant, B, N, H)
-        bh, nbp = B * H, l.nbp
+        bh, nbp, S = B * H, l.nbp, l.kv_splits
         assert l.wcnt >= 0 and l.qcount - l.wcnt >= bh * (nbp // 64) * nbp
-        assert l.order - l.qcount >= bh * nbp * 4 and l.total_bytes - l.order >= bh * nbp * 4
+        assert l.order - l.qcount >= bh * S * nbp * 4 and l.total_bytes - l.order >= bh * S * nbp * 4
         assert l.wcnt % 256 == 0 and l.qcount % 256 == 0 and l.order % 256 == 0
     for variant in (2, 3, 5):
         l = _lib.workspace_layout(variant, B, N, H)

@@ -345,6 +345,11 @@ def test_kv_splits_with_batch_sink_and_ragged_tail():
     mask_check(gsel, ref["sel"], ref["s_hat"], ref["tau_i"], forced)
     want = np.concatenate([oracle_rows(q, k, v, b, h, i, gsel[b, h, i])
                            for b in range(B) for h in range(H) for i in range(nb)])
+    for kv in (2, 4):
+        # each (head, split) gets its own order, by the counts within the split's key range
+        _, m_kv, ws_kv = bsa.debug_routing(1, qg, kg, vg, tau, "diag", s0, st, kv_splits=kv)
+        assert torch.equal(m_kv, masks)
+        order_check(1, ws_kv, gsel, B, N, H, kv_splits=kv)
     outs = {}
     for kv in (1, 2, 4):
         out = bsa.sol_attn(qg, kg, vg, tau, "diag", s0, st, kv_splits=kv)
