@@ -44,7 +44,7 @@ class WsLayout(ctypes.Structure):
         "q8", "k8", "qscale", "kscale", "qhat", "gk", "gv", "glogn", "ghi", "qanc", "kv_splits", "opart", "olse",
         "sel", "tmu", "tnu", "tlz", "v8t", "vbmax", "vscale", "lse", "mrow", "mcol", "ld", "dkbar", "dvbar",
         "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz", "aextra", "gdk", "gdv", "ofp", "kcovp",
-        "wcnt", "qcount", "order")]
+        "wcnt", "qcount", "order", "bqord", "bkord")]
 
 
 class SolAttnError(RuntimeError):
@@ -521,6 +521,8 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
             ld=view(L.ld, torch.float32, (batch, heads, tp, 2)),
             dkbar=view(L.dkbar, torch.float32, (batch, heads, nbp, 128)),
             dvbar=view(L.dvbar, torch.float32, (batch, heads, nbp, 128)),
+            bqord=view(L.bqord, torch.int32, (batch, heads, nbp)),
+            bkord=view(L.bkord, torch.int32, (batch, heads, nbp)),
         )
     if variant == SOL_VARIANT_SOL2_TRAIN:
         tp = nbp * 64
@@ -540,6 +542,8 @@ def workspace_views(variant: int, workspace: torch.Tensor, batch: int, tokens: i
             aextra=view(L.aextra, torch.float32, (batch, heads, nbp, 2, 128)),
             gdk=view(L.gdk, torch.float32, (batch, heads, nbp, 2, 128)),
             gdv=view(L.gdv, torch.float32, (batch, heads, nbp, 2, 128)),
+            bqord=view(L.bqord, torch.int32, (batch, heads, nbp)),
+            bkord=view(L.bkord, torch.int32, (batch, heads, nbp)),
         )
     if variant == SOL_VARIANT_SOL2_PV8:
         tp = nbp * 64

@@ -152,6 +152,8 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->aextra = take(bh * 2 * nbp * kDim * 4);
     L->gdk = take(bh * nbp * 2 * kDim * 4);
     L->gdv = take(bh * nbp * 2 * kDim * 4);
+    L->bqord = take(bh * nbp * 4);
+    L->bkord = take(bh * nbp * 4);
   }
   // forward state for the backward, and backward scratch (Sol-Attn training)
   if (variant == SOL_VARIANT_SOL1_TRAIN) {
@@ -162,6 +164,8 @@ int layout(int variant, int64_t batch, int64_t tokens, int64_t heads, int64_t he
     L->ld = take(bh * tp * 2 * 4);
     L->dkbar = take(bh * nbp * kDim * 4);
     L->dvbar = take(bh * nbp * kDim * 4);
+    L->bqord = take(bh * nbp * 4);
+    L->bkord = take(bh * nbp * 4);
   }
   L->total_bytes = off;
   return SOL_OK;
@@ -224,6 +228,8 @@ solattn::Workspace resolve(const sol_ws_layout& L, void* ws) {
   w.wcnt = (uint8_t*)at(L.wcnt);
   w.qcount = (int*)at(L.qcount);
   w.order = (int*)at(L.order);
+  w.bqord = (int*)at(L.bqord);
+  w.bkord = (int*)at(L.bkord);
   return w;
 }
 

@@ -62,6 +62,10 @@ struct BwdArgs {
   int sol2;
   const uint64_t* ghi; const float* gdk; const float* gdv;
   const float* dlam; const float* tmu; const float* aextra;
+  // work orders (NULL = block order): query blocks by descending number of exact key blocks
+  // (the dQ pass) and key blocks by descending number of query blocks that select them (the
+  // exact dK / dV pass), [B][H][nbp] each
+  const int* qord; const int* kord;
 };
 
 // Slot swizzle of a 64 x 256-byte tile that is read both by rows (16 consecutive rows,
@@ -231,8 +235,9 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
     c = __builtin_amdgcn_readfirstlane(rest % nchunks);
     bh = __builtin_amdgcn_readfirstlane(rest / nchunks);
   } else {
-    jb = __builtin_amdgcn_readfirstlane(item % a.nb);
+    const int j0 = __builtin_amdgcn_readfirstlane(item % a.nb);
     bh = __builtin_amdgcn_readfirstlane(item / a.nb);
+    jb = a.kord ? __builtin_amdgcn_readfirstlane(a.kord[(size_t)bh * a.nbp + j0]) : j0;
   }
   const int h = __builtin_amdgcn_readfirstlane(bh % a.H), b = __builtin_amdgcn_readfirstlane(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
@@ -427,8 +432,9 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
   const int nchunks = a.nbp / 64;
   const int total = a.B * a.H * a.nb;
   const int item = xcd_remap(blockIdx.x, total);
-  const int i = __builtin_amdgcn_readfirstlane(item % a.nb);
+  const int i0 = __builtin_amdgcn_readfirstlane(item % a.nb);
   const int bh = __builtin_amdgcn_readfirstlane(item / a.nb);
+  const int i = a.qord ? __builtin_amdgcn_readfirstlane(a.qord[(size_t)bh * a.nbp + i0]) : i0;
   const int h = __builtin_amdgcn_readfirstlane(bh % a.H), b = __builtin_amdgcn_readfirstlane(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, kg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1000,6 +1006,29 @@ __global__ __launch_bounds__(128, 1) void bwd2_group_grad_kernel(Bwd2Args a) {
     }
 }
 
+// Work orders of the exact-token passes, one workgroup per (batch, head) and kind: y = 0 sorts
+// the query blocks by their number of exact key blocks (popcounts of the routing rows), y = 1
+// the key blocks by how many query blocks select them (popcounts of the transposed rows), both
+// descending, so that the longest work items start first and the workgroups that share an
+// XCD's L2 stream their tiles at similar rates.  The orders only schedule work.
+__global__ __launch_bounds__(256) void bwd_order_kernel(const uint64_t* __restrict__ mrow,
+                                                        const uint64_t* __restrict__ mcol, int nb, int nbw,
+                                                        int nbp, int* __restrict__ qord, int* __restrict__ kord) {
+  extern __shared__ int sm[];
+  int* slot = sm;                                        // [nb + 1]
+  unsigned short* qc = (unsigned short*)(sm + nb + 1);   // [nb] counts (<= nb <= 8192)
+  __shared__ int part[256];
+  const int bh = blockIdx.x, kind = blockIdx.y;
+  const uint64_t* words = (kind == 0 ? mrow : mcol) + (size_t)bh * nb * nbw;
+  for (int i = threadIdx.x; i < nb; i += 256) {
+    int c = 0;
+    for (int cc = 0; cc < nbw; ++cc) c += __builtin_popcountll(words[(size_t)i * nbw + cc]);
+    qc[i] = c;
+  }
+  __syncthreads();
+  sort_desc_counts(qc, slot, part, nb, (kind == 0 ? qord : kord) + (size_t)bh * nbp);
+}
+
 }  // namespace
 
 hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,
@@ -1018,6 +1047,7 @@ hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.dkbar = ws.dkbar; a.dvbar = ws.dvbar;
   a.sol2 = 0;
   a.ghi = nullptr; a.gdk = nullptr; a.gdv = nullptr; a.dlam = nullptr; a.tmu = nullptr; a.aextra = nullptr;
+  a.qord = ws.bqord; a.kord = ws.bkord;
   // pooled keys: enough (chunk, query range) workgroups to fill the chip twice over
   const int bhc = s.B * s.H * nchunks;
   int nrange = (2048 + bhc - 1) / bhc;
@@ -1036,6 +1066,12 @@ hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t*
   const size_t nt = (size_t)s.B * s.H * ws.nb * nchunks;
   hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.qord != nullptr && a.kord != nullptr) {
+    hipLaunchKernelGGL(bwd_order_kernel, dim3(s.B * s.H, 2), dim3(256),
+                       (ws.nb + 1) * sizeof(int) + ws.nb * sizeof(unsigned short), stream, ws.mrow, ws.mcol, ws.nb,
+                       nchunks, ws.nbp, ws.bqord, ws.bkord);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(bwd_kv_kernel<true>, dim3(bhc * a.nrange), dim3(128), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_kv_kernel<false>, dim3(s.B * s.H * ws.nb), dim3(128), 0, stream, a);
@@ -1078,6 +1114,7 @@ hipError_t launch_backward2(const uint16_t* q, const uint16_t* k, const uint16_t
   a.nrange = 1; a.bpr = ws.nb;
   a.sol2 = 1;
   a.ghi = ws.ghi; a.gdk = ws.gdk; a.gdv = ws.gdv; a.dlam = ws.dlam; a.tmu = ws.tmu; a.aextra = ws.aextra;
+  a.qord = ws.bqord; a.kord = ws.bkord;
 
   const size_t rows16 = (size_t)s.B * s.N * s.H * 16;
   const int nt = (ws.nb + 31) / 32;
@@ -1088,6 +1125,12 @@ hipError_t launch_backward2(const uint16_t* q, const uint16_t* k, const uint16_t
   const size_t ntr = (size_t)bhn * ws.nb * nchunks;
   hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)((ntr + 255) / 256)), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.qord != nullptr && a.kord != nullptr) {
+    hipLaunchKernelGGL(bwd_order_kernel, dim3(bhn, 2), dim3(256),
+                       (ws.nb + 1) * sizeof(int) + ws.nb * sizeof(unsigned short), stream, ws.sel, ws.mcol, ws.nb,
+                       nchunks, ws.nbp, ws.bqord, ws.bkord);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(bwd2_anchor_kernel, dim3(ws.nbp, bhn), dim3(256), 0, stream, t);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd2_tail_dq_kernel, dim3(bhn * nt), dim3(128), 0, stream, t);

@@ -48,6 +48,43 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Counting sort by descending count for one workgroup of 256 threads: qc[0 .. nb) in LDS holds
+// counts in [0, nb]; out[rank] receives each index, larger counts first (equal counts in any
+// order: the orders built with it only schedule work).  slot (nb + 1 ints) and part (256 ints)
+// are LDS scratch.  A histogram of the counts, its exclusive scan from the largest count down
+// (each thread scans a contiguous run of bins, one thread scans the 256 run totals), then one
+// slot per index taken with an LDS atomic.
+__device__ __forceinline__ void sort_desc_counts(const unsigned short* qc, int* slot, int* part, int nb, int* out) {
+  const int tid = threadIdx.x;
+  for (int v = tid; v <= nb; v += 256) slot[v] = 0;
+  __syncthreads();
+  for (int i = tid; i < nb; i += 256) atomicAdd(&slot[qc[i]], 1);
+  __syncthreads();
+  const int per = (nb + 1 + 255) / 256;
+  const int u0 = tid * per, u1 = min(nb + 1, (tid + 1) * per);
+  int local = 0;
+  for (int u = u0; u < u1; ++u) local += slot[nb - u];
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int x = part[t];
+      part[t] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  int acc = part[tid];
+  for (int u = u0; u < u1; ++u) {
+    const int x = slot[nb - u];
+    slot[nb - u] = acc;
+    acc += x;
+  }
+  __syncthreads();
+  for (int i = tid; i < nb; i += 256) out[atomicAdd(&slot[qc[i]], 1)] = i;
+}
+
 // Map a hardware workgroup id to a logical work item so that each of the 8
 // XCDs (which receive workgroups round-robin) walks a contiguous range of the
 // logical order; keeps a head's pooled keys and nearby KV blocks in one L2.

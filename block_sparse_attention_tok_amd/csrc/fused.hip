@@ -506,42 +506,21 @@ __global__ __launch_bounds__(256) void count_kernel(const float* __restrict__ qb
 __global__ __launch_bounds__(256) void order_kernel(const uint8_t* __restrict__ wcnt, int nb, int nbp, int cps,
                                                     int* __restrict__ qcount, int* __restrict__ order) {
   extern __shared__ int sm[];
-  int* slot = sm;                                        // [nb + 1] histogram, then next free slot per count
+  int* slot = sm;                                        // [nb + 1]
   unsigned short* qc = (unsigned short*)(sm + nb + 1);   // [nb] counts (<= nb <= 8192)
   __shared__ int part[256];
   const int sp = blockIdx.x, S = gridDim.x, bh = blockIdx.y, nchunks = nbp / 64, tid = threadIdx.x;
   const int c0 = sp * cps, c1 = min(nchunks, c0 + cps);
   const uint8_t* wc = wcnt + (size_t)bh * nchunks * nbp;
   const size_t row = ((size_t)bh * S + sp) * nbp;
-  for (int v = tid; v <= nb; v += 256) slot[v] = 0;
-  __syncthreads();
   for (int i = tid; i < nb; i += 256) {
     int c = 0;
     for (int ch = c0; ch < c1; ++ch) c += wc[(size_t)ch * nbp + i];
     qc[i] = c;
     qcount[row + i] = c;
-    atomicAdd(&slot[c], 1);
   }
   __syncthreads();
-  // exclusive scan from count nb down to 0: thread t owns the bins v with nb - v in [t per, (t + 1) per)
-  const int per = (nb + 1 + 255) / 256;
-  int local = 0;
-  for (int u = tid * per; u < min(nb + 1, (tid + 1) * per); ++u) local += slot[nb - u];
-  part[tid] = local;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int t = 0; t < 256; ++t) { const int x = part[t]; part[t] = acc; acc += x; }
-  }
-  __syncthreads();
-  int acc = part[tid];
-  for (int u = tid * per; u < min(nb + 1, (tid + 1) * per); ++u) {
-    const int x = slot[nb - u];
-    slot[nb - u] = acc;
-    acc += x;
-  }
-  __syncthreads();
-  for (int i = tid; i < nb; i += 256) order[row + atomicAdd(&slot[qc[i]], 1)] = i;
+  sort_desc_counts(qc, slot, part, nb, order + row);
 }
 
 // Merge of the key-range splits: o = sum_s 2^(lse_s - lse) o_s / sum_s 2^(lse_s - lse), the

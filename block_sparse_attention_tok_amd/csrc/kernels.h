@@ -61,6 +61,8 @@ struct Workspace {
   uint8_t* wcnt;    // [B][H][nbp / 64][nbp] Sol-Attn: exact blocks per (routing chunk, query block)
   int* qcount;      // [B][H][S][nbp] Sol-Attn: exact blocks per query block within each key split
   int* order;       // [B][H][S][nbp] Sol-Attn: query blocks by descending qcount per (head, split) (stage 2's work order)
+  int* bqord;       // [B][H][nbp] training: query blocks by descending exact-block count (dQ pass order)
+  int* bkord;       // [B][H][nbp] training: key blocks by descending selecting-block count (dK / dV pass order)
 };
 
 struct Shape {

@@ -116,6 +116,10 @@ typedef enum {
  *   ld       float [B][H][tp][2]      (lse, dO . O) per query row (backward scratch)
  *   dkbar, dvbar float [B][H][nbp][128] gradients w.r.t. the pooled keys (times 1/sqrt(d))
  *                                      and pooled values (backward scratch)
+ *   bqord, bkord int32 [B][H][nbp]   the backward's work orders (scratch; both training
+ *                                      layouts): query blocks by descending number of exact key
+ *                                      blocks, key blocks by descending number of query blocks
+ *                                      that select them (equal counts in any order)
  * SOL_VARIANT_SOL2_TRAIN (the Sol-Attn2 arrays above, then): sel uint64 [B][H][nb][nbp/64]
  * (the routing words the forward's exact pass decided, bit j % 64 of word j / 64 set iff
  * block j is exact for query block i, sink included), lse and ld as for Sol-Attn
@@ -147,6 +151,7 @@ typedef struct {
     int64_t qd, kd, dlam, qab, dmub, dnub, alz, aextra, gdk, gdv;
     int64_t ofp, kcovp;
     int64_t wcnt, qcount, order;
+    int64_t bqord, bkord;
 } sol_ws_layout;
 
 /* Static description of a status code (never NULL). */

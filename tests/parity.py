@@ -101,3 +101,18 @@ def order_check(variant, ws, gsel, B, N, H, kv_splits=0):
                 np.testing.assert_array_equal(np.sort(order[b, h, sp]), np.arange(nb))
                 c = qcount[b, h, sp][order[b, h, sp]]
                 assert (np.diff(c) <= 0).all(), "order is not by descending count"
+
+
+def bwd_order_check(views, gsel):
+    """The backward's work orders: bqord lists each head's query blocks by descending number
+    of exact key blocks (row sums of the forward's masks), bkord its key blocks by descending
+    number of query blocks that select them (column sums); both are permutations, so every
+    query block's dQ and every key block's dK / dV is computed once."""
+    B, H, nb, _ = gsel.shape
+    rows, cols = gsel.sum(-1), gsel.sum(-2)
+    for name, cnt in (("bqord", rows), ("bkord", cols)):
+        order = views[name].cpu().numpy()[..., :nb]
+        for b in range(B):
+            for h in range(H):
+                np.testing.assert_array_equal(np.sort(order[b, h]), np.arange(nb), err_msg=name)
+                assert (np.diff(cnt[b, h][order[b, h]]) <= 0).all(), f"{name} is not by descending count"

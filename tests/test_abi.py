@@ -112,7 +112,7 @@ def test_training_layout_extends_the_sol_attn_layout(L, B, N, H):
     from block_sparse_attention_tok_amd import _lib
     l1 = _lib.workspace_layout(1, B, N, H)
     l4 = _lib.workspace_layout(4, B, N, H)
-    extra = ("lse", "mrow", "mcol", "ld", "dkbar", "dvbar")
+    extra = ("lse", "mrow", "mcol", "ld", "dkbar", "dvbar", "bqord", "bkord")
     for name, _ in _lib.WsLayout._fields_:
         if name in ("total_bytes",) + extra:
             continue
@@ -125,6 +125,8 @@ def test_training_layout_extends_the_sol_attn_layout(L, B, N, H):
     assert l4.mrow - l4.lse >= B * H * tp * 4
     assert l4.mcol - l4.mrow >= B * H * l4.nb * nbw * 8
     assert l4.dvbar - l4.dkbar >= B * H * l4.nbp * 128 * 4
+    assert l4.bqord - l4.dvbar >= B * H * l4.nbp * 128 * 4
+    assert l4.bkord - l4.bqord >= B * H * l4.nbp * 4 and l4.total_bytes - l4.bkord >= B * H * l4.nbp * 4
 
 
 @pytest.mark.parametrize("B,N,H", [(1, 1024, 2), (1, 14040, 12), (2, 333, 3), (1, 32768, 32)])
@@ -152,7 +154,7 @@ def test_sol2_training_layout_extends_the_sol2_layout(L, B, N, H):
     l2 = _lib.workspace_layout(2, B, N, H)
     l5 = _lib.workspace_layout(5, B, N, H)
     extra = ("sel", "lse", "ofp", "mcol", "ld", "kh", "vh", "qd", "kd", "dlam", "qab", "dmub", "dnub", "alz",
-             "aextra", "gdk", "gdv")
+             "aextra", "gdk", "gdv", "bqord", "bkord")
     for name, _ in _lib.WsLayout._fields_:
         if name in ("total_bytes",) + extra:
             continue
@@ -167,7 +169,7 @@ def test_sol2_training_layout_extends_the_sol2_layout(L, B, N, H):
     need = dict(sel=bh * nb * (nbp // 64) * 8, lse=bh * tp * 4, ofp=bh * tp * 512, mcol=bh * nb * (nbp // 64) * 8, ld=bh * tp * 8, kh=bh * N * 256, vh=bh * N * 256,
                 qd=bh * N * 256, kd=bh * N * 256, dlam=bh * tp * 4, qab=bh * 2 * nbp * 256,
                 dmub=bh * 2 * nbp * 256, dnub=bh * 2 * nbp * 256, alz=bh * 2 * nbp * 8, aextra=bh * 2 * nbp * 512,
-                gdk=bh * 2 * nbp * 512, gdv=bh * 2 * nbp * 512)
+                gdk=bh * 2 * nbp * 512, gdv=bh * 2 * nbp * 512, bqord=bh * nbp * 4, bkord=bh * nbp * 4)
     for a, b in zip(extra, offs[1:]):
         assert b - getattr(l5, a) >= need[a], a
 

@@ -17,7 +17,7 @@ import torch
 import block_sparse_attention_tok_amd as bsa
 from oracle import sol_attn as sa
 from oracle import sol_attn_bwd as sb
-from parity import mask_check, say, to_gpu
+from parity import bwd_order_check, mask_check, say, to_gpu
 from workloads import block_offset_tensor, long_sink, operator_bench, wan_dit
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +68,7 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, seed=0):
     forced = np.zeros((B, H, nb, nb), dtype=bool)
     forced[..., sa.sink_block_mask(N, sink_start, sink_tokens)] = True
     mask_check(gsel, ref["sel"], ref["s_hat"], ref["tau_i"], forced)
+    bwd_order_check(views, gsel)
     lse = views["lse"].cpu().numpy()
     errs = []
     for b in range(B):

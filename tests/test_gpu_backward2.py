@@ -24,7 +24,7 @@ import block_sparse_attention_tok_amd as bsa
 from oracle import sol_attn as sa
 from oracle import sol_attn2 as s2
 from oracle import sol_attn2_bwd as sb2
-from parity import say, to_gpu
+from parity import bwd_order_check, say, to_gpu
 from workloads import block_offset_tensor, long_sink, operator_bench, wan_dit
 
 pytestmark = pytest.mark.gpu
@@ -84,6 +84,7 @@ def run_case(q, k, v, tau, sink_start=None, sink_tokens=0, heads=None, seed=0, t
     torch.cuda.synchronize()
     assert torch.equal(out, plain), "the training forward changed the output"
     gsel, gmasks, views = _state(ws, B, N, H)
+    bwd_order_check(views, gsel)
     lse = views["lse"].cpu().numpy()
     errs = []
     for b in range(B):
