@@ -77,7 +77,7 @@ struct DmaOffsetsD {
   uint32_t o[4];
 };
 
-// Wave w, instruction n fills rows 32 w + 4 n + lane / 16, slot lane % 16 (see dma_tile).
+// Wave w, instruction n fills rows 32 w + 4 n + lane / 16, slot lane % 16 (see dma_tile_asm).
 __device__ __forceinline__ DmaOffsetsD dma_offsets_d(uint32_t row_bytes, int w, int lane) {
   const int row = 32 * w + (lane >> 4);
   DmaOffsetsD d;
@@ -86,11 +86,53 @@ __device__ __forceinline__ DmaOffsetsD dma_offsets_d(uint32_t row_bytes, int w, 
   return d;
 }
 
-__device__ __forceinline__ void dma_tile_d(unsigned char* lds, __amdgpu_buffer_rsrc_t rsrc, uint32_t tile_off,
-                                           uint32_t row_bytes, const DmaOffsetsD& off, int w) {
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource as four SGPRs (the form an asm operand takes): base, stride 0,
+// num_records = bytes, raw-buffer flags (as make_rsrc).
+__device__ __forceinline__ intx4 rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return intx4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
+               (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
+               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// DMA of wave w's half of a 64 x 128 bf16 tile into LDS: eight buffer_load_dwordx4 ... lds
+// (1 KB each, rows and slots as dma_offsets_d), rows past the resource's end reading as
+// zeros.  Issued from asm: the tile loops read one buffer while the DMA fills the other, the
+// buffer chosen at run time, and for a DMA that it issues itself the compiler cannot tell the
+// two apart and waits for the DMA before every LDS read of the tile.  These asm loads are not
+// tracked by the compiler: every read of the buffer they fill is ordered by the loop's own
+// vmcnt wait and barrier.  The asm writes no register (M0 and SCC are clobbered) and carries
+// its hazard padding: s_nop 4 for a resource or base written through v_readfirstlane just
+// before, s_nop 0 between each M0 write and the load that uses it.
+__device__ __forceinline__ void dma_tile_asm(unsigned char* lds, intx4 rsrc, uint32_t tile_off, uint32_t row_bytes,
+                                             const DmaOffsetsD& off, int w) {
+  uint32_t vo[8];
 #pragma unroll
-  for (int n = 0; n < 8; ++n)
-    dma16_buf(rsrc, off.o[n & 3] + tile_off + (uint32_t)n * 4 * row_bytes, 0, lds + (w * 8 + n) * 1024);
+  for (int n = 0; n < 8; ++n) vo[n] = off.o[n & 3] + tile_off + (uint32_t)n * 4 * row_bytes;
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(lds + w * 8 * 1024));
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds\n\t"
+      "s_add_u32 m0, %1, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %0, 0 offen lds\n\t"
+      "s_add_u32 m0, %1, 0x800\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %0, 0 offen lds\n\t"
+      "s_add_u32 m0, %1, 0xc00\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %0, 0 offen lds\n\t"
+      "s_add_u32 m0, %1, 0x1000\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %0, 0 offen lds\n\t"
+      "s_add_u32 m0, %1, 0x1400\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %0, 0 offen lds\n\t"
+      "s_add_u32 m0, %1, 0x1800\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %0, 0 offen lds\n\t"
+      "s_add_u32 m0, %1, 0x1c00\n\ts_nop 0\n\tbuffer_load_dwordx4 %9, %0, 0 offen lds"
+      ::"s"(rsrc), "s"(base), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]), "v"(vo[5]), "v"(vo[6]),
+        "v"(vo[7])
+      : "memory", "m0", "scc");
+}
+
+// One 16-byte-per-lane load into LDS (dma16_buf) issued from asm, for the same reason.
+__device__ __forceinline__ void dma16_asm(intx4 rsrc, uint32_t voffset, unsigned char* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds"
+               ::"s"(rsrc), "s"(base), "v"(voffset)
+               : "memory", "m0");
 }
 
 // Row-read offsets: A operand row 32 mt + l32 (mt adds 32 rows, same swizzle), k-step ks
@@ -146,6 +188,30 @@ __device__ __forceinline__ void row_product(const unsigned char* L, const int (&
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, breg[ks], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, breg[ks], s1, 0, 0, 0);
   }
+}
+
+// Scheduling pattern for a run of kN MFMAs that take kR LDS reads each: every MFMA's reads
+// are issued kAhead MFMAs before it, so that the LDS latency overlaps the products (left to
+// itself the scheduler places each read just before its MFMA and waits for it).  Placed
+// after the products it orders, in the same basic block; the closing sched_barrier keeps
+// the instructions after it out of the pattern.
+template <int kN, int kR, int kAhead>
+__device__ __forceinline__ void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kR * kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < kN - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kR, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Keeps a loop-carried accumulator in AGPRs, where its MFMAs read and write it: without the
+// pin the register allocator keeps it in VGPRs and copies it to AGPRs and back every tile.
+__device__ __forceinline__ void pin_agpr(floatx16 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+a"(acc[mt]));
 }
 
 __device__ __forceinline__ void load_row_frags(const uint16_t* row, bf16x8 (&r)[8], int kg) {
@@ -303,11 +369,11 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
   const DmaOffsetsD doff = dma_offsets_d(row_bytes, w, lane);
   auto issue = [&](int i, int buf) {
     const uint32_t toff = (uint32_t)i * 64 * row_bytes;
-    dma_tile_d(Ql[buf], make_rsrc(uniform_ptr(a.q + head_off), span_in), toff, row_bytes, doff, w);
-    dma_tile_d(Gl[buf], make_rsrc(uniform_ptr(a.dout + head_off), span_in), toff, row_bytes, doff, w);
+    dma_tile_asm(Ql[buf], rsrc4(a.q + head_off, span_in), toff, row_bytes, doff, w);
+    dma_tile_asm(Gl[buf], rsrc4(a.dout + head_off, span_in), toff, row_bytes, doff, w);
     if (w == 0)   // 64 (lse, D) pairs = 512 bytes; lanes 32..63 repeat lanes 0..31 into the copy half
-      dma16_buf(make_rsrc(uniform_ptr(a.ld + (size_t)bh * a.tp * 2), (uint32_t)a.tp * 8),
-                (uint32_t)i * 512 + (lane & 31) * 16, 0, (unsigned char*)St[buf]);
+      dma16_asm(rsrc4(a.ld + (size_t)bh * a.tp * 2, (uint32_t)a.tp * 8), (uint32_t)i * 512 + (lane & 31) * 16,
+                (unsigned char*)St[buf]);
   };
 
   int roff[8];
@@ -336,6 +402,7 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
     floatx16 s0, s1, d0, d1;
     row_product(Q, roff, kreg, s0, s1);                      // S = Q K^T (rows = queries)
     row_product(G, roff, vreg, d0, d1);                      // dP = dO V^T
+    sched_reads_ahead<32, 1, 4>();
     bf16x8 pp[4], pd[4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -361,6 +428,9 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
     }
     tr_product(dvT, G, toff, pp);                            // dV^T += dO^T P
     tr_product(dkT, Q, toff, pd);                            // dK^T += Q^T dS
+    sched_reads_ahead<32, 2, 4>();
+    pin_agpr(dvT);
+    pin_agpr(dkT);
     buf ^= 1;
     cur = nxt;
   }
@@ -468,12 +538,12 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
   auto issue = [&](int code, int buf) {
     if (code < 0) {
       const uint32_t toff = (uint32_t)(-code - 1) * 64 * row_bytes;
-      dma_tile_d(Kl[buf], make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool), toff, row_bytes, doff, w);
-      dma_tile_d(Vl[buf], make_rsrc(uniform_ptr(a.vbar_h + pooled_head), span_pool), toff, row_bytes, doff, w);
+      dma_tile_asm(Kl[buf], rsrc4(a.kbar_h + pooled_head, span_pool), toff, row_bytes, doff, w);
+      dma_tile_asm(Vl[buf], rsrc4(a.vbar_h + pooled_head, span_pool), toff, row_bytes, doff, w);
     } else {
       const uint32_t toff = (uint32_t)code * 64 * row_bytes;
-      dma_tile_d(Kl[buf], make_rsrc(uniform_ptr(a.kh + kv_head), span_in), toff, row_bytes, doff, w);
-      dma_tile_d(Vl[buf], make_rsrc(uniform_ptr(a.vh + kv_head), span_in), toff, row_bytes, doff, w);
+      dma_tile_asm(Kl[buf], rsrc4(a.kh + kv_head, span_in), toff, row_bytes, doff, w);
+      dma_tile_asm(Vl[buf], rsrc4(a.vh + kv_head, span_in), toff, row_bytes, doff, w);
     }
   };
   // tile order: per chunk, the pooled tile (code -(c + 1)) if the chunk has unselected
@@ -521,6 +591,7 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
     floatx16 s0, s1, d0, d1;
     row_product(K, roff, qreg, s0, s1);                      // S^T = K Q^T (rows = keys)
     row_product(V, roff, greg, d0, d1);                      // dP^T = V dO^T
+    sched_reads_ahead<32, 1, 4>();
     uint64_t colmask;
     float b_full, b_last;
     int last_key;
@@ -549,6 +620,8 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
       pd[2 + (idx >> 3)][idx & 7] = (__bf16)(p1 * (d1[idx] - dd));
     }
     tr_product(dqT, K, toff, pd);                            // dQ^T += K^T dS^T
+    sched_reads_ahead<16, 2, 4>();
+    pin_agpr(dqT);
     buf ^= 1;
     cur = nxt;
   }
@@ -827,11 +900,11 @@ __global__ __launch_bounds__(128, 1) void bwd2_tail_dq_kernel(Bwd2Args a) {
   const DmaOffsetsD doff = dma_offsets_d(row_bytes, w, lane);
   auto issue = [&](int gt, int buf) {
     const uint32_t toff = (uint32_t)gt * 64 * row_bytes;
-    dma_tile_d(Kl[buf], make_rsrc(uniform_ptr(a.gk + rows_bh * kDim), span), toff, row_bytes, doff, w);
-    dma_tile_d(Vl[buf], make_rsrc(uniform_ptr(a.gv + rows_bh * kDim), span), toff, row_bytes, doff, w);
+    dma_tile_asm(Kl[buf], rsrc4(a.gk + rows_bh * kDim, span), toff, row_bytes, doff, w);
+    dma_tile_asm(Vl[buf], rsrc4(a.gv + rows_bh * kDim, span), toff, row_bytes, doff, w);
     if (w == 0)   // 64 floats = 256 bytes; lanes 16..63 repeat lanes 0..15 into the copies
-      dma16_buf(make_rsrc(uniform_ptr(a.glogn + rows_bh), (uint32_t)(2 * a.nbp) * 4),
-                (uint32_t)gt * 256 + (lane & 15) * 16, 0, (unsigned char*)Bl[buf]);
+      dma16_asm(rsrc4(a.glogn + rows_bh, (uint32_t)(2 * a.nbp) * 4), (uint32_t)gt * 256 + (lane & 15) * 16,
+                (unsigned char*)Bl[buf]);
   };
   int roff[8];
   row_offsets(lane, roff);
@@ -926,12 +999,12 @@ __global__ __launch_bounds__(128, 1) void bwd2_group_grad_kernel(Bwd2Args a) {
   const DmaOffsetsD doff = dma_offsets_d(row_bytes, w, lane);
   auto issue = [&](int at, int buf) {
     const uint32_t toff = (uint32_t)at * 64 * row_bytes;
-    dma_tile_d(Ql[buf], make_rsrc(uniform_ptr(a.qab + rows_bh * kDim), span), toff, row_bytes, doff, w);
-    dma_tile_d(Ml[buf], make_rsrc(uniform_ptr(a.dmub + rows_bh * kDim), span), toff, row_bytes, doff, w);
-    dma_tile_d(Nl[buf], make_rsrc(uniform_ptr(a.dnub + rows_bh * kDim), span), toff, row_bytes, doff, w);
+    dma_tile_asm(Ql[buf], rsrc4(a.qab + rows_bh * kDim, span), toff, row_bytes, doff, w);
+    dma_tile_asm(Ml[buf], rsrc4(a.dmub + rows_bh * kDim, span), toff, row_bytes, doff, w);
+    dma_tile_asm(Nl[buf], rsrc4(a.dnub + rows_bh * kDim, span), toff, row_bytes, doff, w);
     if (w == 0)   // 64 (log2 Z, D) pairs = 512 bytes; lanes 32..63 repeat lanes 0..31 into the copy
-      dma16_buf(make_rsrc(uniform_ptr(a.alz + rows_bh * 2), (uint32_t)(2 * a.nbp) * 8),
-                (uint32_t)at * 512 + (lane & 31) * 16, 0, (unsigned char*)St[buf]);
+      dma16_asm(rsrc4(a.alz + rows_bh * 2, (uint32_t)(2 * a.nbp) * 8), (uint32_t)at * 512 + (lane & 31) * 16,
+                (unsigned char*)St[buf]);
   };
   int roff[8];
   row_offsets(lane, roff);
