@@ -214,6 +214,43 @@ __device__ __forceinline__ void pin_agpr(floatx16 (&acc)[4]) {
   for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+a"(acc[mt]));
 }
 
+// row_product written as asm MFMAs, for the loops whose loop-carried accumulators take all
+// the AGPRs they can get: the results c0 / c1 land in VGPRs, where the softmax VALU reads
+// them, and the B fragments breg sit in AGPRs, so that the compiler's own MFMAs (the dK /
+// dV / dQ products) keep their accumulators in AGPRs instead of copying them between
+// register files on every tile.  Hazard padding carried by the asm: s_nop 1 before each
+// pair of MFMAs (an operand written by a VALU op needs two wait states before an MFMA
+// reads it); row_products_end() adds 21 wait states after the chains, before c0 / c1 are
+// read (an MFMA result needs up to 19 before a VALU op reads it).  The A operands are all
+// read from LDS before the first MFMA (the LDS read queue keeps them in order).
+__device__ __forceinline__ void row_product_v(const unsigned char* L, const int (&roff)[8], const bf16x8 (&breg)[8],
+                                              floatx16& c0, floatx16& c1) {
+  bf16x8 a[16];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    a[2 * ks] = *(const bf16x8*)(L + roff[ks]);
+    a[2 * ks + 1] = *(const bf16x8*)(L + 32 * 256 + roff[ks]);
+  }
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %4, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %3, %4, 0"
+      : "=&v"(c0), "=&v"(c1)
+      : "v"(a[0]), "v"(a[1]), "a"(breg[0]));
+#pragma unroll
+  for (int ks = 1; ks < 8; ++ks)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %3, %4, %1"
+        : "+v"(c0), "+v"(c1)
+        : "v"(a[2 * ks]), "v"(a[2 * ks + 1]), "a"(breg[ks]));
+}
+
+__device__ __forceinline__ void row_products_end(floatx16& s0, floatx16& s1, floatx16& d0, floatx16& d1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s0), "+v"(s1), "+v"(d0), "+v"(d1));
+}
+
 __device__ __forceinline__ void load_row_frags(const uint16_t* row, bf16x8 (&r)[8], int kg) {
   const uint4v* src = (const uint4v*)row;
 #pragma unroll
@@ -400,9 +437,9 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
     bool ok = key_ok;
     if constexpr (kPooled) ok = ok && !((uniform64(mw_s[cur - range0]) >> (32 * w + l32)) & 1ull);
     floatx16 s0, s1, d0, d1;
-    row_product(Q, roff, kreg, s0, s1);                      // S = Q K^T (rows = queries)
-    row_product(G, roff, vreg, d0, d1);                      // dP = dO V^T
-    sched_reads_ahead<32, 1, 4>();
+    row_product_v(Q, roff, kreg, s0, s1);                    // S = Q K^T (rows = queries)
+    row_product_v(G, roff, vreg, d0, d1);                    // dP = dO V^T
+    row_products_end(s0, s1, d0, d1);
     bf16x8 pp[4], pd[4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -419,7 +456,10 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
           const int idx = 4 * q4 + e;
           const float sv = half ? s1[idx] : s0[idx];
           const float dv = half ? d1[idx] : d0[idx];
-          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, kScaleLog2B, bias - lse4[e])) : 0.f;
+          // exact keys: a key column past the sequence only feeds its own dK / dV column,
+          // which is not stored, so it needs no mask
+          const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, kScaleLog2B, bias - lse4[e]));
+          const float p = kPooled ? (ok ? e2 : 0.f) : e2;
           const float ds = p * (dv - dd4[e]);
           pp[2 * half + (idx >> 3)][idx & 7] = (__bf16)p;
           pd[2 * half + (idx >> 3)][idx & 7] = (__bf16)ds;
@@ -589,35 +629,46 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
     const unsigned char* K = Kl[buf];
     const unsigned char* V = Vl[buf];
     floatx16 s0, s1, d0, d1;
-    row_product(K, roff, qreg, s0, s1);                      // S^T = K Q^T (rows = keys)
-    row_product(V, roff, greg, d0, d1);                      // dP^T = V dO^T
-    sched_reads_ahead<32, 1, 4>();
-    uint64_t colmask;
-    float b_full, b_last;
-    int last_key;
-    if (cur < 0) {
-      const int cc = -cur - 1;
-      colmask = uniform64(prox_s[cc]);
-      b_full = 6.0f;                                         // log2 64
-      b_last = last_bias;
-      last_key = a.nb - 1 - cc * 64;
-    } else {
-      const int nvalid = min(kBlock, a.N - cur * kBlock);
-      colmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
-      b_full = 0.f;
-      b_last = 0.f;
-      last_key = -1;
-    }
+    row_product_v(K, roff, qreg, s0, s1);                    // S^T = K Q^T (rows = keys)
+    row_product_v(V, roff, greg, d0, d1);                    // dP^T = V dO^T
+    row_products_end(s0, s1, d0, d1);
     bf16x8 pd[4];
+    if (cur >= 0 && cur * kBlock + kBlock <= a.N) {
+      // exact block of 64 keys: every key counts, no bias
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
-      const float x0 = __builtin_fmaf(s0[idx], kScaleLog2B, (key0 == last_key ? b_last : b_full) - lse);
-      const float x1 = __builtin_fmaf(s1[idx], kScaleLog2B, (key0 + 32 == last_key ? b_last : b_full) - lse);
-      const float p0 = ((colmask >> key0) & 1) ? __builtin_amdgcn_exp2f(x0) : 0.f;
-      const float p1 = ((colmask >> (key0 + 32)) & 1) ? __builtin_amdgcn_exp2f(x1) : 0.f;
-      pd[idx >> 3][idx & 7] = (__bf16)(p0 * (d0[idx] - dd));
-      pd[2 + (idx >> 3)][idx & 7] = (__bf16)(p1 * (d1[idx] - dd));
+      for (int idx = 0; idx < 16; ++idx) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], kScaleLog2B, -lse));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], kScaleLog2B, -lse));
+        pd[idx >> 3][idx & 7] = (__bf16)(p0 * (d0[idx] - dd));
+        pd[2 + (idx >> 3)][idx & 7] = (__bf16)(p1 * (d1[idx] - dd));
+      }
+    } else {
+      uint64_t colmask;
+      float b_full, b_last;
+      int last_key;
+      if (cur < 0) {
+        const int cc = -cur - 1;
+        colmask = uniform64(prox_s[cc]);
+        b_full = 6.0f;                                       // log2 64
+        b_last = last_bias;
+        last_key = a.nb - 1 - cc * 64;
+      } else {
+        const int nvalid = min(kBlock, a.N - cur * kBlock);
+        colmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+        b_full = 0.f;
+        b_last = 0.f;
+        last_key = -1;
+      }
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
+        const float x0 = __builtin_fmaf(s0[idx], kScaleLog2B, (key0 == last_key ? b_last : b_full) - lse);
+        const float x1 = __builtin_fmaf(s1[idx], kScaleLog2B, (key0 + 32 == last_key ? b_last : b_full) - lse);
+        const float p0 = ((colmask >> key0) & 1) ? __builtin_amdgcn_exp2f(x0) : 0.f;
+        const float p1 = ((colmask >> (key0 + 32)) & 1) ? __builtin_amdgcn_exp2f(x1) : 0.f;
+        pd[idx >> 3][idx & 7] = (__bf16)(p0 * (d0[idx] - dd));
+        pd[2 + (idx >> 3)][idx & 7] = (__bf16)(p1 * (d1[idx] - dd));
+      }
     }
     tr_product(dqT, K, toff, pd);                            // dQ^T += K^T dS^T
     sched_reads_ahead<16, 2, 4>();
