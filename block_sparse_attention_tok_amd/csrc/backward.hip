@@ -251,6 +251,61 @@ __device__ __forceinline__ void row_products_end(floatx16& s0, floatx16& s1, flo
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s0), "+v"(s1), "+v"(d0), "+v"(d1));
 }
 
+// One k-step of two row-product chains as asm (see row_product_v): c0 += a0 x b0 and
+// c1 += a1 x b1, or c0 = a0 x b0, c1 = a1 x b1 for the first step.
+template <bool kFirst>
+__device__ __forceinline__ void mfma_pair(floatx16& c0, floatx16& c1, const bf16x8& a0, const bf16x8& a1,
+                                          const bf16x8& b0, const bf16x8& b1) {
+  if constexpr (kFirst)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %4, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %3, %5, 0"
+        : "=&v"(c0), "=&v"(c1)
+        : "v"(a0), "v"(a1), "a"(b0), "a"(b1));
+  else
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %3, %5, %1"
+        : "+v"(c0), "+v"(c1)
+        : "v"(a0), "v"(a1), "a"(b0), "a"(b1));
+}
+
+// First k-step with c0 starting from its current value (a bias) and c1 from zero.
+__device__ __forceinline__ void mfma_pair_c0(floatx16& c0, floatx16& c1, const bf16x8& a0, const bf16x8& a1,
+                                             const bf16x8& b0, const bf16x8& b1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %3, %5, 0"
+      : "+v"(c0), "=&v"(c1)
+      : "v"(a0), "v"(a1), "a"(b0), "a"(b1));
+}
+
+// 21 wait states after the last MFMA of a chain before its results are read.
+__device__ __forceinline__ void chain_end(floatx16& c0, floatx16& c1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(c0), "+v"(c1));
+}
+
+// acc += a x b as asm with acc in AGPRs: a loop-carried accumulator that every MFMA takes
+// through this asm stays in the same AGPRs across the branches of a tile loop.  s_nop 1 for a
+// b written by a VALU op just before; the final read of acc needs acc_end() first.
+__device__ __forceinline__ void mfma_acc(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void acc_end(floatx16 (&acc)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+}
+
+// The transposed-read A operand of tr_product for (mt, st).
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* L, const int (&toff)[4][2], int mt, int st) {
+  const uint2v lo = lds_read_tr16(L + toff[mt][0] + st * 16 * 256);
+  const uint2v hi = lds_read_tr16(L + toff[mt][1] + st * 16 * 256);
+  return __builtin_bit_cast(bf16x8, uint4v{lo[0], lo[1], hi[0], hi[1]});
+}
+
 __device__ __forceinline__ void load_row_frags(const uint16_t* row, bf16x8 (&r)[8], int kg) {
   const uint4v* src = (const uint4v*)row;
 #pragma unroll
@@ -436,6 +491,17 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
     const unsigned char* G = Gl[buf];
     bool ok = key_ok;
     if constexpr (kPooled) ok = ok && !((uniform64(mw_s[cur - range0]) >> (32 * w + l32)) & 1ull);
+    // (lse, D) pairs of rows 32 half + 8 q4 + 4 kg + 0..3 (32 bytes each), read before the
+    // products so that they have arrived when the softmax needs them
+    floatx4 ldr[2][4][2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float* st = St[buf] + 2 * (32 * half + 8 * q4 + 4 * kg);
+        ldr[half][q4][0] = *(const floatx4*)st;
+        ldr[half][q4][1] = *(const floatx4*)(st + 4);
+      }
     floatx16 s0, s1, d0, d1;
     row_product_v(Q, roff, kreg, s0, s1);                    // S = Q K^T (rows = queries)
     row_product_v(G, roff, vreg, d0, d1);                    // dP = dO V^T
@@ -445,10 +511,8 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        // rows 32 half + 8 q4 + 4 kg + 0..3: (lse, D) pairs, 32 bytes
-        const float* st = St[buf] + 2 * (32 * half + 8 * q4 + 4 * kg);
-        const floatx4 ld0 = *(const floatx4*)st;
-        const floatx4 ld1 = *(const floatx4*)(st + 4);
+        const floatx4 ld0 = ldr[half][q4][0];
+        const floatx4 ld1 = ldr[half][q4][1];
         const float lse4[4] = {ld0[0], ld0[2], ld1[0], ld1[2]};
         const float dd4[4] = {ld0[1], ld0[3], ld1[1], ld1[3]};
 #pragma unroll
@@ -466,6 +530,7 @@ __global__ __launch_bounds__(128, 1) void bwd_kv_kernel(BwdArgs a) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     tr_product(dvT, G, toff, pp);                            // dV^T += dO^T P
     tr_product(dkT, Q, toff, pd);                            // dK^T += Q^T dS
     sched_reads_ahead<32, 2, 4>();
@@ -618,6 +683,30 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
   floatx16 dqT[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) dqT[mt] = floatx16{};
+  pin_agpr(dqT);
+
+  // Each tile is hand-interleaved so that the softmax of one 32-key half runs under the MFMAs
+  // of the other (one wave per SIMD leaves no other wave to fill the gaps): S^T, dP^T of keys
+  // 0..31; then those of keys 32..63 with the dS of keys 0..31 between their MFMAs; then
+  // dQ^T over keys 0..31 with the dS of keys 32..63; then dQ^T over keys 32..63.  Each
+  // sched_barrier keeps the code between two of them in place.  A pooled tile's weights
+  // log2 n_j and masks, and a partial block's masks, enter as the initial value of the S^T
+  // accumulators (bias / scale, or -inf), so that every tile runs the same code; every MFMA
+  // that touches dQ^T is asm on AGPRs, which keeps the accumulator in place.
+  auto ds_pair = [&](const floatx16& sv, const floatx16& dv, bf16x8 (&pd)[4], int half, int j) {
+    const int idx = 2 * j;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[idx], kScaleLog2B, -lse));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[idx + 1], kScaleLog2B, -lse));
+    pd[2 * half + (idx >> 3)][idx & 7] = (__bf16)(p0 * (dv[idx] - dd));
+    pd[2 * half + (idx >> 3)][(idx & 7) + 1] = (__bf16)(p1 * (dv[idx + 1] - dd));
+  };
+  auto load_tr = [&](const unsigned char* K, bf16x8 (&ta)[8], int half) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) ta[2 * mt + st] = tr_operand(K, toff, mt, 2 * half + st);
+  };
+
   int cur = next_tile();
   int buf = 0;
   if (cur != kEndB) issue(cur, 0);
@@ -628,33 +717,23 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
     if (nxt != kEndB) issue(nxt, buf ^ 1);
     const unsigned char* K = Kl[buf];
     const unsigned char* V = Vl[buf];
+    const bool full = cur >= 0 && cur * kBlock + kBlock <= a.N;
     floatx16 s0, s1, d0, d1;
-    row_product_v(K, roff, qreg, s0, s1);                    // S^T = K Q^T (rows = keys)
-    row_product_v(V, roff, greg, d0, d1);                    // dP^T = V dO^T
-    row_products_end(s0, s1, d0, d1);
-    bf16x8 pd[4];
-    if (cur >= 0 && cur * kBlock + kBlock <= a.N) {
-      // exact block of 64 keys: every key counts, no bias
-#pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], kScaleLog2B, -lse));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[idx], kScaleLog2B, -lse));
-        pd[idx >> 3][idx & 7] = (__bf16)(p0 * (d0[idx] - dd));
-        pd[2 + (idx >> 3)][idx & 7] = (__bf16)(p1 * (d1[idx] - dd));
-      }
-    } else {
+    if (!full) {
+      // initial S^T rows: 0 for a counted key of an exact block, log2 n_j / scale for a
+      // pooled key of an unselected block, -inf for the rest
       uint64_t colmask;
       float b_full, b_last;
       int last_key;
       if (cur < 0) {
         const int cc = -cur - 1;
         colmask = uniform64(prox_s[cc]);
-        b_full = 6.0f;                                       // log2 64
-        b_last = last_bias;
+        b_full = 6.0f / kScaleLog2B;                         // log2 64
+        b_last = last_bias / kScaleLog2B;
         last_key = a.nb - 1 - cc * 64;
       } else {
         const int nvalid = min(kBlock, a.N - cur * kBlock);
-        colmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+        colmask = (1ull << nvalid) - 1;                      // nvalid < 64 here
         b_full = 0.f;
         b_last = 0.f;
         last_key = -1;
@@ -662,20 +741,53 @@ __global__ __launch_bounds__(128, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const int key0 = 8 * (idx >> 2) + 4 * kg + (idx & 3);
-        const float x0 = __builtin_fmaf(s0[idx], kScaleLog2B, (key0 == last_key ? b_last : b_full) - lse);
-        const float x1 = __builtin_fmaf(s1[idx], kScaleLog2B, (key0 + 32 == last_key ? b_last : b_full) - lse);
-        const float p0 = ((colmask >> key0) & 1) ? __builtin_amdgcn_exp2f(x0) : 0.f;
-        const float p1 = ((colmask >> (key0 + 32)) & 1) ? __builtin_amdgcn_exp2f(x1) : 0.f;
-        pd[idx >> 3][idx & 7] = (__bf16)(p0 * (d0[idx] - dd));
-        pd[2 + (idx >> 3)][idx & 7] = (__bf16)(p1 * (d1[idx] - dd));
+        s0[idx] = ((colmask >> key0) & 1) ? (key0 == last_key ? b_last : b_full) : kNegInf;
+        s1[idx] = ((colmask >> (key0 + 32)) & 1) ? (key0 + 32 == last_key ? b_last : b_full) : kNegInf;
       }
     }
-    tr_product(dqT, K, toff, pd);                            // dQ^T += K^T dS^T
-    sched_reads_ahead<16, 2, 4>();
-    pin_agpr(dqT);
+    bf16x8 ka[8], va[8], kb[8], vb[8], pd[4], ta[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      ka[ks] = *(const bf16x8*)(K + roff[ks]);
+      va[ks] = *(const bf16x8*)(V + roff[ks]);
+    }
+    if (full) mfma_pair<true>(s0, d0, ka[0], va[0], qreg[0], greg[0]);
+    else mfma_pair_c0(s0, d0, ka[0], va[0], qreg[0], greg[0]);
+#pragma unroll
+    for (int ks = 1; ks < 8; ++ks) mfma_pair<false>(s0, d0, ka[ks], va[ks], qreg[ks], greg[ks]);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kb[ks] = *(const bf16x8*)(K + 32 * 256 + roff[ks]);
+      vb[ks] = *(const bf16x8*)(V + 32 * 256 + roff[ks]);
+    }
+    if (full) mfma_pair<true>(s1, d1, kb[0], vb[0], qreg[0], greg[0]);
+    else mfma_pair_c0(s1, d1, kb[0], vb[0], qreg[0], greg[0]);
+    chain_end(s0, d0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 1; ks < 8; ++ks) {
+      mfma_pair<false>(s1, d1, kb[ks], vb[ks], qreg[ks], greg[ks]);
+      ds_pair(s0, d0, pd, 0, ks - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_tr(K, ta, 0);
+    ds_pair(s0, d0, pd, 0, 7);
+    chain_end(s1, d1);
+    __builtin_amdgcn_sched_barrier(0);
+    // dQ^T over keys 0..31 (k-steps 0, 1), one dS pair of keys 32..63 per MFMA
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mfma_acc(dqT[i >> 1], ta[i], pd[i & 1]);
+      ds_pair(s1, d1, pd, 1, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_tr(K, ta, 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mfma_acc(dqT[i >> 1], ta[i], pd[2 + (i & 1)]);
     buf ^= 1;
     cur = nxt;
   }
+  acc_end(dqT);
 
   if (qrow < a.N) {
     uint16_t* dst = a.dq + head_off + (size_t)qrow * rs;
