@@ -86,17 +86,6 @@ __device__ __forceinline__ DmaOffsetsD dma_offsets_d(uint32_t row_bytes, int w, 
   return d;
 }
 
-typedef int intx4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource as four SGPRs (the form an asm operand takes): base, stride 0,
-// num_records = bytes, raw-buffer flags (as make_rsrc).
-__device__ __forceinline__ intx4 rsrc4(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)base;
-  return intx4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
-               (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
-               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
-}
-
 // DMA of wave w's half of a 64 x 128 bf16 tile into LDS: eight buffer_load_dwordx4 ... lds
 // (1 KB each, rows and slots as dma_offsets_d), rows past the resource's end reading as
 // zeros.  Issued from asm: the tile loops read one buffer while the DMA fills the other, the
@@ -1284,9 +1273,13 @@ hipError_t launch_backward(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.sol2 = 0;
   a.ghi = nullptr; a.gdk = nullptr; a.gdv = nullptr; a.dlam = nullptr; a.tmu = nullptr; a.aextra = nullptr;
   a.qord = ws.bqord; a.kord = ws.bkord;
-  // pooled keys: enough (chunk, query range) workgroups to fill the chip twice over
+  // pooled keys: (chunk, query range) workgroups for about one wave of workgroups over the
+  // chip (two per CU) and no more: the ranges of a chunk finish together and add into the
+  // same dkbar / dvbar rows, and those atomics cost more than the extra occupancy gains
+  // (operator shape, 256 (b, h, chunk) items, ms per backward: 1 / 2 / 3 / 4 ranges 9.37 /
+  // 8.86 / 9.06 / 8.99 on one box; 4 / 8 / 16 / 32 ranges 9.33 / 9.62 / 10.2 / 11.9 on another)
   const int bhc = s.B * s.H * nchunks;
-  int nrange = (2048 + bhc - 1) / bhc;
+  int nrange = (512 + bhc - 1) / bhc;
   if (nrange < (ws.nb + kMaxRange - 1) / kMaxRange) nrange = (ws.nb + kMaxRange - 1) / kMaxRange;
   if (nrange > ws.nb) nrange = ws.nb;
   if (nrange < 1) nrange = 1;
