@@ -86,6 +86,17 @@ __device__ __forceinline__ DmaOffsetsD dma_offsets_d(uint32_t row_bytes, int w, 
   return d;
 }
 
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource as four SGPRs (the form an asm operand takes): base, stride 0,
+// num_records = bytes, raw-buffer flags (as make_rsrc).
+__device__ __forceinline__ intx4 rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return intx4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
+               (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
+               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
 // DMA of wave w's half of a 64 x 128 bf16 tile into LDS: eight buffer_load_dwordx4 ... lds
 // (1 KB each, rows and slots as dma_offsets_d), rows past the resource's end reading as
 // zeros.  Issued from asm: the tile loops read one buffer while the DMA fills the other, the

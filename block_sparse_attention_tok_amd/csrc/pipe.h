@@ -46,17 +46,6 @@ __device__ __forceinline__ void dma_tile(unsigned char* lds, __amdgpu_buffer_rsr
     dma16_buf(rsrc, (kIsV ? off.v : off.k[n & 3]) + tile_off + (uint32_t)n * 4 * row_bytes, 0, lds + (w * 8 + n) * 1024);
 }
 
-typedef int intx4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource as four SGPRs (the form an asm operand takes): base, stride 0,
-// num_records = bytes, raw-buffer flags (as make_rsrc).
-__device__ __forceinline__ intx4 rsrc4(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)base;
-  return intx4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
-               (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
-               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
-}
-
 __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
