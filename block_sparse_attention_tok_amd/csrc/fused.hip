@@ -197,8 +197,9 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   int voff[4];                                               // V^T operand (transposed read)
   v_operand_offsets(lane, voff);
 
-  // S^T = K Q^T for the 64-row K tile at LDS `kl` (two 32-key m-tiles).
-  auto scores = [&](const unsigned char* kl, floatx16& s0, floatx16& s1) {
+  // S^T = K Q^T for the 64-row K tile at LDS `kl` (two 32-key m-tiles), with the 8 DMA
+  // instructions that `dma` issues (this tile's V) spread over the first eight products.
+  auto scores = [&](const unsigned char* kl, floatx16& s0, floatx16& s1, auto&& dma) {
     s0 = floatx16{};
     s1 = floatx16{};
     bf16x8 ak[16];
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
       ak[2 * ks] = *(const bf16x8*)(kl + koff[ks]);
       ak[2 * ks + 1] = *(const bf16x8*)(kl + 32 * 256 + koff[ks]);
     }
+    dma();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[2 * ks], qreg[ks], s0, 0, 0, 0);
@@ -218,6 +220,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     for (int i = 0; i < 16 - kSAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, kSAhead, 0);
   };
@@ -237,19 +240,17 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   const int last_n = a.N - (a.nb - 1) * kBlock;
   const float last_bias = __log2f((float)last_n);
 
-  // Issue the DMA of one buffer (K or V) of tile `code`; returns the tile's valid rows.
-  auto issue = [&](int code_in, bool is_v) -> int {
+  // Issue the DMA of one buffer (K or V) of tile `code` (pooled tiles from K-bar / V-bar,
+  // exact ones from the head-major copies).  The source is chosen with scalar selects, not
+  // branches, so that the DMA can share a scheduling region with the products around it.
+  auto issue = [&](int code_in, auto is_v_tag) {
+    constexpr bool kV = decltype(is_v_tag)::value;
     const int code = __builtin_amdgcn_readfirstlane(code_in);
-    if (code < 0) {
-      const uint32_t tile_off = (uint32_t)(-code - 1) * 64 * row_bytes;
-      if (is_v) dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.vbar_h + pooled_head), span_pool), tile_off, row_bytes, doff, w);
-      else dma_tile<false>(Kl, make_rsrc(uniform_ptr(a.kbar_h + pooled_head), span_pool), tile_off, row_bytes, doff, w);
-      return kBlock;
-    }
-    const uint32_t tile_off = (uint32_t)code * 64 * row_bytes;
-    if (is_v) dma_tile<true>(Vl, make_rsrc(uniform_ptr(a.vh + kv_head), span_in), tile_off, row_bytes, doff, w);
-    else dma_tile<false>(Kl, make_rsrc(uniform_ptr(a.kh + kv_head), span_in), tile_off, row_bytes, doff, w);
-    return min(kBlock, a.N - code * kBlock);
+    const bool pooled = code < 0;
+    const uint16_t* base = pooled ? (kV ? a.vbar_h : a.kbar_h) + pooled_head : (kV ? a.vh : a.kh) + kv_head;
+    const uint32_t tile_off = (uint32_t)(pooled ? -code - 1 : code) * 64 * row_bytes;
+    dma_tile<kV>(kV ? Vl : Kl, make_rsrc(uniform_ptr(base), pooled ? span_pool : span_in), tile_off, row_bytes,
+                 doff, w);
   };
 
   // The tile stream of this split (pooled tiles first, then the exact blocks).
@@ -260,15 +261,15 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     constexpr bool kSafe = decltype(safe_tag)::value;
     TileIter it{0, 0, 0};
     int cur = next_tile(it, sel_s, nchunks, c_begin);
-    if (cur != kEnd && !first_issued) issue(cur, false);
+    if (cur != kEnd && !first_issued) issue(cur, BoolTag<false>{});
     while (cur != kEnd) {
       const int nxt = next_tile(it, sel_s, nchunks, c_begin);
       wait_vm0();
       lds_barrier();                                         // K(cur) landed; V buffer free
-      const int valid = issue(cur, true);
+      const int valid = cur < 0 ? kBlock : min(kBlock, a.N - cur * kBlock);
 
       floatx16 s0, s1;
-      scores(Kl, s0, s1);
+      scores(Kl, s0, s1, [&]() { issue(cur, BoolTag<true>{}); });
       const int mode = cur < 0 ? kProxy : (valid == kBlock ? kExactFull : kExactPartial);
       bf16x8 pa[4];
       if constexpr (!kSafe) {
@@ -380,10 +381,12 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
 
       wait_vm0();
       lds_barrier();                                         // V(cur) landed; K buffer free
-      if (nxt != kEnd) issue(nxt, false);
-      pv_tile(o, Vl, voff, pa);                              // O^T += V^T P^T
+      // O^T += V^T P^T, with the next tile's K DMA (after the last tile, the current K again,
+      // so that every iteration has the same shape; it lands before the loop exits)
+      pv_tile_dma(o, Vl, voff, pa, [&]() { issue(nxt != kEnd ? nxt : cur, BoolTag<false>{}); });
       cur = nxt;
     }
+    wait_vm0();
   };
 
   run_tiles(BoolTag<false>{}, true);

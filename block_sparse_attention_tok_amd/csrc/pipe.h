@@ -113,7 +113,7 @@ __device__ __forceinline__ void v_operand_offsets(int lane, int (&voff)[4]) {
 }
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+constexpr int kSchedMfma = 0x008, kSchedVmem = 0x010, kSchedDsRead = 0x100;
 // The V^T operand of each PV product is read this many products ahead, so that the LDS
 // latency overlaps the products before it (the scheduler otherwise places each read just
 // before its MFMA under the register limit of two waves per SIMD).
@@ -142,6 +142,37 @@ __device__ __forceinline__ void pv_tile(floatx16 (&o)[4], const unsigned char* V
   for (int i = 0; i < 16 - kPvAhead; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvAhead, 0);
+}
+
+// pv_tile with the 8 DMA instructions that `dma` issues (the next tile's K) spread one per
+// product over the first eight products, so the wave reaches its first MFMA without first
+// waiting for the issue of the whole DMA burst.
+template <class Dma>
+__device__ __forceinline__ void pv_tile_dma(floatx16 (&o)[4], const unsigned char* Vl, const int (&voff)[4],
+                                            const bf16x8 (&pa)[4], Dma&& dma) {
+  uint4v av[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int mt = i >> 2, st = i & 3;
+    const int vo = voff[mt] + st * 16 * 256;
+    const uint2v lo = lds_read_tr16(Vl + vo);
+    const uint2v hi = lds_read_tr16(Vl + vo + 8 * 256);
+    av[i] = uint4v{lo[0], lo[1], hi[0], hi[1]};
+  }
+  dma();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int mt = i >> 2, st = i & 3;
+    o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]), pa[st], o[mt], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 16 - kPvAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    if (i < 8) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvAhead, 0);
 }
