@@ -688,8 +688,10 @@ __device__ __forceinline__ int swz8v(int r) { return (r >> 2) & 3; }
 // 8 consecutive rows on 8 distinct slots with 32 banks.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// The bf16-V instance fits three waves per SIMD (its LDS allows five workgroups per CU);
+// the FP8-PV instance needs more registers and runs two.
 template <bool kPv8>
-__global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
+__global__ __launch_bounds__(128, kPv8 ? 2 : 3) void sol2_fused_kernel(Fused2Args a) {
   __shared__ __attribute__((aligned(1024))) unsigned char K8l[64 * 128];
   __shared__ __attribute__((aligned(1024))) unsigned char Vl[64 * 256];
   __shared__ uint64_t sel_s[kMaxChunks2];
@@ -827,6 +829,9 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
     constexpr bool kPartial = decltype(partial_tag)::value;
     constexpr bool kSafe = kPv8 || decltype(safe_tag)::value;
     floatx16 s0 = {}, s1 = {};
+    // This block's V DMA is issued here, its instructions spread over the score products
+    // (two per product for the bf16 tile, one for the FP8 one) instead of as one burst.
+    issue_v(cur);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint4v a0l = *(const uint4v*)(K8l + k8off[ks][0]), a0h = *(const uint4v*)(K8l + k8off[ks][1]);
@@ -836,6 +841,15 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
       const intx8 a1 = {(int)a1l[0], (int)a1l[1], (int)a1l[2], (int)a1l[3], (int)a1h[0], (int)a1h[1], (int)a1h[2], (int)a1h[3]};
       s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qf[ks], s0, 0, 0, 0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qf[ks], s1, 0, 0, 0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVmem, kPv8 ? 1 : 2, 0);
+      }
     }
     // logits in log2 units are f * s (f = s_q s_k log2(e) / sqrt(d) > 0, so the max of the
     // raw scores gives the max of the logits)
@@ -890,7 +904,9 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
                           0x38383838, 0x38383838, 0x38383838, 0x38383838};
       wait_vm0();
       lds_barrier();                                       // V(cur) landed; K buffer free
-      if (nxt >= 0) issue_k(nxt);
+      // the next block's K DMA (after the last block, this block's again, so that every
+      // block has the same shape), one instruction per PV product
+      issue_k(nxt >= 0 ? nxt : cur);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const uint4v lo = *(const uint4v*)(Vl + mt * 32 * 64 + v8off[0]);
@@ -899,6 +915,13 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
         o[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pc, o[mt], 0, 0, 0, 0, 0, 0);
       }
       ol = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pc, ol, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     } else {
       const float neg_m = -m_use;
       bf16x8 pa[4];
@@ -928,11 +951,11 @@ __global__ __launch_bounds__(128, 2) void sol2_fused_kernel(Fused2Args a) {
       const int nxt = next_sel();
       wait_vm0();
       lds_barrier();                                       // K8(cur) landed; V buffer free
-      issue_v(cur);
       if (cur == last_partial) tile(BoolTag<true>{}, safe_tag, cur, nxt);
       else tile(BoolTag<false>{}, safe_tag, cur, nxt);
       cur = nxt;
     }
+    wait_vm0();                                            // FP8 PV: the last block's repeated K DMA
   };
   if constexpr (kPv8) {
     run_tiles(BoolTag<true>{});
