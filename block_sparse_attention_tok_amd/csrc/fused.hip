@@ -198,7 +198,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
   v_operand_offsets(lane, voff);
 
   // S^T = K Q^T for the 64-row K tile at LDS `kl` (two 32-key m-tiles), with the 8 DMA
-  // instructions that `dma` issues (this tile's V) spread over the first eight products.
+  // instructions that `dma` issues (this tile's V) spread over the first products.
   auto scores = [&](const unsigned char* kl, floatx16& s0, floatx16& s1, auto&& dma) {
     s0 = floatx16{};
     s1 = floatx16{};
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(128, 2) void sol_fused_kernel(FusedArgs a) {
     for (int i = 0; i < 16 - kSAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+      if (i < 8 / kDmaPerProduct) __builtin_amdgcn_sched_group_barrier(kSchedVmem, kDmaPerProduct, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, kSAhead, 0);
   };

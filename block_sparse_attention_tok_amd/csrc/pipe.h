@@ -146,8 +146,11 @@ __device__ __forceinline__ void pv_tile(floatx16 (&o)[4], const unsigned char* V
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvAhead, 0);
 }
 
-// pv_tile with the 8 DMA instructions that `dma` issues (the next tile's K) spread one per
-// product over the first eight products, so the wave reaches its first MFMA without first
+// DMA instructions placed after each product when a tile's DMA is spread over a product chain.
+constexpr int kDmaPerProduct = 1;
+
+// pv_tile with the 8 DMA instructions that `dma` issues (the next tile's K) spread over the
+// first products, kDmaPerProduct after each, so the wave reaches its first MFMA without first
 // waiting for the issue of the whole DMA burst.
 template <class Dma>
 __device__ __forceinline__ void pv_tile_dma(floatx16 (&o)[4], const unsigned char* Vl, const int (&voff)[4],
@@ -172,7 +175,7 @@ __device__ __forceinline__ void pv_tile_dma(floatx16 (&o)[4], const unsigned cha
   for (int i = 0; i < 16 - kPvAhead; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-    if (i < 8) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+    if (i < 8 / kDmaPerProduct) __builtin_amdgcn_sched_group_barrier(kSchedVmem, kDmaPerProduct, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvAhead, 0);
 }
