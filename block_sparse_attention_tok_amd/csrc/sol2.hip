@@ -664,7 +664,7 @@ hipError_t launch_tail2(Shape s, const Workspace& ws, int sink_b0, int sink_b1, 
 //     codes, lambda_t = ln Z_a + delta_t, and Eq. (3) with the exact state.
 // ---------------------------------------------------------------------------
 constexpr int kMaxChunks2 = 128;
-constexpr int kPv8ThreeWaveChunks = 16;   // 65536 tokens
+constexpr int kThreeWaveChunks = 8;   // 32768 tokens
 
 struct Fused2Args {
   const uint16_t* v; uint16_t* out;
@@ -689,11 +689,10 @@ __device__ __forceinline__ int swz8v(int r) { return (r >> 2) & 3; }
 // 8 consecutive rows on 8 distinct slots with 32 banks.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// kWaves: waves per SIMD the register budget is cut for.  The bf16-V instance fits three
-// (its LDS allows five workgroups per CU).  The FP8-PV instance comes in both forms: three
-// waves (a few spilled registers) for sequences of up to kPv8ThreeWaveChunks routing chunks,
-// where the extra occupancy hides more of its memory waits, and two (no spills) beyond, where
-// more workgroups in flight cost more in L2 misses than they hide.
+// kWaves: waves per SIMD the register budget is cut for.  Both instances come in two forms:
+// three waves (bf16 V: 163 VGPRs; FP8 PV: 168 with a few spilled) for sequences of up to
+// kThreeWaveChunks routing chunks, where the extra occupancy hides more of the memory waits,
+// and two beyond, where more workgroups in flight cost more in L2 misses than they hide.
 template <bool kPv8, int kWaves>
 __global__ __launch_bounds__(128, kWaves) void sol2_fused_kernel(Fused2Args a) {
   __shared__ __attribute__((aligned(1024))) unsigned char K8l[64 * 128];
@@ -1046,10 +1045,14 @@ hipError_t launch_fused2(const uint16_t* v, uint16_t* out, Shape s, const Worksp
     if (e0 != hipSuccess) return e0;
   }
   const int total = s.B * s.H * ws.nb;
-  if (!pv8) hipLaunchKernelGGL((sol2_fused_kernel<false, 3>), dim3(total), dim3(128), 0, stream, a);
-  else if (ws.nbp / 64 <= kPv8ThreeWaveChunks)
-    hipLaunchKernelGGL((sol2_fused_kernel<true, 3>), dim3(total), dim3(128), 0, stream, a);
-  else hipLaunchKernelGGL((sol2_fused_kernel<true, 2>), dim3(total), dim3(128), 0, stream, a);
+  const bool three = ws.nbp / 64 <= kThreeWaveChunks;
+  if (pv8) {
+    if (three) hipLaunchKernelGGL((sol2_fused_kernel<true, 3>), dim3(total), dim3(128), 0, stream, a);
+    else hipLaunchKernelGGL((sol2_fused_kernel<true, 2>), dim3(total), dim3(128), 0, stream, a);
+  } else {
+    if (three) hipLaunchKernelGGL((sol2_fused_kernel<false, 3>), dim3(total), dim3(128), 0, stream, a);
+    else hipLaunchKernelGGL((sol2_fused_kernel<false, 2>), dim3(total), dim3(128), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
