@@ -402,6 +402,38 @@ struct Tail2Args {
 constexpr int kTailBufs = 3;               // tiles in flight: the one computed and two more
 constexpr int kTailDmaPerTile = 9;         // buffer loads per wave per tile
 
+// The tail pass's tile DMA is issued from asm.  Its three tile buffers are one LDS array,
+// so for a DMA the compiler issues itself it cannot tell the buffer being filled from the
+// one being read and waits for the newest DMA before the tile's first LDS read, which
+// undoes the two-tile lead.  The compiler does not track these loads: every read of a
+// buffer they fill is ordered by the loop's own vmcnt wait and barrier.  Hazard padding as
+// in the asm: s_nop 4 after the v_readfirstlane writes of the resource and the LDS base,
+// s_nop 0 between the M0 write and the load.
+typedef int tail_intx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ tail_intx4 tail_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return tail_intx4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
+                    (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
+                    (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane to lds + 16 lane.
+__device__ __forceinline__ void tail_dma16(tail_intx4 rsrc, uint32_t voffset, unsigned char* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds"
+               ::"s"(rsrc), "s"(base), "v"(voffset)
+               : "memory", "m0");
+}
+
+// buffer_load_dword ... lds: 4 bytes per lane to lds + 4 lane; lanes outside the buffer store zeros.
+__device__ __forceinline__ void tail_dma4(tail_intx4 rsrc, uint32_t voffset, unsigned char* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %0, 0 offen lds"
+               ::"s"(rsrc), "s"(base), "v"(voffset)
+               : "memory", "m0");
+}
+
 __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   // Per buffer, filled by buffer DMA: the 32 group mean keys and mean values (32 rows x
   // 256 B each, 16-byte slots swizzled by swz_g so that both the row reads of the scores
@@ -513,16 +545,16 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
   const int ntiles = a.nbp / 16;
   auto issue_tile = [&](int t, int buf) {
     const uint32_t gbytes = (uint32_t)a.nbp * 2 * 256;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(a.gk + (size_t)bh * a.nbp * 2 * kDim), gbytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(a.gv + (size_t)bh * a.nbp * 2 * kDim), gbytes);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(uniform_ptr(a.glogn + (size_t)bh * a.nbp * 2), (uint32_t)a.nbp * 2 * 4);
+    const tail_intx4 rk = tail_rsrc(a.gk + (size_t)bh * a.nbp * 2 * kDim, gbytes);
+    const tail_intx4 rv = tail_rsrc(a.gv + (size_t)bh * a.nbp * 2 * kDim, gbytes);
+    const tail_intx4 rl = tail_rsrc(a.glogn + (size_t)bh * a.nbp * 2, (uint32_t)a.nbp * 2 * 4);
     const uint32_t toff_g = (uint32_t)t * 32 * 256;          // 32 group rows per tile
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      dma16_buf(rk, toff_g + gdma[n], 0, Gk_s[buf] + 1024 * (4 * w + n));
-      dma16_buf(rv, toff_g + gdma[n], 0, Gv_s[buf] + 1024 * (4 * w + n));
+      tail_dma16(rk, toff_g + gdma[n], Gk_s[buf] + 1024 * (4 * w + n));
+      tail_dma16(rv, toff_g + gdma[n], Gv_s[buf] + 1024 * (4 * w + n));
     }
-    dma4_buf(rl, lane < 16 ? (uint32_t)t * 32 * 4 + gldma : kPastEnd, 0, (unsigned char*)gl_s[buf][w]);
+    tail_dma4(rl, lane < 16 ? (uint32_t)t * 32 * 4 + gldma : kPastEnd, (unsigned char*)gl_s[buf][w]);
   };
 
   floatx16 num[8];                                        // rows: dims (0..127 mu, 128..255 nu); cols: anchors
@@ -551,12 +583,22 @@ __global__ __launch_bounds__(128) void sol2_tail_kernel(Tail2Args a) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(Gk_s[buf] + goff[ks]), qa[ks], s, 0, 0, 0);
       // routing bits of the anchor's query block for the tile's 16 key blocks
       const uint32_t mine = (uint32_t)(wsel[qr * a.nbw + (t >> 2)] >> (16 * (t & 3))) & 0xffffu;
+      // ln n_g of the lane's 16 groups: rows 8 q4 + 4 kg .. + 3, four 16-byte LDS reads taken
+      // up front (read under the tail condition, each would be a branch with its own wait)
+      float4 lng4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int g0 = 8 * q4 + 4 * kg;
+        lng4[q4] = *(const float4*)&gl_s[buf][g0 >> 4][g0 & 15];
+      }
       float mx = kNegInf;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const int g = 8 * (idx >> 2) + 4 * kg + (idx & 3);  // group row of the tile
         const bool tail = !((mine >> (g >> 1)) & 1) && j0 + (g >> 1) < a.nb;
-        s[idx] = tail ? (s[idx] * kScale2 + gl_s[buf][g >> 4][g & 15]) * kLog2e : kNegInf;
+        const float4 l4 = lng4[idx >> 2];
+        const float lng = (idx & 3) == 0 ? l4.x : (idx & 3) == 1 ? l4.y : (idx & 3) == 2 ? l4.z : l4.w;
+        s[idx] = tail ? (s[idx] * kScale2 + lng) * kLog2e : kNegInf;
         mx = fmaxf(mx, s[idx]);
       }
       mx = max_with_partner(mx);
